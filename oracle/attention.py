@@ -1,0 +1,223 @@
+"""Softmax attention in float64, score matrix materialised (oracle; test infrastructure).
+
+Steps, in the order the definition gives them (page "Agent 帮我写 CUDA：一个
+Softmax Attention 算子的开发全记录", section 二, softmax(QK^T/sqrt(D))V; mask and
+head-sharing readings as stated in this package's docstring):
+
+1. S = (Q_h K_g^T) * scale for each query head h and its KV head g.
+2. If softcap c > 0: S <- c * tanh(S / c).
+3. Disallowed (i, j) become -inf.
+4. m_i = max_j S_ij; P_ij = exp(S_ij - m_i); l_i = sum_j P_ij.
+5. O_i = (sum_j P_ij V_j) / l_i; LSE_i = m_i + ln l_i.
+   A row with no allowed key gives O_i = 0, LSE_i = -inf.
+
+No blocking, fusion or reordering beyond what a library matmul does internally.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+def _allowed(nq: int, nk: int, *, causal: bool, window: int, q_pos: np.ndarray,
+             nq_total: int, nk_valid: Optional[int] = None) -> Optional[np.ndarray]:
+    """Boolean [Nq, Nk] mask, or None when every pair is allowed."""
+    delta = nk - nq_total
+    j = np.arange(nk)[None, :]
+    i = q_pos[:, None]
+    mask = None
+    if causal:
+        mask = j <= i + delta
+    if window > 0:
+        w = j > i + delta - window
+        mask = w if mask is None else (mask & w)
+    if nk_valid is not None and nk_valid < nk:
+        v = np.broadcast_to(j < nk_valid, (nq, nk))
+        mask = v if mask is None else (mask & v)
+    return mask
+
+
+def attention_probs(q: np.ndarray, k: np.ndarray, *, scale: float, causal: bool = False,
+                    window: int = 0, softcap: float = 0.0) -> np.ndarray:
+    """The normalised weights P [Hq, Nq, Nk] (tiny shapes only; for the pins)."""
+    hq, nq, _ = q.shape
+    hkv, nk, _ = k.shape
+    group = hq // hkv
+    mask = _allowed(nq, nk, causal=causal, window=window, q_pos=np.arange(nq), nq_total=nq)
+    out = np.zeros((hq, nq, nk))
+    for h in range(hq):
+        s = (q[h] @ k[h // group].T) * scale
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
+        if mask is not None:
+            s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1)
+        ok = np.isfinite(m)
+        p = np.zeros_like(s)
+        p[ok] = np.exp(s[ok] - m[ok, None])
+        p[ok] /= p[ok].sum(axis=1, keepdims=True)
+        out[h] = p
+    return out
+
+
+def sdpa_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, causal: bool = False,
+              window: int = 0, softcap: float = 0.0, q_pos: Optional[np.ndarray] = None,
+              nq_total: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """One sequence: q [Hq, Nq, D], k/v [Hkv, Nk, D] (float64) -> o [Hq, Nq, D], lse [Hq, Nq].
+
+    ``q_pos`` gives the positions (0-based, within a query sequence of length
+    ``nq_total``) of the supplied query rows, so that a sample of rows can be
+    checked on its own; by default the rows are 0..Nq-1 of an Nq-row sequence.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, nq, d = q.shape
+    hkv, nk, _ = k.shape
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    q_pos = np.arange(nq) if q_pos is None else np.asarray(q_pos, dtype=np.int64)
+    nq_total = nq if nq_total is None else int(nq_total)
+    mask = _allowed(nq, nk, causal=causal, window=window, q_pos=q_pos, nq_total=nq_total)
+    o = np.zeros((hq, nq, v.shape[2]))
+    lse = np.full((hq, nq), -np.inf)
+    if nk == 0:
+        return o, lse
+    for h in range(hq):
+        g = h // group
+        s = (q[h] @ k[g].T) * scale
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
+        if mask is not None:
+            s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1)
+        ok = np.isfinite(m)
+        if not ok.all():
+            s = s[ok]
+            m = m[ok]
+        p = np.exp(s - m[:, None])
+        l = p.sum(axis=1)
+        o[h, ok] = (p @ v[g]) / l[:, None]
+        lse[h, ok] = m + np.log(l)
+    return o, lse
+
+
+def prefill_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, causal: bool = False,
+                  window: int = 0, softcap: float = 0.0, q_rows: Optional[np.ndarray] = None,
+                  heads: Optional[np.ndarray] = None):
+    """Batched dense: q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] -> o [B, Hq', Nq', D], lse [B, Hq', Nq'].
+
+    ``q_rows`` / ``heads`` restrict the output to a sample of query rows / query
+    heads (the mask still uses each row's position in the full sequence).
+    """
+    b_, hq, nq, _ = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    heads = np.arange(hq) if heads is None else np.asarray(heads)
+    rows = np.arange(nq) if q_rows is None else np.asarray(q_rows)
+    o = np.zeros((b_, len(heads), len(rows), v.shape[3]))
+    lse = np.zeros((b_, len(heads), len(rows)))
+    for b in range(b_):
+        for n, h in enumerate(heads):
+            g = h // group
+            ob, lb = sdpa_fp64(q[b][h][rows][None], k[b][g][None], v[b][g][None], scale=scale,
+                               causal=causal, window=window, softcap=softcap, q_pos=rows,
+                               nq_total=nq)
+            o[b, n] = ob[0]
+            lse[b, n] = lb[0]
+    return o, lse
+
+
+def prefill_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: np.ndarray, cu_k: np.ndarray, *,
+                   scale: float, causal: bool = True, window: int = 0, softcap: float = 0.0,
+                   seqs: Optional[np.ndarray] = None, rows_per_seq: Optional[dict] = None,
+                   heads: Optional[np.ndarray] = None):
+    """Ragged batch: q [T, Hq, D], k/v [Tk, Hkv, D] packed token-major by cu_seqlens.
+
+    Sequences are independent; sequence b's queries attend to its own keys with
+    the mask offset Nk_b - Nq_b. Returns (o [T, Hq, D], lse [Hq, T]) with rows
+    outside the requested sample left as NaN.
+    """
+    hq = q.shape[1]
+    heads = np.arange(hq) if heads is None else np.asarray(heads)
+    o = np.full((q.shape[0], hq, v.shape[2]), np.nan)
+    lse = np.full((hq, q.shape[0]), np.nan)
+    seqs = range(len(cu_q) - 1) if seqs is None else seqs
+    for b in seqs:
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        rows = np.arange(q1 - q0)
+        if rows_per_seq is not None and b in rows_per_seq:
+            rows = np.asarray(rows_per_seq[b])
+        qb = np.transpose(q[q0 + rows], (1, 0, 2))[heads]
+        kb = np.transpose(k[k0:k1], (1, 0, 2))
+        vb = np.transpose(v[k0:k1], (1, 0, 2))
+        group = hq // k.shape[1]
+        for n, h in enumerate(heads):
+            g = h // group
+            ob, lb = sdpa_fp64(qb[n:n + 1], kb[g:g + 1], vb[g:g + 1], scale=scale, causal=causal,
+                               window=window, softcap=softcap, q_pos=rows, nq_total=q1 - q0)
+            o[q0 + rows, h] = ob[0]
+            lse[h, q0 + rows] = lb[0]
+    return o, lse
+
+
+def gather_pages(cache: np.ndarray, block_table_row: np.ndarray, seq_len: int,
+                 page_size: int = 16) -> np.ndarray:
+    """Logical [L, Hkv, D] view of one sequence: token t sits in physical page
+    block_table_row[t // page_size], slot t % page_size (integer work)."""
+    t = np.arange(seq_len)
+    pages = np.asarray(block_table_row)[t // page_size]
+    return cache[pages, t % page_size]
+
+
+def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+                 seq_lens: np.ndarray, *, scale: float, k_scale: Optional[np.ndarray] = None,
+                 v_scale: Optional[np.ndarray] = None, seqs: Optional[np.ndarray] = None,
+                 page_size: int = 16):
+    """Single-token decode over a paged cache.
+
+    q [S, Hq, D]; caches [P, page_size, Hkv, D] already widened to float64 (for
+    fp8, the code values); k_scale / v_scale [Hkv] multiply the code values of
+    KV head g. Sequence s's query attends to all of its seq_lens[s] cached keys.
+    Returns (o [S', Hq, D], lse [S', Hq]) for the sequences in ``seqs``.
+    """
+    seqs = np.arange(q.shape[0]) if seqs is None else np.asarray(seqs)
+    hq, d = q.shape[1], q.shape[2]
+    o = np.zeros((len(seqs), hq, v_cache.shape[3]))
+    lse = np.zeros((len(seqs), hq))
+    for n, s in enumerate(seqs):
+        L = int(seq_lens[s])
+        kl = gather_pages(k_cache, block_table[s], L, page_size)  # [L, Hkv, D]
+        vl = gather_pages(v_cache, block_table[s], L, page_size)
+        if k_scale is not None:
+            kl = kl * np.asarray(k_scale, dtype=np.float64)[None, :, None]
+        if v_scale is not None:
+            vl = vl * np.asarray(v_scale, dtype=np.float64)[None, :, None]
+        ob, lb = sdpa_fp64(q[s][:, None, :], np.transpose(kl, (1, 0, 2)),
+                           np.transpose(vl, (1, 0, 2)), scale=scale)
+        o[n] = ob[:, 0]
+        lse[n] = lb[:, 0]
+    return o, lse
+
+
+def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge results computed on disjoint key ranges (axis 0 indexes the ranges).
+
+    With LSE_k the natural-log log-sum-exp of range k and O_k its normalised
+    output: LSE = log sum_k exp(LSE_k) and O = sum_k exp(LSE_k - LSE) O_k.
+    Ranges with LSE_k = -inf (no allowed key) carry zero weight.
+    """
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe[None])
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(tot > 0, m_safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    coef = np.where(tot[None] > 0, w / np.where(tot > 0, tot, 1.0)[None], 0.0)
+    o = (coef[..., None] * o_parts).sum(axis=0)
+    return o, lse

@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than itself: scalar brute
+force, the page's online recurrence, closed forms, invariants, or library
+special cases. Together they are chosen so that a dropped term, a wrong sign,
+a wrong index or a transposed operand anywhere in the oracle fails at least one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+from workloads import make_decode, make_prefill, make_prefill_varlen
+
+RNG = np.random.default_rng(12345)
+
+
+def _rand(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+def _tolist(a):
+    return np.asarray(a).tolist()
+
+
+# ---------------------------------------------------------------- brute force ----
+
+@pytest.mark.parametrize("hq,hkv,nq,nk,d", [(1, 1, 1, 1, 1), (2, 2, 5, 5, 3), (4, 2, 7, 7, 4),
+                                            (4, 1, 3, 9, 2), (2, 1, 9, 4, 4), (4, 4, 8, 8, 1)])
+@pytest.mark.parametrize("causal,window,softcap", [(False, 0, 0.0), (True, 0, 0.0), (True, 3, 0.0),
+                                                   (True, 1, 0.0), (False, 0, 2.5), (True, 2, 1.5),
+                                                   (False, 4, 0.0)])
+def test_brute_force_matches(hq, hkv, nq, nk, d, causal, window, softcap):
+    q, k, v = _rand(hq, nq, d, scale=1.5), _rand(hkv, nk, d, scale=1.5), _rand(hkv, nk, d)
+    scale = oracle.default_scale(d)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=scale, causal=causal, window=window, softcap=softcap)
+    ob, lb = brute.brute_sdpa(_tolist(q), _tolist(k), _tolist(v), scale=scale, causal=causal,
+                              window=window, softcap=softcap)
+    ob, lb = np.array(ob), np.array(lb)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    fin = np.isfinite(lb)
+    assert (np.isfinite(lse) == fin).all()
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
+
+
+def test_online_recurrence_equals_definition():
+    for nk, d in [(1, 3), (6, 4), (17, 8)]:
+        q, k, v = _rand(1, 1, d, scale=2.0), _rand(1, nk, d, scale=2.0), _rand(1, nk, d)
+        scale = 1.0 / math.sqrt(d)
+        o, _ = oracle.sdpa_fp64(q, k, v, scale=scale)
+        row = brute.online_row(q[0, 0].tolist(), k[0].tolist(), v[0].tolist(), scale)
+        np.testing.assert_allclose(o[0, 0], row, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms ----
+
+def test_identical_keys_give_mean_of_values():
+    n, d = 9, 4
+    q = _rand(2, n, d)
+    k = np.repeat(_rand(1, 1, d), n, axis=1).repeat(2, axis=0)
+    v = _rand(2, n, d)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.3)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape), atol=1e-12)
+    oc, _ = oracle.sdpa_fp64(q, k, v, scale=0.3, causal=True)
+    for i in range(n):
+        np.testing.assert_allclose(oc[:, i], v[:, :i + 1].mean(axis=1), atol=1e-12)
+    w = 3
+    ow, _ = oracle.sdpa_fp64(q, k, v, scale=0.3, causal=True, window=w)
+    for i in range(n):
+        np.testing.assert_allclose(ow[:, i], v[:, max(0, i - w + 1):i + 1].mean(axis=1), atol=1e-12)
+
+
+def test_dominant_score_selects_value_row():
+    n, d = 12, 8
+    for target in (0, 5, 11):
+        q = np.zeros((1, 1, d)); q[0, 0, 0] = 10.0
+        k = _rand(1, n, d, scale=0.01); k[0, :, 0] = 0.0; k[0, target, 0] = 4.0
+        v = _rand(1, n, d)
+        o, _ = oracle.sdpa_fp64(q, k, v, scale=1.0)  # gap >= 40 - 0.01*... in natural units
+        np.testing.assert_allclose(o[0, 0], v[0, target], atol=n * math.exp(-39))
+
+
+def test_probabilities_sum_to_one_and_masked_exactly_zero():
+    q, k = _rand(2, 7, 4), _rand(1, 7, 4)
+    for causal, window, cap in [(False, 0, 0.0), (True, 0, 0.0), (True, 3, 5.0)]:
+        p = oracle.attention_probs(q, k, scale=0.5, causal=causal, window=window, softcap=cap)
+        assert (p >= 0).all()
+        np.testing.assert_allclose(p.sum(axis=2), 1.0, atol=1e-12)
+        i, j = np.meshgrid(np.arange(7), np.arange(7), indexing="ij")
+        masked = np.zeros((7, 7), bool)
+        if causal:
+            masked |= j > i
+        if window:
+            masked |= j <= i - window
+        assert (p[:, masked] == 0.0).all()
+        assert (p[:, ~masked] > 0.0).all()
+
+
+def test_equal_scores_lse_is_log_count():
+    n, d = 6, 3
+    q = np.zeros((1, n, d)); k = _rand(1, n, d); v = _rand(1, n, d)
+    _, lse = oracle.sdpa_fp64(q, k, v, scale=1.0)
+    np.testing.assert_allclose(lse[0], math.log(n), atol=1e-12)
+    _, lsec = oracle.sdpa_fp64(q, k, v, scale=1.0, causal=True)
+    np.testing.assert_allclose(lsec[0], np.log(np.arange(1, n + 1)), atol=1e-12)
+
+
+def test_single_key_and_head_dim_one():
+    q, k, v = _rand(3, 1, 5), _rand(3, 1, 5), _rand(3, 1, 5)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.7)
+    np.testing.assert_allclose(o, v, atol=1e-15)
+    np.testing.assert_allclose(lse[:, 0], 0.7 * np.einsum("hd,hd->h", q[:, 0], k[:, 0]), atol=1e-12)
+    # D = 1, two keys: weights form a logistic sigmoid of the score difference
+    a, b0, b1, v0, v1 = 0.9, -1.3, 2.1, 3.0, -5.0
+    o, lse = oracle.sdpa_fp64(np.array([[[a]]]), np.array([[[b0], [b1]]]),
+                              np.array([[[v0], [v1]]]), scale=1.0)
+    w1 = 1.0 / (1.0 + math.exp(a * b0 - a * b1))
+    np.testing.assert_allclose(o[0, 0, 0], (1 - w1) * v0 + w1 * v1, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], math.log(math.exp(a * b0) + math.exp(a * b1)), atol=1e-13)
+
+
+def test_golden_closed_forms():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+    with open(path) as f:
+        cases = json.load(f)["cases"]
+    assert len(cases) >= 3
+    for c in cases:
+        q, k, v = (np.array(c[x], dtype=np.float64) for x in ("q", "k", "v"))
+        o, lse = oracle.sdpa_fp64(q, k, v, scale=c["scale"], causal=c.get("causal", False))
+        np.testing.assert_allclose(o, np.array(c["o"]), rtol=0, atol=1e-12, err_msg=c["name"])
+        np.testing.assert_allclose(lse, np.array(c["lse"]), rtol=0, atol=1e-12, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------- invariants ----
+
+def test_shift_invariance():
+    n, d = 8, 4
+    q, k, v = _rand(1, n, d), _rand(1, n, d), _rand(1, n, d)
+    c = 0.75
+    k[0, :, 2] = c
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.4, causal=True)
+    q2 = q.copy(); q2[0, :, 2] += 1.9
+    o2, lse2 = oracle.sdpa_fp64(q2, k, v, scale=0.4, causal=True)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + 1.9 * c * 0.4, atol=1e-12)
+
+
+def test_key_permutation_invariance():
+    q, k, v = _rand(2, 5, 4), _rand(2, 11, 4), _rand(2, 11, 4)
+    perm = RNG.permutation(11)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.5, softcap=3.0)
+    o2, lse2 = oracle.sdpa_fp64(q, k[:, perm], v[:, perm], scale=0.5, softcap=3.0)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    q, k, v = _rand(8, 6, 4), _rand(2, 6, 4), _rand(2, 6, 4)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.5, causal=True)
+    o2, lse2 = oracle.sdpa_fp64(q, np.repeat(k, 4, axis=0), np.repeat(v, 4, axis=0), scale=0.5,
+                                causal=True)
+    np.testing.assert_allclose(o, o2, atol=1e-15)
+    np.testing.assert_allclose(lse, lse2, atol=1e-15)
+    # consecutive grouping: head h reads KV head h // 4, not h % 2
+    o3, _ = oracle.sdpa_fp64(q, np.tile(k, (4, 1, 1)), np.tile(v, (4, 1, 1)), scale=0.5, causal=True)
+    assert not np.allclose(o, o3)
+
+
+def test_varlen_equals_concatenated_dense():
+    case = make_prefill_varlen(lengths_q=[3, 7, 1, 5], num_q_heads=4, num_kv_heads=2, head_dim=8,
+                               dtype="f32", seed=7, causal=True, window=3)
+    q, k, v = (oracle.tensor_to_f64(t, "f32") for t in (case.q, case.k, case.v))
+    cu = case.cu_seqlens_q
+    o, lse = oracle.prefill_varlen(q, k, v, cu, cu, scale=0.35, causal=True, window=3)
+    for b in range(4):
+        a, z = cu[b], cu[b + 1]
+        ob, lb = oracle.sdpa_fp64(q[a:z].transpose(1, 0, 2), k[a:z].transpose(1, 0, 2),
+                                  v[a:z].transpose(1, 0, 2), scale=0.35, causal=True, window=3)
+        np.testing.assert_allclose(o[a:z], ob.transpose(1, 0, 2), atol=1e-15)
+        np.testing.assert_allclose(lse[:, a:z], lb, atol=1e-15)
+
+
+def test_varlen_different_q_and_k_lengths_bottom_right():
+    case = make_prefill_varlen(lengths_q=[2, 4], lengths_k=[6, 5], num_q_heads=2, num_kv_heads=1,
+                               head_dim=4, dtype="f32", seed=8, causal=True)
+    q, k, v = (oracle.tensor_to_f64(t, "f32") for t in (case.q, case.k, case.v))
+    o, lse = oracle.prefill_varlen(q, k, v, case.cu_seqlens_q, case.cu_seqlens_k, scale=0.5)
+    ob, lb = brute.brute_sdpa(_tolist(q[0:2].transpose(1, 0, 2)), _tolist(k[0:6].transpose(1, 0, 2)),
+                              _tolist(v[0:6].transpose(1, 0, 2)), scale=0.5, causal=True)
+    np.testing.assert_allclose(o[0:2], np.array(ob).transpose(1, 0, 2), atol=1e-12)
+    np.testing.assert_allclose(lse[:, 0:2], np.array(lb), atol=1e-12)
+
+
+def test_sampled_rows_equal_full_rows():
+    case = make_prefill(batch=1, num_q_heads=2, num_kv_heads=1, seqlen_q=20, head_dim=4,
+                        dtype="f32", seed=9, causal=True, window=5)
+    q, k, v = (oracle.tensor_to_f64(t, "f32") for t in (case.q, case.k, case.v))
+    o, lse = oracle.prefill_dense(q, k, v, scale=0.5, causal=True, window=5)
+    rows = np.array([0, 4, 5, 19])
+    o2, lse2 = oracle.prefill_dense(q, k, v, scale=0.5, causal=True, window=5, q_rows=rows,
+                                    heads=np.array([1]))
+    np.testing.assert_allclose(o2[:, 0], o[:, 1, rows], atol=0)
+    np.testing.assert_allclose(lse2[:, 0], lse[:, 1, rows], atol=0)
+
+
+def test_fully_masked_rows():
+    # causal with Nq > Nk: the first Nq - Nk rows see no key
+    q, k, v = _rand(1, 5, 3), _rand(1, 2, 3), _rand(1, 2, 3)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=1.0, causal=True)
+    assert (o[0, :3] == 0).all() and np.isneginf(lse[0, :3]).all()
+    assert np.isfinite(lse[0, 3:]).all()
+    np.testing.assert_allclose(o[0, 3], v[0, 0], atol=1e-15)
+
+
+def test_paged_equals_dense_decode_and_gather_is_exact():
+    case = make_decode(lengths=[5, 33, 16, 1], num_q_heads=4, num_kv_heads=2, head_dim=8,
+                       kv_dtype="bf16", seed=11, keep_logical=True)
+    kc = oracle.tensor_to_f64(case.k_cache, "bf16")
+    vc = oracle.tensor_to_f64(case.v_cache, "bf16")
+    q = oracle.tensor_to_f64(case.q, "bf16")
+    for s in range(case.num_seqs):
+        L = int(case.seq_lens[s])
+        g = oracle.gather_pages(kc, case.block_table[s], L)
+        np.testing.assert_array_equal(g, oracle.tensor_to_f64(case.k_logical[s], "bf16"))
+        assert not np.isnan(g).any()
+    o, lse = oracle.decode_paged(q, kc, vc, case.block_table, case.seq_lens, scale=0.3)
+    for s in range(case.num_seqs):
+        kl = oracle.tensor_to_f64(case.k_logical[s], "bf16").transpose(1, 0, 2)
+        vl = oracle.tensor_to_f64(case.v_logical[s], "bf16").transpose(1, 0, 2)
+        ob, lb = brute.brute_sdpa(_tolist(q[s][:, None, :]), _tolist(kl), _tolist(vl), scale=0.3)
+        np.testing.assert_allclose(o[s], np.array(ob)[:, 0], atol=1e-12)
+        np.testing.assert_allclose(lse[s], np.array(lb)[:, 0], atol=1e-12)
+
+
+def test_fp8_decode_uses_code_times_scale():
+    case = make_decode(lengths=[20, 3], num_q_heads=2, num_kv_heads=2, head_dim=4,
+                       kv_dtype="fp8_e4m3", seed=12, keep_logical=True)
+    q = oracle.tensor_to_f64(case.q, "bf16")
+    kc = oracle.tensor_to_f64(case.k_cache, "fp8_e4m3")
+    vc = oracle.tensor_to_f64(case.v_cache, "fp8_e4m3")
+    o, lse = oracle.decode_paged(q, kc, vc, case.block_table, case.seq_lens, scale=0.5,
+                                 k_scale=case.k_scale, v_scale=case.v_scale)
+    for s in range(2):
+        kl = oracle.tensor_to_f64(case.k_logical[s], "fp8_e4m3") * case.k_scale[None, :, None]
+        vl = oracle.tensor_to_f64(case.v_logical[s], "fp8_e4m3") * case.v_scale[None, :, None]
+        ob, lb = brute.brute_sdpa(_tolist(q[s][:, None, :]), _tolist(kl.transpose(1, 0, 2)),
+                                  _tolist(vl.transpose(1, 0, 2)), scale=0.5)
+        np.testing.assert_allclose(o[s], np.array(ob)[:, 0], atol=1e-12)
+        np.testing.assert_allclose(lse[s], np.array(lb)[:, 0], atol=1e-12)
+
+
+def test_split_combine_associativity():
+    q, k, v = _rand(3, 4, 6), _rand(3, 40, 6), _rand(3, 40, 6)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.6, softcap=4.0)
+    bounds = [0, 7, 8, 23, 40]
+    parts = [oracle.sdpa_fp64(q, k[:, a:b], v[:, a:b], scale=0.6, softcap=4.0)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    oc, lc = oracle.combine_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(oc, o, atol=1e-12)
+    np.testing.assert_allclose(lc, lse, atol=1e-12)
+    # an empty range carries zero weight
+    empty = oracle.sdpa_fp64(q, k[:, :0], v[:, :0], scale=0.6)
+    oc2, lc2 = oracle.combine_partials(np.stack([empty[0]] + [p[0] for p in parts]),
+                                       np.stack([empty[1]] + [p[1] for p in parts]))
+    np.testing.assert_allclose(oc2, o, atol=1e-12)
+    np.testing.assert_allclose(lc2, lse, atol=1e-12)
+
+
+def test_softcap_limits():
+    q, k, v = _rand(2, 6, 4, scale=3), _rand(2, 6, 4, scale=3), _rand(2, 6, 4)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.5, causal=True)
+    o2, lse2 = oracle.sdpa_fp64(q, k, v, scale=0.5, causal=True, softcap=1e9)
+    np.testing.assert_allclose(o2, o, atol=1e-9)
+    np.testing.assert_allclose(lse2, lse, atol=1e-9)
+    cap = 0.25
+    _, lse3 = oracle.sdpa_fp64(q, k, v, scale=0.5, softcap=cap)
+    assert (lse3 < cap + math.log(6)).all() and (lse3 > -cap + math.log(6)).all()
+
+
+def test_window_limits():
+    q, k, v = _rand(2, 9, 4), _rand(2, 9, 4), _rand(2, 9, 4)
+    oc, lc = oracle.sdpa_fp64(q, k, v, scale=0.5, causal=True)
+    ow, lw = oracle.sdpa_fp64(q, k, v, scale=0.5, causal=True, window=9)
+    np.testing.assert_array_equal(ow, oc)
+    o1, _ = oracle.sdpa_fp64(q, k, v, scale=0.5, causal=True, window=1)
+    np.testing.assert_allclose(o1, v, atol=1e-15)
+    # bottom-right alignment: with Nk = Nq + 3, W = 1 selects key i + 3
+    k2, v2 = _rand(2, 12, 4), _rand(2, 12, 4)
+    o2, _ = oracle.sdpa_fp64(q, k2, v2, scale=0.5, causal=True, window=1)
+    np.testing.assert_allclose(o2, v2[:, 3:], atol=1e-15)
+
+
+# ---------------------------------------------------------------- formats ----
+
+def test_e4m3_table_matches_torch_float8_e4m3fn():
+    table = oracle.e4m3_code_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(table) == nan).all()
+    np.testing.assert_array_equal(table[~nan], ref[~nan])
+    assert np.flatnonzero(nan).tolist() == [0x7F, 0xFF]
+    assert np.nanmax(table) == 448.0 and table[1] == 2.0 ** -9
+
+
+def test_widening_matches_torch():
+    x = torch.from_numpy(RNG.standard_normal(4096).astype(np.float32) * 100)
+    for name, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        t = x.to(dt)
+        np.testing.assert_array_equal(oracle.tensor_to_f64(t, name), t.to(torch.float64).numpy())
+    special = torch.tensor([0.0, -0.0, float("inf"), -float("inf"), 1e-40], dtype=torch.float32)
+    t = special.to(torch.bfloat16)
+    np.testing.assert_array_equal(oracle.tensor_to_f64(t, "bf16"), t.to(torch.float64).numpy())
+
+
+def test_default_scale_is_binary32_rounding():
+    for d in (32, 64, 128, 96):
+        s = oracle.default_scale(d)
+        assert s == float(np.float32(1 / math.sqrt(d)))
+        assert abs(s - 1 / math.sqrt(d)) <= 2 ** -24 / math.sqrt(d)
