@@ -1,0 +1,196 @@
+"""MI355X (gfx950) fused attention forward: Python binding of libattn.so.
+
+Every step of the computation runs in the HIP kernels behind the C ABI of
+include/attn.h; this module only checks tensor metadata, allocates outputs
+with torch (device memory and the current stream are torch's), and passes
+pointers. If the library is missing it raises: there is no CPU fallback.
+
+    fwd(q, k, v, ...)            softmax(Q K^T * scale [+ mask]) V (prefill)
+    decode_paged(q, k_cache, ...) one query token per sequence over a paged cache
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import AttnError, AttnInvalidValue, AttnNotSupported
+
+__all__ = ["fwd", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
+           "AttnError", "AttnInvalidValue", "AttnNotSupported"]
+
+_DTYPES = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
+           torch.float8_e4m3fn: _lib.ATTN_FP8_E4M3}
+
+
+def library_path() -> str:
+    _lib.lib()
+    return _lib.LIB_PATH
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False, window: int = 0,
+        softcap: float = 0.0, softmax_scale: float = 0.0, cu_seqlens_q: Optional[torch.Tensor] = None,
+        cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+        max_seqlen_k: Optional[int] = None, return_lse: bool = False, out: Optional[torch.Tensor] = None,
+        lse_out: Optional[torch.Tensor] = None):
+    """Fused attention forward.
+
+    Dense: q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (any strides with D contiguous).
+    Ragged: q [T, Hq, D], k/v [Tk, Hkv, D] with int32 cu_seqlens_q/k [B+1] on the
+    GPU and host-side upper bounds max_seqlen_q/k.
+    Returns o (like q), and lse (float32; dense [B, Hq, Nq], ragged [Hq, T]) if
+    return_lse.
+    """
+    _require_cuda(q, k, v)
+    if q.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise AttnNotSupported(_lib.ATTN_ERROR_NOT_SUPPORTED, f"dtype {q.dtype} not supported")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    ragged = cu_seqlens_q is not None
+    a = _lib.FwdArgs()
+    if ragged:
+        if cu_seqlens_k is None or max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("ragged batches need cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k")
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+            raise ValueError("ragged q/k/v must be [T, H, D]")
+        for cu in (cu_seqlens_q, cu_seqlens_k):
+            if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+                raise ValueError("cu_seqlens must be contiguous int32 GPU vectors")
+        a.batch = cu_seqlens_q.numel() - 1
+        a.num_q_heads, a.num_kv_heads, a.head_dim = q.shape[1], k.shape[1], q.shape[2]
+        a.seqlen_q, a.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+        qs = (0, q.stride(1), q.stride(0))
+        ks = (0, k.stride(1), k.stride(0))
+        vs = (0, v.stride(1), v.stride(0))
+        a.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        a.cu_seqlens_k = cu_seqlens_k.data_ptr()
+        lse_shape = (q.shape[1], q.shape[0])
+    else:
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+            raise ValueError("dense q/k/v must be [B, H, N, D]")
+        a.batch, a.num_q_heads, a.seqlen_q, a.head_dim = q.shape
+        a.num_kv_heads, a.seqlen_k = k.shape[1], k.shape[2]
+        if k.shape[0] != q.shape[0] or v.shape[:3] != k.shape[:3]:
+            raise ValueError("k/v shapes do not match q")
+        qs = (q.stride(0), q.stride(1), q.stride(2))
+        ks = (k.stride(0), k.stride(1), k.stride(2))
+        vs = (v.stride(0), v.stride(1), v.stride(2))
+        lse_shape = (q.shape[0], q.shape[1], q.shape[2])
+    if q.stride(-1) != 1 or k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous")
+    if k.shape[-1] != a.head_dim or v.shape[-1] != a.head_dim:
+        raise ValueError("q, k and v must share head_dim")
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.stride(-1) != 1:
+        raise ValueError("out must match q's shape and dtype")
+    os_ = (0, o.stride(1), o.stride(0)) if ragged else (o.stride(0), o.stride(1), o.stride(2))
+    lse = None
+    if return_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+        if lse.shape != lse_shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse_out must be a contiguous float32 tensor of shape {lse_shape}")
+    a.dtype = _DTYPES[q.dtype]
+    a.causal = 1 if causal else 0
+    a.window = int(window)
+    a.softmax_scale = float(softmax_scale)
+    a.softcap = float(softcap)
+    for name, st in (("q_stride", qs), ("k_stride", ks), ("v_stride", vs), ("o_stride", os_)):
+        arr = getattr(a, name)
+        for i in range(3):
+            arr[i] = int(st[i])
+    status = _lib.lib().attn_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 _stream_handle(q.device))
+    _lib.check(status)
+    return (o, lse) if return_lse else o
+
+
+def _decode_args(*, num_seqs, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, max_seq_len,
+                 q_dtype, kv_dtype, softmax_scale=0.0, num_splits=0, page_size=16) -> _lib.DecodeArgs:
+    a = _lib.DecodeArgs()
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
+    a.page_size = page_size
+    a.max_pages_per_seq = max_pages_per_seq
+    a.max_seq_len = int(max_seq_len)
+    a.q_dtype = _DTYPES[q_dtype] if isinstance(q_dtype, torch.dtype) else int(q_dtype)
+    a.kv_dtype = _DTYPES[kv_dtype] if isinstance(kv_dtype, torch.dtype) else int(kv_dtype)
+    a.softmax_scale = float(softmax_scale)
+    a.num_splits = int(num_splits)
+    return a
+
+
+def decode_plan(**kw):
+    """(split_len, max_splits) the library uses for these decode arguments."""
+    a = _decode_args(**kw)
+    n_len, n_max = ctypes.c_int32(), ctypes.c_int32()
+    _lib.check(_lib.lib().attn_decode_plan(ctypes.byref(a), ctypes.byref(n_len), ctypes.byref(n_max)))
+    return n_len.value, n_max.value
+
+
+def decode_workspace_size(**kw) -> int:
+    a = _decode_args(**kw)
+    return int(_lib.lib().attn_decode_paged_workspace_size(ctypes.byref(a)))
+
+
+def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, max_seq_len: int, *, k_scale: Optional[torch.Tensor] = None,
+                 v_scale: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, num_splits: int = 0,
+                 return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None):
+    """Paged split-KV decode.
+
+    q [S, Hq, D]; k_cache/v_cache [P, 16, Hkv, D] (bf16/f16, or float8_e4m3fn with
+    float32 k_scale/v_scale [Hkv]); block_table int32 [S, max_pages]; seq_lens int32
+    [S]; max_seq_len a host-side bound of seq_lens. Returns o [S, Hq, D] (and lse
+    [S, Hq] float32 if return_lse).
+    """
+    _require_cuda(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale)
+    for t in (q, k_cache, v_cache, block_table, seq_lens):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must be [P, page, Hkv, D] of one dtype")
+    S, hq, d = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_table must be [S, max_pages] and seq_lens [S]")
+    kw = dict(num_seqs=S, num_q_heads=hq, num_kv_heads=k_cache.shape[2], head_dim=d,
+              max_pages_per_seq=block_table.shape[1], max_seq_len=max_seq_len, q_dtype=q.dtype,
+              kv_dtype=k_cache.dtype, softmax_scale=softmax_scale, num_splits=num_splits,
+              page_size=k_cache.shape[1])
+    if k_cache.shape[3] != d:
+        raise ValueError("head_dim mismatch between q and the caches")
+    for sc in (k_scale, v_scale):
+        if sc is not None and (sc.dtype != torch.float32 or not sc.is_contiguous()):
+            raise ValueError("k_scale / v_scale must be contiguous float32")
+    a = _decode_args(**kw)
+    L = _lib.lib()
+    need = int(L.attn_decode_paged_workspace_size(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must match q")
+    lse = torch.empty((S, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    status = L.attn_decode_paged(ctypes.byref(a), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                 _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), _ptr(o), _ptr(lse),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream_handle(q.device))
+    _lib.check(status)
+    return (o, lse) if return_lse else o

@@ -1,0 +1,276 @@
+// C ABI of the attention library: argument validation, routing, split planning and
+// launch. Every check runs on the host before any HIP call; nothing here allocates,
+// copies or synchronises, so a call costs one or two kernel launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/attn.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error.clear();
+  return ATTN_SUCCESS;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) {
+  switch (dtype) {
+    case ATTN_F32: return 4;
+    case ATTN_F16: return 2;
+    case ATTN_BF16: return 2;
+    case ATTN_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+float resolve_scale(float s, int head_dim) {
+  return s > 0.0f ? s : (float)(1.0 / sqrt((double)head_dim));
+}
+
+constexpr double kLog2eD = 1.4426950408889634;
+constexpr int kPageSize = 16;
+constexpr int kMaxSplits = 256;
+
+attn_status_t check_strides(const char* name, const int64_t st[3], int esize, int64_t min_token) {
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(ATTN_ERROR_INVALID_VALUE, "%s_stride[%d] is negative", name, i);
+    if ((st[i] * esize) % 16 != 0)
+      return fail(ATTN_ERROR_NOT_SUPPORTED, "%s_stride[%d]=%lld elements is not a multiple of 16 bytes",
+                  name, i, (long long)st[i]);
+  }
+  if (st[2] < min_token)
+    return fail(ATTN_ERROR_INVALID_VALUE, "%s token stride %lld is smaller than head_dim", name,
+                (long long)st[2]);
+  return ATTN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_abi_version(void) { return 100; }
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_SUCCESS: return "ATTN_SUCCESS";
+    case ATTN_ERROR_INVALID_VALUE: return "ATTN_ERROR_INVALID_VALUE";
+    case ATTN_ERROR_NOT_SUPPORTED: return "ATTN_ERROR_NOT_SUPPORTED";
+    case ATTN_ERROR_WORKSPACE_TOO_SMALL: return "ATTN_ERROR_WORKSPACE_TOO_SMALL";
+    case ATTN_ERROR_LAUNCH_FAILED: return "ATTN_ERROR_LAUNCH_FAILED";
+    default: return "ATTN_STATUS_UNKNOWN";
+  }
+}
+
+const char* attn_last_error_message(void) { return g_last_error.c_str(); }
+
+attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, const void* v, void* o,
+                       float* lse, void* stream) {
+  if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
+  if (a->batch < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(ATTN_ERROR_INVALID_VALUE, "batch, num_q_heads and num_kv_heads must be >= 1");
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(ATTN_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->seqlen_q < 0 || a->seqlen_k < 0)
+    return fail(ATTN_ERROR_INVALID_VALUE, "sequence lengths must be >= 0");
+  if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of 32, 64, 128", a->head_dim);
+  if (a->dtype != ATTN_F32 && a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "dtype %d is not F32, F16 or BF16", a->dtype);
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  if (a->window > 0 && !a->causal)
+    return fail(ATTN_ERROR_INVALID_VALUE, "a sliding window requires causal = 1");
+  if (!(a->softcap == a->softcap) || !(a->softmax_scale == a->softmax_scale) || isinf(a->softcap) ||
+      isinf(a->softmax_scale))
+    return fail(ATTN_ERROR_INVALID_VALUE, "softcap and softmax_scale must be finite");
+  if ((a->cu_seqlens_q == nullptr) != (a->cu_seqlens_k == nullptr))
+    return fail(ATTN_ERROR_INVALID_VALUE, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+  if (a->num_q_heads > 65535 || a->batch > 65535)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_q_heads and batch are limited to 65535");
+  if (a->seqlen_q == 0) return ok();  // nothing to compute
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return fail(ATTN_ERROR_INVALID_VALUE, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "q, k, v and o must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(ATTN_ERROR_INVALID_VALUE, "lse must be 4-byte aligned");
+  const int es = elem_size(a->dtype);
+  attn_status_t st;
+  if ((st = check_strides("q", a->q_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
+  if ((st = check_strides("k", a->k_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
+  if ((st = check_strides("v", a->v_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
+  if ((st = check_strides("o", a->o_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
+
+  attn::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = a->q_stride[i];
+    p.ks[i] = a->k_stride[i];
+    p.vs[i] = a->v_stride[i];
+    p.os[i] = a->o_stride[i];
+  }
+  p.batch = a->batch;
+  p.hq = a->num_q_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.nq = a->seqlen_q;
+  p.nk = a->seqlen_k;
+  p.causal = a->causal;
+  p.window = a->window > 0 ? a->window : 0;
+  const double scale = resolve_scale(a->softmax_scale, a->head_dim);
+  p.scale_log2 = (float)(scale * kLog2eD);
+  if (a->softcap > 0.0f) {
+    p.cap_in = (float)(scale / (double)a->softcap);
+    p.cap_out = (float)((double)a->softcap * kLog2eD);
+  } else {
+    p.cap_in = 0.0f;
+    p.cap_out = 0.0f;
+  }
+  const int bm = attn::fwd_block_rows(a->dtype, a->head_dim);
+  p.q_tiles = (a->seqlen_q + bm - 1) / bm;
+
+  hipError_t e = attn::launch_fwd(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static attn_status_t check_decode_args(const attn_decode_args_t* a) {
+  if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
+  if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(ATTN_ERROR_INVALID_VALUE, "num_seqs, num_q_heads and num_kv_heads must be >= 1");
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(ATTN_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->num_q_heads / a->num_kv_heads > 16)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "more than 16 query heads per KV head");
+  if (a->head_dim != 128) return fail(ATTN_ERROR_NOT_SUPPORTED, "decode supports head_dim 128 only");
+  if (a->page_size != kPageSize) return fail(ATTN_ERROR_NOT_SUPPORTED, "page_size must be 16");
+  if (a->max_pages_per_seq < 1) return fail(ATTN_ERROR_INVALID_VALUE, "max_pages_per_seq must be >= 1");
+  if (a->max_seq_len < 1) return fail(ATTN_ERROR_INVALID_VALUE, "max_seq_len must be >= 1");
+  if ((int64_t)a->max_seq_len > (int64_t)a->max_pages_per_seq * kPageSize)
+    return fail(ATTN_ERROR_INVALID_VALUE, "max_seq_len %d exceeds max_pages_per_seq * page_size",
+                a->max_seq_len);
+  if (a->q_dtype != ATTN_BF16 && a->q_dtype != ATTN_F16)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "q_dtype must be BF16 or F16");
+  const bool kv_ok = a->kv_dtype == ATTN_FP8_E4M3 || a->kv_dtype == a->q_dtype;
+  if (!kv_ok) return fail(ATTN_ERROR_NOT_SUPPORTED, "kv_dtype must equal q_dtype or be FP8_E4M3");
+  if (a->num_splits < 0) return fail(ATTN_ERROR_INVALID_VALUE, "num_splits must be >= 0");
+  if (a->num_seqs > 65535 || a->num_kv_heads > 65535)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_seqs and num_kv_heads are limited to 65535");
+  if (!(a->softmax_scale == a->softmax_scale) || isinf(a->softmax_scale))
+    return fail(ATTN_ERROR_INVALID_VALUE, "softmax_scale must be finite");
+  return ATTN_SUCCESS;
+}
+
+attn_status_t attn_decode_plan(const attn_decode_args_t* a, int32_t* split_len, int32_t* max_splits) {
+  attn_status_t st = check_decode_args(a);
+  if (st != ATTN_SUCCESS) return st;
+  int64_t len;
+  if (a->num_splits > 0) {
+    const int64_t per = ((int64_t)a->max_seq_len + a->num_splits - 1) / a->num_splits;
+    len = (per + kPageSize - 1) / kPageSize * kPageSize;
+  } else {
+    // Aim at about 8192 single-wave work items when lengths average half the maximum,
+    // keeping each split between 256 and 4096 tokens, rounded to a power of two.
+    const int64_t want = (int64_t)a->num_seqs * a->num_kv_heads * a->max_seq_len / (2 * 8192);
+    len = 256;
+    while (len < want && len < 4096) len *= 2;
+  }
+  const int64_t cap = ((int64_t)a->max_seq_len + kMaxSplits - 1) / kMaxSplits;
+  if (len < cap) len = (cap + kPageSize - 1) / kPageSize * kPageSize;
+  const int64_t n = ((int64_t)a->max_seq_len + len - 1) / len;
+  if (split_len) *split_len = (int32_t)len;
+  if (max_splits) *max_splits = (int32_t)n;
+  return ok();
+}
+
+size_t attn_decode_paged_workspace_size(const attn_decode_args_t* a) {
+  int32_t len = 0, n = 0;
+  if (attn_decode_plan(a, &len, &n) != ATTN_SUCCESS) return 0;
+  const size_t slots = (size_t)a->num_seqs * a->num_q_heads * n;
+  const size_t o_bytes = slots * a->head_dim * sizeof(float);
+  const size_t l_bytes = (slots * sizeof(float) + 15) / 16 * 16;
+  return o_bytes + l_bytes;
+}
+
+attn_status_t attn_decode_paged(const attn_decode_args_t* a, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t split_len = 0, max_splits = 0;
+  attn_status_t st = attn_decode_plan(a, &split_len, &max_splits);
+  if (st != ATTN_SUCCESS) return st;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || o == nullptr || workspace == nullptr)
+    return fail(ATTN_ERROR_INVALID_VALUE,
+                "q, k_cache, v_cache, block_table, seq_lens, o and workspace must be non-NULL");
+  const bool fp8 = a->kv_dtype == ATTN_FP8_E4M3;
+  if (fp8 && (k_scale == nullptr || v_scale == nullptr))
+    return fail(ATTN_ERROR_INVALID_VALUE, "fp8 KV needs k_scale and v_scale");
+  if (!fp8 && (k_scale != nullptr || v_scale != nullptr))
+    return fail(ATTN_ERROR_INVALID_VALUE, "k_scale / v_scale are only accepted with fp8 KV");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "q, caches, o and workspace must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(ATTN_ERROR_INVALID_VALUE, "block_table, seq_lens and lse must be 4-byte aligned");
+  const size_t need = attn_decode_paged_workspace_size(a);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+
+  attn::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  const size_t slots = (size_t)a->num_seqs * a->num_q_heads * max_splits;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + slots * a->head_dim;
+  p.o = o;
+  p.lse = lse;
+  p.num_seqs = a->num_seqs;
+  p.hq = a->num_q_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.max_pages = a->max_pages_per_seq;
+  p.split_len = split_len;
+  p.max_splits = max_splits;
+  p.scale_log2 = (float)(resolve_scale(a->softmax_scale, a->head_dim) * kLog2eD);
+  hipError_t e = attn::launch_decode(p, a->q_dtype, a->kv_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Host-side kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// One prefill launch. Pointers are device pointers; strides are in elements for
+// the [batch, head, token] dimensions (head_dim contiguous).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_q;  // null for dense batches
+  const int32_t* cu_k;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int32_t batch, hq, hkv, group;
+  int32_t nq, nk;       // dense lengths, or the upper bounds for ragged batches
+  int32_t causal, window;
+  float scale_log2;     // softmax scale * log2(e)
+  float cap_in;         // softcap: multiplier of the raw dot product inside tanh (scale / c)
+  float cap_out;        // softcap: c * log2(e); 0 = off
+  int32_t q_tiles;      // query tiles per sequence
+};
+
+// One paged-decode launch (split kernel + combine kernel).
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* part_o;        // [S, Hq, max_splits, D]
+  float* part_lse;      // [S, Hq, max_splits], log2 domain
+  void* o;
+  float* lse;
+  int32_t num_seqs, hq, hkv, group, max_pages;
+  int32_t split_len, max_splits;
+  float scale_log2;
+};
+
+// Block-rows of the prefill kernels for a given dtype/head_dim (the host needs it
+// to size the grid).
+int fwd_block_rows(int dtype, int head_dim);
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t stream);
+
+}  // namespace attn

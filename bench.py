@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one pass of the whole hot path over resident synthetic inputs:
+  * prefill: attn_fwd on B=1, H=32, N=8192, D=128, bf16, dense non-causal
+    (Q, K, V = 0.5 * N(0,1));
+  * decode:  attn_decode_paged on 64 sequences, L ~ U[512, 32768], Hq=32, Hkv=8,
+    D=128, bf16 KV in 16-token pages at permuted block-table indices.
+Each launch is bracketed by HIP events on the stream it runs on, so the average
+kernel durations come from inside the timed region.
+
+Prints ONE JSON line: value = prefill TFLOP/s (4*B*H*N^2*D per call / average
+prefill duration); "roofline" prices the prefill kernel against the bf16 dense
+matrix-core peak; "decode" reports the algorithmic bytes / duration of the paged
+decode against the HBM peak; "cpu_baseline" times the CPU oracle (float64, one
+or more whole heads of the same prefill workload) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBPS = 8000.0
+
+
+def prefill_flops(b, h, nq, nk, d):
+    return 4.0 * b * h * nq * nk * d
+
+
+def decode_bytes(case, kv_elt: int, q_elt: int = 2) -> float:
+    L = case.seq_lens.astype(np.int64)
+    hkv, d, hq, S = case.num_kv_heads, case.head_dim, case.num_q_heads, case.num_seqs
+    kv = float((L * hkv * d * 2 * kv_elt).sum())
+    q_o = 2.0 * S * hq * d * q_elt
+    tables = 4.0 * float(((L + 15) // 16).sum()) + 4.0 * S
+    scales = 8.0 * hkv if kv_elt == 1 else 0.0
+    return kv + q_o + tables + scales
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true", help="time the prefill only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with measured HBM bytes per prefill launch (from counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import attention_forward_03_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- inputs ----
+    pc = workloads.config_headline()
+    q, k, v = pc.q.to(dev), pc.k.to(dev), pc.v.to(dev)
+    o = torch.empty_like(q)
+    flops = prefill_flops(pc.batch, pc.num_q_heads, pc.seqlen_q, pc.seqlen_k, pc.head_dim)
+
+    dec = None
+    if not args.no_decode:
+        dc = workloads.config_decode("bf16")
+        dt = {"q": dc.q.to(dev), "k": dc.k_cache.to(dev), "v": dc.v_cache.to(dev),
+              "bt": torch.from_numpy(dc.block_table).to(dev), "sl": torch.from_numpy(dc.seq_lens).to(dev)}
+        ws_bytes = attn.decode_workspace_size(num_seqs=dc.num_seqs, num_q_heads=dc.num_q_heads,
+                                              num_kv_heads=dc.num_kv_heads, head_dim=dc.head_dim,
+                                              max_pages_per_seq=dc.max_pages, max_seq_len=dc.max_seq_len,
+                                              q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16)
+        dt["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        dt["o"] = torch.empty_like(dt["q"])
+        dec = (dc, dt, decode_bytes(dc, kv_elt=2))
+        del dc.k_cache, dc.v_cache  # host copies no longer needed
+
+    def run_prefill():
+        attn.fwd(q, k, v, out=o)
+
+    def run_decode():
+        dc, dt, _ = dec
+        attn.decode_paged(dt["q"], dt["k"], dt["v"], dt["bt"], dt["sl"], dc.max_seq_len, out=dt["o"],
+                          workspace=dt["ws"])
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------- timing ----
+    for _ in range(args.warmup):
+        run_prefill()
+        if dec:
+            run_decode()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run_prefill()
+        ev[i][1].record(stream)
+        if dec:
+            ev[i][2].record(stream)
+            run_decode()
+            ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    pre_avg = float(np.mean(pre_ms))
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    out = {
+        "metric": "attn fwd TFLOP/s & % bf16 MFMA peak (N=8192,D=128); decode GB/s % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, no weights)",
+        "config": {"workload": "dense non-causal attention fwd B=1 H=32 N=8192 D=128 bf16"
+                               + ("" if args.no_decode else
+                                  " + paged split-KV decode 64 seqs L~U[512,32768] Hq=32 Hkv=8 D=128 bf16 KV"),
+                   "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
+        "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4), "max": round(max(pre_ms), 4)},
+    }
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("prefill_hbm_bytes_per_launch")
+    out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                       "kernel": "fwd_mfma16_kernel<128,...,bf16>",
+                       "flops_per_launch": flops}
+    if dec:
+        dc, _, nbytes = dec
+        dms = [e[2].elapsed_time(e[3]) for e in ev]
+        davg = float(np.mean(dms))
+        gbps = nbytes / (davg * 1e-3) / 1e9
+        out["decode"] = {"gbps": round(gbps, 1), "ms": round(davg, 4), "bytes_per_launch": nbytes,
+                         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                                      "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                                      "kernels": "decode_split_kernel + decode_combine_kernel"}}
+
+    # ------------------------------------------------------------ CPU baseline ----
+    if not args.no_cpu:
+        import oracle
+        qh = oracle.tensor_to_f64(pc.q[0, :1], "bf16")
+        cores = len(os.sched_getaffinity(0))
+        scale = oracle.default_scale(pc.head_dim)
+        done, spent = 0, 0.0
+        while done < pc.num_q_heads and spent < args.cpu_seconds:
+            h = done
+            qh = oracle.tensor_to_f64(pc.q[0, h:h + 1], "bf16")
+            kh = oracle.tensor_to_f64(pc.k[0, h:h + 1], "bf16")
+            vh = oracle.tensor_to_f64(pc.v[0, h:h + 1], "bf16")
+            t = time.perf_counter()
+            oracle.sdpa_fp64(qh, kh, vh, scale=scale)
+            spent += time.perf_counter() - t
+            done += 1
+        cpu_tflops = prefill_flops(1, done, pc.seqlen_q, pc.seqlen_k, pc.head_dim) / spent / 1e12
+        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"{done} of 32 heads of the same N=8192 D=128 prefill, float64 numpy, "
+                                         f"{spent:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,169 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * Two operations:
+ *
+ *   attn_fwd           O = softmax(Q K^T * scale [+ mask]) V for a batch of
+ *                      sequences (prefill), computed tile by tile with an online
+ *                      softmax so the score matrix never reaches memory.
+ *   attn_decode_paged  the same for one query token per sequence over a paged
+ *                      KV cache, split along the keys across workgroups and
+ *                      merged with an LSE-weighted combine.
+ *
+ * The operation is the softmax attention of the page "Agent 帮我写 CUDA：一个
+ * Softmax Attention 算子的开发全记录" (section 二, reference baseline and the
+ * note on D; section 四, the online-softmax recurrence that lets the score
+ * matrix stay on chip). The variants (causal, sliding window, tanh softcap,
+ * grouped-query heads, ragged batches, paged KV, split-KV decode, fp8 KV) are
+ * the scenario axes of "Ask, Don't Equip: Question-Driven Coding Agents for
+ * Deep Kernel Optimization", section 研究动机. Where those pages only name a
+ * variant, this header states the definition used.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP device memory) owned by the
+ *    caller. The library never allocates, frees or synchronises; it only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns. Buffers must stay valid until the stream has passed the work.
+ *  - Every argument check is done on the host, synchronously, before any HIP
+ *    call; a failed check enqueues nothing and returns a non-zero status, with
+ *    a detail string available from attn_last_error_message() (thread-local).
+ *  - Contents of device-resident index arrays (cu_seqlens, block_table,
+ *    seq_lens) are trusted: the library does not read them on the host.
+ *  - Every base pointer and every stride in bytes of the token / head / batch
+ *    dimensions must be a multiple of 16 bytes (128-bit loads); the head_dim
+ *    dimension must be contiguous (stride 1).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_SUCCESS = 0,
+  ATTN_ERROR_INVALID_VALUE = 1,      /* null pointer, bad size, bad stride, bad combination */
+  ATTN_ERROR_NOT_SUPPORTED = 2,      /* head_dim / dtype / alignment outside what is built */
+  ATTN_ERROR_WORKSPACE_TOO_SMALL = 3,
+  ATTN_ERROR_LAUNCH_FAILED = 4       /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+typedef enum {
+  ATTN_F32 = 0,
+  ATTN_F16 = 1,
+  ATTN_BF16 = 2,
+  ATTN_FP8_E4M3 = 3 /* OCP E4M3 ("e4m3fn"): bias 7, max 448, S.1111.111 = NaN, no inf */
+} attn_dtype_t;
+
+/* ---------------------------------------------------------------- prefill ---- */
+
+typedef struct {
+  int32_t batch;         /* B >= 1 (ragged: number of sequences) */
+  int32_t num_q_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
+  int32_t seqlen_q;      /* dense: Nq; ragged: an upper bound of every sequence's query length */
+  int32_t seqlen_k;      /* dense: Nk; ragged: an upper bound of every sequence's key length */
+  int32_t head_dim;      /* D in {32, 64, 128} */
+  int32_t dtype;         /* attn_dtype_t: ATTN_F32, ATTN_F16 or ATTN_BF16, shared by Q, K, V, O */
+  int32_t causal;        /* 0/1. Bottom-right aligned: key j allowed for query i iff j <= i + (Nk - Nq) */
+  int32_t window;        /* <= 0: off. W > 0 (requires causal): also j > i + (Nk - Nq) - W,
+                            i.e. the W most recent keys, the diagonal included */
+  float softmax_scale;   /* <= 0: 1/sqrt(D) computed in double and rounded once to float */
+  float softcap;         /* <= 0: off. c > 0: s <- c * tanh(s / c) on the scaled score, before the mask */
+  /* Strides in ELEMENTS for the [batch, head, token] dimensions of q, k, v, o
+   * (head_dim is contiguous). Ragged batches ignore the batch stride: token t
+   * of the packed [T, H, D] tensor is at t * stride[2] + h * stride[1]. */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  /* Ragged batches: both NULL (dense) or both set. Device int32 arrays of
+   * length batch + 1, non-decreasing, starting at 0: sequence b owns query
+   * tokens [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key tokens
+   * [cu_seqlens_k[b], cu_seqlens_k[b+1]); sequences are independent and the
+   * mask offset is Nk_b - Nq_b. Every length must be <= seqlen_q / seqlen_k. */
+  const int32_t *cu_seqlens_q;
+  const int32_t *cu_seqlens_k;
+} attn_fwd_args_t;
+
+/*
+ * attn_fwd - fused attention forward (prefill).
+ *
+ *   q   [B, Hq, Nq, D] (or ragged [T, Hq, D]) in args->dtype
+ *   k,v [B, Hkv, Nk, D] (or ragged [Tk, Hkv, D]) in args->dtype
+ *   o   same layout as q (strides o_stride), written in args->dtype
+ *   lse nullable, float32, natural-log log-sum-exp of each row's final scores:
+ *       dense [B, Hq, Nq] contiguous; ragged [Hq, T] contiguous.
+ *       A row with no allowed key gets O = 0 and LSE = -inf.
+ *
+ * Accumulation is float32 throughout; Q K^T and P V run on the matrix cores
+ * (bf16/f16 inputs: P is rounded to the input type before P V).
+ */
+attn_status_t attn_fwd(const attn_fwd_args_t *args, const void *q, const void *k, const void *v,
+                       void *o, float *lse, void *stream);
+
+/* ----------------------------------------------------------------- decode ---- */
+
+typedef struct {
+  int32_t num_seqs;          /* S >= 1 */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16 */
+  int32_t head_dim;          /* D == 128 */
+  int32_t page_size;         /* tokens per page; must be 16 */
+  int32_t max_pages_per_seq; /* row length of block_table */
+  int32_t max_seq_len;       /* host-known upper bound of seq_lens[]; sizes the split grid */
+  int32_t q_dtype;           /* ATTN_BF16 or ATTN_F16; O has q_dtype */
+  int32_t kv_dtype;          /* ATTN_BF16, ATTN_F16 or ATTN_FP8_E4M3 */
+  float softmax_scale;       /* <= 0: 1/sqrt(D) as for attn_fwd */
+  int32_t num_splits;        /* 0: the library plans the split length; > 0: split the
+                                longest sequence into exactly this many pieces */
+} attn_decode_args_t;
+
+/* Split plan: every sequence s is cut into ceil(seq_lens[s] / split_len)
+ * pieces of split_len tokens (a multiple of page_size); max_splits =
+ * ceil(max_seq_len / split_len). Deterministic function of the args only. */
+attn_status_t attn_decode_plan(const attn_decode_args_t *args, int32_t *split_len,
+                               int32_t *max_splits);
+
+/* Bytes of workspace attn_decode_paged needs for these args (0 on bad args). */
+size_t attn_decode_paged_workspace_size(const attn_decode_args_t *args);
+
+/*
+ * attn_decode_paged - one query token per sequence over a paged KV cache.
+ *
+ *   q            [S, Hq, D] contiguous, q_dtype
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, Hkv, D] contiguous, kv_dtype. Token t of
+ *                sequence s lives in page block_table[s * max_pages_per_seq + t / page_size],
+ *                slot t % page_size.
+ *   k_scale,
+ *   v_scale      device float32 [Hkv], required iff kv_dtype == ATTN_FP8_E4M3, else NULL:
+ *                the value of a stored code c of KV head g is c * scale[g]
+ *   block_table  device int32 [S, max_pages_per_seq]
+ *   seq_lens     device int32 [S], 1 <= seq_lens[s] <= max_seq_len; the query attends
+ *                to all seq_lens[s] cached keys (the current token included)
+ *   o            [S, Hq, D] contiguous, q_dtype
+ *   lse          nullable float32 [S, Hq], natural log
+ *   workspace    device buffer of at least attn_decode_paged_workspace_size(args) bytes,
+ *                16-byte aligned; holds the per-split partial results
+ */
+attn_status_t attn_decode_paged(const attn_decode_args_t *args, const void *q, const void *k_cache,
+                                const void *v_cache, const float *k_scale, const float *v_scale,
+                                const int32_t *block_table, const int32_t *seq_lens, void *o,
+                                float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ misc ---- */
+
+const char *attn_status_string(attn_status_t status);
+const char *attn_last_error_message(void);
+/* Library ABI version (major * 100 + minor). */
+int32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

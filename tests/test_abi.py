@@ -1,0 +1,161 @@
+"""The C-ABI library loads, exports every symbol include/attn.h declares, and rejects bad
+arguments on the host before any HIP call (CPU only: no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_03_amd import _lib
+import attention_forward_03_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert L.attn_abi_version() == 100
+
+
+def test_library_links_no_vendor_kernel_libraries():
+    # the hot path is hand-written: no BLAS / CK / MIOpen / Triton dependency
+    import subprocess
+    out = subprocess.run(["ldd", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    for bad in ("rocblas", "hipblaslt", "MIOpen", "composable", "triton", "torch"):
+        assert bad.lower() not in out.lower(), bad
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.attn_status_string(0) == b"ATTN_SUCCESS"
+    assert L.attn_status_string(3) == b"ATTN_ERROR_WORKSPACE_TOO_SMALL"
+    assert L.attn_status_string(99) == b"ATTN_STATUS_UNKNOWN"
+
+
+def _fwd_args(**kw):
+    a = _lib.FwdArgs()
+    base = dict(batch=2, num_q_heads=4, num_kv_heads=4, seqlen_q=64, seqlen_k=64, head_dim=32,
+                dtype=_lib.ATTN_F32, causal=0, window=0, softmax_scale=0.0, softcap=0.0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        arr = getattr(a, name)
+        st = kw.get(name, (4 * 64 * 32, 64 * 32, 32))
+        for i in range(3):
+            arr[i] = st[i]
+    return a
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(num_q_heads=6, num_kv_heads=4), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(head_dim=96), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(dtype=_lib.ATTN_FP8_E4M3), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(window=16), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(causal=2), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(seqlen_q=-1), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(softcap=float("nan")), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(q_stride=(8192, 2048, 30)), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(k_stride=(8192, 2048, 16)), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(v_stride=(8192, -2048, 32)), _lib.ATTN_ERROR_INVALID_VALUE),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    L = _lib.lib()
+    a = _fwd_args(**kw)
+    st = L.attn_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == status, L.attn_last_error_message()
+    assert len(L.attn_last_error_message()) > 0
+
+
+def test_fwd_rejects_null_and_misaligned_pointers():
+    L = _lib.lib()
+    a = _fwd_args()
+    assert L.attn_fwd(None, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    assert L.attn_fwd(ctypes.byref(a), None, FAKE, FAKE, FAKE, None, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    assert L.attn_fwd(ctypes.byref(a), FAKE + 8, FAKE, FAKE, FAKE, None, None) == _lib.ATTN_ERROR_NOT_SUPPORTED
+    assert L.attn_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE + 2, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    a.cu_seqlens_q = FAKE
+    assert L.attn_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, None, None) == _lib.ATTN_ERROR_INVALID_VALUE
+
+
+def test_fwd_empty_query_is_a_no_op():
+    L = _lib.lib()
+    a = _fwd_args(seqlen_q=0)
+    assert L.attn_fwd(ctypes.byref(a), None, None, None, None, None, None) == _lib.ATTN_SUCCESS
+
+
+def _dec_kw(**kw):
+    base = dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, max_pages_per_seq=2048,
+                max_seq_len=32768, q_dtype=_lib.ATTN_BF16, kv_dtype=_lib.ATTN_BF16)
+    base.update(kw)
+    return base
+
+
+def test_decode_plan_is_a_deterministic_integer_function():
+    assert attn.decode_plan(**_dec_kw()) == (1024, 32)
+    assert attn.decode_plan(**_dec_kw(num_splits=7)) == (4688, 7)
+    assert attn.decode_plan(**_dec_kw(num_splits=1)) == (32768, 1)
+    # a short single sequence still gets 256-token splits
+    assert attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=1000, max_pages_per_seq=63)) == (256, 4)
+    # never more than 256 splits
+    ln, n = attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=2_000_000, max_pages_per_seq=125000,
+                                       num_splits=1000))
+    assert n <= 256 and ln % 16 == 0 and ln * n >= 2_000_000
+    for forced in (1, 2, 3, 7, 31, 64, 100):
+        ln, n = attn.decode_plan(**_dec_kw(num_splits=forced))
+        assert ln % 16 == 0 and n == -(-32768 // ln) and n <= forced
+
+
+def test_decode_workspace_size():
+    ln, n = attn.decode_plan(**_dec_kw())
+    assert attn.decode_workspace_size(**_dec_kw()) == 64 * 32 * n * 128 * 4 + 64 * 32 * n * 4
+    assert attn.decode_workspace_size(**_dec_kw(head_dim=64)) == 0  # invalid args -> 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(num_q_heads=32, num_kv_heads=1), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(head_dim=64), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(max_seq_len=40000), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(q_dtype=_lib.ATTN_F32), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(kv_dtype=_lib.ATTN_F16), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(num_splits=-1), _lib.ATTN_ERROR_INVALID_VALUE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    L = _lib.lib()
+    a = attn._decode_args(**_dec_kw(**kw))
+    st = L.attn_decode_paged(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None,
+                             FAKE, 1 << 30, None)
+    assert st == status, L.attn_last_error_message()
+
+
+def test_decode_checks_scales_and_workspace():
+    L = _lib.lib()
+    a = attn._decode_args(**_dec_kw(kv_dtype=_lib.ATTN_FP8_E4M3))
+    st = L.attn_decode_paged(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None,
+                             FAKE, 1 << 30, None)
+    assert st == _lib.ATTN_ERROR_INVALID_VALUE
+    a = attn._decode_args(**_dec_kw())
+    st = L.attn_decode_paged(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                             FAKE, 1 << 30, None)
+    assert st == _lib.ATTN_ERROR_INVALID_VALUE
+    st = L.attn_decode_paged(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None,
+                             FAKE, 1024, None)
+    assert st == _lib.ATTN_ERROR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,186 @@
+"""GPU parity of attn_fwd (the HIP prefill kernels, through the C ABI) against the oracle."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_support import (check_prefill_full, check_prefill_sampled, compare, note, oracle_prefill,
+                         run_prefill, widen)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_small_fp32_config():
+    """B=2 H=4 N=64 D=32 fp32, all outputs, max-abs 1e-4."""
+    stats = check_prefill_full(workloads.config_small_f32(), "fp32 B2 H4 N64 D32")
+    note(f"  stats {stats}")
+    assert stats["max_abs"] < 1e-5  # the page's fp32 kernel reports 8.3e-7 at this shape
+
+
+SHAPES = [  # (batch, Hq, Hkv, Nq, Nk)
+    (1, 2, 2, 1, 1),
+    (2, 2, 1, 300, 300),
+    (1, 4, 2, 129, 257),
+    (1, 2, 2, 200, 77),
+    (2, 1, 1, 64, 1000),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_dense_noncausal_shapes(dtype, d, shape):
+    b, hq, hkv, nq, nk = shape
+    case = workloads.make_prefill(batch=b, num_q_heads=hq, num_kv_heads=hkv, seqlen_q=nq, seqlen_k=nk,
+                                  head_dim=d, dtype=dtype, seed=zlib.crc32(repr((dtype, d, shape)).encode()))
+    check_prefill_full(case, f"dense {dtype} D{d} {shape}")
+
+
+MASKS = [  # (causal, window, softcap)
+    (True, 0, 0.0),
+    (True, 1, 0.0),
+    (True, 37, 0.0),
+    (True, 200, 0.0),
+    (False, 0, 5.0),
+    (True, 64, 30.0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("shape", [(2, 4, 1, 333, 333), (1, 4, 4, 150, 400), (1, 2, 2, 5, 3)])
+def test_masked_variants(dtype, mask, shape):
+    causal, window, softcap = mask
+    b, hq, hkv, nq, nk = shape
+    case = workloads.make_prefill(batch=b, num_q_heads=hq, num_kv_heads=hkv, seqlen_q=nq, seqlen_k=nk,
+                                  head_dim=128 if dtype == "bf16" else 64, dtype=dtype,
+                                  seed=zlib.crc32(repr((dtype, mask, shape)).encode()), causal=causal, window=window,
+                                  softcap=softcap)
+    check_prefill_full(case, f"masked {dtype} {mask} {shape}")
+
+
+def test_fully_masked_rows_give_zero_and_neg_inf():
+    # causal with Nq > Nk: the first Nq - Nk rows have no allowed key
+    for dtype in ("f32", "bf16"):
+        case = workloads.make_prefill(batch=1, num_q_heads=2, num_kv_heads=2, seqlen_q=100, seqlen_k=40,
+                                      head_dim=64, dtype=dtype, seed=5, causal=True)
+        check_prefill_full(case, f"fully-masked rows {dtype}")
+        o, lse = run_prefill(case)
+        assert (widen(o, dtype)[:, :, :60] == 0).all()
+        assert np.isneginf(lse.numpy()[:, :, :60]).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_ragged_batches(dtype):
+    lengths = [1, 129, 300, 64, 0, 77]
+    for causal, window, cap in [(True, 0, 0.0), (True, 50, 0.0), (True, 0, 10.0)]:
+        case = workloads.make_prefill_varlen(lengths_q=lengths, num_q_heads=4, num_kv_heads=2,
+                                             head_dim=128, dtype=dtype, seed=17, causal=causal,
+                                             window=window, softcap=cap)
+        check_prefill_full(case, f"ragged {dtype} causal={causal} W={window} cap={cap}")
+
+
+def test_ragged_query_shorter_than_keys():
+    # chunk-style ragged batch: each sequence's queries are the last Nq_b of its Nk_b keys
+    case = workloads.make_prefill_varlen(lengths_q=[16, 100, 1, 130], lengths_k=[300, 100, 65, 500],
+                                         num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                                         seed=23, causal=True)
+    check_prefill_full(case, "ragged Nq<Nk")
+
+
+def test_strided_output_and_guard_bands():
+    case = workloads.make_prefill(batch=2, num_q_heads=3, num_kv_heads=3, seqlen_q=150, seqlen_k=150,
+                                  head_dim=64, dtype="bf16", seed=29, causal=True)
+    big = torch.full((2, 3, 160, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = big[:, :, 5:155]
+    o, _ = run_prefill(case, out=out)
+    big_c = big.cpu()
+    assert torch.isnan(big_c[:, :, :5].float()).all() and torch.isnan(big_c[:, :, 155:].float()).all()
+    ro, _ = oracle_prefill(case)
+    compare(widen(big_c[:, :, 5:155], "bf16"), ro, "bf16", "strided O")
+
+
+def test_deterministic():
+    case = workloads.make_prefill(batch=1, num_q_heads=4, num_kv_heads=2, seqlen_q=500, head_dim=128,
+                                  dtype="bf16", seed=31, causal=True)
+    o1, l1 = run_prefill(case)
+    o2, l2 = run_prefill(case)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------- dominance probes ----
+
+def _probe(targets, *, dtype="bf16", n=300, d=128, hq=4, hkv=2, causal=False, window=0):
+    case = workloads.dominance_prefill(batch=2, num_q_heads=hq, num_kv_heads=hkv, seqlen=n, head_dim=d,
+                                       dtype=dtype, targets=targets, seed=41, causal=causal, window=window)
+    o, _ = run_prefill(case)
+    return case, o
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_dominance_probe_selects_target_row_bit_exactly(dtype):
+    n = 300
+    rng = np.random.default_rng(3)
+    cases = {
+        "random": (rng.integers(0, n, size=n), dict()),
+        "first": (np.zeros(n, dtype=np.int64), dict()),
+        "last": (np.full(n, n - 1), dict()),
+        "diagonal": (np.arange(n), dict(causal=True)),
+        "window-oldest": (np.maximum(np.arange(n) - 36, 0), dict(causal=True, window=37)),
+    }
+    for name, (targets, kw) in cases.items():
+        note(f"[probe] {dtype} {name}")
+        case, o = _probe(targets, dtype=dtype, n=n, **kw)
+        group = case.num_q_heads // case.num_kv_heads
+        for b in range(case.batch):
+            for h in range(case.num_q_heads):
+                want = case.v[b, h // group][torch.from_numpy(np.asarray(targets)).long()]
+                got = o[b, h]
+                same = (got.view(torch.int16) == want.view(torch.int16)) if dtype != "f32" else (got == want)
+                assert bool(same.all()), f"{name}: b={b} h={h} first bad row {int((~same.all(1)).nonzero()[0])}"
+
+
+def test_dominance_probe_masked_targets_follow_oracle():
+    n = 300
+    # target just past the causal diagonal / just before the window: must NOT be selected
+    for name, targets, kw in [("past-diagonal", np.minimum(np.arange(n) + 1, n - 1), dict(causal=True)),
+                              ("before-window", np.maximum(np.arange(n) - 37, 0), dict(causal=True, window=37))]:
+        case, o = _probe(targets, n=n, **kw)
+        ro, _ = oracle_prefill(case)
+        compare(widen(o, "bf16"), ro, "bf16", f"masked probe {name}")
+
+
+# ------------------------------------------------------------- full-size workloads ----
+
+def _rows(n, count=48, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.integers(0, n, size=count)]))
+
+
+def test_headline_shape_sampled():
+    """B=1 H=32 N=8192 D=128 bf16 (inputs 0.5*N(0,1)): every head, sampled rows."""
+    case = workloads.config_headline()
+    stats = check_prefill_sampled(case, "headline N8192 D128", rows=_rows(8192, 32), heads=np.arange(32))
+    note(f"  stats {stats}")
+
+
+@pytest.mark.parametrize("variant", workloads.GQA_VARIANTS)
+def test_gqa_configs_sampled(variant):
+    """B=4 Hq=32 Hkv=8 N=4096 D=128 bf16: causal / window 1024 / softcap 30 / ragged."""
+    case = workloads.config_gqa(variant)
+    stats = check_prefill_sampled(case, f"gqa {variant}", rows=_rows(4096, 24, seed=1),
+                                  heads=np.array([0, 3, 4, 17, 31]))
+    note(f"  stats {stats}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", workloads.SWEEP_N)
+@pytest.mark.parametrize("d", workloads.SWEEP_D)
+def test_sweep_points_sampled(dtype, n, d):
+    """B=2 H=8 dense non-causal sweep, every head, sampled rows."""
+    case = workloads.config_sweep(n, d, dtype)
+    check_prefill_sampled(case, f"sweep {dtype} N{n} D{d}", rows=_rows(n, 16, seed=n + d),
+                          heads=np.arange(8))

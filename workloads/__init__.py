@@ -21,6 +21,8 @@ Equip: Question-Driven Coding Agents for Deep Kernel Optimization", section
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional, Sequence
 
 import numpy as np
@@ -201,31 +203,38 @@ def make_decode(*, lengths: Sequence[int], num_q_heads: int, num_kv_heads: int, 
     k_cache[poison] = nan
     v_cache[poison] = nan
     block_table = np.full((S, max_p), poison, dtype=np.int32)
-    k_log, v_log = ([], []) if keep_logical else (None, None)
-    off = 0
-    for s in range(S):
+    offsets = np.concatenate([[0], np.cumsum(pages_per_seq)]).astype(np.int64)
+
+    def one_sequence(s):
         L = int(lengths[s])
         n_p = int(pages_per_seq[s])
         crng = np.random.Generator(np.random.PCG64(children[s]))
-        kx = _normal(crng, (L, Hkv, D))
-        vx = _normal(crng, (L, Hkv, D))
-        if kv_dtype == "fp8_e4m3":
-            kx = kx / k_scale[None, :, None]
-            vx = vx / v_scale[None, :, None]
-        kt = torch.full((n_p * PAGE_SIZE, Hkv, D), float("nan"), dtype=torch.float32)
-        vt = torch.full((n_p * PAGE_SIZE, Hkv, D), float("nan"), dtype=torch.float32)
-        kt[:L] = torch.from_numpy(kx)
-        vt[:L] = torch.from_numpy(vx)
-        kt = kt.to(tdt).view(n_p, PAGE_SIZE, Hkv, D)
-        vt = vt.to(tdt).view(n_p, PAGE_SIZE, Hkv, D)
-        ids = perm[off:off + n_p]
-        k_cache[torch.from_numpy(ids).long()] = kt
-        v_cache[torch.from_numpy(ids).long()] = vt
-        block_table[s, :n_p] = ids
-        if keep_logical:
-            k_log.append(kt.reshape(n_p * PAGE_SIZE, Hkv, D)[:L].clone())
-            v_log.append(vt.reshape(n_p * PAGE_SIZE, Hkv, D)[:L].clone())
-        off += n_p
+        out = []
+        for scale in ((k_scale, v_scale) if kv_dtype == "fp8_e4m3" else (None, None)):
+            x = _normal(crng, (L, Hkv, D))
+            if scale is not None:
+                x /= scale[None, :, None]
+            t = torch.empty((n_p * PAGE_SIZE, Hkv, D), dtype=tdt)
+            t[:L] = torch.from_numpy(x).to(tdt)
+            if n_p * PAGE_SIZE > L:
+                t[L:] = nan[0, 0, 0]
+            out.append(t.view(n_p, PAGE_SIZE, Hkv, D))
+        return out
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    k_log, v_log = ([], []) if keep_logical else (None, None)
+    with ThreadPoolExecutor(workers) as ex:
+        for s, (kt, vt) in enumerate(ex.map(one_sequence, range(S))):
+            n_p = int(pages_per_seq[s])
+            ids = perm[offsets[s]:offsets[s] + n_p]
+            idx = torch.from_numpy(ids).long()
+            k_cache[idx] = kt
+            v_cache[idx] = vt
+            block_table[s, :n_p] = ids
+            if keep_logical:
+                L = int(lengths[s])
+                k_log.append(kt.reshape(n_p * PAGE_SIZE, Hkv, D)[:L].clone())
+                v_log.append(vt.reshape(n_p * PAGE_SIZE, Hkv, D)[:L].clone())
     return DecodeCase(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
                       seq_lens=lengths.astype(np.int32), num_q_heads=Hq, num_kv_heads=Hkv,
                       head_dim=D, q_dtype=q_dtype, kv_dtype=kv_dtype, k_scale=k_scale,
@@ -292,3 +301,70 @@ def config_decode(kv_dtype: str, seed: int = 5, num_seqs: int = 64,
     sub = int(np.random.Generator(np.random.PCG64(child)).integers(0, 2**63))
     return make_decode(lengths=lengths, num_q_heads=32, num_kv_heads=8, head_dim=128,
                        q_dtype="bf16", kv_dtype=kv_dtype, seed=sub + (1 if kv_dtype != "bf16" else 0))
+
+
+# ----------------------------------------------------------------------------------------
+# Dominance probes: inputs where, for every query, one chosen key scores far above all
+# others, so the exact result is that key's value row. Keys carry their position as a
+# one-hot digit code; a query carries the code of its target scaled by ``amp``. A key
+# matching all digits scores 3*amp, one differing in a digit at most 2*amp.
+# ----------------------------------------------------------------------------------------
+
+def position_code(pos: np.ndarray, dim: int, base: int = 16, digits: int = 3) -> np.ndarray:
+    """[len(pos), dim] float32 one-hot digit code of each position (base ** digits > pos)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    if base * digits > dim:
+        raise ValueError("code does not fit the head dimension")
+    out = np.zeros((pos.shape[0], dim), dtype=np.float32)
+    rest = pos.copy()
+    for dgt in range(digits):
+        out[np.arange(pos.shape[0]), dgt * base + rest % base] = 1.0
+        rest //= base
+    if (rest != 0).any():
+        raise ValueError("position exceeds the code range")
+    return out
+
+
+def dominance_prefill(*, batch: int, num_q_heads: int, num_kv_heads: int, seqlen: int, head_dim: int,
+                      dtype: str, targets: np.ndarray, seed: int, amp: float = 512.0,
+                      causal: bool = False, window: int = 0, base: int = 16) -> PrefillCase:
+    """Dense self-attention probe: query i of every (b, h) targets key targets[i]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    digits = int(np.ceil(np.log(max(seqlen, 2)) / np.log(base)))
+    kcode = position_code(np.arange(seqlen), head_dim, base, digits)
+    qcode = position_code(np.asarray(targets), head_dim, base, digits) * np.float32(amp)
+    q = np.broadcast_to(qcode, (batch, num_q_heads, seqlen, head_dim)).copy()
+    k = np.broadcast_to(kcode, (batch, num_kv_heads, seqlen, head_dim)).copy()
+    v = _normal(rng, (batch, num_kv_heads, seqlen, head_dim))
+    return PrefillCase(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), batch=batch,
+                       num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, seqlen_q=seqlen,
+                       seqlen_k=seqlen, head_dim=head_dim, dtype=dtype, causal=causal, window=window,
+                       seed=seed)
+
+
+def dominance_decode(case: DecodeCase, targets: np.ndarray, amp: float = 1024.0,
+                     base: int = 32) -> DecodeCase:
+    """Overwrite a decode case's K cache and Q with the digit code: query (s, h) targets
+    logical token targets[s, h] of sequence s. For fp8 caches the stored K code is
+    1/k_scale times the digit (choose power-of-two scales so it is exact)."""
+    S, Hq, D = case.q.shape
+    Hkv = case.num_kv_heads
+    digits = 3
+    kc = torch.zeros_like(case.k_cache, dtype=torch.float32)
+    kc[case.poison_page] = float("nan")
+    for s in range(S):
+        L = int(case.seq_lens[s])
+        t = np.arange(L)
+        code = torch.from_numpy(position_code(t, D, base, digits))  # [L, D]
+        phys = torch.from_numpy(case.block_table[s, t // PAGE_SIZE].astype(np.int64))
+        slot = torch.from_numpy((t % PAGE_SIZE).astype(np.int64))
+        vals = code[:, None, :].expand(L, Hkv, D)
+        if case.k_scale is not None:
+            vals = vals / torch.from_numpy(case.k_scale)[None, :, None]
+        kc[phys, slot] = vals
+        tail = torch.arange(L, ((L + PAGE_SIZE - 1) // PAGE_SIZE) * PAGE_SIZE)
+        if tail.numel():
+            kc[torch.from_numpy(case.block_table[s, tail.numpy() // PAGE_SIZE].astype(np.int64)),
+               tail % PAGE_SIZE] = float("nan")
+    qv = position_code(np.asarray(targets).reshape(-1), D, base, digits).reshape(S, Hq, D) * np.float32(amp)
+    return dataclasses.replace(case, k_cache=kc.to(case.k_cache.dtype), q=_cast(qv, case.q_dtype))
