@@ -59,6 +59,9 @@ attn_status_t check_strides(const char* name, const int64_t st[3], int esize, in
       return fail(ATTN_ERROR_NOT_SUPPORTED, "%s_stride[%d]=%lld elements is not a multiple of 16 bytes",
                   name, i, (long long)st[i]);
   }
+  if (st[2] >= (int64_t)1 << 24)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "%s token stride %lld is 2^24 elements or more", name,
+                (long long)st[2]);
   if (st[2] < min_token)
     return fail(ATTN_ERROR_INVALID_VALUE, "%s token stride %lld is smaller than head_dim", name,
                 (long long)st[2]);

@@ -18,21 +18,13 @@
 // In the 32x32 matrix-core result layout a lane holds one column (= one query) and
 // 16 rows (= keys, or head-dim entries), so the row max / row sum are lane-local
 // except for one exchange with lane l^32, and alpha is a per-lane scalar.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace attn {
 namespace {
-
-// Position of key k inside its 16-key group in the transposed V tile. The middle two
-// groups of four are swapped: the eight keys a lane contributes to one P.V k-step
-// (keys {0-3, 8-11} for lanes 0-31, {4-7, 12-15} for lanes 32-63, as produced by the
-// S^T result layout) then sit contiguously and load with one 128-bit LDS read.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int grp = (k >> 2) & 3;
-  const int sw = ((grp & 1) << 1) | (grp >> 1);
-  return (k & ~15) | (sw << 2) | (k & 3);
-}
 
 struct RowRange {
   int wend, wbeg;  // keys any row of the wave may see: [wbeg, wend)
@@ -98,28 +90,88 @@ __device__ __forceinline__ float softmax_tile(const FwdParams& p, f32x16_t (&s)[
 }
 
 // ----------------------------------------------------------------- 16-bit inputs ----
+// K and V tiles live in LDS row-major with 16-byte chunks XOR-swizzled per row (no
+// padding), filled straight from global memory by direct-to-LDS loads: each load
+// instruction moves 64 lanes x 16 bytes into one contiguous 1 KiB LDS block, and the
+// swizzle is applied by choosing which global chunk each lane fetches.
+//   K reads (A operand of S^T): 16 consecutive rows at one chunk -> 16 bank groups.
+//   V reads use the transposing LDS read: in each 16-lane group, lane i receives element
+//   i%4 of the 4-element rows addressed by lanes i/4 + 4e (e = 0..3). Lanes address 4
+//   consecutive head-dim entries of 4 keys, so every lane ends up with 4 keys of one
+//   head-dim entry: exactly the A operand of O^T = V^T . P^T, with no transposition on
+//   the way into LDS. A 4-key x 4-chunk read hits 16 distinct bank groups.
 
+template <int D>
+struct Swizzle {
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __device__ static __forceinline__ int k(int row, int c) { return c ^ ((row / (16 / CPR)) % CPR); }
+  __device__ static __forceinline__ int v(int row, int c) {
+    if constexpr (D == 128) return c ^ ((row & 3) << 2);
+    else if constexpr (D == 64) return c ^ (((row >> 1) & 1) << 2);
+    else return c;
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// 16 bytes per lane from global memory straight into LDS; the LDS address of lane l is
+// the (wave-uniform) base + 16 * l.
+__device__ __forceinline__ void load_lds16(const void* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Lanes l and l^32 hold the two halves of a query row's keys; they exchange through the
+// LDS crossbar (ds_bpermute).
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, xor_shuffle(x, 32)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + xor_shuffle(x, 32); }
+
+// Probabilities are formed against a reference max that may trail the true running max
+// by up to this many binary orders of magnitude; the accumulator is rescaled only when
+// a tile would exceed it (p <= 2^8, far from overflow). The result is unchanged: the
+// same reference max is used for P, for l and for the final LSE.
+constexpr float kRescaleSlack = 8.0f;
+
+// Sum of two packed 16-bit probabilities into an fp32 accumulator (one dot2 op): the
+// row sum is taken over the same rounded values the P.V product uses.
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
+  if constexpr (BF16) {
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), ones, acc, false);
+  } else {
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), ones, acc, false);
+  }
+}
+
+// One workgroup = NW waves; each wave owns 32 query rows and walks all key tiles of the
+// workgroup's range. K and V tiles are double-buffered: the loads of tile j+1 are issued
+// before tile j is computed and waited for at the per-tile barrier.
 template <int D, int NW, int BN, bool BF16>
-__global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) {
-  constexpr int NT = NW * 64;
+__global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
-  constexpr int KLD = D + 8;   // padded K row: consecutive rows shift by 16 bytes
-  constexpr int VLD = BN + 8;  // padded V^T row
-  constexpr int KT = BN * KLD;
-  constexpr int VT = D * VLD;
+  constexpr int TILE = BN * D;  // elements per K or V tile
   constexpr int NKB = BN / 32;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
   constexpr int NPS = BN / 16;
-  constexpr int KCH = BN * D / 8;
-  constexpr int KCH_T = (KCH + NT - 1) / NT;
-  constexpr int VU = (BN / 4) * (D / 8);
-  constexpr int VU_T = (VU + NT - 1) / NT;
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  constexpr int CPR = D / 8;
+  constexpr int ROWS_PER_LOAD = 64 / CPR;
+  constexpr int LOADS = BN / ROWS_PER_LOAD;  // load instructions per tile (K or V)
+  constexpr int LPW = (LOADS + NW - 1) / NW;  // per wave
+  static_assert(BN % 32 == 0 && D % 32 == 0 && BN % ROWS_PER_LOAD == 0, "tile shape");
+  using SW = Swizzle<D>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
-  uint16_t* const k_lds = smem;
-  uint16_t* const v_lds = smem + 2 * KT;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+  uint16_t* const k_lds = smem;             // [2][BN][D]
+  uint16_t* const v_lds = smem + 2 * TILE;  // [2][BN][D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,10 +179,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int qt = blockIdx.x;
+  // XCD-aware work order: consecutive workgroup ids land on different XCDs, so the
+  // linear work index is taken XCD-major; the query tiles of one head then run on one
+  // XCD at the same time and share that XCD's L2 copy of the head's K and V.
+  const int nblk = gridDim.x;
+  int u = blockIdx.x;
+  if ((nblk & 7) == 0) u = (u & 7) * (nblk >> 3) + (u >> 3);
+  int qt = u % p.q_tiles;
+  const int h = (u / p.q_tiles) % p.hq;
+  const int b = u / (p.q_tiles * p.hq);
   if (p.causal) qt = p.q_tiles - 1 - qt;  // longest rows first
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+
   int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
   if (p.cu_q != nullptr) {
     q_off = p.cu_q[b];
@@ -151,9 +210,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) 
                        (int64_t)hk * p.vs[1] + (int64_t)k_off * p.vs[2];
   uint16_t* og = static_cast<uint16_t*>(p.o) + (ragged ? 0 : (int64_t)b * p.os[0]) +
                  (int64_t)h * p.os[1] + (int64_t)q_off * p.os[2];
-  const int64_t qs2 = p.qs[2], ks2 = p.ks[2], vs2 = p.vs[2], os2 = p.os[2];
+  const int64_t qs2 = p.qs[2], os2 = p.os[2];
+  const int ks2 = (int)p.ks[2], vs2 = (int)p.vs[2];  // host guarantees 64 * stride < 2^31
 
-  // Key range of the whole block, aligned down to the tile grid.
   const int r1 = min(Lq, r0 + BM);
   const int kend = p.causal ? min(Lk, r1 + delta) : Lk;
   int kbeg = p.window > 0 ? max(0, r0 + delta - p.window + 1) : 0;
@@ -164,6 +223,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) 
   const bool wave_live = w0 < Lq;
   const int qrow = w0 + l32;
   const RowRange rr = wave_key_range(p, w0, Lk, delta);
+  // this lane's allowed keys: [key_lo, key_lo + key_n)
+  const int key_lo = p.window > 0 ? qrow + delta - p.window + 1 : 0;
+  const int key_hi = p.causal ? min(Lk, qrow + delta + 1) : Lk;
+  const uint32_t key_n = (uint32_t)max(key_hi - key_lo, 0);
 
   u32x4_t qf[NKS];
 #pragma unroll
@@ -172,60 +235,44 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) 
     if (qrow < Lq) qf[ks] = load_global<u32x4_t>(qg + qrow * qs2 + ks * 16 + hi * 8);
   }
 
-  u32x4_t kreg[KCH_T];
-  u32x4_t vreg[VU_T][4];
-  auto load_tile = [&](int kt) {
+  // Per-lane constant offsets (elements). Direct-to-LDS loads: load n of this wave fills
+  // LDS block i = wave + n * NW (rows i*ROWS_PER_LOAD ...) of a tile.
+  int ld_row[LPW], ld_k[LPW], ld_v[LPW];
 #pragma unroll
-    for (int i = 0; i < KCH_T; ++i) {
-      const int c = tid + i * NT;
-      kreg[i] = u32x4_t{0, 0, 0, 0};
-      if (KCH % NT == 0 || c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        const int key = kt + row;
-        if (key < Lk) kreg[i] = load_global<u32x4_t>(kg + key * ks2 + col * 8);
-      }
-    }
+  for (int n = 0; n < LPW; ++n) {
+    const int i = wave + n * NW;
+    const int row = i * ROWS_PER_LOAD + lane / CPR;
+    const int slot = lane % CPR;
+    ld_row[n] = row;
+    ld_k[n] = row * ks2 + SW::k(row, slot) * 8;
+    ld_v[n] = row * vs2 + SW::v(row, slot) * 8;
+  }
+  // K reads: chunk 2*ks + hi of row kb*32 + l32 (the swizzle does not depend on kb)
+  int rd_k[NKS];
 #pragma unroll
-    for (int i = 0; i < VU_T; ++i) {
-      const int u = tid + i * NT;
-      if (VU % NT == 0 || u < VU) {
-        const int kq = u % (BN / 4), dc = u / (BN / 4);
+  for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+  // V transposing reads: rows t*16 + vrow (+8), head-dim block db
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * hi + (gi >> 2);
+  int rd_v[NDB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt + kq * 4 + r;
-          vreg[i][r] = u32x4_t{0, 0, 0, 0};
-          if (key < Lk) vreg[i][r] = load_global<u32x4_t>(vg + key * vs2 + dc * 8);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* kl = k_lds + buf * KT;
-    uint16_t* vl = v_lds + buf * VT;
+  for (int db = 0; db < NDB; ++db) {
+    const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
+    rd_v[db] = vrow * D + SW::v(vrow, c) * 8 + (gi & 1) * 4;
+  }
+
+  // Direct-to-LDS loads of one K or V tile. In the tail tile, rows past the last key
+  // re-read the last key (always in bounds); the mask gives them zero weight.
+  auto load_rows = [&](const uint16_t* gbase, int stride, const int (&off)[LPW], int kt,
+                       uint16_t* dst) __attribute__((always_inline)) {
+    const uint16_t* g = gbase + (int64_t)kt * stride;
+    const bool full_tile = kt + BN <= Lk;
 #pragma unroll
-    for (int i = 0; i < KCH_T; ++i) {
-      const int c = tid + i * NT;
-      if (KCH % NT == 0 || c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<u32x4_t*>(kl + row * KLD + col * 8) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VU_T; ++i) {
-      const int u = tid + i * NT;
-      if (VU % NT == 0 || u < VU) {
-        const int kq = u % (BN / 4), dc = u / (BN / 4);
-        const int pos = vt_pos(kq * 4);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // column 2w gathers the low halves of dword w of the four rows, 2w+1 the high halves
-          const u32x2_t even = {__builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], 0x05040100u),
-                                __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], 0x05040100u)};
-          const u32x2_t odd = {__builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], 0x07060302u),
-                               __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], 0x07060302u)};
-          *reinterpret_cast<u32x2_t*>(vl + (dc * 8 + 2 * w) * VLD + pos) = even;
-          *reinterpret_cast<u32x2_t*>(vl + (dc * 8 + 2 * w + 1) * VLD + pos) = odd;
-        }
+    for (int n = 0; n < LPW; ++n) {
+      const int i = wave + n * NW;
+      if (LOADS % NW == 0 || i < LOADS) {
+        const int shift = full_tile ? 0 : min(ld_row[n], Lk - 1 - kt) - ld_row[n];
+        load_lds16(g + off[n] + shift * stride, dst + i * 512);
       }
     }
   };
@@ -236,60 +283,110 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = kNegInf, l = 0.0f;
+  const f32x16_t zero16 = {};
+  f32x16_t s[NKB];
 
-  if (ntiles > 0) {
-    load_tile(kbeg);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  auto needs = [&](int it) {
     const int kt = kbeg + it * BN;
-    const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) load_tile(kt + BN);
-    if (wave_live && kt < rr.wend && kt + BN > rr.wbeg) {
-      const uint16_t* kl = k_lds + buf * KT;
-      const uint16_t* vl = v_lds + buf * VT;
-      f32x16_t s[NKB];
+    return wave_live && kt < rr.wend && kt + BN > rr.wbeg;
+  };
+  auto scores = [&](const uint16_t* kl) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + (kb * 32 + l32) * KLD + ks * 16 + hi * 8);
-          s[kb] = mfma32x32x16<BF16>(a, qf[ks], s[kb]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[ks]);
+        s[kb] = mfma32x32x16<BF16>(a, qf[ks], ks == 0 ? zero16 : s[kb]);
       }
-      const bool full = kt >= rr.fbeg && kt + BN <= rr.fend;
-      const float alpha = softmax_tile<NKB>(p, s, m, l, full, kt, qrow, Lk, delta, hi);
+  };
+  // softcap / mask / online-softmax update of tile `it` (in s), then O^T += V^T . P^T
+  auto softmax_pv = [&](int it, const uint16_t* vl) __attribute__((always_inline)) {
+    const int kt = kbeg + it * BN;
+    float sc = p.scale_log2;
+    if (p.cap_out > 0.0f) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_out * tanh_via_exp2(s[kb][r] * p.cap_in);
+      sc = 1.0f;
+    }
+    if (!(kt >= rr.fbeg && kt + BN <= rr.fend)) {
+      // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
+      const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) >= key_n) s[kb][r] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float mxs = pair_max(mx) * sc;
+    if (__any(mxs > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mxs);
+      // rows with no allowed key yet keep m = -inf (their l and O are still zero)
+      const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      u32x4_t pf[NPS];
-#pragma unroll
-      for (int t = 0; t < NPS; ++t) {
-        const int kb = t >> 1, base = (t & 1) * 8;
-        pf[t] = u32x4_t{pack2<BF16>(s[kb][base + 0], s[kb][base + 1]),
-                        pack2<BF16>(s[kb][base + 2], s[kb][base + 3]),
-                        pack2<BF16>(s[kb][base + 4], s[kb][base + 5]),
-                        pack2<BF16>(s[kb][base + 6], s[kb][base + 7])};
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int t = 0; t < NPS; ++t) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vl + (db * 32 + l32) * VLD + t * 16 + hi * 8);
-          o[db] = mfma32x32x16<BF16>(a, pf[t], o[db]);
-        }
+      m = m_new;
     }
-    if (more) store_tile(buf ^ 1);
+    const float m_use = (m == kNegInf) ? 0.0f : m;
+    u32x4_t pf[NPS];
+#pragma unroll
+    for (int t = 0; t < NPS; ++t) {
+      const int kb = t >> 1, base = (t & 1) * 8;
+      float e[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][base + x], sc, -m_use));
+      pf[t] = u32x4_t{pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]), pack2<BF16>(e[4], e[5]),
+                      pack2<BF16>(e[6], e[7])};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) l = dot2_ones<BF16>(pf[t][w], l);
+    }
+#pragma unroll
+    for (int t = 0; t < NPS; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t lo = lds_read_tr16(vl + t * 16 * D + rd_v[db]);
+        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * D + rd_v[db]);
+        o[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pf[t], o[db]);
+      }
+  };
+
+  auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;  // it % 2
+    const int kt = kbeg + it * BN;
+    if (it + 1 < ntiles) {
+      load_rows(kg, ks2, ld_k, kt + BN, k_lds + (BUF ^ 1) * TILE);
+      load_rows(vg, vs2, ld_v, kt + BN, v_lds + (BUF ^ 1) * TILE);
+    }
+    if (needs(it)) {
+      scores(k_lds + BUF * TILE);
+      softmax_pv(it, v_lds + BUF * TILE);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    load_rows(kg, ks2, ld_k, kbeg, k_lds);
+    load_rows(vg, vs2, ld_v, kbeg, v_lds);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it + 1);
   }
 
   if (!wave_live) return;
-  const float lt = l + xor_shuffle(l, 32);
+  const float lt = pair_sum(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (qrow < Lq) {
     uint16_t* orow = og + qrow * os2;
@@ -317,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma16_kernel(const FwdParams p) 
 // needs a single element per product, so no transposition is required).
 
 template <int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_f32_kernel(const FwdParams p) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   constexpr int LD = D + 4;
@@ -502,15 +599,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(const FwdParams p) {
   }
 }
 
-constexpr int kNW16 = 4;   // waves per workgroup, 16-bit inputs
-constexpr int kBN16 = 64;  // keys per tile, 16-bit inputs
+#ifndef ATTN_PREFILL_WAVES
+#define ATTN_PREFILL_WAVES 8
+#endif
+#ifndef ATTN_PREFILL_KEYS
+#define ATTN_PREFILL_KEYS 64
+#endif
+constexpr int kNW16 = ATTN_PREFILL_WAVES;  // waves per workgroup, 16-bit inputs
+constexpr int kBN16 = ATTN_PREFILL_KEYS;   // keys per tile, 16-bit inputs
 constexpr int kNW32 = 4;
 constexpr int kBN32 = 32;
 
 template <int D, bool BF16>
 hipError_t launch16(const FwdParams& p, hipStream_t st) {
-  dim3 grid(p.q_tiles, p.hq, p.batch);
-  hipLaunchKernelGGL((fwd_mfma16_kernel<D, kNW16, kBN16, BF16>), grid, dim3(kNW16 * 64), 0, st, p);
+  const int64_t blocks = (int64_t)p.q_tiles * p.hq * p.batch;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_mfma16_kernel<D, kNW16, kBN16, BF16>), dim3((unsigned)blocks), dim3(kNW16 * 64), 0,
+                     st, p);
   return hipGetLastError();
 }
 

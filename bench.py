@@ -49,6 +49,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="time the prefill only")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="run only the decode (per-kernel counter passes; prints decode timing only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -90,7 +92,8 @@ def main(argv=None):
         del dc.k_cache, dc.v_cache  # host copies no longer needed
 
     def run_prefill():
-        attn.fwd(q, k, v, out=o)
+        if not args.no_prefill:
+            attn.fwd(q, k, v, out=o)
 
     def run_decode():
         dc, dt, _ = dec
@@ -126,6 +129,12 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    if args.no_prefill:
+        if dec:
+            dms = [e[2].elapsed_time(e[3]) for e in ev]
+            print(json.dumps({"decode_ms": round(float(np.mean(dms)), 4),
+                              "decode_gbps": round(dec[2] / (float(np.mean(dms)) * 1e-3) / 1e9, 1)}))
+        return 0
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     pre_avg = float(np.mean(pre_ms))
     tflops = flops / (pre_avg * 1e-3) / 1e12
