@@ -50,7 +50,7 @@ float resolve_scale(float s, int head_dim) {
 
 constexpr double kLog2eD = 1.4426950408889634;
 constexpr int kPageSize = 16;
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplitTokens = 4096;
 
 attn_status_t check_strides(const char* name, const int64_t st[3], int esize, int64_t min_token) {
   for (int i = 0; i < 3; ++i) {
@@ -201,14 +201,16 @@ attn_status_t attn_decode_plan(const attn_decode_args_t* a, int32_t* split_len, 
     const int64_t per = ((int64_t)a->max_seq_len + a->num_splits - 1) / a->num_splits;
     len = (per + kPageSize - 1) / kPageSize * kPageSize;
   } else {
-    // Aim at about 8192 single-wave work items when lengths average half the maximum,
-    // keeping each split between 256 and 4096 tokens, rounded to a power of two.
-    const int64_t want = (int64_t)a->num_seqs * a->num_kv_heads * a->max_seq_len / (2 * 8192);
+#ifndef ATTN_DECODE_ITEMS
+#define ATTN_DECODE_ITEMS 8192
+#endif
+    // Aim at about ATTN_DECODE_ITEMS single-wave work items when lengths average half the
+    // maximum, keeping each split between 256 and 4096 tokens, rounded to a power of two.
+    const int64_t want = (int64_t)a->num_seqs * a->num_kv_heads * a->max_seq_len / (2 * ATTN_DECODE_ITEMS);
     len = 256;
-    while (len < want && len < 4096) len *= 2;
+    while (len < want && len < kMaxSplitTokens) len *= 2;
   }
-  const int64_t cap = ((int64_t)a->max_seq_len + kMaxSplits - 1) / kMaxSplits;
-  if (len < cap) len = (cap + kPageSize - 1) / kPageSize * kPageSize;
+  if (len > kMaxSplitTokens) len = kMaxSplitTokens;  // the split kernel's page window
   const int64_t n = ((int64_t)a->max_seq_len + len - 1) / len;
   if (split_len) *split_len = (int32_t)len;
   if (max_splits) *max_splits = (int32_t)n;

@@ -85,6 +85,26 @@ __device__ __forceinline__ float tanh_via_exp2(float x) {
 
 __device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One direct-to-LDS load: every lane moves 16 bytes from global address base + voff
+// (bytes) to LDS address lds_base + 16 * lane (lds_base must be wave-uniform).
+// Written as inline asm: with the compiler builtin for this load, every later
+// transposing LDS read (ds_read_b64_tr_b16) is made to wait for all loads still in
+// flight, which would serialise the K/V prefetch with the P.V product. Completion is
+// awaited explicitly (s_waitcnt vmcnt) by the callers. M0 carries the LDS base and is
+// written only here (no compiler-generated code in these kernels uses M0).
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory");
+}
+
+// Wait (visibly to the compiler) for this wave's ordinary global loads, so that the
+// hot loops that follow start with no compiler-tracked load outstanding and no wait
+// for them is placed inside the loop (where it would also stall on prefetches).
+__device__ __forceinline__ void settle_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <typename T>
 __device__ __forceinline__ T load_global(const void* p) {
   return *reinterpret_cast<const T*>(p);

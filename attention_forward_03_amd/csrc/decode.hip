@@ -29,6 +29,10 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kPage = 16;
+constexpr int kMaxSplitPages = 256;  // the host plans splits of at most 4096 tokens
+#ifndef ATTN_DECODE_HEAD_MAJOR
+#define ATTN_DECODE_HEAD_MAJOR 1
+#endif
 
 enum KvKind { KV_BF16 = 0, KV_F16 = 1, KV_FP8 = 2 };
 
@@ -48,16 +52,75 @@ __device__ __forceinline__ u32x4_t fp8x8_to_16(u32x2_t codes) {
   return r;
 }
 
-template <int KV, bool QBF16>
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 16x16x16 matrix-core product on 16-bit inputs (4 per lane): lane l supplies row l%16 of
+// A and column l%16 of B, k-slots 4*(l/16) .. +3; result register r of lane l is row
+// 4*(l/16) + r, column l%16.
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma16x16x16(u32x2_t a, u32x2_t b, f32x4_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+}
+
+// Pages of one split stream through an LDS ring of NST stages per wave, filled by
+// direct-to-LDS loads issued NST-1 pages ahead (each load instruction moves 1 KiB of
+// whole token rows, so global accesses are fully coalesced). A stage holds the page's
+// K rows then its V rows, row-major with 16-byte chunks XOR-swizzled per row:
+//   K: the score operand reads (16 token rows at one chunk) hit 16 bank groups;
+//   V (16-bit): the transposing reads of the P.V operand (16 rows x 2 chunks) hit each
+//      bank group twice, the minimum for 512 bytes.
+template <int KV>
+struct PageLayout {
+  static constexpr int ELT = KV == KV_FP8 ? 1 : 2;           // bytes per element
+  static constexpr int ROW = kD * ELT;                       // bytes per token row
+  static constexpr int CPR = ROW / 16;                       // 16-byte chunks per row
+  static constexpr int HALF = kPage * ROW;                   // bytes of K (or V) per page
+  static constexpr int STAGE = 2 * HALF;
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW;
+  static constexpr int LOADS = kPage / ROWS_PER_LOAD;        // per K (or V) page
+  __device__ static __forceinline__ int k_slot(int row, int c) {
+    return c ^ ((row / (16 / CPR)) % CPR);
+  }
+  __device__ static __forceinline__ int v_slot(int row, int c) {
+    if constexpr (KV == KV_FP8) return c ^ ((row / 2) % CPR);
+    else return c ^ (2 * (row % 8));
+  }
+};
+
+template <int KV, bool QBF16, int NST>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
+  using PL = PageLayout<KV>;
   constexpr bool KBF16 = (KV == KV_FP8) ? QBF16 : (KV == KV_BF16);
   static_assert(KV == KV_FP8 || KBF16 == QBF16, "16-bit K must match the query type");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * PL::STAGE];
+
+#if ATTN_DECODE_HEAD_MAJOR
+  // the KV heads of one split are adjacent workgroups: the slices of each physical page
+  // that belong to different heads are fetched at about the same time
+  const int g = blockIdx.x;
+  const int split = blockIdx.y;
+#else
   const int split = blockIdx.x;
   const int g = blockIdx.y;
+#endif
   const int s = blockIdx.z;
   const int lane = threadIdx.x;
-  const int col = lane & 15;   // query column (head g*G + col when col < G)
-  const int quad = lane >> 4;  // key slots 4*quad .. 4*quad+3 / head_dim block 32*quad
+  const int col = lane & 15;   // query column (head g*G + col when col < G) / token slot
+  const int quad = lane >> 4;  // token slots 4*quad .. 4*quad+3 of the score tile
 
   const int L = p.seq_lens[s];
   const int t0 = split * p.split_len;
@@ -65,7 +128,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int t1 = min(L, t0 + p.split_len);
   const int G = p.group;
 
-  // Q as the B operand: k-step ks, slot group quad <-> head_dim 32*quad + 8*ks .. +7.
+  // Q as the B operand of the score product: k-step ks, slot group quad <-> head_dim
+  // 32*quad + 8*ks .. +7.
   u32x4_t qf[4];
   const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.hq + g * G + col) * kD + 32 * quad;
 #pragma unroll
@@ -74,8 +138,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     if (col < G) qf[ks] = load_global<u32x4_t>(qrow + 8 * ks);
   }
 
-  const int64_t tok_stride = (int64_t)p.hkv * kD;        // elements between token slots
-  const int64_t page_stride = kPage * tok_stride;
+  const int64_t tok_bytes = (int64_t)p.hkv * PL::ROW;  // bytes between token slots
+  const int64_t page_bytes = kPage * tok_bytes;
+  const uint8_t* kc = static_cast<const uint8_t*>(p.k_cache) + (int64_t)g * PL::ROW;
+  const uint8_t* vc = static_cast<const uint8_t*>(p.v_cache) + (int64_t)g * PL::ROW;
   const int32_t* bt = p.block_table + (int64_t)s * p.max_pages;
   float ksc = 1.0f, vsc = 1.0f;
   if constexpr (KV == KV_FP8) {
@@ -84,49 +150,90 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   }
   const float sl2 = p.scale_log2 * ksc;
 
+  // per-lane load pattern: load i of a half-page fills rows i*ROWS_PER_LOAD + lane/CPR
+  int ld_row[PL::LOADS], ld_k[PL::LOADS], ld_v[PL::LOADS];
+#pragma unroll
+  for (int i = 0; i < PL::LOADS; ++i) {
+    const int row = i * PL::ROWS_PER_LOAD + lane / PL::CPR;
+    const int slot = lane % PL::CPR;
+    ld_row[i] = row;
+    ld_k[i] = row * (int)tok_bytes + PL::k_slot(row, slot) * 16;
+    ld_v[i] = row * (int)tok_bytes + PL::v_slot(row, slot) * 16;
+  }
+
+  const int pg0 = t0 / kPage;
+  const int pg1 = (t1 + kPage - 1) / kPage;
+  // The split's block-table entries, lane i holding entry pg0 + i + 64 * c (a split spans
+  // at most kMaxSplitPages pages); read with one vector load per 64 pages up front.
+  int btv[kMaxSplitPages / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
+    const int e = pg0 + lane + 64 * c;
+    btv[c] = (64 * c < pg1 - pg0 && e < pg1) ? bt[e] : 0;
+  }
+  auto phys_page = [&](int idx) __attribute__((always_inline)) {  // idx = pg - pg0, uniform
+    int v = btv[0];
+#pragma unroll
+    for (int c = 1; c < kMaxSplitPages / 64; ++c)
+      if (idx >= 64 * c) v = btv[c];
+    return __builtin_amdgcn_readlane(v, idx & 63);
+  };
+  auto issue = [&](int pg) __attribute__((always_inline)) {
+    uint8_t* st = ring + ((pg - pg0) % NST) * PL::STAGE;
+    const int64_t base = (int64_t)phys_page(pg - pg0) * page_bytes;
+    const int valid = t1 - pg * kPage;  // rows past the end re-read the last valid row
+#pragma unroll
+    for (int i = 0; i < PL::LOADS; ++i) {
+      const int shift = valid >= kPage ? 0 : (min(ld_row[i], valid - 1) - ld_row[i]) * (int)tok_bytes;
+      load_lds16(kc + base, (uint32_t)(ld_k[i] + shift), st + i * 1024);
+      load_lds16(vc + base, (uint32_t)(ld_v[i] + shift), st + PL::HALF + i * 1024);
+    }
+  };
+
   f32x4_t o[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m = kNegInf, l = 0.0f;
 
-  // Registers of one page: K operand (4 k-steps) and 4 V rows of 8 entries.
-  using KRaw = typename std::conditional<KV == KV_FP8, u32x2_t, u32x4_t>::type;
-  KRaw kr[4], kn[4];
-  KRaw vr[4], vn[4];
-  auto load_page = [&](int pg, KRaw (&kk)[4], KRaw (&vv)[4]) {
-    const int64_t phys = bt[pg];
-    const int64_t kbase = phys * page_stride + (int64_t)col * tok_stride + (int64_t)g * kD + 32 * quad;
-    const int64_t vbase = phys * page_stride + (int64_t)g * kD + 8 * col;
-    if constexpr (KV == KV_FP8) {
-      const uint8_t* kc = static_cast<const uint8_t*>(p.k_cache);
-      const uint8_t* vc = static_cast<const uint8_t*>(p.v_cache);
+  settle_global_loads();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kk[ks] = load_global<u32x2_t>(kc + kbase + 8 * ks);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vv[r] = load_global<u32x2_t>(vc + vbase + (4 * quad + r) * tok_stride);
-    } else {
-      const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache);
-      const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kk[ks] = load_global<u32x4_t>(kc + kbase + 8 * ks);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vv[r] = load_global<u32x4_t>(vc + vbase + (4 * quad + r) * tok_stride);
-    }
-  };
+  for (int i = 0; i < NST - 1; ++i)
+    if (pg0 + i < pg1) issue(pg0 + i);
 
-  const int pg0 = t0 / kPage;
-  const int pg1 = (t1 + kPage - 1) / kPage;
-  load_page(pg0, kr, vr);
   for (int pg = pg0; pg < pg1; ++pg) {
-    if (pg + 1 < pg1) load_page(pg + 1, kn, vn);
-    // scores
+    if (pg + NST - 1 < pg1) {
+      issue(pg + NST - 1);
+      // the loads of this page are complete once at most those of the NST-1 later pages
+      // remain outstanding
+      if constexpr (2 * PL::LOADS * (NST - 1) <= 63) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PL::LOADS * (NST - 1)) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const uint8_t* kst = ring + ((pg - pg0) % NST) * PL::STAGE;
+    const uint8_t* vst = kst + PL::HALF;
+
+    // scores S^T[slot][query] = K . Q^T
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KV == KV_FP8) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4_t a;
-      if constexpr (KV == KV_FP8) a = fp8x8_to_16<QBF16>(kr[ks]);
-      else a = kr[ks];
-      sc = mfma16x16x32<QBF16>(a, qf[ks], sc);
+      for (int j = 0; j < 2; ++j) {
+        // 16 codes = head_dim 32*quad + 16*j .. +15 of token slot `col`
+        const int c = 2 * quad + j;
+        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kst + col * PL::ROW + PL::k_slot(col, c) * 16);
+        sc = mfma16x16x32<QBF16>(fp8x8_to_16<QBF16>(u32x2_t{raw[0], raw[1]}), qf[2 * j], sc);
+        sc = mfma16x16x32<QBF16>(fp8x8_to_16<QBF16>(u32x2_t{raw[2], raw[3]}), qf[2 * j + 1], sc);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = 4 * quad + ks;
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kst + col * PL::ROW + PL::k_slot(col, c) * 16);
+        sc = mfma16x16x32<QBF16>(a, qf[ks], sc);
+      }
     }
     const int tb = pg * kPage + 4 * quad;  // token of register r is tb + r
     const bool partial = (pg + 1) * kPage > t1;
@@ -138,52 +245,59 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     }
     mx = fmaxf(mx, xor_shuffle(mx, 16));
     mx = fmaxf(mx, xor_shuffle(mx, 32));
-    const float m_new = fmaxf(m, mx * sl2);  // every page holds at least one valid token
-    const float alpha = fast_exp2(m - m_new);
-    float pr[4];
-    float rs = 0.0f;
+    // The reference max may trail the running max by up to 2^8; the accumulator is rescaled
+    // only when a page would exceed that (every page holds at least one valid token, so
+    // the new max is finite).
+    const float mxs = mx * sl2;
+    if (__any(mxs > m + 8.0f)) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = fast_exp2(sc[r] * sl2 - m_new);
-      rs += pr[r];
+      for (int c = 0; c < 8; ++c) o[c] *= alpha;
+      m = m_new;
     }
-    l = l * alpha + rs;
-    m = m_new;
+    float pr[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[c] *= alpha;
-    // values: row r of this lane is token tb + r; zero the rows past the end (the
-    // cache tail may hold anything, and 0 * NaN would poison the sum)
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] * sl2 - m);
+
+    if constexpr (KV == KV_FP8) {
+      l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      // O^T += V^T . P^T on the fp32 16x16x4 product: lane l reads 8 head_dim entries
+      // (8*col .. +7) of token slot 4*quad + r and feeds entry c to product c
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float vf[8];
-      if constexpr (KV == KV_FP8) {
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r;
+        const int c = col / 2;
+        const u32x2_t raw = *reinterpret_cast<const u32x2_t*>(vst + row * PL::ROW + PL::v_slot(row, c) * 16 + (col & 1) * 8);
+        float vf[8];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-          const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)vr[r][w], false);
-          const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)vr[r][w], true);
+          const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false);
+          const f32x2_t b2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true);
           vf[4 * w + 0] = a[0];
           vf[4 * w + 1] = a[1];
-          vf[4 * w + 2] = c[0];
-          vf[4 * w + 3] = c[1];
+          vf[4 * w + 2] = b2[0];
+          vf[4 * w + 3] = b2[1];
         }
-      } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          vf[2 * w] = lo16<KBF16>(vr[r][w]);
-          vf[2 * w + 1] = hi16<KBF16>(vr[r][w]);
-        }
+        for (int c8 = 0; c8 < 8; ++c8) o[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[c8], pr[r], o[c8], 0, 0, 0);
       }
-      if (partial && tb + r >= t1) {
+    } else {
+      // P packed to 16 bit as the B operand (keys 4*quad .. +3 of this lane's column);
+      // the row sum is taken over the same rounded values
+      const u32x2_t pb = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3])};
+      l += (lo16<QBF16>(pb[0]) + hi16<QBF16>(pb[0])) + (lo16<QBF16>(pb[1]) + hi16<QBF16>(pb[1]));
+      // O^T += V^T . P^T, 16 head_dim entries per product: the transposing read gives lane
+      // l the 4 keys 4*quad .. +3 of head_dim 16*db + col
+      const int vr = 4 * quad + (col >> 2);
+      const int vc2 = (col & 3);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) vf[c] = 0.0f;
+      for (int db = 0; db < 8; ++db) {
+        const int c = 2 * db + (vc2 >> 1);
+        const u32x2_t a = lds_read_tr16(vst + vr * PL::ROW + PL::v_slot(vr, c) * 16 + (vc2 & 1) * 8);
+        o[db] = mfma16x16x16<KBF16>(a, pb, o[db]);
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[c], pr[r], o[c], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = kn[i];
-      vr[i] = vn[i];
     }
   }
 
@@ -192,14 +306,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   if (col < G) {
     const int h = g * G + col;
     const int64_t slot = ((int64_t)s * p.hq + h) * p.max_splits + split;
-    float* dst = p.part_o + slot * kD + 32 * quad;
+    float* dst = p.part_o + slot * kD;
     const float inv = vsc / lt;
+    if constexpr (KV == KV_FP8) {
+      // product c, row i holds head_dim 8*i + c: lane (col, quad) has 32*quad + 8*rr + c
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      *reinterpret_cast<f32x4_t*>(dst + 8 * rr) =
-          f32x4_t{o[0][rr] * inv, o[1][rr] * inv, o[2][rr] * inv, o[3][rr] * inv};
-      *reinterpret_cast<f32x4_t*>(dst + 8 * rr + 4) =
-          f32x4_t{o[4][rr] * inv, o[5][rr] * inv, o[6][rr] * inv, o[7][rr] * inv};
+      for (int rr = 0; rr < 4; ++rr) {
+        *reinterpret_cast<f32x4_t*>(dst + 32 * quad + 8 * rr) =
+            f32x4_t{o[0][rr] * inv, o[1][rr] * inv, o[2][rr] * inv, o[3][rr] * inv};
+        *reinterpret_cast<f32x4_t*>(dst + 32 * quad + 8 * rr + 4) =
+            f32x4_t{o[4][rr] * inv, o[5][rr] * inv, o[6][rr] * inv, o[7][rr] * inv};
+      }
+    } else {
+      // block db, row r holds head_dim 16*db + 4*quad + r
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * quad) = o[db] * inv;
     }
     if (quad == 0) p.part_lse[slot] = m + fast_log2(lt);
   }
@@ -242,10 +364,26 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
   if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)s * p.hq + h] = (mx + fast_log2(wsum)) * kLn2;
 }
 
+#ifndef ATTN_DECODE_STAGES
+#define ATTN_DECODE_STAGES 3
+#endif
+#ifndef ATTN_DECODE_STAGES_FP8
+#define ATTN_DECODE_STAGES_FP8 3
+#endif
+// LDS ring depth per wave: fewer stages leave room for more resident waves, which on
+// this memory system pays more than a deeper prefetch per wave (measured).
+constexpr int kStages16 = ATTN_DECODE_STAGES;     // 16-bit KV, 8 KiB per stage
+constexpr int kStages8 = ATTN_DECODE_STAGES_FP8;  // fp8 KV, 4 KiB per stage
+
 template <int KV, bool QBF16>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
+#if ATTN_DECODE_HEAD_MAJOR
+  dim3 grid(p.hkv, p.max_splits, p.num_seqs);
+#else
   dim3 grid(p.max_splits, p.hkv, p.num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<KV, QBF16>), grid, dim3(64), 0, st, p);
+#endif
+  constexpr int nst = KV == KV_FP8 ? kStages8 : kStages16;
+  hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst>), grid, dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<QBF16>), dim3(p.num_seqs * p.hq), dim3(64), 0, st, p);

@@ -112,15 +112,8 @@ struct Swizzle {
   }
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-// 16 bytes per lane from global memory straight into LDS; the LDS address of lane l is
-// the (wave-uniform) base + 16 * l.
-__device__ __forceinline__ void load_lds16(const void* g, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
-}
 
 __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
   const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
@@ -272,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
       const int i = wave + n * NW;
       if (LOADS % NW == 0 || i < LOADS) {
         const int shift = full_tile ? 0 : min(ld_row[n], Lk - 1 - kt) - ld_row[n];
-        load_lds16(g + off[n] + shift * stride, dst + i * 512);
+        load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
       }
     }
   };
@@ -374,6 +367,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
     __syncthreads();
   };
 
+  settle_global_loads();
   if (ntiles > 0) {
     load_rows(kg, ks2, ld_k, kbeg, k_lds);
     load_rows(vg, vs2, ld_v, kbeg, v_lds);

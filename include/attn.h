@@ -118,13 +118,15 @@ typedef struct {
   int32_t q_dtype;           /* ATTN_BF16 or ATTN_F16; O has q_dtype */
   int32_t kv_dtype;          /* ATTN_BF16, ATTN_F16 or ATTN_FP8_E4M3 */
   float softmax_scale;       /* <= 0: 1/sqrt(D) as for attn_fwd */
-  int32_t num_splits;        /* 0: the library plans the split length; > 0: split the
-                                longest sequence into exactly this many pieces */
+  int32_t num_splits;        /* 0: the library plans the split length; n > 0: split_len =
+                                ceil(max_seq_len / n) rounded up to a whole page, capped at
+                                4096 tokens (the longest split the kernel handles) */
 } attn_decode_args_t;
 
 /* Split plan: every sequence s is cut into ceil(seq_lens[s] / split_len)
- * pieces of split_len tokens (a multiple of page_size); max_splits =
- * ceil(max_seq_len / split_len). Deterministic function of the args only. */
+ * pieces of split_len tokens (a multiple of page_size, at most 4096);
+ * max_splits = ceil(max_seq_len / split_len). Deterministic function of the
+ * args only. */
 attn_status_t attn_decode_plan(const attn_decode_args_t *args, int32_t *split_len,
                                int32_t *max_splits);
 

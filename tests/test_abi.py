@@ -110,17 +110,19 @@ def _dec_kw(**kw):
 
 def test_decode_plan_is_a_deterministic_integer_function():
     assert attn.decode_plan(**_dec_kw()) == (1024, 32)
-    assert attn.decode_plan(**_dec_kw(num_splits=7)) == (4688, 7)
-    assert attn.decode_plan(**_dec_kw(num_splits=1)) == (32768, 1)
+    assert attn.decode_plan(**_dec_kw(num_splits=9)) == (3648, 9)
+    # a split never exceeds 4096 tokens, whatever is asked for
+    assert attn.decode_plan(**_dec_kw(num_splits=7)) == (4096, 8)
+    assert attn.decode_plan(**_dec_kw(num_splits=1)) == (4096, 8)
     # a short single sequence still gets 256-token splits
     assert attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=1000, max_pages_per_seq=63)) == (256, 4)
-    # never more than 256 splits
     ln, n = attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=2_000_000, max_pages_per_seq=125000,
                                        num_splits=1000))
-    assert n <= 256 and ln % 16 == 0 and ln * n >= 2_000_000
-    for forced in (1, 2, 3, 7, 31, 64, 100):
+    assert ln == 2000 and n == 1000
+    for forced in (1, 2, 3, 7, 9, 31, 64, 100):
         ln, n = attn.decode_plan(**_dec_kw(num_splits=forced))
-        assert ln % 16 == 0 and n == -(-32768 // ln) and n <= forced
+        assert ln % 16 == 0 and ln <= 4096 and n == -(-32768 // ln)
+        assert (n <= forced and ln == -(-(-(-32768 // forced)) // 16) * 16) or ln == 4096
 
 
 def test_decode_workspace_size():
