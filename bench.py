@@ -43,6 +43,78 @@ def decode_bytes(case, kv_elt: int, q_elt: int = 2) -> float:
     return kv + q_o + tables + scales
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+PREFILL_KERNEL = "fwd_mfma16_kernel<128"
+DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
+
+
+def kernel_source_digest() -> str:
+    """Digest of the kernel sources: counter-derived traffic is only reported while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("prefill.hip", "decode.hip", "common.hpp"):
+        with open(os.path.join(HERE, "attention_forward_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, out_path: str) -> dict:
+    """HBM traffic per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE).
+
+    Both counters are in KiB per dispatch. Each is scaled by what it reads for the plain
+    device copy of ``copy_mib`` MiB that the same run performs (the copy reads and writes
+    exactly that many bytes), which calibrates the counter to bytes.
+    """
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    known = copy_mib * (1 << 20)
+    # the calibration copy is the largest copy dispatch of the run (small runtime copies
+    # also appear under the same kernel name)
+    copy_f = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
+    copy_w = max(v for k, vs in write.items() if "copyBuffer" in k for v in vs)
+    f_scale = known / (copy_f * 1024.0)
+    w_scale = known / (copy_w * 1024.0)
+    fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
+    write = {k: sum(v) / len(v) for k, v in write.items()}
+    res = {"source_digest": kernel_source_digest(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_mib": copy_mib, "kernels": {}}
+    for k in set(fetch) | set(write):
+        if "copyBuffer" in k:
+            continue
+        fb = fetch.get(k, 0.0) * 1024.0 * f_scale
+        wb = write.get(k, 0.0) * 1024.0 * w_scale
+        res["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def load_traffic(kernel_substr):
+    """Counter-measured HBM bytes per launch of the kernels whose name contains any of the
+    given substrings, or None when absent or taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_digest") != kernel_source_digest():
+        return None
+    subs = (kernel_substr,) if isinstance(kernel_substr, str) else kernel_substr
+    tot = [v["hbm_bytes"] for k, v in t["kernels"].items() if any(s in k for s in subs)]
+    return round(sum(tot)) if tot else None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -55,9 +127,16 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with measured HBM bytes per prefill launch (from counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE, WRITE_SIZE) of runs made with --calib-copy-mib")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        res = summarize_counters(*args.summarize_counters, copy_mib=args.calib_copy_mib or 1024,
+                                 out_path=TRAFFIC_FILE)
+        print(json.dumps(res, indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -156,11 +235,9 @@ def main(argv=None):
                                   " + paged split-KV decode 64 seqs L~U[512,32768] Hq=32 Hkv=8 D=128 bf16 KV"),
                    "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4), "max": round(max(pre_ms), 4)},
+        "kernel_source_digest": kernel_source_digest(),
     }
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("prefill_hbm_bytes_per_launch")
+    traffic = load_traffic(PREFILL_KERNEL)
     out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                        "kernel": "fwd_mfma16_kernel<128,...,bf16>",
@@ -173,6 +250,7 @@ def main(argv=None):
         out["decode"] = {"gbps": round(gbps, 1), "ms": round(davg, 4), "bytes_per_launch": nbytes,
                          "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                                       "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                                      "traffic": load_traffic(DECODE_KERNELS),
                                       "kernels": "decode_split_kernel + decode_combine_kernel"}}
 
     # ------------------------------------------------------------ CPU baseline ----
