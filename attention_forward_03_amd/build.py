@@ -4,7 +4,8 @@
 
 Sources are compiled in parallel with hipcc, then linked into a shared library
 next to this file. Packed fp32 VALU instructions are disabled for every HIP
-translation unit.
+translation unit. The instruction stream of the head_dim-128 prefill loop is
+written by csrc/gen_prefill_r2.py into _build/gen first (prefill.hip includes it).
 """
 from __future__ import annotations
 
@@ -35,15 +36,26 @@ def common_flags():
             "-Wno-unused-command-line-argument"]
 
 
+def generate(out_dir: str) -> str:
+    """Run the prefill loop generator; returns the include directory it wrote."""
+    gen_dir = os.path.join(out_dir, "gen")
+    cmd = [sys.executable, os.path.join(CSRC, "gen_prefill_r2.py"), gen_dir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"generating the prefill loop failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return gen_dir
+
+
 def build(verbose: bool = False) -> str:
     out_dir = os.path.join(HERE, "_build")
     os.makedirs(out_dir, exist_ok=True)
     hipcc = _hipcc()
+    gen_dir = generate(out_dir)
 
     def compile_one(src):
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *common_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *common_flags(), "-I", gen_dir, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

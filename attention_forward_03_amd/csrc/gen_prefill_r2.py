@@ -1,0 +1,857 @@
+"""Writes the main loop of the 64-rows-per-wave prefill kernel (head_dim 128, 16-bit
+inputs) as the text of one inline-asm statement, with every register and every wait
+chosen here.
+
+Why generated: with one wave per SIMD the wave has to interleave the vector softmax with
+its own matrix-core products instruction by instruction, while the output accumulators,
+the Q fragments, two score tiles and two probability tiles stay resident. Left to the
+compiler, the register allocation of such a loop is not stable (accumulators move
+between AGPRs, Q fragments get staged before every product), so the schedule and the
+register map are fixed here. The algorithm is the one described at the head of
+fwd_r2_kernel in prefill.hip; this file only lays out its instruction stream.
+
+Usage: python gen_prefill_r2.py OUT_DIR  -> OUT_DIR/prefill_r2_{bf16,f16}_m{0,1,2}.inc and
+OUT_DIR/prefill_r2_clobbers.inc (a macro with the registers the statement writes). Each
+.inc holds one string literal (the asm template; labels use %= so that every
+instantiation has its own).
+
+Modes: 0 = no mask at all (every tile full, no causal / window / ragged tail); 1 = a mask
+(causal, window, tail); 2 = softcap, with or without a mask.
+
+Schedule of a phase X(i) (one 32-key sub-tile): 32 steps, each with one matrix-core
+product (even steps S(i+1) = K Q^T, odd steps O^T += V^T P(i-1)^T) and a slice of the
+vector work on sub-tile i, software-pipelined so that no step waits on its own results:
+  step g: softcap / mask of score g (and, where row maxima are tracked, at odd g the max
+  of the pair);   step g+1: FMA (scale, minus the reference) of score g;   step g+2:
+  exp2 of score g;   step 2u+4: pack pair u to 16 bits;   steps 2u+4, 2u+5: add its two
+  values to the row sum (in fp32: a packed dot product would hold up the matrix core for
+  about 14 cycles).
+The last four steps of that pipeline run in the first steps of the next phase. The wave
+issues one instruction at a time, so every vector instruction in a step takes issue
+slots from the 32 cycles of its product: the stream keeps the vector work per step to a
+handful (no address arithmetic: every LDS address is a per-lane register plus an
+immediate, the tile loop being unrolled over the three LDS buffers).
+
+Two bodies per tile: "plain" (no mask, every row already has its reference max: no row
+maxima at all; a running max of each phase's row sums guards against a probability
+past the slack, checked once per pass) and "tracked" (mask, row maxima, and after each
+phase one compare per row block: a row whose max passed its threshold sends the wave to
+an out-of-line block that handles first unmasked keys and sets the redo flag).
+
+Hardware rules the stream keeps (gfx950): a matrix-core result is not touched by any
+other instruction for 12 wait states; a register written by a vector instruction is not
+read by a product for 2; an exp2 / rcp / log result is not read in the next slot; a
+permlane swap's operands are not touched for 2 before or after it; M0 is written one slot
+before the LDS-DMA load that uses it; every LDS read is waited for (s_waitcnt lgkmcnt)
+before its product, counting the reads issued after it in program order.
+
+Register map:
+  a[0:127]      O^T accumulators, block (rb, db) at a[(rb*4+db)*16 : +15]
+  a[128:191]    Q fragments, (rb, ks) at a[128 + (rb*8+ks)*4 : +3]
+  inputs (set by the C++ code before the statement):
+  v[0:1] v[2:3]   Q fragment addresses (row block 0, 1)
+  v[4:5] v[6:7]   O row addresses        v[8:9] v[10:11]  LSE addresses
+  v12 v13         4*hi - key_lo          v14 v15          key_n (allowed keys per row)
+  v16 v17         query rows             v19 v20          K / V load lane offsets (bytes)
+  v21 v22         K / V LDS read lane offsets (bytes, within a buffer)
+  s[40:41] s[42:43]  K / V bases    s44 s45  K / V token strides (elements)
+  s46 Lk   s47 first key   s48 tiles   s49 score scale (log2 units, > 0)
+  s50 softcap: scale / c   s51 softcap: c log2(e)   s53 wave   s54 Lq   s55 LSE wanted
+  s56 LDS base (bytes)   s57 s58  the wave's keys that need no mask: [s57, s58)
+LDS: K buffers 0..2, V buffers 3..5 (16 KiB each: 64 keys x 128 x 2 bytes, swizzled),
+the redo flag after them.
+"""
+import os
+import sys
+
+TB = 16384       # bytes of one 64 x 128 K or V tile
+HALF = 8192      # bytes of 32 rows
+NKS = 8          # 16-wide k-steps of D
+NDB = 4          # 32-wide blocks of D
+RB = 2           # 32-row query blocks per wave
+PF = 2           # fragments read ahead
+NSTEP = 32       # products per phase
+FLAG = 6 * TB    # LDS byte offset of the redo flag
+LN2 = "0x3f317218"
+RSRC_FLAGS = "0x20000"     # raw buffer, 32-bit elements
+
+# VGPRs used by the stream
+S_X, S_Y = 24, 56      # scores of even / odd sub-tiles; row block rb at +16*rb
+P_X, P_Y = 88, 104     # probabilities; (rb, t) at +(rb*2+t)*4
+KF, VF = 120, 136      # fragment rings, 4 slots of 4
+ET = 152               # exp-pipeline temporaries, 4 per sub-tile parity
+LSUB2 = 160            # row sums of odd sub-tiles [rb] (LSUB: even)
+MT = 162               # [rb] raw-score threshold of the per-phase check
+RSC = 164              # 1 / score scale
+LMX = 166              # [rb] running max of the phase row sums
+T0, T1, T2, T3 = 168, 169, 170, 171
+M, MU, L, LSUB, MXA, KBASE = 172, 174, 176, 178, 180, 182
+VNINF, VM2C = 186, 187
+MXS = 194              # [rb]
+VCAPK = 197
+ZERO = 200             # 4 registers
+EP = 208               # 8 epilogue temporaries
+INV = 216              # [rb]
+LT = 218               # [rb]
+KR = 220               # [ks] K read address of fragment ks (buffer 0, rows 0..31)
+VR = 228               # [db] V read address of column block db (buffer 3, rows 0..31)
+KO = 232               # [n] K load lane offset of load n
+VO = 236               # [n] V load lane offset of load n
+NVGPR = 240            # first unused
+
+# SGPRs used by the stream
+SJ, SKT, ST, ST2, ST3 = 60, 61, 62, 63, 64
+SKROW, SVROW, SWB, SKT2, SATT, SUNM = 65, 66, 67, 68, 69, 70
+SMASK, SMASK2, SEXEC, SPAIR = 80, 82, 84, 86   # pairs
+SCHK = SEXEC             # check of row block 0 (the loop), exec save (the epilogue)
+RSK, RSV = 88, 92        # buffer resources (4 each)
+NSGPR_LO, NSGPR_HI = 60, 96
+
+
+def v(i, n=1):
+    return f"v{i}" if n == 1 else f"v[{i}:{i + n - 1}]"
+
+
+def a(i, n=1):
+    return f"a{i}" if n == 1 else f"a[{i}:{i + n - 1}]"
+
+
+def s(i, n=1):
+    return f"s{i}" if n == 1 else f"s[{i}:{i + n - 1}]"
+
+
+def kbuf(c, h):
+    """Immediate offset of half h (rows 32h..32h+31) of buffer c (K: c, V: 3 + c)."""
+    return c * TB + h * HALF
+
+
+class Gen:
+    def __init__(self, bf16, mode):
+        self.bf16 = bf16
+        self.mode = mode
+        # slack: P < 2^slack; fp16 probabilities must stay below 2^16
+        self.slack_bits = "0x42200000" if bf16 else "0x41700000"   # 40 / 15
+        self.sum_limit = "0x53800000" if bf16 else "0x47000000"    # 2^40 / 2^15
+        self.out = []
+        self.lds = []   # tags of LDS reads that may be in flight, in issue order
+        self.n = 0
+        self.rare = []
+        self.et, self.lsub = ET, LSUB
+
+    def emit(self, line):
+        self.out.append(line)
+
+    def uniq(self, name):
+        self.n += 1
+        return f"L_{name}{self.n}_%="
+
+    # ------------------------------------------------------------------ LDS waits
+    def lds_op(self, tag):
+        self.lds.append(tag)
+
+    def wait_for(self, tag):
+        hits = [i for i, t in enumerate(self.lds) if t == tag]
+        if not hits:  # already waited for
+            return
+        idx = max(hits)
+        after = len(self.lds) - 1 - idx
+        if after < 15:
+            self.emit(f"s_waitcnt lgkmcnt({after})")
+        self.lds = self.lds[idx + 1:]
+
+    def relabel(self):
+        # the read-ahead of the phase that just ended feeds the next phase
+        self.lds = [("k", t[1]) if t[0] == "kn" else ("v", t[1]) if t[0] == "vn" else ("-", 0) for t in self.lds]
+
+    # ------------------------------------------------------------------ pieces
+    def mfma(self, d, av, bv, c):
+        op = "v_mfma_f32_32x32x16_bf16" if self.bf16 else "v_mfma_f32_32x32x16_f16"
+        self.emit(f"{op} {d}, {av}, {bv}, {c}")
+
+    def read_k(self, ofs, ks, slot, tag):
+        self.emit(f"ds_read_b128 {v(KF + 4 * slot, 4)}, {v(KR + ks)} offset:{ofs}")
+        self.lds_op(tag)
+
+    def read_v(self, ofs, f, slot, tag):
+        t, db = f // NDB, f % NDB
+        off = ofs + t * 16 * 256
+        self.emit(f"ds_read_b64_tr_b16 {v(VF + 4 * slot, 2)}, {v(VR + db)} offset:{off}")
+        self.emit(f"ds_read_b64_tr_b16 {v(VF + 4 * slot + 2, 2)}, {v(VR + db)} offset:{off + 8 * 256}")
+        self.lds_op(tag)
+        self.lds_op(tag)
+
+    def score(self, sbase, g):
+        """Register of score g (0..31) of a sub-tile: row block g // 16, element g % 16."""
+        return sbase + 16 * (g // 16) + g % 16
+
+    def pword(self, pbase, u):
+        """Register of the packed probabilities of pair u (0..15)."""
+        rr, e = u // 8, 2 * (u % 8)
+        return pbase + (rr * 2 + e // 8) * 4 + (e % 8) // 2
+
+    def fma_elem(self, sbase, g):
+        scale = "1.0" if self.mode == 2 else s(49)
+        self.emit(f"v_fma_f32 {v(self.et + g % 4)}, {v(self.score(sbase, g))}, {scale}, -{v(MU + g // 16)}")
+
+    def exp_elem(self, g):
+        self.emit(f"v_exp_f32 {v(self.et + g % 4)}, {v(self.et + g % 4)}")
+
+    def cvt_pair(self, pbase, u):
+        g0 = 2 * u
+        pw = self.pword(pbase, u)
+        cvt = "v_cvt_pk_bf16_f32" if self.bf16 else "v_cvt_pk_f16_f32"
+        self.emit(f"{cvt} {v(pw)}, {v(self.et + g0 % 4)}, {v(self.et + (g0 + 1) % 4)}")
+
+    def sum_elem(self, g):
+        """Row sum of the probabilities in fp32."""
+        self.emit(f"v_add_f32 {v(self.lsub + g // 16)}, {v(self.et + g % 4)}, {v(self.lsub + g // 16)}")
+
+    def exp_unit(self, sbase, pbase, u):
+        """All of P for pair u at once (the rare path)."""
+        g0 = 2 * u
+        self.fma_elem(sbase, g0)
+        self.fma_elem(sbase, g0 + 1)
+        self.exp_elem(g0)
+        self.exp_elem(g0 + 1)
+        self.emit("s_nop 0")
+        self.cvt_pair(pbase, u)
+        self.sum_elem(g0)
+        self.sum_elem(g0 + 1)
+
+    def softcap(self, src, dst):
+        # s <- c - 2c / (2^(s k) + 1)  (c tanh(s scale / c) in log2 units)
+        self.emit(f"v_mul_f32 {v(T2)}, {v(VCAPK)}, {v(src)}")
+        self.emit(f"v_exp_f32 {v(T2)}, {v(T2)}")
+        self.emit("s_nop 0")
+        self.emit(f"v_add_f32 {v(T2)}, 1.0, {v(T2)}")
+        self.emit(f"v_rcp_f32 {v(T2)}, {v(T2)}")
+        self.emit("s_nop 0")
+        self.emit(f"v_fma_f32 {v(dst)}, {v(T2)}, {v(VM2C)}, {s(51)}")
+
+    def mask(self, src, dst, rr, e):
+        """dst = src if key e of row block rr is allowed, else -inf (KBASE set)."""
+        off = (e >> 2) * 8 + (e & 3)
+        self.emit(f"v_add_u32 {v(T3)}, {off}, {v(KBASE + rr)}")
+        self.emit(f"v_cmp_gt_u32 vcc, {v(14 + rr)}, {v(T3)}")
+        self.emit(f"v_cndmask_b32 {v(dst)}, {v(VNINF)}, {v(src)}, vcc")
+
+    def seed_max_unit(self, sbase, u, masked):
+        """Max of score pair u into MXA, the scores left as they are (results in epilogue
+        temporaries)."""
+        rr, e = u // 8, 2 * (u % 8)
+        x = [sbase + 16 * rr + e, sbase + 16 * rr + e + 1]
+        for k in range(2):
+            if self.mode == 2:
+                self.softcap(x[k], EP + k)
+                x[k] = EP + k
+            if masked:
+                self.mask(x[k], EP + k, rr, e + k)
+                x[k] = EP + k
+        self.emit(f"v_max3_f32 {v(MXA + rr)}, {v(MXA + rr)}, {v(x[0])}, {v(x[1])}")
+
+    def mask_elem(self, sbase, g, masked):
+        """Softcap (mode 2) and mask of score g of a sub-tile, in place."""
+        rr, e = g // 16, g % 16
+        r = sbase + 16 * rr + e
+        if self.mode == 2:
+            self.softcap(r, r)
+        if masked:
+            self.mask(r, r, rr, e)
+
+    def max_pair(self, sbase, u):
+        rr, e = u // 8, 2 * (u % 8)
+        r = sbase + 16 * rr + e
+        self.emit(f"v_max3_f32 {v(MXA + rr)}, {v(MXA + rr)}, {v(r)}, {v(r + 1)}")
+
+    def gap(self):
+        self.emit("s_nop 7")
+        self.emit("s_nop 3")
+
+    def exchange_max(self):
+        """MXS[rb] = max of MXA[rb] over lanes l and l^32 (the two halves of a row), in log2
+        units (MXA holds raw scores)."""
+        self.emit(f"v_mov_b32 {v(T0)}, {v(MXA)}")
+        self.emit(f"v_mov_b32 {v(T1)}, {v(MXA)}")
+        self.emit(f"v_mov_b32 {v(T2)}, {v(MXA + 1)}")
+        self.emit(f"v_mov_b32 {v(T3)}, {v(MXA + 1)}")
+        self.emit("s_nop 1")
+        self.emit(f"v_permlane32_swap_b32 {v(T0)}, {v(T1)}")
+        self.emit(f"v_permlane32_swap_b32 {v(T2)}, {v(T3)}")
+        self.emit("s_nop 1")
+        self.emit(f"v_max_f32 {v(MXS)}, {v(T0)}, {v(T1)}")
+        self.emit(f"v_max_f32 {v(MXS + 1)}, {v(T2)}, {v(T3)}")
+        if self.mode != 2:
+            self.emit(f"v_mul_f32 {v(MXS)}, {s(49)}, {v(MXS)}")
+            self.emit(f"v_mul_f32 {v(MXS + 1)}, {s(49)}, {v(MXS + 1)}")
+
+    # ------------------------------------------------------------------ tile loads
+    def rsrc(self, which, key_sreg):
+        """Buffer resource for the tile of K ('k') or V ('v') starting at key key_sreg:
+        base at that key, records up to the last key (so rows past Lk read as zero)."""
+        base, stride, r = (40, 44, RSK) if which == "k" else (42, 45, RSV)
+        self.emit(f"s_mul_i32 {s(SPAIR)}, {s(key_sreg)}, {s(stride)}")
+        self.emit(f"s_mul_hi_u32 {s(SPAIR + 1)}, {s(key_sreg)}, {s(stride)}")
+        self.emit(f"s_lshl_b64 {s(SPAIR, 2)}, {s(SPAIR, 2)}, 1")
+        self.emit(f"s_add_u32 {s(r)}, {s(base)}, {s(SPAIR)}")
+        self.emit(f"s_addc_u32 {s(r + 1)}, {s(base + 1)}, {s(SPAIR + 1)}")
+        self.emit(f"s_and_b32 {s(r + 1)}, {s(r + 1)}, 0xffff")
+        self.emit(f"s_sub_i32 {s(ST3)}, {s(46)}, {s(key_sreg)}")
+        self.emit(f"s_min_i32 {s(ST3)}, {s(ST3)}, 64")
+        self.emit(f"s_mul_i32 {s(r + 2)}, {s(ST3)}, {s(stride)}")
+        self.emit(f"s_lshl_b32 {s(r + 2)}, {s(r + 2)}, 1")
+        self.emit(f"s_mov_b32 {s(r + 3)}, {RSRC_FLAGS}")
+
+    def load(self, which, n, buf):
+        """Load n (0..3) of this wave: 16 bytes per lane of rows (wave + 4 n)*4 + lane/16 into
+        the 1 KiB block (wave + 4 n) of LDS buffer buf (0..5)."""
+        off, r = (KO, RSK) if which == "k" else (VO, RSV)
+        self.emit(f"s_add_u32 m0, {s(SWB)}, {buf * TB + 4096 * n}")
+        self.emit("s_nop 0")
+        self.emit(f"buffer_load_dwordx4 {v(off + n)}, {s(r, 4)}, 0 offen lds")
+
+    def tile_key(self, plus):
+        """ST = first key of tile min(j + plus, n - 1)."""
+        self.emit(f"s_sub_u32 {s(ST2)}, {s(48)}, 1")
+        self.emit(f"s_add_u32 {s(ST)}, {s(SJ)}, {plus}")
+        self.emit(f"s_min_u32 {s(ST)}, {s(ST)}, {s(ST2)}")
+        self.emit(f"s_lshl_b32 {s(ST)}, {s(ST)}, 6")
+        self.emit(f"s_add_u32 {s(ST)}, {s(ST)}, {s(47)}")
+
+    # ------------------------------------------------------------------ one phase
+    def tail_ops(self, st, prev):
+        """The part of the previous soft phase's pipeline that runs in this phase's first
+        steps: FMA of score 31, exp2 of 30 and 31, packing of pairs 14 and 15, sums of 28..31,
+        then l += the previous phase's row sums (and their running max)."""
+        sx, px, et, lsub = prev
+        keep = (self.et, self.lsub)
+        self.et, self.lsub = et, lsub
+        if st == 0:
+            self.fma_elem(sx, 31)
+            self.exp_elem(30)
+            self.cvt_pair(px, 14)
+            self.sum_elem(28)
+        elif st == 1:
+            self.exp_elem(31)
+            self.sum_elem(29)
+        elif st == 2:
+            self.cvt_pair(px, 15)
+            self.sum_elem(30)
+        elif st == 3:
+            self.sum_elem(31)
+        elif st == 4:
+            for rb in range(RB):
+                self.emit(f"v_add_f32 {v(L + rb)}, {v(L + rb)}, {v(lsub + rb)}")
+        elif st == 5:
+            for rb in range(RB):
+                self.emit(f"v_max_f32 {v(LMX + rb)}, {v(LMX + rb)}, {v(lsub + rb)}")
+        self.et, self.lsub = keep
+
+    def phase(self, *, s_next, pv, soft, masked, track, maxonly, kofs, vofs, knofs, vnofs, dma, sx, sy, px, py,
+              kt_sreg, tail=None, advance=()):
+        """Phase X(i): S(i+1) into sy (K at kofs), O += V^T py^T (V at vofs), mask / max /
+        P of the scores sx of sub-tile i into px (first key kt_sreg); read-ahead of the next
+        phase's first K and V fragments (knofs / vnofs, None: none); tile loads into the
+        buffers dma = (K buffer, V buffer) or None.
+        track: row maxima and the per-phase check; tail: the previous soft phase (its
+        pipeline ends here); advance: groups of scalar instructions spread over the steps.
+        Returns the state a later phase needs to finish this one's pipeline."""
+        par = 0 if sx == S_X else 1
+        self.et, self.lsub = ET + 4 * par, (LSUB, LSUB2)[par]
+        advance = list(advance)
+        for st in range(NSTEP):
+            q = st // 2
+            if st % 2 == 0:
+                ks, rb = q // RB, q % RB
+                if s_next:
+                    if rb == 0 and ks + PF < NKS:
+                        self.read_k(kofs, ks + PF, (ks + PF) % 4, ("k", ks + PF))
+                    self.wait_for(("k", ks))
+                    c = "0" if ks == 0 else v(sy + 16 * rb, 16)
+                    self.mfma(v(sy + 16 * rb, 16), v(KF + 4 * (ks % 4), 4), a(128 + (rb * NKS + ks) * 4, 4), c)
+                if knofs is not None and rb == 0 and ks >= NKS - PF:
+                    g = ks - (NKS - PF)
+                    self.read_k(knofs, g, g, ("kn", g))
+                if dma is not None and q < 8:
+                    if q < 4:
+                        self.load("k", q, dma[0])
+                    elif dma[1] is not None:
+                        self.load("v", q - 4, dma[1])
+            else:
+                f, rb = q // RB, q % RB
+                if pv:
+                    if rb == 0 and f + PF < 2 * NDB:
+                        self.read_v(vofs, f + PF, (f + PF) % 4, ("v", f + PF))
+                    self.wait_for(("v", f))
+                    t, db = f // NDB, f % NDB
+                    blk = a((rb * NDB + db) * 16, 16)
+                    self.mfma(blk, v(VF + 4 * (f % 4), 4), v(py + (rb * 2 + t) * 4, 4), blk)
+                if vnofs is not None and rb == 0 and f >= 2 * NDB - PF:
+                    g = f - (2 * NDB - PF)
+                    self.read_v(vnofs, g, g, ("vn", g))
+            if tail is not None:
+                self.tail_ops(st, tail)
+            if soft:
+                if st == 0:
+                    if track:
+                        self.emit(f"v_mov_b32 {v(MXA)}, {v(VNINF)}")
+                        self.emit(f"v_mov_b32 {v(MXA + 1)}, {v(VNINF)}")
+                    if not maxonly:
+                        self.emit(f"v_mov_b32 {v(self.lsub)}, 0")
+                        self.emit(f"v_mov_b32 {v(self.lsub + 1)}, 0")
+                    if masked:
+                        self.emit(f"v_add_u32 {v(KBASE)}, {s(kt_sreg)}, {v(12)}")
+                        self.emit(f"v_add_u32 {v(KBASE + 1)}, {s(kt_sreg)}, {v(13)}")
+                if st == 0 and maxonly:
+                    # without the products of V, the scores of the last steps are younger
+                    self.emit("s_nop 4")
+                # step g: mask score g (odd g: max of the pair); g+1: FMA; g+2: exp2;
+                # 2u+4: pack pair u and add score 2u to the row sum; 2u+5: add score 2u+1
+                self.mask_elem(sx, st, masked)
+                if track and st % 2 == 1:
+                    self.max_pair(sx, st // 2)
+                if not maxonly:
+                    if st >= 1:
+                        self.fma_elem(sx, st - 1)
+                    if st >= 2:
+                        self.exp_elem(st - 2)
+                    if st >= 4:
+                        if st % 2 == 0:
+                            self.cvt_pair(px, (st - 4) // 2)
+                        self.sum_elem(st - 4)
+                    if track and st == 16:
+                        self.emit(f"v_cmp_gt_f32_e64 {s(SCHK, 2)}, {v(MXA)}, {v(MT)}")
+            if advance and 1 <= st <= 28:
+                per = -(-len(advance) // (29 - st))
+                for _ in range(per):
+                    for line in advance.pop(0):
+                        self.emit(line)
+        assert not advance
+        if soft and track and not maxonly:
+            # any row max past its threshold (reference + slack, or a first unmasked key)?
+            ret, rare = self.uniq("ret"), self.uniq("rare")
+            self.emit(f"v_cmp_gt_f32_e64 {s(SMASK, 2)}, {v(MXA + 1)}, {v(MT + 1)}")
+            self.emit(f"s_or_b64 {s(SMASK, 2)}, {s(SMASK, 2)}, {s(SCHK, 2)}")
+            self.emit(f"s_cbranch_scc1 {rare}")
+            self.emit(f"{ret}:")
+            self.rare.append((rare, ret, sx, px, self.et, self.lsub))
+        if soft and maxonly:
+            for rb in range(RB):
+                self.emit(f"v_max_f32 {v(M + rb)}, {v(M + rb)}, {v(MXA + rb)}")
+        return (sx, px, self.et, self.lsub)
+
+    def thresholds(self):
+        """MU = reference (0 for a row without one), MT = raw-score threshold of the check."""
+        for rb in range(RB):
+            self.emit(f"v_cmp_eq_f32 vcc, {v(VNINF)}, {v(M + rb)}")
+            self.emit(f"v_cndmask_b32_e64 {v(MU + rb)}, {v(M + rb)}, 0, vcc")
+            self.emit(f"v_add_f32 {v(MT + rb)}, {self.slack_bits}, {v(M + rb)}")
+            self.emit(f"v_mul_f32 {v(MT + rb)}, {v(MT + rb)}, {v(RSC)}")
+
+    def set_flag(self):
+        self.emit(f"v_mov_b32 {v(T0)}, 1")
+        self.emit(f"v_mov_b32 {v(T1)}, {FLAG}")
+        self.emit(f"v_add_u32 {v(T1)}, {s(56)}, {v(T1)}")
+        self.emit(f"ds_write_b32 {v(T1)}, {v(T0)}")
+        self.emit("s_waitcnt lgkmcnt(0)")
+
+    def rare_block(self, rare, ret, sx, px, et, lsub):
+        """Out of line. Rows whose first unmasked keys arrived take the sub-tile max as their
+        reference and P(i) so far is formed again; a row max past a finite reference by more
+        than the slack sets the redo flag (and the checks are switched off for the pass)."""
+        self.et, self.lsub = et, lsub
+        no_risk, back = self.uniq("norisk"), self.uniq("back")
+        self.emit(f"{rare}:")
+        self.exchange_max()
+        self.emit(f"s_mov_b64 {s(SMASK, 2)}, 0")
+        self.emit(f"s_mov_b64 {s(SMASK2, 2)}, 0")
+        for rb in range(RB):
+            self.emit(f"v_cmp_eq_f32 vcc, {v(VNINF)}, {v(M + rb)}")              # m == -inf
+            self.emit(f"v_cmp_neq_f32_e64 {s(SPAIR, 2)}, {v(VNINF)}, {v(MXS + rb)}")
+            self.emit(f"s_and_b64 {s(SPAIR, 2)}, {s(SPAIR, 2)}, vcc")            # first
+            self.emit(f"s_or_b64 {s(SMASK, 2)}, {s(SMASK, 2)}, {s(SPAIR, 2)}")
+            self.emit(f"v_cndmask_b32_e64 {v(M + rb)}, {v(M + rb)}, {v(MXS + rb)}, {s(SPAIR, 2)}")
+            self.emit(f"v_add_f32 {v(T0)}, {self.slack_bits}, {v(M + rb)}")
+            self.emit(f"v_cmp_gt_f32_e64 {s(SPAIR, 2)}, {v(MXS + rb)}, {v(T0)}")
+            self.emit(f"s_andn2_b64 {s(SPAIR, 2)}, {s(SPAIR, 2)}, vcc")          # risk (m was finite)
+            self.emit(f"s_or_b64 {s(SMASK2, 2)}, {s(SMASK2, 2)}, {s(SPAIR, 2)}")
+        self.emit(f"s_cmp_eq_u64 {s(SMASK2, 2)}, 0")
+        self.emit(f"s_cbranch_scc1 {no_risk}")
+        self.set_flag()
+        # this pass will be run again: no more checks in it
+        self.emit(f"v_mov_b32 {v(MT)}, 0x7f800000")
+        self.emit(f"v_mov_b32 {v(MT + 1)}, 0x7f800000")
+        self.emit(f"s_branch {back}")
+        self.emit(f"{no_risk}:")
+        self.emit(f"s_cmp_eq_u64 {s(SMASK, 2)}, 0")
+        self.emit(f"s_cbranch_scc1 {back}")
+        self.thresholds()
+        self.emit(f"v_mov_b32 {v(lsub)}, 0")
+        self.emit(f"v_mov_b32 {v(lsub + 1)}, 0")
+        # everything the pipeline did up to the last step, against the new reference
+        for u in range(14):
+            self.exp_unit(sx, px, u)
+        for g in (28, 29):
+            self.fma_elem(sx, g)
+        for g in (28, 29):
+            self.exp_elem(g)
+        self.fma_elem(sx, 30)
+        self.emit("s_nop 0")
+        self.emit(f"{back}:")
+        self.emit(f"s_branch {ret}")
+
+    # ------------------------------------------------------------------ a pass
+    def advance_groups(self, exact, first):
+        """Scalar work that prepares tile j+1 (first=False) or tile 0 (first=True): buffer
+        resources of the loads made in its first phase, and which body it takes."""
+        out = []
+
+        def grab(fn):
+            keep = self.out
+            self.out = []
+            fn()
+            out.append(self.out)
+            self.out = keep
+
+        if not first:
+            out.append([f"s_add_u32 {s(SJ)}, {s(SJ)}, 1", f"s_add_u32 {s(SKT)}, {s(SKT)}, 64"])
+        grab(lambda: (self.tile_key(2), self.rsrc("k", ST)))
+        if not exact:
+            grab(lambda: (self.tile_key(1), self.rsrc("v", ST)))
+            if self.mode >= 1:
+                # plain iff every row has its reference already (kt > s57: a row's first
+                # allowed key lies in an earlier tile) and no key of [kt, kt + 64) is masked
+                out.append([f"s_add_i32 {s(ST)}, {s(SKT)}, 64",
+                            f"s_cmp_le_i32 {s(ST)}, {s(58)}",
+                            f"s_cselect_b32 {s(SUNM)}, 1, 0",
+                            f"s_cmp_gt_i32 {s(SKT)}, {s(57)}",
+                            f"s_cselect_b32 {s(SUNM)}, {s(SUNM)}, 0"])
+        return out
+
+    def tile_body(self, exact, c, plain, prev):
+        """Both phases of a tile j with j % 3 == c (loads of K(j+2), V(j+1) in the first);
+        the second prepares tile j+1."""
+        c1, c2 = (c + 1) % 3, (c + 2) % 3
+        masked = self.mode >= 1 and not plain
+        track = exact or not plain
+        # X(2j): S(2j+1) from K(j) rows 32..63; P(2j-1) V(j-1) rows 32..63
+        st = self.phase(s_next=True, pv=not exact, soft=True, masked=masked, track=track, maxonly=exact,
+                        kofs=kbuf(c, 1), vofs=kbuf(c2, 1), knofs=kbuf(c1, 0),
+                        vnofs=None if exact else kbuf(c, 0), dma=(c2, None if exact else 3 + c1), sx=S_X, sy=S_Y, px=P_X,
+                        py=P_Y, kt_sreg=SKT, tail=None if exact else prev)
+        self.relabel()
+        self.emit(f"s_add_u32 {s(SKT2)}, {s(SKT)}, 32")
+        # X(2j+1): S(2j+2) from K(j+1) rows 0..31; P(2j) V(j) rows 0..31
+        st = self.phase(s_next=True, pv=not exact, soft=True, masked=masked, track=track, maxonly=exact,
+                        kofs=kbuf(c1, 0), vofs=kbuf(c, 0), knofs=kbuf(c1, 1),
+                        vnofs=None if exact else kbuf(c, 1), dma=None, sx=S_Y, sy=S_X, px=P_Y, py=P_X,
+                        kt_sreg=SKT2, tail=None if exact else st, advance=self.advance_groups(exact, False))
+        self.relabel()
+        return st
+
+    def tile(self, exact, c, prev):
+        """Tile j (j % 3 == c), in the body its scalar flag selects."""
+        if self.mode == 0 or exact:
+            return self.tile_body(exact, c, not exact, prev)
+        tracked, end = self.uniq("tracked"), self.uniq("tiledone")
+        self.emit(f"s_cmp_eq_u32 {s(SUNM)}, 0")
+        self.emit(f"s_cbranch_scc1 {tracked}")
+        start = list(self.lds)
+        st = self.tile_body(exact, c, True, prev)
+        self.emit(f"s_branch {end}")
+        self.emit(f"{tracked}:")
+        self.lds = start
+        st2 = self.tile_body(exact, c, False, prev)
+        assert st2 == st
+        self.emit(f"{end}:")
+        return st
+
+    def zero_v5(self):
+        """LDS V buffer 5 = 0: it stands for V(-1), read (times P = 0) in the first phase."""
+        self.emit(f"v_mbcnt_lo_u32_b32 {v(T0)}, -1, 0")
+        self.emit(f"v_mbcnt_hi_u32_b32 {v(T0)}, -1, {v(T0)}")
+        self.emit(f"v_lshlrev_b32 {v(T0)}, 4, {v(T0)}")
+        self.emit(f"s_lshl_b32 {s(ST)}, {s(53)}, 12")
+        self.emit(f"s_add_u32 {s(ST)}, {s(ST)}, {s(56)}")
+        self.emit(f"s_add_u32 {s(ST)}, {s(ST)}, {5 * TB}")
+        self.emit(f"v_add_u32 {v(T0)}, {s(ST)}, {v(T0)}")
+        for i in range(4):
+            self.emit(f"ds_write_b128 {v(T0)}, {v(ZERO, 4)} offset:{i * 1024}")
+
+    def run_pass(self, exact):
+        tag = "x" if exact else "n"
+        self.emit(f"s_mov_b32 {s(SJ)}, 0")
+        self.emit(f"s_mov_b32 {s(SKT)}, {s(47)}")
+        # K(0) -> buffer 0, V(0) -> buffer 3, K(min(1, n-1)) -> buffer 1
+        self.rsrc("k", 47)
+        for n in range(4):
+            self.load("k", n, 0)
+        if not exact:
+            self.rsrc("v", 47)
+            for n in range(4):
+                self.load("v", n, 3)
+            self.zero_v5()
+            for rb in range(RB):
+                self.emit(f"v_mov_b32 {v(LMX + rb)}, 0")
+        self.emit("s_waitcnt vmcnt(0)")
+        self.tile_key(1)
+        self.rsrc("k", ST)
+        for n in range(4):
+            self.load("k", n, 1)
+        self.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+        self.emit("s_barrier")
+        if not exact:
+            # P(-1) = 0, and the pipeline "tail" of sub-tile -1 produces zeros
+            for r in range(P_Y, P_Y + 16):
+                self.emit(f"v_mov_b32 {v(r)}, 0")
+            self.emit(f"v_mov_b32 {v(ET + 4)}, 0")
+            self.emit(f"v_mov_b32 {v(ET + 5)}, 0")
+            self.emit(f"v_mov_b32 {v(ET + 6)}, {v(VNINF)}")
+            self.emit(f"v_mov_b32 {v(S_Y + 31)}, {v(VNINF)}")
+            self.emit(f"v_mov_b32 {v(LSUB2)}, 0")
+            self.emit(f"v_mov_b32 {v(LSUB2 + 1)}, 0")
+        # phase I: S(0) from K(0) rows 0..31; read ahead K(0) rows 32..63 and V(-1) rows 32..63
+        self.lds = []
+        for g in range(PF):
+            self.read_k(kbuf(0, 0), g, g, ("k", g))
+        self.phase(s_next=True, pv=False, soft=False, masked=False, track=False, maxonly=exact,
+                   kofs=kbuf(0, 0), vofs=None, knofs=kbuf(0, 1), vnofs=None if exact else kbuf(2, 1),
+                   dma=None, sx=S_Y, sy=S_X, px=P_Y, py=P_X, kt_sreg=SKT,
+                   advance=self.advance_groups(exact, True))
+        self.relabel()
+        prev = (S_Y, P_Y, ET + 4, LSUB2)
+        if not exact:
+            # reference max of each row from sub-tile 0 (kept when already larger)
+            self.gap()
+            self.emit(f"v_mov_b32 {v(MXA)}, {v(VNINF)}")
+            self.emit(f"v_mov_b32 {v(MXA + 1)}, {v(VNINF)}")
+            if self.mode >= 1:
+                self.emit(f"v_add_u32 {v(KBASE)}, {s(SKT)}, {v(12)}")
+                self.emit(f"v_add_u32 {v(KBASE + 1)}, {s(SKT)}, {v(13)}")
+            for u in range(16):
+                self.seed_max_unit(S_X, u, self.mode >= 1)
+            self.exchange_max()
+            for rb in range(RB):
+                self.emit(f"v_max_f32 {v(M + rb)}, {v(M + rb)}, {v(MXS + rb)}")
+            self.thresholds()
+        loop_state = list(self.lds)
+        exits = []
+        self.emit(f"L_{tag}tile_%=:")
+        for c in range(3):
+            assert self.lds == loop_state, (self.lds, loop_state)
+            prev = self.tile(exact, c, prev)
+            assert self.lds == loop_state, (self.lds, loop_state)
+            self.emit("s_waitcnt vmcnt(0)")
+            self.emit("s_barrier")
+            if c < 2:
+                lbl = self.uniq(f"{tag}exit")
+                exits.append((lbl, c))
+                self.emit(f"s_cmp_ge_u32 {s(SJ)}, {s(48)}")
+                self.emit(f"s_cbranch_scc1 {lbl}")
+            else:
+                self.emit(f"s_cmp_lt_u32 {s(SJ)}, {s(48)}")
+                self.emit(f"s_cbranch_scc1 L_{tag}tile_%=")
+        done = self.uniq(f"{tag}passdone")
+        if not exact:
+            # last: P(2n-1) V(n-1) rows 32..63 (first fragments read ahead); the pipeline of
+            # sub-tile 2n-1 ends here. V(n-1) sits in buffer 3 + (n-1) % 3.
+            for lbl, c in [(None, 2)] + exits:
+                if lbl is not None:
+                    self.emit(f"{lbl}:")
+                self.lds = list(loop_state)
+                self.phase(s_next=False, pv=True, soft=False, masked=False, track=False, maxonly=False,
+                           kofs=None, vofs=kbuf(c, 1), knofs=None, vnofs=None, dma=None, sx=S_X, sy=S_Y,
+                           px=P_X, py=P_Y, kt_sreg=SKT, tail=prev)
+                self.emit(f"s_branch {done}")
+            self.emit(f"{done}:")
+            # a phase's row sums past the slack: the pass is run again
+            ok = self.uniq("sumsok")
+            self.emit(f"v_cmp_lt_f32 vcc, {self.sum_limit}, {v(LMX)}")
+            self.emit(f"s_mov_b64 {s(SMASK, 2)}, vcc")
+            self.emit(f"v_cmp_lt_f32 vcc, {self.sum_limit}, {v(LMX + 1)}")
+            self.emit(f"s_or_b64 {s(SMASK, 2)}, {s(SMASK, 2)}, vcc")
+            self.emit(f"s_cbranch_scc0 {ok}")
+            self.set_flag()
+            self.emit(f"{ok}:")
+        else:
+            for lbl, c in exits:
+                self.emit(f"{lbl}:")
+            # the halves of each row exchange their maxima
+            self.emit(f"v_mov_b32 {v(MXA)}, {v(M)}")
+            self.emit(f"v_mov_b32 {v(MXA + 1)}, {v(M + 1)}")
+            self.exchange_max()
+            for rb in range(RB):
+                self.emit(f"v_mov_b32 {v(M + rb)}, {v(MXS + rb)}")
+        self.emit("s_waitcnt lgkmcnt(0)")
+        self.lds = []
+        self.gap()
+
+    # ------------------------------------------------------------------ whole stream
+    def build(self):
+        e = self.emit
+        e(f"v_mov_b32 {v(VNINF)}, 0xff800000")
+        e(f"v_mul_f32 {v(VM2C)}, -2.0, {s(51)}")
+        e(f"v_mov_b32 {v(VCAPK)}, 0x4038aa3b")
+        e(f"v_mul_f32 {v(VCAPK)}, {s(50)}, {v(VCAPK)}")
+        if self.mode == 2:
+            e(f"v_mov_b32 {v(RSC)}, 1.0")
+        else:
+            e(f"v_rcp_f32 {v(RSC)}, {s(49)}")
+        e(f"s_lshl_b32 {s(SWB)}, {s(53)}, 10")
+        e(f"s_add_u32 {s(SWB)}, {s(SWB)}, {s(56)}")
+        e(f"s_lshl_b32 {s(SKROW)}, {s(44)}, 5")
+        e(f"s_lshl_b32 {s(SVROW)}, {s(45)}, 5")
+        # per-lane LDS read addresses (swizzle applied) and load offsets
+        for ks in range(NKS):
+            e(f"v_xor_b32 {v(KR + ks)}, {ks << 5}, {v(21)}")
+            e(f"v_add_u32 {v(KR + ks)}, {s(56)}, {v(KR + ks)}")
+        for db in range(NDB):
+            e(f"v_xor_b32 {v(VR + db)}, {db << 6}, {v(22)}")
+            e(f"v_add_u32 {v(VR + db)}, {s(56)}, {v(VR + db)}")
+            e(f"v_add_u32 {v(VR + db)}, {3 * TB}, {v(VR + db)}")
+        for n in range(4):
+            e(f"s_mul_i32 {s(ST3)}, {s(SKROW)}, {n}")
+            e(f"v_add_u32 {v(KO + n)}, {s(ST3)}, {v(19)}")
+            e(f"s_mul_i32 {s(ST3)}, {s(SVROW)}, {n}")
+            e(f"v_add_u32 {v(VO + n)}, {s(ST3)}, {v(20)}")
+        for r in range(ZERO, ZERO + 4):
+            e(f"v_mov_b32 {v(r)}, 0")
+        # Q fragments straight into AGPRs
+        for rb in range(RB):
+            for ks in range(NKS):
+                e(f"global_load_dwordx4 {a(128 + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
+        # redo flag = 0 (wave 0), ordered before any write of 1 by the first barrier
+        skip = self.uniq("noinit")
+        e(f"s_cmp_lg_u32 {s(53)}, 0")
+        e(f"s_cbranch_scc1 {skip}")
+        e(f"v_mov_b32 {v(T1)}, {FLAG}")
+        e(f"v_add_u32 {v(T1)}, {s(56)}, {v(T1)}")
+        e(f"ds_write_b32 {v(T1)}, {v(ZERO)}")
+        e("s_waitcnt lgkmcnt(0)")
+        e(f"{skip}:")
+        e(f"s_mov_b32 {s(SATT)}, 0")
+        for rb in range(RB):
+            e(f"v_mov_b32 {v(M + rb)}, {v(VNINF)}")
+        e("L_attempt_%=:")
+        for rb in range(RB):
+            e(f"v_mov_b32 {v(L + rb)}, 0")
+        e("s_nop 1")
+        for blk in range(RB * NDB):
+            self.mfma(a(blk * 16, 16), v(ZERO, 4), v(ZERO, 4), "0")
+        self.run_pass(exact=False)
+        # redo? (read after every wave has finished writing it)
+        done = "L_done_%="
+        e("s_barrier")
+        e(f"s_cmp_lg_u32 {s(SATT)}, 0")
+        e(f"s_cbranch_scc1 {done}")
+        e(f"v_mov_b32 {v(T1)}, {FLAG}")
+        e(f"v_add_u32 {v(T1)}, {s(56)}, {v(T1)}")
+        e(f"ds_read_b32 {v(T0)}, {v(T1)}")
+        e("s_waitcnt lgkmcnt(0)")
+        e(f"v_readfirstlane_b32 {s(ST)}, {v(T0)}")
+        e(f"s_cmp_eq_u32 {s(ST)}, 0")
+        e(f"s_cbranch_scc1 {done}")
+        # exact row max first, then the pass again against it
+        e(f"s_mov_b32 {s(SATT)}, 1")
+        for rb in range(RB):
+            e(f"v_mov_b32 {v(M + rb)}, {v(VNINF)}")
+        self.run_pass(exact=True)
+        e("s_barrier")
+        e("s_branch L_attempt_%=")
+        e(f"{done}:")
+        self.epilogue()
+        e("s_branch L_end_%=")
+        for blk in self.rare:
+            self.rare_block(*blk)
+        e("L_end_%=:")
+        return self.out
+
+    def epilogue(self):
+        e = self.emit
+        e(f"v_mov_b32 {v(T0)}, {v(L)}")
+        e(f"v_mov_b32 {v(T1)}, {v(L)}")
+        e(f"v_mov_b32 {v(T2)}, {v(L + 1)}")
+        e(f"v_mov_b32 {v(T3)}, {v(L + 1)}")
+        e("s_nop 1")
+        e(f"v_permlane32_swap_b32 {v(T0)}, {v(T1)}")
+        e(f"v_permlane32_swap_b32 {v(T2)}, {v(T3)}")
+        e("s_nop 1")
+        e(f"v_add_f32 {v(LT)}, {v(T0)}, {v(T1)}")
+        e(f"v_add_f32 {v(LT + 1)}, {v(T2)}, {v(T3)}")
+        for rb in range(RB):
+            # 1/l (0 for a row with no allowed key)
+            e(f"v_rcp_f32 {v(INV + rb)}, {v(LT + rb)}")
+            e("s_nop 0")
+            e(f"v_cmp_lt_f32 vcc, 0, {v(LT + rb)}")
+            e(f"v_cndmask_b32 {v(INV + rb)}, 0, {v(INV + rb)}, vcc")
+        for rb in range(RB):
+            skip = self.uniq("nostore")
+            e(f"v_cmp_gt_i32 vcc, {s(54)}, {v(16 + rb)}")
+            e(f"s_and_saveexec_b64 {s(SEXEC, 2)}, vcc")
+            e(f"s_cbranch_execz {skip}")
+            for db in range(NDB):
+                for g4 in range(4):
+                    base = (rb * NDB + db) * 16 + g4 * 4
+                    for k in range(4):
+                        e(f"v_accvgpr_read_b32 {v(EP + k)}, {a(base + k)}")
+                    for k in range(4):
+                        e(f"v_mul_f32 {v(EP + k)}, {v(EP + k)}, {v(INV + rb)}")
+                    cvt = "v_cvt_pk_bf16_f32" if self.bf16 else "v_cvt_pk_f16_f32"
+                    e(f"{cvt} {v(EP + 4)}, {v(EP)}, {v(EP + 1)}")
+                    e(f"{cvt} {v(EP + 5)}, {v(EP + 2)}, {v(EP + 3)}")
+                    e(f"global_store_dwordx2 {v(4 + 2 * rb, 2)}, {v(EP + 4, 2)}, off offset:{db * 64 + g4 * 16}")
+            e(f"{skip}:")
+            e(f"s_mov_b64 exec, {s(SEXEC, 2)}")
+        nolse = self.uniq("nolse")
+        e(f"s_cmp_eq_u32 {s(55)}, 0")
+        e(f"s_cbranch_scc1 {nolse}")
+        for rb in range(RB):
+            skip = self.uniq("nolserow")
+            # LSE = ln2 (m + log2 l), -inf for a row with no allowed key; lanes 0..31 store
+            e(f"v_log_f32 {v(T0)}, {v(LT + rb)}")
+            e("s_nop 0")
+            e(f"v_add_f32 {v(T0)}, {v(MU + rb)}, {v(T0)}")
+            e(f"v_mul_f32 {v(T0)}, {LN2}, {v(T0)}")
+            e(f"v_cmp_lt_f32 vcc, 0, {v(LT + rb)}")
+            e(f"v_cndmask_b32 {v(T0)}, {v(VNINF)}, {v(T0)}, vcc")
+            e(f"v_cmp_gt_i32 vcc, {s(54)}, {v(16 + rb)}")
+            e(f"v_mbcnt_lo_u32_b32 {v(T1)}, -1, 0")
+            e(f"v_mbcnt_hi_u32_b32 {v(T1)}, -1, {v(T1)}")
+            e(f"v_cmp_gt_u32_e64 {s(SPAIR, 2)}, 32, {v(T1)}")
+            e(f"s_and_b64 vcc, vcc, {s(SPAIR, 2)}")
+            e(f"s_and_saveexec_b64 {s(SEXEC, 2)}, vcc")
+            e(f"s_cbranch_execz {skip}")
+            e(f"global_store_dword {v(8 + 2 * rb, 2)}, {v(T0)}, off")
+            e(f"{skip}:")
+            e(f"s_mov_b64 exec, {s(SEXEC, 2)}")
+        e(f"{nolse}:")
+
+
+def render(lines):
+    return "\n".join('"' + ln + '\\n\\t"' for ln in lines) + "\n"
+
+
+def clobbers():
+    regs = [f'"v{i}"' for i in range(24, NVGPR)] + [f'"a{i}"' for i in range(192)]
+    regs += [f'"s{i}"' for i in range(NSGPR_LO, NSGPR_HI)]
+    # m0 and exec are written too (m0 for the LDS-DMA loads, exec around the row-masked
+    # stores, restored); nothing follows the statement in the kernel, so they are not listed
+    regs += ['"vcc"', '"scc"', '"memory"']
+    return ", ".join(regs)
+
+
+def main(out_dir):
+    os.makedirs(out_dir, exist_ok=True)
+    for bf16 in (True, False):
+        for mode in (0, 1, 2):
+            lines = Gen(bf16, mode).build()
+            name = f"prefill_r2_{'bf16' if bf16 else 'f16'}_m{mode}.inc"
+            with open(os.path.join(out_dir, name), "w") as f:
+                f.write(f"// generated by gen_prefill_r2.py: {len(lines)} lines\n")
+                f.write(render(lines))
+    with open(os.path.join(out_dir, "prefill_r2_clobbers.inc"), "w") as f:
+        f.write("// generated by gen_prefill_r2.py\n")
+        f.write("#define ATTN_R2_CLOBBERS " + clobbers() + "\n")
+
+
+if __name__ == "__main__":
+    main(sys.argv[1] if len(sys.argv) > 1 else ".")

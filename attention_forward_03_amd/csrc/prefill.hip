@@ -401,6 +401,191 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   }
 }
 
+// ------------------------------------------- 16-bit inputs, 64 query rows per wave ----
+// head_dim 128. Each wave owns two 32-row blocks of queries, so every K or V fragment read
+// from LDS feeds two matrix-core products: half the LDS reads per flop of the 32-row
+// kernel, at the price of one wave per SIMD (the accumulators and Q fragments of two row
+// blocks take 192 AGPRs). With a single wave there is no other wave to hide the softmax
+// behind the matrix cores, so the wave overlaps them itself, in program order: keys are
+// taken in sub-tiles of 32, and phase X(i) issues, alternately, the products of
+// S(i+1) = K Q^T and of O^T += V^T P(i-1)^T while the vector unit forms
+// P(i) = 2^(S(i) sc - m) and its row sums.
+//
+// The reference max m. The recurrence of the tiled-attention section of the page keeps O
+// scaled to the running max; any fixed reference gives the same O / l as long as no
+// 2^(s sc - m) overflows the 16-bit P (or loses all its bits to underflow). So each row
+// takes as its reference the max of its first sub-tile that has an unmasked key (O and l
+// are still zero then), and it stays: no rescale of O ever. A later score may exceed the
+// reference by up to a slack (15 for fp16 P, whose range ends at 2^16; 40 for bf16). A
+// pass in which that fails for some row flags the workgroup; it then takes the exact row
+// maxima in a pass of S products only and runs the attention pass again against them.
+// Tiles of 64 keys with no mask, once every row of the wave has its reference, take a
+// body without row maxima: the max of each phase's row sums stands guard (a P past the
+// slack makes its sum pass it). The others take a body with the mask and the row maxima,
+// checked after every phase, that also fixes the first references.
+//
+// K and V arrive in 64-key tiles by range-checked buffer loads straight into LDS, spread
+// over the first phase of each tile, three LDS buffers each and one barrier per tile; the
+// tile loop is unrolled over the three buffers so that every LDS address is a lane
+// register plus an immediate.
+// The loop is one inline-asm statement written by gen_prefill_r2.py (register map and
+// schedule fixed there); this function computes its inputs.
+#include "prefill_r2_clobbers.inc"
+
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
+  constexpr int D = 128, BN = 64, RB = 2, NW = 4;
+  constexpr int BM = NW * 32 * RB;
+  constexpr int TILE = BN * D;
+  using SW = Swizzle<D>;
+  // K x3, V x3, then the redo flag
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[6 * TILE + 2];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int nblk = gridDim.x;
+  int u = blockIdx.x;
+  if ((nblk & 7) == 0) u = (u & 7) * (nblk >> 3) + (u >> 3);
+  int qt = u % p.q_tiles;
+  const int h = (u / p.q_tiles) % p.hq;
+  const int b = u / (p.q_tiles * p.hq);
+  if (p.causal) qt = p.q_tiles - 1 - qt;
+
+  int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
+  if (p.cu_q != nullptr) {
+    q_off = p.cu_q[b];
+    Lq = p.cu_q[b + 1] - q_off;
+    k_off = p.cu_k[b];
+    Lk = p.cu_k[b + 1] - k_off;
+  }
+  const int r0 = qt * BM;
+  if (r0 >= Lq) return;
+  const int hk = h / p.group;
+  const int delta = Lk - Lq;
+  const bool ragged = p.cu_q != nullptr;
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (ragged ? 0 : (int64_t)b * p.qs[0]) +
+                       (int64_t)h * p.qs[1] + (int64_t)q_off * p.qs[2];
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (ragged ? 0 : (int64_t)b * p.ks[0]) +
+                       (int64_t)hk * p.ks[1] + (int64_t)k_off * p.ks[2];
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (ragged ? 0 : (int64_t)b * p.vs[0]) +
+                       (int64_t)hk * p.vs[1] + (int64_t)k_off * p.vs[2];
+  uint16_t* og = static_cast<uint16_t*>(p.o) + (ragged ? 0 : (int64_t)b * p.os[0]) +
+                 (int64_t)h * p.os[1] + (int64_t)q_off * p.os[2];
+  const int64_t qs2 = p.qs[2], os2 = p.os[2];
+  const int ks2 = (int)p.ks[2], vs2 = (int)p.vs[2];
+
+  const int r1 = min(Lq, r0 + BM);
+  const int kend = p.causal ? min(Lk, r1 + delta) : Lk;
+  int kbeg = p.window > 0 ? max(0, r0 + delta - p.window + 1) : 0;
+  kbeg = (kbeg / BN) * BN;
+  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+
+  const int w0 = r0 + wave * 32 * RB;
+  int qrow[RB];
+  uint32_t khi[RB], key_n[RB];
+  const uint16_t* qa[RB];
+  uint16_t* oa[RB];
+  float* la[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    qrow[rb] = w0 + rb * 32 + l32;
+    const int key_lo = p.window > 0 ? qrow[rb] + delta - p.window + 1 : 0;
+    const int key_hi = p.causal ? min(Lk, qrow[rb] + delta + 1) : Lk;
+    key_n[rb] = (uint32_t)max(key_hi - key_lo, 0);
+    khi[rb] = (uint32_t)(hi * 4 - key_lo);
+    qa[rb] = qg + min(qrow[rb], Lq - 1) * qs2 + hi * 8;  // rows past Lq read the last row (never stored)
+    oa[rb] = og + qrow[rb] * os2 + hi * 4;
+    la[rb] = p.lse;
+    if (p.lse != nullptr)
+      la[rb] = p.lse + (ragged ? (int64_t)h * p.cu_q[p.batch] + q_off + qrow[rb]
+                               : ((int64_t)b * p.hq + h) * p.nq + qrow[rb]);
+  }
+  if (ntiles == 0) {  // no allowed key for any row: O = 0, LSE = -inf
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      if (qrow[rb] < Lq) {
+#pragma unroll
+        for (int c = 0; c < D / 8; c += 2)
+          *reinterpret_cast<u32x2_t*>(oa[rb] + c * 8) = u32x2_t{0, 0};
+        if (hi == 0 && p.lse != nullptr) *la[rb] = kNegInf;
+      }
+    return;
+  }
+  // byte offsets of this lane's 16 bytes in load 0 of a tile (rows wave*4 + lane/16),
+  // columns swizzled as the reads expect; load n adds 16 rows
+  const int ld_row0 = wave * 4 + lane / 16;
+  const uint32_t ld_k0 = (uint32_t)(ld_row0 * ks2 + SW::k(ld_row0, lane % 16) * 8) * 2u;
+  const uint32_t ld_v0 = (uint32_t)(ld_row0 * vs2 + SW::v(ld_row0, lane % 16) * 8) * 2u;
+  // keys that every row of this wave may see: a 64-key tile inside [wlo, whi) needs no mask
+  const int wlast = min(w0 + 32 * RB - 1, Lq - 1);
+  const int wlo = p.window > 0 ? max(0, wlast + delta - p.window + 1) : 0;
+  const int whi = p.causal ? max(0, min(Lk, w0 + delta + 1)) : Lk;
+  const uint32_t k_rd = (uint32_t)(l32 * D + SW::k(l32, hi) * 8) * 2u;
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * hi + (gi >> 2);
+  const uint32_t v_rd =
+      (uint32_t)(vrow * D + SW::v(vrow, (grp & 1) * 2 + ((gi & 3) >> 1)) * 8 + (gi & 1) * 4) * 2u;
+  // wave-uniform inputs of the statement, made visibly uniform for the SGPR constraints
+  auto uni = [](auto x) __attribute__((always_inline)) {
+    if constexpr (sizeof(x) == 8) {
+      const uint64_t w = __builtin_bit_cast(uint64_t, x);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)w);
+      const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
+      return __builtin_bit_cast(decltype(x), ((uint64_t)hi32 << 32) | lo);
+    } else {
+      return __builtin_bit_cast(decltype(x), __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, x)));
+    }
+  };
+  const float sc = uni(MODE == 2 ? 1.0f : fmaxf(p.scale_log2, 1.17549435e-38f));  // > 0: its reciprocal is taken
+  const float cap_in = uni(p.cap_in), cap_c = uni(p.cap_out);
+  const int has_lse = uni((int)(p.lse != nullptr));
+  const uint16_t* const kg_u = uni(kg);
+  const uint16_t* const vg_u = uni(vg);
+  const int ks2_u = uni(ks2), vs2_u = uni(vs2), Lk_u = uni(Lk), kbeg_u = uni(kbeg), ntiles_u = uni(ntiles);
+  const int Lq_u = uni(Lq), wlo_u = uni(wlo), whi_u = uni(whi);
+  const uint32_t lds_u = uni(lds0);
+
+#define ATTN_R2_INPUTS                                                                                        \
+  "{v[0:1]}"(qa[0]), "{v[2:3]}"(qa[1]), "{v[4:5]}"(oa[0]), "{v[6:7]}"(oa[1]), "{v[8:9]}"(la[0]),              \
+      "{v[10:11]}"(la[1]), "{v12}"(khi[0]), "{v13}"(khi[1]), "{v14}"(key_n[0]), "{v15}"(key_n[1]),            \
+      "{v16}"(qrow[0]), "{v17}"(qrow[1]), "{v19}"(ld_k0), "{v20}"(ld_v0), "{v21}"(k_rd),                      \
+      "{v22}"(v_rd), "{s[40:41]}"(kg_u), "{s[42:43]}"(vg_u), "{s44}"(ks2_u), "{s45}"(vs2_u), "{s46}"(Lk_u),   \
+      "{s47}"(kbeg_u), "{s48}"(ntiles_u), "{s49}"(sc), "{s50}"(cap_in), "{s51}"(cap_c),                         \
+      "{s53}"(wave), "{s54}"(Lq_u), "{s55}"(has_lse), "{s56}"(lds_u), "{s57}"(wlo_u),             \
+      "{s58}"(whi_u)
+  if constexpr (BF16 && MODE == 0) {
+    asm volatile(
+#include "prefill_r2_bf16_m0.inc"
+        : : ATTN_R2_INPUTS : ATTN_R2_CLOBBERS);
+  } else if constexpr (BF16 && MODE == 1) {
+    asm volatile(
+#include "prefill_r2_bf16_m1.inc"
+        : : ATTN_R2_INPUTS : ATTN_R2_CLOBBERS);
+  } else if constexpr (BF16) {
+    asm volatile(
+#include "prefill_r2_bf16_m2.inc"
+        : : ATTN_R2_INPUTS : ATTN_R2_CLOBBERS);
+  } else if constexpr (MODE == 0) {
+    asm volatile(
+#include "prefill_r2_f16_m0.inc"
+        : : ATTN_R2_INPUTS : ATTN_R2_CLOBBERS);
+  } else if constexpr (MODE == 1) {
+    asm volatile(
+#include "prefill_r2_f16_m1.inc"
+        : : ATTN_R2_INPUTS : ATTN_R2_CLOBBERS);
+  } else {
+    asm volatile(
+#include "prefill_r2_f16_m2.inc"
+        : : ATTN_R2_INPUTS : ATTN_R2_CLOBBERS);
+  }
+#undef ATTN_R2_INPUTS
+}
+
 // ------------------------------------------------------------------ fp32 inputs ----
 // 32x32x2 fp32 matrix-core products. Q.K^T contracts over head_dim with lanes 0-31
 // taking the first half of D and lanes 32-63 the second; P.V contracts over keys in
@@ -608,6 +793,17 @@ template <int D, bool BF16>
 hipError_t launch16(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = (int64_t)p.q_tiles * p.hq * p.batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if constexpr (D == 128) {
+    const dim3 grid((unsigned)blocks), block(256);
+    if (p.cap_out > 0.0f) {
+      hipLaunchKernelGGL((fwd_r2_kernel<BF16, 2>), grid, block, 0, st, p);
+    } else if (p.causal || p.window > 0 || p.cu_q != nullptr || p.nk % 64 != 0) {
+      hipLaunchKernelGGL((fwd_r2_kernel<BF16, 1>), grid, block, 0, st, p);
+    } else {
+      hipLaunchKernelGGL((fwd_r2_kernel<BF16, 0>), grid, block, 0, st, p);
+    }
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fwd_mfma16_kernel<D, kNW16, kBN16, BF16>), dim3((unsigned)blocks), dim3(kNW16 * 64), 0,
                      st, p);
   return hipGetLastError();

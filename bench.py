@@ -45,7 +45,7 @@ def decode_bytes(case, kv_elt: int, q_elt: int = 2) -> float:
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
-PREFILL_KERNEL = "fwd_mfma16_kernel<128"
+PREFILL_KERNEL = "fwd_r2_kernel<true, 0>"
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
 
 
@@ -53,7 +53,7 @@ def kernel_source_digest() -> str:
     """Digest of the kernel sources: counter-derived traffic is only reported while it matches."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("prefill.hip", "decode.hip", "common.hpp"):
+    for name in ("prefill.hip", "gen_prefill_r2.py", "decode.hip", "common.hpp"):
         with open(os.path.join(HERE, "attention_forward_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -240,7 +240,7 @@ def main(argv=None):
     traffic = load_traffic(PREFILL_KERNEL)
     out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                       "kernel": "fwd_mfma16_kernel<128,...,bf16>",
+                       "kernel": "fwd_r2_kernel<bf16, no mask>",
                        "flops_per_launch": flops}
     if dec:
         dc, _, nbytes = dec
