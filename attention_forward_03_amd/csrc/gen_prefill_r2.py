@@ -69,39 +69,43 @@ HALF = 8192      # bytes of 32 rows
 NKS = 8          # 16-wide k-steps of D
 NDB = 4          # 32-wide blocks of D
 RB = 2           # 32-row query blocks per wave
-PF = 2           # fragments read ahead
+PF = int(os.environ.get("ATTN_GEN_PF", "3"))   # fragments read ahead (ring of 4)
+DMA_EVERY = int(os.environ.get("ATTN_GEN_DMA_EVERY", "4"))  # steps between tile loads
 NSTEP = 32       # products per phase
 FLAG = 6 * TB    # LDS byte offset of the redo flag
 LN2 = "0x3f317218"
 RSRC_FLAGS = "0x20000"     # raw buffer, 32-bit elements
 
-# VGPRs used by the stream
+# VGPRs used by the stream (the epilogue's temporaries reuse the fragment rings)
 S_X, S_Y = 24, 56      # scores of even / odd sub-tiles; row block rb at +16*rb
 P_X, P_Y = 88, 104     # probabilities; (rb, t) at +(rb*2+t)*4
 KF, VF = 120, 136      # fragment rings, 4 slots of 4
-ET = 152               # exp-pipeline temporaries, 4 per sub-tile parity
-LSUB2 = 160            # row sums of odd sub-tiles [rb] (LSUB: even)
-MT = 162               # [rb] raw-score threshold of the per-phase check
-RSC = 164              # 1 / score scale
-LMX = 166              # [rb] running max of the phase row sums
-T0, T1, T2, T3 = 168, 169, 170, 171
-M, MU, L, LSUB, MXA, KBASE = 172, 174, 176, 178, 180, 182
-VNINF, VM2C = 186, 187
-MXS = 194              # [rb]
-VCAPK = 197
-ZERO = 200             # 4 registers
-EP = 208               # 8 epilogue temporaries
-INV = 216              # [rb]
-LT = 218               # [rb]
-KR = 220               # [ks] K read address of fragment ks (buffer 0, rows 0..31)
-VR = 228               # [db] V read address of column block db (buffer 3, rows 0..31)
-KO = 232               # [n] K load lane offset of load n
-VO = 236               # [n] V load lane offset of load n
-NVGPR = 240            # first unused
+NMB = 152              # [rb] 16 copies of -MU: the first S product of a sub-tile starts there
+ET = 184               # exp-pipeline temporaries, 4 per sub-tile parity
+KR = 192               # [ks] K read address of fragment ks (buffer 0, rows 0..31)
+VR = 200               # [db] V read address of column block db (buffer 3, rows 0..31)
+KO = 204               # [n] K load lane offset of load n
+VO = 208               # [n] V load lane offset of load n
+ZERO = 212             # 4 registers
+M, MU, L, LSUB, LSUB2 = 216, 218, 220, 222, 224   # [rb] each; LSUB: row sums of even
+                                                   # sub-tiles, LSUB2: of odd ones
+MT = 226               # [rb] threshold of the per-phase check (scores relative to MU)
+LMX = 228              # [rb] running max of the phase row sums
+MXA, KBASE = 230, 232  # [rb] running row max of a sub-tile; first key offset per lane
+CM = 234               # [rb] softcap: c log2(e) - MU
+MXS = 236              # [rb]
+DELTA, MUOLD = 238, 240  # [rb] change of the reference, its old value (rare block, seed)
+T0, T1, T2, T3 = 242, 243, 244, 245
+VNINF, VM2C, VCAPK = 246, 247, 248
+NVGPR = 249            # first unused
+EP = KF                # 8 epilogue temporaries
+INV = KF + 8           # [rb]
+LT = KF + 10           # [rb]
 
 # SGPRs used by the stream
 SJ, SKT, ST, ST2, ST3 = 60, 61, 62, 63, 64
 SKROW, SVROW, SWB, SKT2, SATT, SUNM = 65, 66, 67, 68, 69, 70
+KSTEP, VSTEP, KEYK, KEYV, SK2, SV2 = 72, 73, 74, 75, 76, 77   # tile-load resource stepping
 SMASK, SMASK2, SEXEC, SPAIR = 80, 82, 84, 86   # pairs
 SCHK = SEXEC             # check of row block 0 (the loop), exec save (the epilogue)
 RSK, RSV = 88, 92        # buffer resources (4 each)
@@ -189,12 +193,9 @@ class Gen:
         rr, e = u // 8, 2 * (u % 8)
         return pbase + (rr * 2 + e // 8) * 4 + (e % 8) // 2
 
-    def fma_elem(self, sbase, g):
-        scale = "1.0" if self.mode == 2 else s(49)
-        self.emit(f"v_fma_f32 {v(self.et + g % 4)}, {v(self.score(sbase, g))}, {scale}, -{v(MU + g // 16)}")
-
-    def exp_elem(self, g):
-        self.emit(f"v_exp_f32 {v(self.et + g % 4)}, {v(self.et + g % 4)}")
+    def exp_elem(self, sbase, g):
+        """P of score g: its register holds the score in log2 units minus the reference."""
+        self.emit(f"v_exp_f32 {v(self.et + g % 4)}, {v(self.score(sbase, g))}")
 
     def cvt_pair(self, pbase, u):
         g0 = 2 * u
@@ -209,25 +210,21 @@ class Gen:
     def exp_unit(self, sbase, pbase, u):
         """All of P for pair u at once (the rare path)."""
         g0 = 2 * u
-        self.fma_elem(sbase, g0)
-        self.fma_elem(sbase, g0 + 1)
-        self.exp_elem(g0)
-        self.exp_elem(g0 + 1)
+        self.exp_elem(sbase, g0)
+        self.exp_elem(sbase, g0 + 1)
         self.emit("s_nop 0")
         self.cvt_pair(pbase, u)
         self.sum_elem(g0)
         self.sum_elem(g0 + 1)
-
-    def softcap(self, src, dst):
-        # s <- c - 2c / (2^(s k) + 1)  (c tanh(s scale / c) in log2 units)
-        self.emit(f"v_mul_f32 {v(T2)}, {v(VCAPK)}, {v(src)}")
-        self.emit(f"v_exp_f32 {v(T2)}, {v(T2)}")
+    def softcap(self, src, dst, rr):
+        # capped - MU = (c log2 e - MU) - 2 c log2 e / (2^x + 1), x = 2 log2(e) s scale / c
+        # (the product with Q pre-scaled by 2 log2(e) scale / c)
+        self.emit(f"v_exp_f32 {v(T2)}, {v(src)}")
         self.emit("s_nop 0")
         self.emit(f"v_add_f32 {v(T2)}, 1.0, {v(T2)}")
         self.emit(f"v_rcp_f32 {v(T2)}, {v(T2)}")
         self.emit("s_nop 0")
-        self.emit(f"v_fma_f32 {v(dst)}, {v(T2)}, {v(VM2C)}, {s(51)}")
-
+        self.emit(f"v_fma_f32 {v(dst)}, {v(T2)}, {v(VM2C)}, {v(CM + rr)}")
     def mask(self, src, dst, rr, e):
         """dst = src if key e of row block rr is allowed, else -inf (KBASE set)."""
         off = (e >> 2) * 8 + (e & 3)
@@ -236,17 +233,17 @@ class Gen:
         self.emit(f"v_cndmask_b32 {v(dst)}, {v(VNINF)}, {v(src)}, vcc")
 
     def seed_max_unit(self, sbase, u, masked):
-        """Max of score pair u into MXA, the scores left as they are (results in epilogue
-        temporaries)."""
+        """Max of score pair u into MXA, the scores left as they are (the capped / masked
+        values go to T0, T1; softcap and mask use T2, T3)."""
         rr, e = u // 8, 2 * (u % 8)
         x = [sbase + 16 * rr + e, sbase + 16 * rr + e + 1]
         for k in range(2):
             if self.mode == 2:
-                self.softcap(x[k], EP + k)
-                x[k] = EP + k
+                self.softcap(x[k], T0 + k, rr)
+                x[k] = T0 + k
             if masked:
-                self.mask(x[k], EP + k, rr, e + k)
-                x[k] = EP + k
+                self.mask(x[k], T0 + k, rr, e + k)
+                x[k] = T0 + k
         self.emit(f"v_max3_f32 {v(MXA + rr)}, {v(MXA + rr)}, {v(x[0])}, {v(x[1])}")
 
     def mask_elem(self, sbase, g, masked):
@@ -254,7 +251,7 @@ class Gen:
         rr, e = g // 16, g % 16
         r = sbase + 16 * rr + e
         if self.mode == 2:
-            self.softcap(r, r)
+            self.softcap(r, r, rr)
         if masked:
             self.mask(r, r, rr, e)
 
@@ -268,8 +265,7 @@ class Gen:
         self.emit("s_nop 3")
 
     def exchange_max(self):
-        """MXS[rb] = max of MXA[rb] over lanes l and l^32 (the two halves of a row), in log2
-        units (MXA holds raw scores)."""
+        """MXS[rb] = max of MXA[rb] over lanes l and l^32 (the two halves of a row)."""
         self.emit(f"v_mov_b32 {v(T0)}, {v(MXA)}")
         self.emit(f"v_mov_b32 {v(T1)}, {v(MXA)}")
         self.emit(f"v_mov_b32 {v(T2)}, {v(MXA + 1)}")
@@ -280,15 +276,13 @@ class Gen:
         self.emit("s_nop 1")
         self.emit(f"v_max_f32 {v(MXS)}, {v(T0)}, {v(T1)}")
         self.emit(f"v_max_f32 {v(MXS + 1)}, {v(T2)}, {v(T3)}")
-        if self.mode != 2:
-            self.emit(f"v_mul_f32 {v(MXS)}, {s(49)}, {v(MXS)}")
-            self.emit(f"v_mul_f32 {v(MXS + 1)}, {s(49)}, {v(MXS + 1)}")
 
     # ------------------------------------------------------------------ tile loads
     def rsrc(self, which, key_sreg):
-        """Buffer resource for the tile of K ('k') or V ('v') starting at key key_sreg:
+        """Buffer resource for the tile of K ('k') or V ('v') starting at key key_sreg (< Lk):
         base at that key, records up to the last key (so rows past Lk read as zero)."""
-        base, stride, r = (40, 44, RSK) if which == "k" else (42, 45, RSV)
+        base, stride, r, key = (40, 44, RSK, KEYK) if which == "k" else (42, 45, RSV, KEYV)
+        self.emit(f"s_mov_b32 {s(key)}, {s(key_sreg)}")
         self.emit(f"s_mul_i32 {s(SPAIR)}, {s(key_sreg)}, {s(stride)}")
         self.emit(f"s_mul_hi_u32 {s(SPAIR + 1)}, {s(key_sreg)}, {s(stride)}")
         self.emit(f"s_lshl_b64 {s(SPAIR, 2)}, {s(SPAIR, 2)}, 1")
@@ -301,51 +295,53 @@ class Gen:
         self.emit(f"s_lshl_b32 {s(r + 2)}, {s(r + 2)}, 1")
         self.emit(f"s_mov_b32 {s(r + 3)}, {RSRC_FLAGS}")
 
-    def load(self, which, n, buf):
-        """Load n (0..3) of this wave: 16 bytes per lane of rows (wave + 4 n)*4 + lane/16 into
-        the 1 KiB block (wave + 4 n) of LDS buffer buf (0..5)."""
-        off, r = (KO, RSK) if which == "k" else (VO, RSV)
+    def advance_rsrc(self, which):
+        """The resource moves on by one tile; past the last key it holds no records (its
+        loads read zeros and fetch nothing)."""
+        r, key, step, s2 = (RSK, KEYK, KSTEP, SK2) if which == "k" else (RSV, KEYV, VSTEP, SV2)
+        self.emit(f"s_add_u32 {s(key)}, {s(key)}, 64")
+        self.emit(f"s_add_u32 {s(r)}, {s(r)}, {s(step)}")
+        self.emit(f"s_addc_u32 {s(r + 1)}, {s(r + 1)}, 0")
+        self.emit(f"s_sub_i32 {s(ST3)}, {s(46)}, {s(key)}")
+        self.emit(f"s_max_i32 {s(ST3)}, {s(ST3)}, 0")
+        self.emit(f"s_min_i32 {s(ST3)}, {s(ST3)}, 64")
+        self.emit(f"s_mul_i32 {s(r + 2)}, {s(ST3)}, {s(s2)}")
+
+    def load_m0(self, n, buf):
+        """M0 for load n (0..3) of this wave: the 1 KiB block (wave + 4 n) of LDS buffer buf."""
         self.emit(f"s_add_u32 m0, {s(SWB)}, {buf * TB + 4096 * n}")
-        self.emit("s_nop 0")
+
+    def load_issue(self, which, n):
+        """16 bytes per lane of tile rows (wave + 4 n)*4 + lane/16 into the block at M0."""
+        off, r = (KO, RSK) if which == "k" else (VO, RSV)
         self.emit(f"buffer_load_dwordx4 {v(off + n)}, {s(r, 4)}, 0 offen lds")
 
-    def tile_key(self, plus):
-        """ST = first key of tile min(j + plus, n - 1)."""
-        self.emit(f"s_sub_u32 {s(ST2)}, {s(48)}, 1")
-        self.emit(f"s_add_u32 {s(ST)}, {s(SJ)}, {plus}")
-        self.emit(f"s_min_u32 {s(ST)}, {s(ST)}, {s(ST2)}")
-        self.emit(f"s_lshl_b32 {s(ST)}, {s(ST)}, 6")
-        self.emit(f"s_add_u32 {s(ST)}, {s(ST)}, {s(47)}")
+    def load(self, which, n, buf):
+        self.load_m0(n, buf)
+        self.emit("s_nop 0")
+        self.load_issue(which, n)
 
     # ------------------------------------------------------------------ one phase
     def tail_ops(self, st, prev):
         """The part of the previous soft phase's pipeline that runs in this phase's first
-        steps: FMA of score 31, exp2 of 30 and 31, packing of pairs 14 and 15, sums of 28..31,
-        then l += the previous phase's row sums (and their running max)."""
+        steps: exp2 of score 31, packing of pair 15, sums of 30 and 31, then l += the previous
+        phase's row sums (and their running max)."""
         sx, px, et, lsub = prev
         keep = (self.et, self.lsub)
         self.et, self.lsub = et, lsub
         if st == 0:
-            self.fma_elem(sx, 31)
-            self.exp_elem(30)
-            self.cvt_pair(px, 14)
-            self.sum_elem(28)
-        elif st == 1:
-            self.exp_elem(31)
-            self.sum_elem(29)
-        elif st == 2:
-            self.cvt_pair(px, 15)
+            self.exp_elem(sx, 31)
             self.sum_elem(30)
-        elif st == 3:
+        elif st == 1:
+            self.cvt_pair(px, 15)
             self.sum_elem(31)
-        elif st == 4:
+        elif st == 2:
             for rb in range(RB):
                 self.emit(f"v_add_f32 {v(L + rb)}, {v(L + rb)}, {v(lsub + rb)}")
-        elif st == 5:
+        elif st == 3:
             for rb in range(RB):
                 self.emit(f"v_max_f32 {v(LMX + rb)}, {v(LMX + rb)}, {v(lsub + rb)}")
         self.et, self.lsub = keep
-
     def phase(self, *, s_next, pv, soft, masked, track, maxonly, kofs, vofs, knofs, vnofs, dma, sx, sy, px, py,
               kt_sreg, tail=None, advance=()):
         """Phase X(i): S(i+1) into sy (K at kofs), O += V^T py^T (V at vofs), mask / max /
@@ -360,22 +356,31 @@ class Gen:
         advance = list(advance)
         for st in range(NSTEP):
             q = st // 2
+            dma_now = None
+            if dma is not None and st % DMA_EVERY == 0 and st // DMA_EVERY < 8:
+                n = st // DMA_EVERY
+                if n < 4:
+                    dma_now = ("k", n)
+                    self.load_m0(n, dma[0])
+                elif dma[1] is not None:
+                    dma_now = ("v", n - 4)
+                    self.load_m0(n - 4, dma[1])
             if st % 2 == 0:
                 ks, rb = q // RB, q % RB
                 if s_next:
                     if rb == 0 and ks + PF < NKS:
                         self.read_k(kofs, ks + PF, (ks + PF) % 4, ("k", ks + PF))
                     self.wait_for(("k", ks))
-                    c = "0" if ks == 0 else v(sy + 16 * rb, 16)
+                    if ks:
+                        c = v(sy + 16 * rb, 16)
+                    else:
+                        c = "0" if self.mode == 2 else v(NMB + 16 * rb, 16)
                     self.mfma(v(sy + 16 * rb, 16), v(KF + 4 * (ks % 4), 4), a(128 + (rb * NKS + ks) * 4, 4), c)
                 if knofs is not None and rb == 0 and ks >= NKS - PF:
                     g = ks - (NKS - PF)
                     self.read_k(knofs, g, g, ("kn", g))
-                if dma is not None and q < 8:
-                    if q < 4:
-                        self.load("k", q, dma[0])
-                    elif dma[1] is not None:
-                        self.load("v", q - 4, dma[1])
+                if dma_now is not None:
+                    self.load_issue(*dma_now)
             else:
                 f, rb = q // RB, q % RB
                 if pv:
@@ -404,20 +409,18 @@ class Gen:
                 if st == 0 and maxonly:
                     # without the products of V, the scores of the last steps are younger
                     self.emit("s_nop 4")
-                # step g: mask score g (odd g: max of the pair); g+1: FMA; g+2: exp2;
-                # 2u+4: pack pair u and add score 2u to the row sum; 2u+5: add score 2u+1
+                # step g: mask score g (odd g: max of the pair); g+1: exp2; g+2: add to the
+                # row sum; 2u+3: pack pair u
                 self.mask_elem(sx, st, masked)
                 if track and st % 2 == 1:
                     self.max_pair(sx, st // 2)
                 if not maxonly:
                     if st >= 1:
-                        self.fma_elem(sx, st - 1)
+                        self.exp_elem(sx, st - 1)
                     if st >= 2:
-                        self.exp_elem(st - 2)
-                    if st >= 4:
-                        if st % 2 == 0:
-                            self.cvt_pair(px, (st - 4) // 2)
-                        self.sum_elem(st - 4)
+                        self.sum_elem(st - 2)
+                    if st >= 3 and st % 2 == 1:
+                        self.cvt_pair(px, (st - 3) // 2)
                     if track and st == 16:
                         self.emit(f"v_cmp_gt_f32_e64 {s(SCHK, 2)}, {v(MXA)}, {v(MT)}")
             if advance and 1 <= st <= 28:
@@ -433,20 +436,41 @@ class Gen:
             self.emit(f"s_or_b64 {s(SMASK, 2)}, {s(SMASK, 2)}, {s(SCHK, 2)}")
             self.emit(f"s_cbranch_scc1 {rare}")
             self.emit(f"{ret}:")
-            self.rare.append((rare, ret, sx, px, self.et, self.lsub))
+            self.rare.append((rare, ret, sx, sy, px, self.et, self.lsub))
         if soft and maxonly:
             for rb in range(RB):
                 self.emit(f"v_max_f32 {v(M + rb)}, {v(M + rb)}, {v(MXA + rb)}")
         return (sx, px, self.et, self.lsub)
 
     def thresholds(self):
-        """MU = reference (0 for a row without one), MT = raw-score threshold of the check."""
+        """From M: MU = reference (0 for a row without one); MT = threshold of the per-phase
+        check on scores relative to MU (the slack; -inf without a reference, so that any
+        unmasked key trips it); NMB = -MU, the start of the S products; CM (softcap)."""
         for rb in range(RB):
             self.emit(f"v_cmp_eq_f32 vcc, {v(VNINF)}, {v(M + rb)}")
             self.emit(f"v_cndmask_b32_e64 {v(MU + rb)}, {v(M + rb)}, 0, vcc")
-            self.emit(f"v_add_f32 {v(MT + rb)}, {self.slack_bits}, {v(M + rb)}")
-            self.emit(f"v_mul_f32 {v(MT + rb)}, {v(MT + rb)}, {v(RSC)}")
+            self.emit(f"v_mov_b32 {v(MT + rb)}, {self.slack_bits}")
+            self.emit(f"v_cndmask_b32 {v(MT + rb)}, {v(MT + rb)}, {v(VNINF)}, vcc")
+            if self.mode == 2:
+                self.emit(f"v_sub_f32 {v(CM + rb)}, {s(51)}, {v(MU + rb)}")
+            else:
+                self.emit(f"v_sub_f32 {v(NMB + 16 * rb)}, 0, {v(MU + rb)}")
+                for i in range(1, 16):
+                    self.emit(f"v_mov_b32 {v(NMB + 16 * rb + i)}, {v(NMB + 16 * rb)}")
 
+    def shift_scores(self, sbase):
+        """Scores of a sub-tile relative to the new reference: minus DELTA (= MU - MUOLD)."""
+        for g in range(32):
+            r = self.score(sbase, g)
+            self.emit(f"v_sub_f32 {v(r)}, {v(r)}, {v(DELTA + g // 16)}")
+
+    def new_reference(self):
+        """thresholds() after M changed, with DELTA = MU - MUOLD."""
+        for rb in range(RB):
+            self.emit(f"v_mov_b32 {v(MUOLD + rb)}, {v(MU + rb)}")
+        self.thresholds()
+        for rb in range(RB):
+            self.emit(f"v_sub_f32 {v(DELTA + rb)}, {v(MU + rb)}, {v(MUOLD + rb)}")
     def set_flag(self):
         self.emit(f"v_mov_b32 {v(T0)}, 1")
         self.emit(f"v_mov_b32 {v(T1)}, {FLAG}")
@@ -454,13 +478,15 @@ class Gen:
         self.emit(f"ds_write_b32 {v(T1)}, {v(T0)}")
         self.emit("s_waitcnt lgkmcnt(0)")
 
-    def rare_block(self, rare, ret, sx, px, et, lsub):
+    def rare_block(self, rare, ret, sx, sy, px, et, lsub):
         """Out of line. Rows whose first unmasked keys arrived take the sub-tile max as their
-        reference and P(i) so far is formed again; a row max past a finite reference by more
-        than the slack sets the redo flag (and the checks are switched off for the pass)."""
+        reference: the scores of this sub-tile and of the next one (already in sy) move to
+        it and P so far is formed again; a row max past a finite reference by more than the
+        slack sets the redo flag (and the checks are switched off for the pass)."""
         self.et, self.lsub = et, lsub
         no_risk, back = self.uniq("norisk"), self.uniq("back")
         self.emit(f"{rare}:")
+        self.gap()  # the S products of the next sub-tile have just been issued
         self.exchange_max()
         self.emit(f"s_mov_b64 {s(SMASK, 2)}, 0")
         self.emit(f"s_mov_b64 {s(SMASK2, 2)}, 0")
@@ -470,8 +496,8 @@ class Gen:
             self.emit(f"s_and_b64 {s(SPAIR, 2)}, {s(SPAIR, 2)}, vcc")            # first
             self.emit(f"s_or_b64 {s(SMASK, 2)}, {s(SMASK, 2)}, {s(SPAIR, 2)}")
             self.emit(f"v_cndmask_b32_e64 {v(M + rb)}, {v(M + rb)}, {v(MXS + rb)}, {s(SPAIR, 2)}")
-            self.emit(f"v_add_f32 {v(T0)}, {self.slack_bits}, {v(M + rb)}")
-            self.emit(f"v_cmp_gt_f32_e64 {s(SPAIR, 2)}, {v(MXS + rb)}, {v(T0)}")
+            self.emit(f"v_mov_b32 {v(T1)}, {self.slack_bits}")
+            self.emit(f"v_cmp_lt_f32_e64 {s(SPAIR, 2)}, {v(T1)}, {v(MXS + rb)}")
             self.emit(f"s_andn2_b64 {s(SPAIR, 2)}, {s(SPAIR, 2)}, vcc")          # risk (m was finite)
             self.emit(f"s_or_b64 {s(SMASK2, 2)}, {s(SMASK2, 2)}, {s(SPAIR, 2)}")
         self.emit(f"s_cmp_eq_u64 {s(SMASK2, 2)}, 0")
@@ -484,21 +510,19 @@ class Gen:
         self.emit(f"{no_risk}:")
         self.emit(f"s_cmp_eq_u64 {s(SMASK, 2)}, 0")
         self.emit(f"s_cbranch_scc1 {back}")
-        self.thresholds()
+        self.new_reference()
+        self.shift_scores(sx)
+        if self.mode != 2:
+            self.shift_scores(sy)   # softcap: the next sub-tile is capped against CM later
         self.emit(f"v_mov_b32 {v(lsub)}, 0")
         self.emit(f"v_mov_b32 {v(lsub + 1)}, 0")
         # everything the pipeline did up to the last step, against the new reference
-        for u in range(14):
+        for u in range(15):
             self.exp_unit(sx, px, u)
-        for g in (28, 29):
-            self.fma_elem(sx, g)
-        for g in (28, 29):
-            self.exp_elem(g)
-        self.fma_elem(sx, 30)
+        self.exp_elem(sx, 30)
         self.emit("s_nop 0")
         self.emit(f"{back}:")
         self.emit(f"s_branch {ret}")
-
     # ------------------------------------------------------------------ a pass
     def advance_groups(self, exact, first):
         """Scalar work that prepares tile j+1 (first=False) or tile 0 (first=True): buffer
@@ -514,9 +538,9 @@ class Gen:
 
         if not first:
             out.append([f"s_add_u32 {s(SJ)}, {s(SJ)}, 1", f"s_add_u32 {s(SKT)}, {s(SKT)}, 64"])
-        grab(lambda: (self.tile_key(2), self.rsrc("k", ST)))
+        grab(lambda: self.advance_rsrc("k"))
         if not exact:
-            grab(lambda: (self.tile_key(1), self.rsrc("v", ST)))
+            grab(lambda: self.advance_rsrc("v"))
             if self.mode >= 1:
                 # plain iff every row has its reference already (kt > s57: a row's first
                 # allowed key lies in an earlier tile) and no key of [kt, kt + 64) is masked
@@ -593,8 +617,7 @@ class Gen:
             for rb in range(RB):
                 self.emit(f"v_mov_b32 {v(LMX + rb)}, 0")
         self.emit("s_waitcnt vmcnt(0)")
-        self.tile_key(1)
-        self.rsrc("k", ST)
+        self.advance_rsrc("k")
         for n in range(4):
             self.load("k", n, 1)
         self.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
@@ -603,9 +626,7 @@ class Gen:
             # P(-1) = 0, and the pipeline "tail" of sub-tile -1 produces zeros
             for r in range(P_Y, P_Y + 16):
                 self.emit(f"v_mov_b32 {v(r)}, 0")
-            self.emit(f"v_mov_b32 {v(ET + 4)}, 0")
-            self.emit(f"v_mov_b32 {v(ET + 5)}, 0")
-            self.emit(f"v_mov_b32 {v(ET + 6)}, {v(VNINF)}")
+            self.emit(f"v_mov_b32 {v(ET + 6)}, 0")
             self.emit(f"v_mov_b32 {v(S_Y + 31)}, {v(VNINF)}")
             self.emit(f"v_mov_b32 {v(LSUB2)}, 0")
             self.emit(f"v_mov_b32 {v(LSUB2 + 1)}, 0")
@@ -630,9 +651,13 @@ class Gen:
             for u in range(16):
                 self.seed_max_unit(S_X, u, self.mode >= 1)
             self.exchange_max()
+            # the sub-tile max is relative to the reference S(0) was formed against
             for rb in range(RB):
-                self.emit(f"v_max_f32 {v(M + rb)}, {v(M + rb)}, {v(MXS + rb)}")
-            self.thresholds()
+                self.emit(f"v_add_f32 {v(T0)}, {v(MXS + rb)}, {v(MU + rb)}")
+                self.emit(f"v_max_f32 {v(M + rb)}, {v(M + rb)}, {v(T0)}")
+            self.new_reference()
+            if self.mode != 2:
+                self.shift_scores(S_X)
         loop_state = list(self.lds)
         exits = []
         self.emit(f"L_{tag}tile_%=:")
@@ -692,14 +717,14 @@ class Gen:
         e(f"v_mul_f32 {v(VM2C)}, -2.0, {s(51)}")
         e(f"v_mov_b32 {v(VCAPK)}, 0x4038aa3b")
         e(f"v_mul_f32 {v(VCAPK)}, {s(50)}, {v(VCAPK)}")
-        if self.mode == 2:
-            e(f"v_mov_b32 {v(RSC)}, 1.0")
-        else:
-            e(f"v_rcp_f32 {v(RSC)}, {s(49)}")
         e(f"s_lshl_b32 {s(SWB)}, {s(53)}, 10")
         e(f"s_add_u32 {s(SWB)}, {s(SWB)}, {s(56)}")
         e(f"s_lshl_b32 {s(SKROW)}, {s(44)}, 5")
         e(f"s_lshl_b32 {s(SVROW)}, {s(45)}, 5")
+        e(f"s_lshl_b32 {s(SK2)}, {s(44)}, 1")
+        e(f"s_lshl_b32 {s(SV2)}, {s(45)}, 1")
+        e(f"s_lshl_b32 {s(KSTEP)}, {s(44)}, 7")
+        e(f"s_lshl_b32 {s(VSTEP)}, {s(45)}, 7")
         # per-lane LDS read addresses (swizzle applied) and load offsets
         for ks in range(NKS):
             e(f"v_xor_b32 {v(KR + ks)}, {ks << 5}, {v(21)}")
@@ -715,10 +740,27 @@ class Gen:
             e(f"v_add_u32 {v(VO + n)}, {s(ST3)}, {v(20)}")
         for r in range(ZERO, ZERO + 4):
             e(f"v_mov_b32 {v(r)}, 0")
-        # Q fragments straight into AGPRs
+        # Q fragments, pre-scaled (by the score scale in log2 units, or for the softcap by the
+        # argument factor of its exponential) and rounded back to 16 bits, into AGPRs
         for rb in range(RB):
             for ks in range(NKS):
-                e(f"global_load_dwordx4 {a(128 + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
+                e(f"global_load_dwordx4 {v(S_X + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
+        e("s_waitcnt vmcnt(0)")
+        qscale = v(VCAPK) if self.mode == 2 else s(49)
+        for i in range(RB * NKS * 4):
+            x = S_X + i
+            if self.bf16:
+                e(f"v_lshlrev_b32 {v(T0)}, 16, {v(x)}")
+                e(f"v_and_b32 {v(T1)}, 0xffff0000, {v(x)}")
+            else:
+                e(f"v_cvt_f32_f16 {v(T0)}, {v(x)}")
+                e(f"v_lshrrev_b32 {v(T1)}, 16, {v(x)}")
+                e(f"v_cvt_f32_f16 {v(T1)}, {v(T1)}")
+            e(f"v_mul_f32 {v(T0)}, {qscale}, {v(T0)}")
+            e(f"v_mul_f32 {v(T1)}, {qscale}, {v(T1)}")
+            cvt = "v_cvt_pk_bf16_f32" if self.bf16 else "v_cvt_pk_f16_f32"
+            e(f"{cvt} {v(T2)}, {v(T0)}, {v(T1)}")
+            e(f"v_accvgpr_write_b32 {a(128 + i)}, {v(T2)}")
         # redo flag = 0 (wave 0), ordered before any write of 1 by the first barrier
         skip = self.uniq("noinit")
         e(f"s_cmp_lg_u32 {s(53)}, 0")
@@ -732,6 +774,7 @@ class Gen:
         for rb in range(RB):
             e(f"v_mov_b32 {v(M + rb)}, {v(VNINF)}")
         e("L_attempt_%=:")
+        self.thresholds()
         for rb in range(RB):
             e(f"v_mov_b32 {v(L + rb)}, 0")
         e("s_nop 1")
@@ -754,6 +797,7 @@ class Gen:
         e(f"s_mov_b32 {s(SATT)}, 1")
         for rb in range(RB):
             e(f"v_mov_b32 {v(M + rb)}, {v(VNINF)}")
+        self.thresholds()
         self.run_pass(exact=True)
         e("s_barrier")
         e("s_branch L_attempt_%=")

@@ -419,6 +419,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
 // reference by up to a slack (15 for fp16 P, whose range ends at 2^16; 40 for bf16). A
 // pass in which that fails for some row flags the workgroup; it then takes the exact row
 // maxima in a pass of S products only and runs the attention pass again against them.
+// Q is scaled by sc (the softmax scale in log2 units) once, when it is loaded, and each
+// sub-tile's S product starts from -m instead of 0, so the product delivers s sc - m and
+// P = 2^S takes a single instruction per score. With a softcap, Q is scaled by the
+// argument factor of the cap's exponential instead, and the cap's last FMA subtracts m.
 // Tiles of 64 keys with no mask, once every row of the wave has its reference, take a
 // body without row maxima: the max of each phase's row sums stands guard (a P past the
 // slack makes its sum pass it). The others take a body with the mask and the row maxima,
