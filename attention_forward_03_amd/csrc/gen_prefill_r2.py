@@ -69,8 +69,8 @@ HALF = 8192      # bytes of 32 rows
 NKS = 8          # 16-wide k-steps of D
 NDB = 4          # 32-wide blocks of D
 RB = 2           # 32-row query blocks per wave
-PF = int(os.environ.get("ATTN_GEN_PF", "3"))   # fragments read ahead (ring of 4)
-DMA_EVERY = int(os.environ.get("ATTN_GEN_DMA_EVERY", "4"))  # steps between tile loads
+PF = 3           # fragments read ahead (ring of 4)
+DMA_EVERY = 4    # steps between tile loads
 NSTEP = 32       # products per phase
 FLAG = 6 * TB    # LDS byte offset of the redo flag
 LN2 = "0x3f317218"
@@ -355,7 +355,7 @@ class Gen:
         self.et, self.lsub = ET + 4 * par, (LSUB, LSUB2)[par]
         advance = list(advance)
         for st in range(NSTEP):
-            q = st // 2
+            is_s, idx, rb = st % 2 == 0, st // 4, (st // 2) % 2
             dma_now = None
             if dma is not None and st % DMA_EVERY == 0 and st // DMA_EVERY < 8:
                 n = st // DMA_EVERY
@@ -365,12 +365,14 @@ class Gen:
                 elif dma[1] is not None:
                     dma_now = ("v", n - 4)
                     self.load_m0(n - 4, dma[1])
-            if st % 2 == 0:
-                ks, rb = q // RB, q % RB
+            if is_s:
+                ks = idx
                 if s_next:
                     if rb == 0 and ks + PF < NKS:
                         self.read_k(kofs, ks + PF, (ks + PF) % 4, ("k", ks + PF))
-                    self.wait_for(("k", ks))
+                    if ks % 2 == 0 and rb == 0:
+                        # one wait per two fragments (each wait takes an issue slot)
+                        self.wait_for(("k", ks + 1))
                     if ks:
                         c = v(sy + 16 * rb, 16)
                     else:
@@ -382,11 +384,12 @@ class Gen:
                 if dma_now is not None:
                     self.load_issue(*dma_now)
             else:
-                f, rb = q // RB, q % RB
+                f = idx
                 if pv:
                     if rb == 0 and f + PF < 2 * NDB:
                         self.read_v(vofs, f + PF, (f + PF) % 4, ("v", f + PF))
-                    self.wait_for(("v", f))
+                    if f % 2 == 0 and rb == 0:
+                        self.wait_for(("v", f + 1))
                     t, db = f // NDB, f % NDB
                     blk = a((rb * NDB + db) * 16, 16)
                     self.mfma(blk, v(VF + 4 * (f % 4), 4), v(py + (rb * 2 + t) * 4, 4), blk)
