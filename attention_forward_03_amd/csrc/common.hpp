@@ -100,6 +100,16 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, cons
                : "memory");
 }
 
+// The same load with the nontemporal hint: for data read once (the paged KV cache in
+// decode), which then does not displace reused lines from the caches. A streaming read
+// of HBM measured 7.0 TB/s with the hint against 6.2 TB/s without on MI355X.
+__device__ __forceinline__ void load_lds16_stream(const void* base, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base),
+               "s"(lds)
+               : "memory");
+}
+
 // Wait (visibly to the compiler) for this wave's ordinary global loads, so that the
 // hot loops that follow start with no compiler-tracked load outstanding and no wait
 // for them is placed inside the loop (where it would also stall on prefetches).

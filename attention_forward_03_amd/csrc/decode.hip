@@ -185,8 +185,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
     for (int i = 0; i < PL::LOADS; ++i) {
       const int shift = valid >= kPage ? 0 : (min(ld_row[i], valid - 1) - ld_row[i]) * (int)tok_bytes;
-      load_lds16(kc + base, (uint32_t)(ld_k[i] + shift), st + i * 1024);
-      load_lds16(vc + base, (uint32_t)(ld_v[i] + shift), st + PL::HALF + i * 1024);
+      load_lds16_stream(kc + base, (uint32_t)(ld_k[i] + shift), st + i * 1024);
+      load_lds16_stream(vc + base, (uint32_t)(ld_v[i] + shift), st + PL::HALF + i * 1024);
     }
   };
 
