@@ -365,10 +365,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
 }
 
 #ifndef ATTN_DECODE_STAGES
-#define ATTN_DECODE_STAGES 3
+#define ATTN_DECODE_STAGES 2
 #endif
 #ifndef ATTN_DECODE_STAGES_FP8
-#define ATTN_DECODE_STAGES_FP8 3
+#define ATTN_DECODE_STAGES_FP8 2
 #endif
 // LDS ring depth per wave: fewer stages leave room for more resident waves, which on
 // this memory system pays more than a deeper prefetch per wave (measured).
