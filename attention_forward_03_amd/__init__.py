@@ -194,3 +194,34 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                                  _stream_handle(q.device))
     _lib.check(status)
     return (o, lse) if return_lse else o
+
+
+# ----------------------------------------------------------------- measurement ----
+def probe_mfma(operands: torch.Tensor, clocks: torch.Tensor, sink: torch.Tensor, *, workgroups: int, iters: int,
+               valu_mix: bool = False) -> None:
+    """Enqueue the matrix-core probe (attn_probe_mfma): operands uint32 [256*8] (as int32),
+    clocks int64 [2*workgroups], sink float32 [256*workgroups], all on one GPU."""
+    _require_cuda(operands, clocks, sink)
+    if operands.numel() < 256 * 8 or clocks.numel() < 2 * workgroups or sink.numel() < 256 * workgroups:
+        raise ValueError("probe_mfma: buffers too small")
+    L = _lib.lib()
+    _lib.check(L.attn_probe_mfma(_ptr(operands), workgroups, iters, 1 if valu_mix else 0, _ptr(clocks), _ptr(sink),
+                                 _stream_handle(operands.device)))
+
+
+def probe_hbm_read(buf: torch.Tensor, sink: torch.Tensor, *, workgroups: int) -> None:
+    """Enqueue the streaming-read probe (attn_probe_hbm_read) over all of buf's bytes."""
+    _require_cuda(buf, sink)
+    if sink.numel() < workgroups:
+        raise ValueError("probe_hbm_read: sink too small")
+    L = _lib.lib()
+    _lib.check(L.attn_probe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
+                                     _stream_handle(buf.device)))
+
+
+def flush_caches(buf: torch.Tensor) -> None:
+    """Enqueue a write of zeros over all of buf (attn_flush_caches)."""
+    _require_cuda(buf)
+    L = _lib.lib()
+    _lib.check(L.attn_flush_caches(_ptr(buf), buf.numel() * buf.element_size(), _stream_handle(buf.device)))
+

@@ -278,4 +278,40 @@ attn_status_t attn_decode_paged(const attn_decode_args_t* a, const void* q, cons
   return ok();
 }
 
+attn_status_t attn_probe_mfma(const uint32_t* operands, int32_t workgroups, int32_t iters, int32_t valu_mix,
+                              uint64_t* clocks, float* sink, void* stream) {
+  if (operands == nullptr || clocks == nullptr || sink == nullptr)
+    return fail(ATTN_ERROR_INVALID_VALUE, "operands, clocks and sink must be non-NULL");
+  if (workgroups < 1 || workgroups > 65535 || iters < 1 || (valu_mix != 0 && valu_mix != 1))
+    return fail(ATTN_ERROR_INVALID_VALUE, "workgroups in [1, 65535], iters >= 1 and valu_mix 0 or 1 required");
+  if ((reinterpret_cast<uintptr_t>(operands) & 3u) || (reinterpret_cast<uintptr_t>(clocks) & 7u) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(ATTN_ERROR_INVALID_VALUE, "operands and sink must be 4-byte, clocks 8-byte aligned");
+  hipError_t e = attn::launch_probe_mfma(operands, workgroups, iters, valu_mix, clocks, sink,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+attn_status_t attn_probe_hbm_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "buf and sink must be non-NULL");
+  if (workgroups < 1 || workgroups > 65535) return fail(ATTN_ERROR_INVALID_VALUE, "workgroups in [1, 65535]");
+  if (bytes == 0 || bytes % ((size_t)workgroups * 32768u) != 0)
+    return fail(ATTN_ERROR_INVALID_VALUE, "bytes must be a non-zero multiple of 32768 * workgroups");
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(ATTN_ERROR_INVALID_VALUE, "buf must be 16-byte and sink 4-byte aligned");
+  hipError_t e = attn::launch_probe_hbm_read(buf, (int64_t)bytes, workgroups, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+attn_status_t attn_flush_caches(void* buf, size_t bytes, void* stream) {
+  if (buf == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "buf must be non-NULL");
+  if (bytes == 0 || bytes % 16 != 0 || !aligned16(buf))
+    return fail(ATTN_ERROR_INVALID_VALUE, "buf must be 16-byte aligned and bytes a non-zero multiple of 16");
+  hipError_t e = attn::launch_flush(buf, (int64_t)bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -51,4 +51,9 @@ int fwd_block_rows(int dtype, int head_dim);
 hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t stream);
 
+hipError_t launch_probe_mfma(const uint32_t* operands, int workgroups, int iters, int valu_mix, uint64_t* clocks,
+                             float* sink, hipStream_t stream);
+hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, int workgroups, uint32_t* sink, hipStream_t stream);
+hipError_t launch_flush(void* buf, int64_t bytes, hipStream_t stream);
+
 }  // namespace attn

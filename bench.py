@@ -115,6 +115,52 @@ def load_traffic(kernel_substr):
     return round(sum(tot)) if tot else None
 
 
+def random_bf16_words(seed: int, n_words: int) -> "np.ndarray":
+    """n_words 32-bit words, each two bf16 values (truncated) of a standard normal draw."""
+    x = np.random.default_rng(seed).standard_normal(2 * n_words).astype(np.float32)
+    b = x.view(np.uint32) >> 16
+    return (b[0::2] | (b[1::2] << 16)).astype(np.uint32)
+
+
+def measure_peaks(attn, torch, dev) -> dict:
+    """The machine's own compute and bandwidth ceilings, from the library's probes
+    (attn_probe_mfma, attn_probe_hbm_read): clocks are not locked, and the clock the
+    matrix cores hold depends on the power their operands draw."""
+    wg, iters = 256, 20000
+    rand = torch.from_numpy(random_bf16_words(7, 256 * 8).view(np.int32)).to(dev)
+    zero = torch.zeros_like(rand)
+    clocks = torch.zeros(2 * wg, dtype=torch.int64, device=dev)
+    sink = torch.empty(256 * wg, dtype=torch.float32, device=dev)
+    out = {}
+    for name, ops, mix in (("zero_operands", zero, False), ("random_operands", rand, False),
+                           ("random_operands_softmax_vector_mix", rand, True)):
+        attn.probe_mfma(ops, clocks, sink, workgroups=wg, iters=200, valu_mix=mix)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        attn.probe_mfma(ops, clocks, sink, workgroups=wg, iters=iters, valu_mix=mix)
+        e[1].record()
+        torch.cuda.synchronize()
+        ms = e[0].elapsed_time(e[1])
+        c = clocks.cpu().numpy().reshape(wg, 2).astype(np.float64)
+        out[name] = {"tflops": round(wg * 4 * 32 * iters * 32768.0 / (ms * 1e-3) / 1e12, 1),
+                     "clock_ghz": round(c[:, 0].sum() / (c[:, 1].sum() / 100e6) / 1e9, 3)}
+    nbytes, rwg = 4 << 30, 8192
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    rsink = torch.empty(rwg, dtype=torch.int32, device=dev)
+    attn.probe_hbm_read(buf, rsink, workgroups=rwg)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(3):
+        attn.probe_hbm_read(buf, rsink, workgroups=rwg)
+    e[1].record()
+    torch.cuda.synchronize()
+    gbps = 3 * nbytes / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_32x32x16_one_wave_per_simd": out, "hbm_read_nontemporal_gbps": round(gbps, 1)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +170,9 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true",
                     help="run only the decode (per-kernel counter passes; prints decode timing only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not flush the caches (1 GiB write) before each timed launch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -170,6 +219,12 @@ def main(argv=None):
         dec = (dc, dt, decode_bytes(dc, kv_elt=2))
         del dc.k_cache, dc.v_cache  # host copies no longer needed
 
+    flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            attn.flush_caches(flush_buf)
+
     def run_prefill():
         if not args.no_prefill:
             attn.fwd(q, k, v, out=o)
@@ -198,10 +253,12 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         ev[i][0].record(stream)
         run_prefill()
         ev[i][1].record(stream)
         if dec:
+            flush()
             ev[i][2].record(stream)
             run_decode()
             ev[i][3].record(stream)
@@ -252,6 +309,19 @@ def main(argv=None):
                                       "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                       "traffic": load_traffic(DECODE_KERNELS),
                                       "kernels": "decode_split_kernel + decode_combine_kernel"}}
+    out["cache_flush_before_each_launch"] = flush_buf is not None
+
+    # ------------------------------------------------------- measured peaks ----
+    if not args.no_probes:
+        peaks = measure_peaks(attn, torch, dev)
+        out["measured_peaks"] = peaks
+        mp = peaks["mfma_bf16_32x32x16_one_wave_per_simd"]["random_operands"]["tflops"]
+        out["roofline"]["measured_peak"] = mp
+        out["roofline"]["frac_of_measured"] = round(tflops / mp, 4)
+        if dec:
+            hp = peaks["hbm_read_nontemporal_gbps"]
+            out["decode"]["roofline"]["measured_peak"] = hp
+            out["decode"]["roofline"]["frac_of_measured"] = round(out["decode"]["gbps"] / hp, 4)
 
     # ------------------------------------------------------------ CPU baseline ----
     if not args.no_cpu:

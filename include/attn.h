@@ -157,6 +157,40 @@ attn_status_t attn_decode_paged(const attn_decode_args_t *args, const void *q, c
                                 const int32_t *block_table, const int32_t *seq_lens, void *o,
                                 float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------- measurement ---- */
+/*
+ * Probes for the two figures a roofline needs, measured on this machine rather than
+ * taken from the specification (clocks are not locked): the roofline of the page
+ * "Agent 帮我写 CUDA：一个 Softmax Attention 算子的开发全记录" (section 七: arithmetic
+ * intensity against a ridge point = compute peak / memory bandwidth). Same conventions
+ * as above: device pointers, enqueue only, host-side checks.
+ *
+ * attn_probe_mfma: `workgroups` workgroups of 4 waves (one per SIMD), each wave issuing
+ *   32 * iters back-to-back v_mfma_f32_32x32x16_bf16 products in two independent chains
+ *   (32768 FLOP each: FLOPs = workgroups * 4 * 32 * iters * 32768).
+ *   operands   device uint32 [256 * 8]: thread t takes its A operand bits from
+ *              operands[8t .. 8t+3] and its B operand bits from [8t+4 .. 8t+7] (the power
+ *              the matrix cores draw, and so the clock they hold, depends on these bits)
+ *   valu_mix   0: products only; 1: beside each product the vector work of the attention
+ *              loop (one exp2, one fp32 add, half a pack to bf16)
+ *   clocks     device uint64 [2 * workgroups]: per workgroup, the shader-clock cycles and
+ *              the 100 MHz reference ticks its first wave spent in the product loop
+ *   sink       device float [256 * workgroups], written (keeps the products live)
+ *
+ * attn_probe_hbm_read: `workgroups` workgroups stream `bytes` of `buf` (workgroup w reads
+ *   the w-th contiguous slice) with 16-byte nontemporal loads and write one uint32 each to
+ *   sink [workgroups]. bytes must be a non-zero multiple of 32768 * workgroups.
+ *
+ * attn_flush_caches: writes zeros over `bytes` of `buf` (16-byte aligned, a multiple of 16),
+ *   so that with bytes above the last-level cache size (L2 4 MiB per XCD, 256 MiB
+ *   Infinity Cache on MI355X) a following launch starts with cold caches.
+ */
+attn_status_t attn_probe_mfma(const uint32_t *operands, int32_t workgroups, int32_t iters, int32_t valu_mix,
+                              uint64_t *clocks, float *sink, void *stream);
+attn_status_t attn_probe_hbm_read(const void *buf, size_t bytes, int32_t workgroups, uint32_t *sink,
+                                  void *stream);
+attn_status_t attn_flush_caches(void *buf, size_t bytes, void *stream);
+
 /* ------------------------------------------------------------------ misc ---- */
 
 const char *attn_status_string(attn_status_t status);

@@ -161,3 +161,38 @@ def test_decode_checks_scales_and_workspace():
     st = L.attn_decode_paged(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None,
                              FAKE, 1024, None)
     assert st == _lib.ATTN_ERROR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("args", [
+    (None, 256, 10, 0, FAKE, FAKE),          # no operands
+    (FAKE, 0, 10, 0, FAKE, FAKE),            # no workgroups
+    (FAKE, 70000, 10, 0, FAKE, FAKE),        # too many workgroups
+    (FAKE, 256, 0, 0, FAKE, FAKE),           # no iterations
+    (FAKE, 256, 10, 2, FAKE, FAKE),          # unknown vector mix
+    (FAKE, 256, 10, 0, FAKE + 4, FAKE),      # clocks not 8-byte aligned
+    (FAKE, 256, 10, 0, None, FAKE),          # no clocks
+])
+def test_probe_mfma_rejects_bad_arguments(args):
+    L = _lib.lib()
+    assert L.attn_probe_mfma(*args, None) == _lib.ATTN_ERROR_INVALID_VALUE, L.attn_last_error_message()
+
+
+@pytest.mark.parametrize("args", [
+    (None, 1 << 20, 32, FAKE),               # no buffer
+    (FAKE, 0, 32, FAKE),                     # no bytes
+    (FAKE, (1 << 20) + 16, 32, FAKE),        # not a multiple of 32768 * workgroups
+    (FAKE, 1 << 20, 0, FAKE),                # no workgroups
+    (FAKE + 8, 1 << 20, 32, FAKE),           # misaligned buffer
+    (FAKE, 1 << 20, 32, None),               # no sink
+])
+def test_probe_hbm_read_rejects_bad_arguments(args):
+    L = _lib.lib()
+    assert L.attn_probe_hbm_read(*args, None) == _lib.ATTN_ERROR_INVALID_VALUE, L.attn_last_error_message()
+
+
+def test_flush_rejects_bad_arguments():
+    L = _lib.lib()
+    assert L.attn_flush_caches(None, 1 << 20, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    assert L.attn_flush_caches(FAKE, 0, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    assert L.attn_flush_caches(FAKE, 24, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    assert L.attn_flush_caches(FAKE + 8, 1 << 20, None) == _lib.ATTN_ERROR_INVALID_VALUE
