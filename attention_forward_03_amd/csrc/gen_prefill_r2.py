@@ -135,7 +135,7 @@ class Gen:
         self.mode = mode
         # slack: P < 2^slack; fp16 probabilities must stay below 2^16
         self.slack_bits = "0x42200000" if bf16 else "0x41700000"   # 40 / 15
-        self.sum_limit = "0x53800000" if bf16 else "0x47000000"    # 2^40 / 2^15
+        self.sum_limit = "0x71800000" if bf16 else "0x47000000"    # 2^100 / 2^15
         self.out = []
         self.lds = []   # tags of LDS reads that may be in flight, in issue order
         self.n = 0
@@ -335,24 +335,28 @@ class Gen:
         elif st == 1:
             self.cvt_pair(px, 15)
             self.sum_elem(31)
-        elif st == 2:
+        elif st == 2 and lsub != L:
             for rb in range(RB):
                 self.emit(f"v_add_f32 {v(L + rb)}, {v(L + rb)}, {v(lsub + rb)}")
-        elif st == 3:
+        elif st == 3 and lsub != L and not self.bf16:
             for rb in range(RB):
                 self.emit(f"v_max_f32 {v(LMX + rb)}, {v(LMX + rb)}, {v(lsub + rb)}")
         self.et, self.lsub = keep
     def phase(self, *, s_next, pv, soft, masked, track, maxonly, kofs, vofs, knofs, vnofs, dma, sx, sy, px, py,
-              kt_sreg, tail=None, advance=()):
+              kt_sreg, tail=None, advance=(), direct=False):
         """Phase X(i): S(i+1) into sy (K at kofs), O += V^T py^T (V at vofs), mask / max /
         P of the scores sx of sub-tile i into px (first key kt_sreg); read-ahead of the next
         phase's first K and V fragments (knofs / vnofs, None: none); tile loads into the
         buffers dma = (K buffer, V buffer) or None.
         track: row maxima and the per-phase check; tail: the previous soft phase (its
-        pipeline ends here); advance: groups of scalar instructions spread over the steps.
+        pipeline ends here); advance: groups of scalar instructions spread over the steps;
+        direct: the row sums go straight into l (bf16, no rare path in this phase).
         Returns the state a later phase needs to finish this one's pipeline."""
         par = 0 if sx == S_X else 1
         self.et, self.lsub = ET + 4 * par, (LSUB, LSUB2)[par]
+        if direct:
+            # no rare path and no per-phase guard: the sums go straight into l
+            self.lsub = L
         advance = list(advance)
         for st in range(NSTEP):
             is_s, idx, rb = st % 2 == 0, st // 4, (st // 2) % 2
@@ -403,7 +407,7 @@ class Gen:
                     if track:
                         self.emit(f"v_mov_b32 {v(MXA)}, {v(VNINF)}")
                         self.emit(f"v_mov_b32 {v(MXA + 1)}, {v(VNINF)}")
-                    if not maxonly:
+                    if not maxonly and self.lsub != L:
                         self.emit(f"v_mov_b32 {v(self.lsub)}, 0")
                         self.emit(f"v_mov_b32 {v(self.lsub + 1)}, 0")
                     if masked:
@@ -564,7 +568,8 @@ class Gen:
         st = self.phase(s_next=True, pv=not exact, soft=True, masked=masked, track=track, maxonly=exact,
                         kofs=kbuf(c, 1), vofs=kbuf(c2, 1), knofs=kbuf(c1, 0),
                         vnofs=None if exact else kbuf(c, 0), dma=(c2, None if exact else 3 + c1), sx=S_X, sy=S_Y, px=P_X,
-                        py=P_Y, kt_sreg=SKT, tail=None if exact else prev)
+                        py=P_Y, kt_sreg=SKT, tail=None if exact else prev,
+                        direct=self.bf16 and plain and not exact)
         self.relabel()
         self.emit(f"s_add_u32 {s(SKT2)}, {s(SKT)}, 32")
         # X(2j+1): S(2j+2) from K(j+1) rows 0..31; P(2j) V(j) rows 0..31
@@ -691,11 +696,14 @@ class Gen:
                            px=P_X, py=P_Y, kt_sreg=SKT, tail=prev)
                 self.emit(f"s_branch {done}")
             self.emit(f"{done}:")
-            # a phase's row sums past the slack: the pass is run again
+            # fp16: a phase's row sums past the slack (P would not fit fp16); bf16: a row
+            # sum past 2^100 or infinite (P may exceed the slack in bf16 freely, but O
+            # must stay finite): the pass is run again
             ok = self.uniq("sumsok")
-            self.emit(f"v_cmp_lt_f32 vcc, {self.sum_limit}, {v(LMX)}")
+            chk = LMX if not self.bf16 else L
+            self.emit(f"v_cmp_lt_f32 vcc, {self.sum_limit}, {v(chk)}")
             self.emit(f"s_mov_b64 {s(SMASK, 2)}, vcc")
-            self.emit(f"v_cmp_lt_f32 vcc, {self.sum_limit}, {v(LMX + 1)}")
+            self.emit(f"v_cmp_lt_f32 vcc, {self.sum_limit}, {v(chk + 1)}")
             self.emit(f"s_or_b64 {s(SMASK, 2)}, {s(SMASK, 2)}, vcc")
             self.emit(f"s_cbranch_scc0 {ok}")
             self.set_flag()
