@@ -609,7 +609,28 @@ class Gen:
         for i in range(4):
             self.emit(f"ds_write_b128 {v(T0)}, {v(ZERO, 4)} offset:{i * 1024}")
 
-    def run_pass(self, exact):
+    def prescale_q(self):
+        """Q fragments (raw, in S_X..S_Y) pre-scaled (by the score scale in log2 units, or for
+        the softcap by the argument factor of its exponential), rounded back to 16 bits, into
+        the AGPRs they stay in."""
+        e = self.emit
+        qscale = v(VCAPK) if self.mode == 2 else s(49)
+        for i in range(RB * NKS * 4):
+            x = S_X + i
+            if self.bf16:
+                e(f"v_lshlrev_b32 {v(T0)}, 16, {v(x)}")
+                e(f"v_and_b32 {v(T1)}, 0xffff0000, {v(x)}")
+            else:
+                e(f"v_cvt_f32_f16 {v(T0)}, {v(x)}")
+                e(f"v_lshrrev_b32 {v(T1)}, 16, {v(x)}")
+                e(f"v_cvt_f32_f16 {v(T1)}, {v(T1)}")
+            e(f"v_mul_f32 {v(T0)}, {qscale}, {v(T0)}")
+            e(f"v_mul_f32 {v(T1)}, {qscale}, {v(T1)}")
+            cvt = "v_cvt_pk_bf16_f32" if self.bf16 else "v_cvt_pk_f16_f32"
+            e(f"{cvt} {v(T2)}, {v(T0)}, {v(T1)}")
+            e(f"v_accvgpr_write_b32 {a(128 + i)}, {v(T2)}")
+
+    def run_pass(self, exact, first=False):
         tag = "x" if exact else "n"
         self.emit(f"s_mov_b32 {s(SJ)}, 0")
         self.emit(f"s_mov_b32 {s(SKT)}, {s(47)}")
@@ -624,11 +645,18 @@ class Gen:
             self.zero_v5()
             for rb in range(RB):
                 self.emit(f"v_mov_b32 {v(LMX + rb)}, 0")
-        self.emit("s_waitcnt vmcnt(0)")
+        # the resource is read when a load issues: K(1) follows without a wait
         self.advance_rsrc("k")
         for n in range(4):
             self.load("k", n, 1)
         self.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+        if first:
+            # the first attempt only: later ones find Q in the AGPRs already
+            done = self.uniq("qready")
+            self.emit(f"s_cmp_lg_u32 {s(SATT)}, 0")
+            self.emit(f"s_cbranch_scc1 {done}")
+            self.prescale_q()
+            self.emit(f"{done}:")
         self.emit("s_barrier")
         if not exact:
             # P(-1) = 0, and the pipeline "tail" of sub-tile -1 produces zeros
@@ -751,27 +779,10 @@ class Gen:
             e(f"v_add_u32 {v(VO + n)}, {s(ST3)}, {v(20)}")
         for r in range(ZERO, ZERO + 4):
             e(f"v_mov_b32 {v(r)}, 0")
-        # Q fragments, pre-scaled (by the score scale in log2 units, or for the softcap by the
-        # argument factor of its exponential) and rounded back to 16 bits, into AGPRs
+        # Q fragments (raw; scaled into AGPRs once the first pass's tile loads are issued)
         for rb in range(RB):
             for ks in range(NKS):
                 e(f"global_load_dwordx4 {v(S_X + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
-        e("s_waitcnt vmcnt(0)")
-        qscale = v(VCAPK) if self.mode == 2 else s(49)
-        for i in range(RB * NKS * 4):
-            x = S_X + i
-            if self.bf16:
-                e(f"v_lshlrev_b32 {v(T0)}, 16, {v(x)}")
-                e(f"v_and_b32 {v(T1)}, 0xffff0000, {v(x)}")
-            else:
-                e(f"v_cvt_f32_f16 {v(T0)}, {v(x)}")
-                e(f"v_lshrrev_b32 {v(T1)}, 16, {v(x)}")
-                e(f"v_cvt_f32_f16 {v(T1)}, {v(T1)}")
-            e(f"v_mul_f32 {v(T0)}, {qscale}, {v(T0)}")
-            e(f"v_mul_f32 {v(T1)}, {qscale}, {v(T1)}")
-            cvt = "v_cvt_pk_bf16_f32" if self.bf16 else "v_cvt_pk_f16_f32"
-            e(f"{cvt} {v(T2)}, {v(T0)}, {v(T1)}")
-            e(f"v_accvgpr_write_b32 {a(128 + i)}, {v(T2)}")
         # redo flag = 0 (wave 0), ordered before any write of 1 by the first barrier
         skip = self.uniq("noinit")
         e(f"s_cmp_lg_u32 {s(53)}, 0")
@@ -791,7 +802,7 @@ class Gen:
         e("s_nop 1")
         for blk in range(RB * NDB):
             self.mfma(a(blk * 16, 16), v(ZERO, 4), v(ZERO, 4), "0")
-        self.run_pass(exact=False)
+        self.run_pass(exact=False, first=True)
         # redo? (read after every wave has finished writing it)
         done = "L_done_%="
         e("s_barrier")
