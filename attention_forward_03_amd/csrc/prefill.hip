@@ -131,19 +131,6 @@ __device__ __forceinline__ float pair_sum(float x) { return x + xor_shuffle(x, 3
 // same reference max is used for P, for l and for the final LSE.
 constexpr float kRescaleSlack = 8.0f;
 
-// Sum of two packed 16-bit probabilities into an fp32 accumulator (one dot2 op): the
-// row sum is taken over the same rounded values the P.V product uses.
-template <bool BF16>
-__device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
-  if constexpr (BF16) {
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), ones, acc, false);
-  } else {
-    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), ones, acc, false);
-  }
-}
-
 // One workgroup = NW waves; each wave owns 32 query rows and walks all key tiles of the
 // workgroup's range. K and V tiles are double-buffered: the loads of tile j+1 are issued
 // before tile j is computed and waited for at the per-tile barrier.
@@ -339,8 +326,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
       for (int x = 0; x < 8; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][base + x], sc, -m_use));
       pf[t] = u32x4_t{pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]), pack2<BF16>(e[4], e[5]),
                       pack2<BF16>(e[6], e[7])};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) l = dot2_ones<BF16>(pf[t][w], l);
+      // row sum in fp32 adds: a packed dot product would hold the matrix core up
+      l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     }
 #pragma unroll
     for (int t = 0; t < NPS; ++t)
