@@ -32,16 +32,18 @@ defining them, and the readings taken here are:
 Function pins (see tests/test_oracle_*.py): brute-force scalar loops, the
 page's online recurrence, closed forms (identical keys, dominant key, N = 1,
 D = 1), invariants (shift, permutation, GQA = MHA, varlen = concatenation,
-paged = dense, split/combine associativity, softcap and window limits) and
+paged = dense, chunked paged prefill = brute force with
+scalar page indexing and = decode at one query, page-permutation invariance,
+split/combine associativity, softcap and window limits) and
 library special cases (torch's bf16 / fp16 / float8_e4m3fn conversions).
 """
 from .numerics import (bf16_bits_to_f64, f16_bits_to_f64, e4m3_code_table, e4m3_codes_to_f64,
                        default_scale, tensor_to_f64)
 from .attention import (sdpa_fp64, prefill_dense, prefill_varlen, gather_pages, decode_paged,
-                        combine_partials, attention_probs)
+                        prefill_paged, combine_partials, attention_probs)
 
 __all__ = [
     "bf16_bits_to_f64", "f16_bits_to_f64", "e4m3_code_table", "e4m3_codes_to_f64",
     "default_scale", "tensor_to_f64", "sdpa_fp64", "prefill_dense", "prefill_varlen",
-    "gather_pages", "decode_paged", "combine_partials", "attention_probs",
+    "gather_pages", "decode_paged", "prefill_paged", "combine_partials", "attention_probs",
 ]

@@ -203,6 +203,31 @@ def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_
     return o, lse
 
 
+def prefill_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+                  cu_q: np.ndarray, seq_lens_k: np.ndarray, *, scale: float, causal: bool = True,
+                  window: int = 0, softcap: float = 0.0, seqs: Optional[np.ndarray] = None,
+                  rows_per_seq: Optional[dict] = None, heads: Optional[np.ndarray] = None,
+                  page_size: int = 16):
+    """Chunked prefill over a paged cache: sequence b's queries q[cu_q[b]:cu_q[b+1]]
+    ([T, Hq, D] packed) are its last Nq_b positions and attend to its Nk_b =
+    seq_lens_k[b] keys, which sit in the cache pages its block-table row names
+    (caches [P, page_size, Hkv, D], float64). The keys are gathered into one
+    token-major array and the ragged definition above applies, with the mask offset
+    Nk_b - Nq_b. Returns (o [T, Hq, D], lse [Hq, T]) (rows outside the sample NaN).
+    """
+    nseq = len(cu_q) - 1
+    parts_k, parts_v, cu_k = [], [], [0]
+    for b in range(nseq):
+        L = int(seq_lens_k[b])
+        parts_k.append(gather_pages(k_cache, block_table[b], L, page_size))
+        parts_v.append(gather_pages(v_cache, block_table[b], L, page_size))
+        cu_k.append(cu_k[-1] + L)
+    k = np.concatenate(parts_k, axis=0)
+    v = np.concatenate(parts_v, axis=0)
+    return prefill_varlen(q, k, v, np.asarray(cu_q), np.asarray(cu_k), scale=scale, causal=causal,
+                          window=window, softcap=softcap, seqs=seqs, rows_per_seq=rows_per_seq, heads=heads)
+
+
 def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
     """Merge results computed on disjoint key ranges (axis 0 indexes the ranges).
 

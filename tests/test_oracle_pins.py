@@ -322,3 +322,81 @@ def test_default_scale_is_binary32_rounding():
         s = oracle.default_scale(d)
         assert s == float(np.float32(1 / math.sqrt(d)))
         assert abs(s - 1 / math.sqrt(d)) <= 2 ** -24 / math.sqrt(d)
+
+
+# ------------------------------------------------------- chunked prefill over pages ----
+
+def _paged_keys_by_loop(cache, row, L, page=16):
+    """Token t of a sequence lives in slot t % page of physical page row[t // page];
+    written with scalar indexing so it shares nothing with the oracle's gather."""
+    out = []
+    for t in range(L):
+        p = int(row[t // page])
+        out.append([[float(x) for x in cache[p, t % page, h]] for h in range(cache.shape[2])])
+    # [L][Hkv][D] -> [Hkv][L][D]
+    return [[out[t][h] for t in range(L)] for h in range(cache.shape[2])]
+
+
+@pytest.mark.parametrize("causal,window,softcap", [(True, 0, 0.0), (False, 0, 0.0), (True, 5, 0.0),
+                                                   (True, 0, 3.0)])
+def test_paged_prefill_brute_force(causal, window, softcap):
+    lens_k = [5, 33, 16, 1, 20]
+    lens_q = [3, 17, 16, 1, 7]
+    case = make_decode(lengths=lens_k, num_q_heads=4, num_kv_heads=2, head_dim=4,
+                       kv_dtype="bf16", seed=21)
+    kc = oracle.tensor_to_f64(case.k_cache, "bf16")
+    vc = oracle.tensor_to_f64(case.v_cache, "bf16")
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    q = _rand(int(cu_q[-1]), 4, 4, scale=1.5)
+    o, lse = oracle.prefill_paged(q, kc, vc, case.block_table, cu_q, case.seq_lens, scale=0.45,
+                                  causal=causal, window=window, softcap=softcap)
+    for b in range(len(lens_k)):
+        a, z = int(cu_q[b]), int(cu_q[b + 1])
+        kb = _paged_keys_by_loop(kc, case.block_table[b], lens_k[b])
+        vb = _paged_keys_by_loop(vc, case.block_table[b], lens_k[b])
+        ob, lb = brute.brute_sdpa(_tolist(q[a:z].transpose(1, 0, 2)), kb, vb, scale=0.45,
+                                  causal=causal, window=window, softcap=softcap)
+        np.testing.assert_allclose(o[a:z], np.array(ob).transpose(1, 0, 2), rtol=0, atol=1e-12)
+        lb = np.array(lb)
+        fin = np.isfinite(lb)
+        assert (np.isfinite(lse[:, a:z]) == fin).all()
+        np.testing.assert_allclose(lse[:, a:z][fin], lb[fin], rtol=0, atol=1e-12)
+
+
+def test_paged_prefill_one_query_is_decode():
+    # causal, one query per sequence: the query is the last position and sees every key
+    lens = [7, 40, 16, 2]
+    case = make_decode(lengths=lens, num_q_heads=4, num_kv_heads=1, head_dim=8,
+                       kv_dtype="bf16", seed=22)
+    kc = oracle.tensor_to_f64(case.k_cache, "bf16")
+    vc = oracle.tensor_to_f64(case.v_cache, "bf16")
+    q = oracle.tensor_to_f64(case.q, "bf16")              # [S, Hq, D]
+    cu_q = np.arange(len(lens) + 1)
+    o, lse = oracle.prefill_paged(q, kc, vc, case.block_table, cu_q, case.seq_lens, scale=0.3)
+    od, ld = oracle.decode_paged(q, kc, vc, case.block_table, case.seq_lens, scale=0.3)
+    np.testing.assert_allclose(o, od, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse.T, ld, rtol=0, atol=1e-13)
+
+
+def test_paged_prefill_page_permutation_invariance():
+    lens_k, lens_q = [33, 9], [33, 4]
+    case = make_decode(lengths=lens_k, num_q_heads=2, num_kv_heads=2, head_dim=4,
+                       kv_dtype="bf16", seed=23)
+    kc = oracle.tensor_to_f64(case.k_cache, "bf16")
+    vc = oracle.tensor_to_f64(case.v_cache, "bf16")
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    q = _rand(int(cu_q[-1]), 2, 4)
+    o, lse = oracle.prefill_paged(q, kc, vc, case.block_table, cu_q, case.seq_lens, scale=0.5,
+                                  window=7)
+    perm = np.random.default_rng(3).permutation(kc.shape[0])
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[perm], vp[perm] = kc, vc                             # old page i is now page perm[i]
+    bt = perm[case.block_table]
+    o2, lse2 = oracle.prefill_paged(q, kp, vp, bt, cu_q, case.seq_lens, scale=0.5, window=7)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    # and a block table that names a wrong page changes the answer
+    bt_bad = case.block_table.copy()
+    bt_bad[0, [0, 1]] = bt_bad[0, [1, 0]]
+    o3, _ = oracle.prefill_paged(q, kc, vc, bt_bad, cu_q, case.seq_lens, scale=0.5, window=7)
+    assert not np.allclose(o3[:33], o[:33])
