@@ -6,6 +6,7 @@ with torch (device memory and the current stream are torch's), and passes
 pointers. If the library is missing it raises: there is no CPU fallback.
 
     fwd(q, k, v, ...)            softmax(Q K^T * scale [+ mask]) V (prefill)
+    fwd_paged(q, k_cache, ...)    chunked prefill over a paged cache
     decode_paged(q, k_cache, ...) one query token per sequence over a paged cache
 """
 from __future__ import annotations
@@ -18,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, AttnInvalidValue, AttnNotSupported
 
-__all__ = ["fwd", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
+__all__ = ["fwd", "fwd_paged", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
            "AttnError", "AttnInvalidValue", "AttnNotSupported"]
 
 _DTYPES = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
@@ -116,6 +117,58 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
             arr[i] = int(st[i])
     status = _lib.lib().attn_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                  _stream_handle(q.device))
+    _lib.check(status)
+    return (o, lse) if return_lse else o
+
+
+def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+              cu_seqlens_q: torch.Tensor, seq_lens_k: torch.Tensor, max_seqlen_q: int, *, causal: bool = True,
+              window: int = 0, softcap: float = 0.0, softmax_scale: float = 0.0, return_lse: bool = False,
+              out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
+    """Chunked prefill over a paged KV cache.
+
+    q [T, Hq, D] packed chunks (int32 cu_seqlens_q [S+1] on the GPU, max_seqlen_q a
+    host-side bound of the chunk lengths); k_cache/v_cache [P, 16, Hkv, D] in q's
+    dtype (bf16/f16); block_table int32 [S, max_pages]; seq_lens_k int32 [S], the
+    keys of each sequence, the chunk's own included. Returns o [T, Hq, D] (and lse
+    [Hq, T] float32 if return_lse).
+    """
+    _require_cuda(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k)
+    for t in (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k):
+        if not t.is_contiguous():
+            raise ValueError("paged prefill tensors must be contiguous")
+    if block_table.dtype != torch.int32 or cu_seqlens_q.dtype != torch.int32 or seq_lens_k.dtype != torch.int32:
+        raise ValueError("block_table, cu_seqlens_q and seq_lens_k must be int32")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must match each other and q's dtype")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape[3] != q.shape[2]:
+        raise ValueError("q must be [T, Hq, D] and the caches [P, page, Hkv, D]")
+    S = seq_lens_k.numel()
+    if block_table.dim() != 2 or block_table.shape[0] != S or cu_seqlens_q.shape != (S + 1,):
+        raise ValueError("block_table must be [S, max_pages] and cu_seqlens_q [S + 1]")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise AttnNotSupported(_lib.ATTN_ERROR_NOT_SUPPORTED, f"dtype {q.dtype} not supported")
+    a = _lib.FwdPagedArgs()
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = S, q.shape[1], k_cache.shape[2], q.shape[2]
+    a.page_size, a.max_pages_per_seq, a.num_pages = k_cache.shape[1], block_table.shape[1], k_cache.shape[0]
+    a.max_seqlen_q = int(max_seqlen_q)
+    a.dtype = _DTYPES[q.dtype]
+    a.causal = 1 if causal else 0
+    a.window = int(window)
+    a.softmax_scale = float(softmax_scale)
+    a.softcap = float(softcap)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must match q")
+    lse = None
+    if return_lse:
+        shape = (q.shape[1], q.shape[0])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+        if lse.shape != shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse_out must be a contiguous float32 tensor of shape {shape}")
+    status = _lib.lib().attn_fwd_paged(ctypes.byref(a), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(cu_seqlens_q), _ptr(seq_lens_k), _ptr(o), _ptr(lse),
+                                       _stream_handle(q.device))
     _lib.check(status)
     return (o, lse) if return_lse else o
 

@@ -165,6 +165,88 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
   return ok();
 }
 
+attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table, const int32_t* cu_seqlens_q,
+                             const int32_t* seq_lens_k, void* o, float* lse, void* stream) {
+  if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
+  if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(ATTN_ERROR_INVALID_VALUE, "num_seqs, num_q_heads and num_kv_heads must be >= 1");
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(ATTN_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of 32, 64, 128", a->head_dim);
+  if (a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "dtype %d is not F16 or BF16", a->dtype);
+  if (a->page_size != kPageSize) return fail(ATTN_ERROR_NOT_SUPPORTED, "page_size must be 16");
+  if (a->max_pages_per_seq < 1 || a->num_pages < 1)
+    return fail(ATTN_ERROR_INVALID_VALUE, "max_pages_per_seq and num_pages must be >= 1");
+  if (a->max_pages_per_seq > (1 << 26))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "max_pages_per_seq is limited to 2^26");
+  if (a->max_seqlen_q < 0) return fail(ATTN_ERROR_INVALID_VALUE, "max_seqlen_q must be >= 0");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  if (a->window > 0 && !a->causal)
+    return fail(ATTN_ERROR_INVALID_VALUE, "a sliding window requires causal = 1");
+  if (!(a->softcap == a->softcap) || !(a->softmax_scale == a->softmax_scale) || isinf(a->softcap) ||
+      isinf(a->softmax_scale))
+    return fail(ATTN_ERROR_INVALID_VALUE, "softcap and softmax_scale must be finite");
+  if (a->num_q_heads > 65535 || a->num_seqs > 65535)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_q_heads and num_seqs are limited to 65535");
+  if ((int64_t)a->num_kv_heads * a->head_dim >= (int64_t)1 << 24)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_kv_heads * head_dim must be below 2^24");
+  if ((int64_t)a->num_q_heads * a->head_dim >= (int64_t)1 << 24)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_q_heads * head_dim must be below 2^24");
+  if (a->max_seqlen_q == 0) return ok();  // nothing to compute
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o == nullptr || block_table == nullptr ||
+      cu_seqlens_q == nullptr || seq_lens_k == nullptr)
+    return fail(ATTN_ERROR_INVALID_VALUE,
+                "q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens_k) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(ATTN_ERROR_INVALID_VALUE, "block_table, cu_seqlens_q, seq_lens_k and lse must be 4-byte aligned");
+
+  const int64_t D = a->head_dim, tok_k = (int64_t)a->num_kv_heads * D, tok_q = (int64_t)a->num_q_heads * D;
+  attn::FwdParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o = o;
+  p.lse = lse;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = nullptr;
+  p.qs[0] = 0, p.qs[1] = D, p.qs[2] = tok_q;
+  p.os[0] = 0, p.os[1] = D, p.os[2] = tok_q;
+  p.ks[0] = kPageSize * tok_k, p.ks[1] = D, p.ks[2] = tok_k;
+  p.vs[0] = kPageSize * tok_k, p.vs[1] = D, p.vs[2] = tok_k;
+  p.batch = a->num_seqs;
+  p.hq = a->num_q_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.nq = a->max_seqlen_q;
+  p.nk = a->max_pages_per_seq * kPageSize;
+  p.causal = a->causal;
+  p.window = a->window > 0 ? a->window : 0;
+  const double scale = resolve_scale(a->softmax_scale, a->head_dim);
+  p.scale_log2 = (float)(scale * kLog2eD);
+  if (a->softcap > 0.0f) {
+    p.cap_in = (float)(scale / (double)a->softcap);
+    p.cap_out = (float)((double)a->softcap * kLog2eD);
+  }
+  const int bm = attn::fwd_paged_block_rows();
+  p.q_tiles = (a->max_seqlen_q + bm - 1) / bm;
+  p.block_table = block_table;
+  p.seq_lens_k = seq_lens_k;
+  p.max_pages = a->max_pages_per_seq;
+  p.num_pages = a->num_pages;
+
+  hipError_t e = attn::launch_fwd_paged(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 static attn_status_t check_decode_args(const attn_decode_args_t* a) {
   if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
   if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)

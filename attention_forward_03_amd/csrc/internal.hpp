@@ -24,6 +24,12 @@ struct FwdParams {
   float cap_in;         // softcap: multiplier of the raw dot product inside tanh (scale / c)
   float cap_out;        // softcap: c * log2(e); 0 = off
   int32_t q_tiles;      // query tiles per sequence
+  // paged keys (chunked prefill): k / v are caches [pages, 16, Hkv, D]; ks[0] / vs[0] are
+  // the page strides and ks[2] / vs[2] the token strides; sequence b has seq_lens_k[b]
+  // keys in the pages that row b of block_table [batch, max_pages] names
+  const int32_t* block_table;
+  const int32_t* seq_lens_k;
+  int32_t max_pages, num_pages;
 };
 
 // One paged-decode launch (split kernel + combine kernel).
@@ -49,6 +55,9 @@ struct DecodeParams {
 int fwd_block_rows(int dtype, int head_dim);
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
+// chunked prefill over a paged cache (16-bit inputs)
+hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
+int fwd_paged_block_rows();
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t stream);
 
 hipError_t launch_probe_mfma(const uint32_t* operands, int workgroups, int iters, int valu_mix, uint64_t* clocks,

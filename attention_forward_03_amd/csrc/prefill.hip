@@ -134,7 +134,14 @@ constexpr float kRescaleSlack = 8.0f;
 // One workgroup = NW waves; each wave owns 32 query rows and walks all key tiles of the
 // workgroup's range. K and V tiles are double-buffered: the loads of tile j+1 are issued
 // before tile j is computed and waited for at the per-tile barrier.
-template <int D, int NW, int BN, bool BF16>
+//
+// PAGED: chunked prefill. Sequence b's queries are its last Nq_b positions (packed rows
+// cu_q[b] ...) and its Nk_b = seq_lens_k[b] keys sit in 16-token cache pages named by
+// row b of the block table, so the causal offset is Nk_b - Nq_b as in the dense case.
+// Key tiles start at multiples of 16, and one direct-to-LDS load covers at most 16 rows,
+// so each load reads inside a single page: its base is the page (a wave-uniform address)
+// and each lane adds its token slot. The page ids of a tile are read one tile ahead.
+template <int D, int NW, int BN, bool BF16, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
   constexpr int TILE = BN * D;  // elements per K or V tile
@@ -147,6 +154,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   constexpr int LOADS = BN / ROWS_PER_LOAD;  // load instructions per tile (K or V)
   constexpr int LPW = (LOADS + NW - 1) / NW;  // per wave
   static_assert(BN % 32 == 0 && D % 32 == 0 && BN % ROWS_PER_LOAD == 0, "tile shape");
+  static_assert(!PAGED || (BN % 16 == 0 && ROWS_PER_LOAD <= 16), "a paged load stays in one page");
   using SW = Swizzle<D>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
@@ -171,9 +179,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   if (p.causal) qt = p.q_tiles - 1 - qt;  // longest rows first
 
   int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
-  if (p.cu_q != nullptr) {
+  if (PAGED || p.cu_q != nullptr) {
     q_off = p.cu_q[b];
     Lq = p.cu_q[b + 1] - q_off;
+  }
+  if constexpr (PAGED) {
+    Lk = min(max(p.seq_lens_k[b], 0), p.max_pages * 16);  // a bad length cannot leave the table row
+  } else if (p.cu_q != nullptr) {
     k_off = p.cu_k[b];
     Lk = p.cu_k[b + 1] - k_off;
   }
@@ -181,13 +193,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   if (r0 >= Lq) return;
   const int hk = h / p.group;
   const int delta = Lk - Lq;
-  const bool ragged = p.cu_q != nullptr;
+  const bool ragged = PAGED || p.cu_q != nullptr;
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (ragged ? 0 : (int64_t)b * p.qs[0]) +
                        (int64_t)h * p.qs[1] + (int64_t)q_off * p.qs[2];
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (ragged ? 0 : (int64_t)b * p.ks[0]) +
-                       (int64_t)hk * p.ks[1] + (int64_t)k_off * p.ks[2];
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (ragged ? 0 : (int64_t)b * p.vs[0]) +
-                       (int64_t)hk * p.vs[1] + (int64_t)k_off * p.vs[2];
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)hk * p.ks[1] +
+                       (PAGED ? 0 : (ragged ? 0 : (int64_t)b * p.ks[0]) + (int64_t)k_off * p.ks[2]);
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)hk * p.vs[1] +
+                       (PAGED ? 0 : (ragged ? 0 : (int64_t)b * p.vs[0]) + (int64_t)k_off * p.vs[2]);
   uint16_t* og = static_cast<uint16_t*>(p.o) + (ragged ? 0 : (int64_t)b * p.os[0]) +
                  (int64_t)h * p.os[1] + (int64_t)q_off * p.os[2];
   const int64_t qs2 = p.qs[2], os2 = p.os[2];
@@ -256,6 +268,44 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
       }
     }
   };
+  // Paged form: load n of a tile reads page pg[n]; its rows past the last key re-read the
+  // last key. The page ids come from the block table (clamped to the cache, so a bad
+  // entry gives wrong values, never an access outside the cache).
+  // read through the constant address space: the table does not change during the launch,
+  // so its wave-uniform entries come in by scalar loads (which the loop's memory-clobbering
+  // direct-to-LDS loads would otherwise turn into vector loads with a wait on every load)
+  typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+  const_i32_t* bt = PAGED ? (const_i32_t*)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
+  const int last_page = (Lk - 1) >> 4, last_slot = (Lk - 1) & 15;
+  int ld_col_k[LPW], ld_col_v[LPW];
+#pragma unroll
+  for (int n = 0; n < LPW; ++n) {
+    ld_col_k[n] = SW::k(ld_row[n], lane % CPR) * 8;
+    ld_col_v[n] = SW::v(ld_row[n], lane % CPR) * 8;
+  }
+  auto page_ids = [&](int kt, int (&pg)[LPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      // a wave-uniform index (the compiler cannot see that tid >> 6 is)
+      const int P = __builtin_amdgcn_readfirstlane((kt + (wave + n * NW) * ROWS_PER_LOAD) >> 4);
+      pg[n] = bt[min(P, last_page)];
+    }
+  };
+  auto load_rows_paged = [&](const uint16_t* gbase, int64_t pstride, int stride, const int (&col)[LPW],
+                             const int (&pg)[LPW], int kt, uint16_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      const int i = wave + n * NW;
+      if (LOADS % NW == 0 || i < LOADS) {
+        const int P = (kt + i * ROWS_PER_LOAD) >> 4;
+        const int slot = ld_row[n] & 15;
+        const int se = P < last_page ? slot : (P == last_page ? min(slot, last_slot) : last_slot);
+        const int page = min(max(pg[n], 0), p.num_pages - 1);
+        load_lds16(gbase + (int64_t)page * pstride, (uint32_t)(se * stride + col[n]) * 2u, dst + i * 512);
+      }
+    }
+  };
+  int pg_next[LPW] = {};
 
   f32x16_t o[NDB];
 #pragma unroll
@@ -343,8 +393,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
     constexpr int BUF = decltype(bufc)::value;  // it % 2
     const int kt = kbeg + it * BN;
     if (it + 1 < ntiles) {
-      load_rows(kg, ks2, ld_k, kt + BN, k_lds + (BUF ^ 1) * TILE);
-      load_rows(vg, vs2, ld_v, kt + BN, v_lds + (BUF ^ 1) * TILE);
+      if constexpr (PAGED) {
+        load_rows_paged(kg, p.ks[0], ks2, ld_col_k, pg_next, kt + BN, k_lds + (BUF ^ 1) * TILE);
+        load_rows_paged(vg, p.vs[0], vs2, ld_col_v, pg_next, kt + BN, v_lds + (BUF ^ 1) * TILE);
+        if (it + 2 < ntiles) page_ids(kt + 2 * BN, pg_next);
+      } else {
+        load_rows(kg, ks2, ld_k, kt + BN, k_lds + (BUF ^ 1) * TILE);
+        load_rows(vg, vs2, ld_v, kt + BN, v_lds + (BUF ^ 1) * TILE);
+      }
     }
     if (needs(it)) {
       scores(k_lds + BUF * TILE);
@@ -355,9 +411,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   };
 
   settle_global_loads();
-  if (ntiles > 0) {
-    load_rows(kg, ks2, ld_k, kbeg, k_lds);
-    load_rows(vg, vs2, ld_v, kbeg, v_lds);
+  if constexpr (PAGED) {
+    if (ntiles > 0) {
+      int pg[LPW];
+      page_ids(kbeg, pg);
+      if (ntiles > 1) page_ids(kbeg + BN, pg_next);
+      load_rows_paged(kg, p.ks[0], ks2, ld_col_k, pg, kbeg, k_lds);
+      load_rows_paged(vg, p.vs[0], vs2, ld_col_v, pg, kbeg, v_lds);
+    }
+  } else {
+    if (ntiles > 0) {
+      load_rows(kg, ks2, ld_k, kbeg, k_lds);
+      load_rows(vg, vs2, ld_v, kbeg, v_lds);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -807,7 +873,31 @@ hipError_t launch32(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, bool BF16>
+hipError_t launch16_paged(const FwdParams& p, hipStream_t st) {
+  const int64_t blocks = (int64_t)p.q_tiles * p.hq * p.batch;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_mfma16_kernel<D, kNW16, kBN16, BF16, true>), dim3((unsigned)blocks), dim3(kNW16 * 64),
+                     0, st, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int fwd_paged_block_rows() { return kNW16 * 32; }
+
+// dtype: 1 = f16, 2 = bf16
+hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStream_t st) {
+  switch (dtype * 1000 + head_dim) {
+    case 1032: return launch16_paged<32, false>(p, st);
+    case 1064: return launch16_paged<64, false>(p, st);
+    case 1128: return launch16_paged<128, false>(p, st);
+    case 2032: return launch16_paged<32, true>(p, st);
+    case 2064: return launch16_paged<64, true>(p, st);
+    case 2128: return launch16_paged<128, true>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 int fwd_block_rows(int dtype, int /*head_dim*/) {
   return dtype == 0 ? kNW32 * 32 : kNW16 * 32;

@@ -5,7 +5,9 @@ One step = one pass of the whole hot path over resident synthetic inputs:
   * prefill: attn_fwd on B=1, H=32, N=8192, D=128, bf16, dense non-causal
     (Q, K, V = 0.5 * N(0,1));
   * decode:  attn_decode_paged on 64 sequences, L ~ U[512, 32768], Hq=32, Hkv=8,
-    D=128, bf16 KV in 16-token pages at permuted block-table indices.
+    D=128, bf16 KV in 16-token pages at permuted block-table indices;
+  * chunked prefill: attn_fwd_paged, 8 chunks of 2048 queries over contexts of
+    U[0, 14336] cached keys in the same page layout, causal, Hq=32, Hkv=8, D=128, bf16.
 Each launch is bracketed by HIP events on the stream it runs on, so the average
 kernel durations come from inside the timed region.
 
@@ -33,6 +35,22 @@ def prefill_flops(b, h, nq, nk, d):
     return 4.0 * b * h * nq * nk * d
 
 
+def allowed_pairs(nq: int, nk: int, causal: bool, window: int = 0) -> int:
+    """(query, key) pairs the mask allows (bottom-right causal alignment, offset nk - nq)."""
+    i = np.arange(nq, dtype=np.int64)
+    hi = np.minimum(nk, i + (nk - nq) + 1) if causal else np.full(nq, nk, dtype=np.int64)
+    lo = np.maximum(0, i + (nk - nq) - window + 1) if window > 0 else np.zeros(nq, dtype=np.int64)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+def chunked_flops(case) -> float:
+    """4 * D * Hq FLOPs per allowed (query, key) pair, summed over the chunks."""
+    c = case.cache
+    nq = np.diff(case.cu_seqlens_q)
+    pairs = sum(allowed_pairs(int(a), int(b), case.causal, case.window) for a, b in zip(nq, c.seq_lens))
+    return 4.0 * c.head_dim * c.num_q_heads * pairs
+
+
 def decode_bytes(case, kv_elt: int, q_elt: int = 2) -> float:
     L = case.seq_lens.astype(np.int64)
     hkv, d, hq, S = case.num_kv_heads, case.head_dim, case.num_q_heads, case.num_seqs
@@ -47,6 +65,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 PREFILL_KERNEL = "fwd_r2_kernel<true, 0>"
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
+CHUNKED_KERNEL = "fwd_mfma16_kernel<128, 8, 64, true, true>"
 
 
 def kernel_source_digest() -> str:
@@ -169,6 +188,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="time the prefill only")
     ap.add_argument("--no-prefill", action="store_true",
                     help="run only the decode (per-kernel counter passes; prints decode timing only)")
+    ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill over the paged cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--no-flush", action="store_true",
@@ -219,6 +239,16 @@ def main(argv=None):
         dec = (dc, dt, decode_bytes(dc, kv_elt=2))
         del dc.k_cache, dc.v_cache  # host copies no longer needed
 
+    chk = None
+    if not args.no_chunked and not args.no_prefill:
+        cc = workloads.config_chunked_prefill()
+        ct = {"q": cc.q.to(dev), "k": cc.cache.k_cache.to(dev), "v": cc.cache.v_cache.to(dev),
+              "bt": torch.from_numpy(cc.cache.block_table).to(dev),
+              "cu": torch.from_numpy(cc.cu_seqlens_q).to(dev), "sl": torch.from_numpy(cc.seq_lens_k).to(dev)}
+        ct["o"] = torch.empty_like(ct["q"])
+        chk = (cc, ct, chunked_flops(cc))
+        del cc.cache.k_cache, cc.cache.v_cache
+
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def flush():
@@ -234,6 +264,11 @@ def main(argv=None):
         attn.decode_paged(dt["q"], dt["k"], dt["v"], dt["bt"], dt["sl"], dc.max_seq_len, out=dt["o"],
                           workspace=dt["ws"])
 
+    def run_chunked():
+        cc, ct, _ = chk
+        attn.fwd_paged(ct["q"], ct["k"], ct["v"], ct["bt"], ct["cu"], ct["sl"], cc.max_seqlen_q, causal=True,
+                       out=ct["o"])
+
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -246,10 +281,12 @@ def main(argv=None):
         run_prefill()
         if dec:
             run_decode()
+        if chk:
+            run_chunked()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -262,6 +299,11 @@ def main(argv=None):
             ev[i][2].record(stream)
             run_decode()
             ev[i][3].record(stream)
+        if chk:
+            flush()
+            ev[i][4].record(stream)
+            run_chunked()
+            ev[i][5].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -289,7 +331,10 @@ def main(argv=None):
         "data": "synthetic (seeded N(0,1) inputs, no weights)",
         "config": {"workload": "dense non-causal attention fwd B=1 H=32 N=8192 D=128 bf16"
                                + ("" if args.no_decode else
-                                  " + paged split-KV decode 64 seqs L~U[512,32768] Hq=32 Hkv=8 D=128 bf16 KV"),
+                                  " + paged split-KV decode 64 seqs L~U[512,32768] Hq=32 Hkv=8 D=128 bf16 KV")
+                               + ("" if chk is None else
+                                  " + chunked prefill 8x2048 queries over U[0,14336] paged context, causal, "
+                                  "Hq=32 Hkv=8 D=128 bf16"),
                    "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4), "max": round(max(pre_ms), 4)},
         "kernel_source_digest": kernel_source_digest(),
@@ -309,6 +354,17 @@ def main(argv=None):
                                       "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                       "traffic": load_traffic(DECODE_KERNELS),
                                       "kernels": "decode_split_kernel + decode_combine_kernel"}}
+    if chk:
+        cc, _, cflops = chk
+        cms = [e[4].elapsed_time(e[5]) for e in ev]
+        cavg = float(np.mean(cms))
+        ctf = cflops / (cavg * 1e-3) / 1e12
+        out["chunked_prefill"] = {"tflops": round(ctf, 2), "ms": round(cavg, 4), "flops_per_launch": cflops,
+                                  "keys_per_sequence": cc.seq_lens_k.tolist(),
+                                  "roofline": {"bound": "mfma", "achieved": round(ctf, 2), "peak": PEAK_BF16_TFLOPS,
+                                               "unit": "TFLOP/s", "frac": round(ctf / PEAK_BF16_TFLOPS, 4),
+                                               "traffic": load_traffic(CHUNKED_KERNEL),
+                                               "kernel": "fwd_mfma16_kernel<128, 8, 64, bf16, paged>"}}
     out["cache_flush_before_each_launch"] = flush_buf is not None
 
     # ------------------------------------------------------- measured peaks ----
@@ -318,6 +374,9 @@ def main(argv=None):
         mp = peaks["mfma_bf16_32x32x16_one_wave_per_simd"]["random_operands"]["tflops"]
         out["roofline"]["measured_peak"] = mp
         out["roofline"]["frac_of_measured"] = round(tflops / mp, 4)
+        if chk:
+            out["chunked_prefill"]["roofline"]["measured_peak"] = mp
+            out["chunked_prefill"]["roofline"]["frac_of_measured"] = round(out["chunked_prefill"]["tflops"] / mp, 4)
         if dec:
             hp = peaks["hbm_read_nontemporal_gbps"]
             out["decode"]["roofline"]["measured_peak"] = hp

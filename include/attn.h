@@ -9,6 +9,9 @@
  *   attn_decode_paged  the same for one query token per sequence over a paged
  *                      KV cache, split along the keys across workgroups and
  *                      merged with an LSE-weighted combine.
+ *   attn_fwd_paged     chunked prefill: a chunk of new query tokens per
+ *                      sequence attends to that sequence's keys in the same
+ *                      paged KV cache.
  *
  * The operation is the softmax attention of the page "Agent 帮我写 CUDA：一个
  * Softmax Attention 算子的开发全记录" (section 二, reference baseline and the
@@ -104,6 +107,54 @@ typedef struct {
  */
 attn_status_t attn_fwd(const attn_fwd_args_t *args, const void *q, const void *k, const void *v,
                        void *o, float *lse, void *stream);
+
+/* ------------------------------------------------- chunked prefill (paged) ---- */
+
+typedef struct {
+  int32_t num_seqs;          /* S >= 1 */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv, Hq % Hkv == 0 */
+  int32_t head_dim;          /* D in {32, 64, 128} */
+  int32_t page_size;         /* tokens per page; must be 16 */
+  int32_t max_pages_per_seq; /* row length of block_table */
+  int32_t num_pages;         /* pages in each cache (rows of k_cache / v_cache) */
+  int32_t max_seqlen_q;      /* host-known upper bound of every chunk's query count; sizes the grid */
+  int32_t dtype;             /* ATTN_F16 or ATTN_BF16: Q, both caches and O */
+  int32_t causal;            /* 0/1, bottom-right aligned as for attn_fwd */
+  int32_t window;            /* as for attn_fwd (requires causal) */
+  float softmax_scale;       /* <= 0: 1/sqrt(D) as for attn_fwd */
+  float softcap;             /* as for attn_fwd */
+} attn_fwd_paged_args_t;
+
+/*
+ * attn_fwd_paged - chunked prefill over a paged KV cache ("分块 prefill" over paged KV,
+ * scenario axes of "Ask, Don't Equip: Question-Driven Coding Agents for Deep Kernel
+ * Optimization", section 研究动机, which names the case without defining it). Reading
+ * used: sequence s already holds seq_lens_k[s] = Nk_s keys in the cache, the last
+ * Nq_s of them being the chunk's own tokens; its Nq_s queries are positions
+ * Nk_s - Nq_s ... Nk_s - 1, so causal masking is bottom-right aligned (offset
+ * Nk_s - Nq_s), exactly as a ragged attn_fwd over the gathered keys.
+ *
+ *   q            [T, Hq, D] contiguous (packed chunks), dtype
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, Hkv, D] contiguous, dtype; token t of sequence s
+ *                lives in page block_table[s * max_pages_per_seq + t / page_size], slot
+ *                t % page_size (the decode layout)
+ *   block_table  device int32 [S, max_pages_per_seq], entries in [0, num_pages)
+ *   cu_seqlens_q device int32 [S + 1], non-decreasing from 0: chunk s owns query rows
+ *                [cu_seqlens_q[s], cu_seqlens_q[s+1]), at most max_seqlen_q of them
+ *   seq_lens_k   device int32 [S], 0 <= Nk_s <= max_pages_per_seq * page_size
+ *   o            [T, Hq, D] contiguous, dtype
+ *   lse          nullable float32 [Hq, T], natural log; a row with no allowed key
+ *                gets O = 0 and LSE = -inf
+ *
+ * The kernel clamps page ids to [0, num_pages) and key counts to the table row, so
+ * out-of-range device indices give wrong values, never an access outside the cache.
+ */
+attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t *args, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *cu_seqlens_q, const int32_t *seq_lens_k, void *o,
+                             float *lse, void *stream);
 
 /* ----------------------------------------------------------------- decode ---- */
 

@@ -216,9 +216,11 @@ def prefill_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block
     Nk_b - Nq_b. Returns (o [T, Hq, D], lse [Hq, T]) (rows outside the sample NaN).
     """
     nseq = len(cu_q) - 1
+    wanted = set(range(nseq)) if seqs is None else {int(b) for b in seqs}
     parts_k, parts_v, cu_k = [], [], [0]
     for b in range(nseq):
-        L = int(seq_lens_k[b])
+        # sequences outside the sample contribute no keys (their rows are not computed)
+        L = int(seq_lens_k[b]) if b in wanted else 0
         parts_k.append(gather_pages(k_cache, block_table[b], L, page_size))
         parts_v.append(gather_pages(v_cache, block_table[b], L, page_size))
         cu_k.append(cu_k[-1] + L)

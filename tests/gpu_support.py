@@ -179,3 +179,45 @@ def oracle_decode(case, seqs=None):
 
 def decode_kind(case) -> str:
     return "fp8_e4m3" if case.kv_dtype == "fp8_e4m3" else case.q_dtype
+
+
+# -------------------------------------------------------------- chunked prefill (paged) ----
+
+def paged_prefill_tensors(case):
+    c = case.cache
+    return dict(q=case.q.cuda(), k_cache=c.k_cache.cuda(), v_cache=c.v_cache.cuda(),
+                block_table=torch.from_numpy(c.block_table).cuda(),
+                cu_seqlens_q=torch.from_numpy(case.cu_seqlens_q).cuda(),
+                seq_lens_k=torch.from_numpy(c.seq_lens).cuda())
+
+
+def run_paged_prefill(case, tensors=None):
+    import attention_forward_03_amd as attn
+    t = paged_prefill_tensors(case) if tensors is None else tensors
+    o, lse = attn.fwd_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["cu_seqlens_q"],
+                            t["seq_lens_k"], case.max_seqlen_q, causal=case.causal, window=case.window,
+                            softcap=case.softcap, return_lse=True)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def oracle_paged_prefill(case, *, seqs=None, rows_per_seq=None, heads=None):
+    """Oracle O [T, Hq, D] / LSE [Hq, T] (float64) of a chunked-prefill case; only the pages
+    of the sampled sequences are widened."""
+    c = case.cache
+    nseq = len(case.cu_seqlens_q) - 1
+    sel = np.arange(nseq) if seqs is None else np.asarray(seqs)
+    used = [c.block_table[s, :(int(c.seq_lens[s]) + 15) // 16] for s in sel]
+    pages = np.unique(np.concatenate(used)) if used else np.zeros(0, dtype=np.int64)
+    remap = np.zeros(c.k_cache.shape[0], dtype=np.int64)
+    remap[pages] = np.arange(len(pages))
+    idx = torch.from_numpy(pages.astype(np.int64))
+    kc = oracle.tensor_to_f64(c.k_cache[idx], c.kv_dtype)
+    vc = oracle.tensor_to_f64(c.v_cache[idx], c.kv_dtype)
+    bt = remap[c.block_table.astype(np.int64)]
+    q = oracle.tensor_to_f64(case.q, c.q_dtype)
+    return oracle.prefill_paged(q, kc, vc, bt, case.cu_seqlens_q, c.seq_lens,
+                                scale=oracle.default_scale(c.head_dim), causal=case.causal,
+                                window=case.window, softcap=case.softcap,
+                                seqs=None if seqs is None else list(sel), rows_per_seq=rows_per_seq,
+                                heads=heads)

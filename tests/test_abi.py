@@ -101,6 +101,64 @@ def test_fwd_empty_query_is_a_no_op():
     assert L.attn_fwd(ctypes.byref(a), None, None, None, None, None, None) == _lib.ATTN_SUCCESS
 
 
+def _paged_args(**kw):
+    a = _lib.FwdPagedArgs()
+    base = dict(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, max_pages_per_seq=64,
+                num_pages=256, max_seqlen_q=512, dtype=_lib.ATTN_BF16, causal=1, window=0, softmax_scale=0.0,
+                softcap=0.0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=0), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(num_q_heads=6, num_kv_heads=4), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(head_dim=96), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(dtype=_lib.ATTN_F32), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(dtype=_lib.ATTN_FP8_E4M3), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(page_size=32), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(max_pages_per_seq=0), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(num_pages=0), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(max_seqlen_q=-1), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(causal=0, window=8), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(causal=3), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(softmax_scale=float("inf")), _lib.ATTN_ERROR_INVALID_VALUE),
+])
+def test_fwd_paged_rejects_bad_arguments(kw, status):
+    L = _lib.lib()
+    a = _paged_args(**kw)
+    st = L.attn_fwd_paged(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == status, L.attn_last_error_message()
+    assert len(L.attn_last_error_message()) > 0
+
+
+def test_fwd_paged_rejects_null_and_misaligned_pointers():
+    L = _lib.lib()
+    a = _paged_args()
+    assert L.attn_fwd_paged(None, *([FAKE] * 7), None, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    for i in range(7):
+        ptrs = [FAKE] * 7
+        ptrs[i] = None
+        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None) == _lib.ATTN_ERROR_INVALID_VALUE, i
+    for i, bad in ((0, FAKE + 8), (1, FAKE + 8), (2, FAKE + 8), (6, FAKE + 8)):
+        ptrs = [FAKE] * 7
+        ptrs[i] = bad
+        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None) == _lib.ATTN_ERROR_NOT_SUPPORTED, i
+    for i in (3, 4, 5):
+        ptrs = [FAKE] * 7
+        ptrs[i] = FAKE + 2
+        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None) == _lib.ATTN_ERROR_INVALID_VALUE, i
+    assert L.attn_fwd_paged(ctypes.byref(a), *([FAKE] * 7), FAKE + 2, None) == _lib.ATTN_ERROR_INVALID_VALUE
+
+
+def test_fwd_paged_empty_chunks_are_a_no_op():
+    L = _lib.lib()
+    a = _paged_args(max_seqlen_q=0)
+    assert L.attn_fwd_paged(ctypes.byref(a), *([None] * 9)) == _lib.ATTN_SUCCESS
+
+
 def _dec_kw(**kw):
     base = dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, max_pages_per_seq=2048,
                 max_seq_len=32768, q_dtype=_lib.ATTN_BF16, kv_dtype=_lib.ATTN_BF16)

@@ -400,3 +400,19 @@ def test_paged_prefill_page_permutation_invariance():
     bt_bad[0, [0, 1]] = bt_bad[0, [1, 0]]
     o3, _ = oracle.prefill_paged(q, kc, vc, bt_bad, cu_q, case.seq_lens, scale=0.5, window=7)
     assert not np.allclose(o3[:33], o[:33])
+
+
+def test_paged_prefill_sample_equals_full():
+    case = make_decode(lengths=[40, 7, 19], num_q_heads=2, num_kv_heads=1, head_dim=4,
+                       kv_dtype="bf16", seed=24)
+    kc = oracle.tensor_to_f64(case.k_cache, "bf16")
+    vc = oracle.tensor_to_f64(case.v_cache, "bf16")
+    cu_q = np.array([0, 9, 16, 35])
+    q = _rand(35, 2, 4)
+    o, lse = oracle.prefill_paged(q, kc, vc, case.block_table, cu_q, case.seq_lens, scale=0.5)
+    o2, lse2 = oracle.prefill_paged(q, kc, vc, case.block_table, cu_q, case.seq_lens, scale=0.5,
+                                    seqs=[2], rows_per_seq={2: [0, 5, 18]}, heads=np.array([1]))
+    rows = 16 + np.array([0, 5, 18])
+    np.testing.assert_array_equal(o2[rows, 1], o[rows, 1])
+    np.testing.assert_array_equal(lse2[1, rows], lse[1, rows])
+    assert np.isnan(o2[:16]).all() and np.isnan(o2[rows, 0]).all()

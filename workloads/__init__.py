@@ -241,6 +241,45 @@ def make_decode(*, lengths: Sequence[int], num_q_heads: int, num_kv_heads: int, 
                       v_scale=v_scale, poison_page=poison, k_logical=k_log, v_logical=v_log)
 
 
+@dataclasses.dataclass
+class PagedPrefillCase:
+    """Chunked prefill over a paged cache: chunk b's queries q[cu_seqlens_q[b]:cu_seqlens_q[b+1]]
+    ([T, Hq, D] packed) are the last positions of sequence b, whose seq_lens_k[b] keys (the
+    chunk's own included) sit in ``cache``'s pages (``cache.q`` is unused)."""
+    q: torch.Tensor
+    cu_seqlens_q: np.ndarray
+    cache: DecodeCase
+    causal: bool = True
+    window: int = 0
+    softcap: float = 0.0
+
+    @property
+    def seq_lens_k(self) -> np.ndarray:
+        return self.cache.seq_lens
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(np.diff(self.cu_seqlens_q).max()) if len(self.cu_seqlens_q) > 1 else 0
+
+
+def make_paged_prefill(*, lengths_q: Sequence[int], lengths_k: Sequence[int], num_q_heads: int,
+                       num_kv_heads: int, head_dim: int, dtype: str = "bf16", seed: int,
+                       causal: bool = True, window: int = 0, softcap: float = 0.0,
+                       keep_logical: bool = False, max_pages: Optional[int] = None) -> PagedPrefillCase:
+    """The cache as make_decode draws it (seed), then Q iid N(0,1) from a generator of its
+    own (seed + 1_000_003)."""
+    lengths_q = [int(x) for x in lengths_q]
+    cache = make_decode(lengths=lengths_k, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, q_dtype=dtype, kv_dtype=dtype, seed=seed,
+                        keep_logical=keep_logical, max_pages=max_pages)
+    cu = np.zeros(len(lengths_q) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths_q)
+    rng = np.random.Generator(np.random.PCG64(seed + 1_000_003))
+    q = _cast(_normal(rng, (int(cu[-1]), num_q_heads, head_dim)), dtype)
+    return PagedPrefillCase(q=q, cu_seqlens_q=cu, cache=cache, causal=causal, window=window,
+                            softcap=softcap)
+
+
 # ----------------------------------------------------------------------------------------
 # The five workload families of the problem statement, by name.
 # ----------------------------------------------------------------------------------------
@@ -309,6 +348,25 @@ def config_decode(kv_dtype: str, seed: int = 5, num_seqs: int = 64,
 # one-hot digit code; a query carries the code of its target scaled by ``amp``. A key
 # matching all digits scores 3*amp, one differing in a digit at most 2*amp.
 # ----------------------------------------------------------------------------------------
+
+def chunked_prefill_lengths(seed: int = 6, num_seqs: int = 8, chunk: int = 2048,
+                            max_context: int = 14336):
+    """A chunk of ``chunk`` new tokens per sequence after a cached context of uniform length
+    in [0, max_context]: (lengths_q, lengths_k)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = rng.integers(0, max_context + 1, size=num_seqs)
+    return [chunk] * num_seqs, [int(c) + chunk for c in ctx]
+
+
+def config_chunked_prefill(seed: int = 6, num_seqs: int = 8, chunk: int = 2048,
+                           max_context: int = 14336) -> PagedPrefillCase:
+    """Chunked prefill after the causal GQA family (Hq=32, Hkv=8, D=128, bf16, values
+    N(0,1)): chunks of 2048 queries over contexts uniform in [0, 14336] in 16-token pages
+    at randomly permuted block-table indices."""
+    lq, lk = chunked_prefill_lengths(seed, num_seqs, chunk, max_context)
+    return make_paged_prefill(lengths_q=lq, lengths_k=lk, num_q_heads=32, num_kv_heads=8,
+                              head_dim=128, dtype="bf16", seed=seed)
+
 
 def position_code(pos: np.ndarray, dim: int, base: int = 16, digits: int = 3) -> np.ndarray:
     """[len(pos), dim] float32 one-hot digit code of each position (base ** digits > pos)."""
