@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, AttnInvalidValue, AttnNotSupported
 
-__all__ = ["fwd", "fwd_paged", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
+__all__ = ["fwd", "fwd_paged", "fwd_paged_workspace_size", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
            "AttnError", "AttnInvalidValue", "AttnNotSupported"]
 
 _DTYPES = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
@@ -124,7 +124,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
 def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
               cu_seqlens_q: torch.Tensor, seq_lens_k: torch.Tensor, max_seqlen_q: int, *, causal: bool = True,
               window: int = 0, softcap: float = 0.0, softmax_scale: float = 0.0, return_lse: bool = False,
-              out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
+              out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, gather: bool = True):
     """Chunked prefill over a paged KV cache.
 
     q [T, Hq, D] packed chunks (int32 cu_seqlens_q [S+1] on the GPU, max_seqlen_q a
@@ -132,6 +133,10 @@ def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     dtype (bf16/f16); block_table int32 [S, max_pages]; seq_lens_k int32 [S], the
     keys of each sequence, the chunk's own included. Returns o [T, Hq, D] (and lse
     [Hq, T] float32 if return_lse).
+
+    gather: use the gathered-key route where the library has one (a workspace of
+    fwd_paged_workspace_size bytes, allocated here unless ``workspace`` is given);
+    gather=False reads the pages in place.
     """
     _require_cuda(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k)
     for t in (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k):
@@ -166,11 +171,36 @@ def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
         lse = torch.empty(shape, dtype=torch.float32, device=q.device) if lse_out is None else lse_out
         if lse.shape != shape or lse.dtype != torch.float32 or not lse.is_contiguous():
             raise ValueError(f"lse_out must be a contiguous float32 tensor of shape {shape}")
-    status = _lib.lib().attn_fwd_paged(ctypes.byref(a), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                       _ptr(cu_seqlens_q), _ptr(seq_lens_k), _ptr(o), _ptr(lse),
-                                       _stream_handle(q.device))
+    L = _lib.lib()
+    ws_bytes = 0
+    if gather:
+        need = int(L.attn_fwd_paged_workspace_size(ctypes.byref(a)))
+        if need > 0 and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if need == 0:
+            workspace = None
+    else:
+        workspace = None
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        ws_bytes = workspace.numel()
+    status = L.attn_fwd_paged(ctypes.byref(a), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                              _ptr(cu_seqlens_q), _ptr(seq_lens_k), _ptr(o), _ptr(lse), _ptr(workspace),
+                              ws_bytes, _stream_handle(q.device))
     _lib.check(status)
     return (o, lse) if return_lse else o
+
+
+def fwd_paged_workspace_size(*, num_seqs, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, num_pages,
+                             dtype, max_seqlen_q=1, page_size=16) -> int:
+    """Bytes of workspace the gathered route of fwd_paged uses (0: no such route)."""
+    a = _lib.FwdPagedArgs()
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
+    a.page_size, a.max_pages_per_seq, a.num_pages, a.max_seqlen_q = page_size, max_pages_per_seq, num_pages, max_seqlen_q
+    a.dtype = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    a.causal = 1
+    return int(_lib.lib().attn_fwd_paged_workspace_size(ctypes.byref(a)))
 
 
 def _decode_args(*, num_seqs, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, max_seq_len,

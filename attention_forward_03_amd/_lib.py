@@ -18,7 +18,7 @@ ATTN_F16 = 1
 ATTN_BF16 = 2
 ATTN_FP8_E4M3 = 3
 
-EXPORTED = ("attn_fwd", "attn_fwd_paged", "attn_decode_plan", "attn_decode_paged_workspace_size", "attn_decode_paged",
+EXPORTED = ("attn_fwd", "attn_fwd_paged", "attn_fwd_paged_workspace_size", "attn_decode_plan", "attn_decode_paged_workspace_size", "attn_decode_paged",
             "attn_probe_mfma", "attn_probe_hbm_read", "attn_flush_caches",
             "attn_status_string", "attn_last_error_message", "attn_abi_version")
 
@@ -93,8 +93,11 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.attn_fwd.restype = ctypes.c_int
-    L.attn_fwd_paged.argtypes = [ctypes.POINTER(FwdPagedArgs)] + [ctypes.c_void_p] * 9
+    L.attn_fwd_paged.argtypes = [ctypes.POINTER(FwdPagedArgs)] + [ctypes.c_void_p] * 9 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
     L.attn_fwd_paged.restype = ctypes.c_int
+    L.attn_fwd_paged_workspace_size.argtypes = [ctypes.POINTER(FwdPagedArgs)]
+    L.attn_fwd_paged_workspace_size.restype = ctypes.c_size_t
     L.attn_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int32),
                                    ctypes.POINTER(ctypes.c_int32)]
     L.attn_decode_plan.restype = ctypes.c_int

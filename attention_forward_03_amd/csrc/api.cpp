@@ -165,9 +165,7 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
   return ok();
 }
 
-attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* block_table, const int32_t* cu_seqlens_q,
-                             const int32_t* seq_lens_k, void* o, float* lse, void* stream) {
+static attn_status_t check_fwd_paged_args(const attn_fwd_paged_args_t* a) {
   if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
   if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
     return fail(ATTN_ERROR_INVALID_VALUE, "num_seqs, num_q_heads and num_kv_heads must be >= 1");
@@ -196,6 +194,38 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, cons
     return fail(ATTN_ERROR_NOT_SUPPORTED, "num_kv_heads * head_dim must be below 2^24");
   if ((int64_t)a->num_q_heads * a->head_dim >= (int64_t)1 << 24)
     return fail(ATTN_ERROR_NOT_SUPPORTED, "num_q_heads * head_dim must be below 2^24");
+  return ATTN_SUCCESS;
+}
+
+// The gathered-key route (head_dim 128): the workspace holds K and V of every sequence in a
+// slot of max_pages_per_seq * page_size tokens each.
+static size_t fwd_paged_gather_bytes(const attn_fwd_paged_args_t* a) {
+  if (a->head_dim != 128) return 0;
+  const size_t half = (size_t)a->num_seqs * a->max_pages_per_seq * kPageSize * a->num_kv_heads * a->head_dim *
+                      (size_t)elem_size(a->dtype);
+  return 2 * ((half + 255) & ~(size_t)255);
+}
+
+size_t attn_fwd_paged_workspace_size(const attn_fwd_paged_args_t* a) {
+  if (check_fwd_paged_args(a) != ATTN_SUCCESS) return 0;
+  return fwd_paged_gather_bytes(a);
+}
+
+attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table, const int32_t* cu_seqlens_q,
+                             const int32_t* seq_lens_k, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  attn_status_t st0 = check_fwd_paged_args(a);
+  if (st0 != ATTN_SUCCESS) return st0;
+  const size_t need = fwd_paged_gather_bytes(a);
+  const bool gather = workspace != nullptr && need > 0;
+  if (gather && workspace_bytes < need)
+    return fail(ATTN_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need);
+  if (gather && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(ATTN_ERROR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  if (gather && (int64_t)a->num_seqs * a->max_pages_per_seq * kPageSize >= ((int64_t)1 << 31))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_seqs * max_pages_per_seq * page_size must be below 2^31");
   if (a->max_seqlen_q == 0) return ok();  // nothing to compute
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o == nullptr || block_table == nullptr ||
       cu_seqlens_q == nullptr || seq_lens_k == nullptr)
@@ -241,7 +271,27 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, cons
   p.max_pages = a->max_pages_per_seq;
   p.num_pages = a->num_pages;
 
-  hipError_t e = attn::launch_fwd_paged(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (gather) {
+    // pages -> per-sequence slots, then the ragged kernel reads the slots
+    char* wk = static_cast<char*>(workspace);
+    char* wv = wk + need / 2;
+    e = attn::launch_gather_kv_pages(k_cache, v_cache, block_table, seq_lens_k, wk, wv, a->num_seqs,
+                                     a->max_pages_per_seq, a->num_pages,
+                                     (int)(kPageSize * tok_k * elem_size(a->dtype)), hs);
+    if (e == hipSuccess) {
+      p.k = wk;
+      p.v = wv;
+      p.ks[0] = p.vs[0] = 0;
+      p.block_table = nullptr;
+      const int bm = attn::fwd_block_rows(a->dtype, a->head_dim);
+      p.q_tiles = (a->max_seqlen_q + bm - 1) / bm;
+      e = attn::launch_fwd(p, a->dtype, a->head_dim, hs);
+    }
+  } else {
+    e = attn::launch_fwd_paged(p, a->dtype, a->head_dim, hs);
+  }
   if (e != hipSuccess)
     return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -26,7 +26,9 @@ struct FwdParams {
   int32_t q_tiles;      // query tiles per sequence
   // paged keys (chunked prefill): k / v are caches [pages, 16, Hkv, D]; ks[0] / vs[0] are
   // the page strides and ks[2] / vs[2] the token strides; sequence b has seq_lens_k[b]
-  // keys in the pages that row b of block_table [batch, max_pages] names
+  // keys in the pages that row b of block_table [batch, max_pages] names. For the ragged
+  // kernels (cu_q set, block_table NULL) a non-NULL seq_lens_k means: sequence b's keys
+  // are tokens [b * max_pages * 16, + seq_lens_k[b]) of the packed k / v (gathered pages)
   const int32_t* block_table;
   const int32_t* seq_lens_k;
   int32_t max_pages, num_pages;
@@ -58,6 +60,10 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t s
 // chunked prefill over a paged cache (16-bit inputs)
 hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
 int fwd_paged_block_rows();
+// page-by-page copy of K and V into per-sequence slots of max_pages * 16 tokens
+hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,
+                                  int num_pages, int page_bytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t stream);
 
 hipError_t launch_probe_mfma(const uint32_t* operands, int workgroups, int iters, int valu_mix, uint64_t* clocks,

@@ -517,8 +517,14 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
   if (p.cu_q != nullptr) {
     q_off = p.cu_q[b];
     Lq = p.cu_q[b + 1] - q_off;
-    k_off = p.cu_k[b];
-    Lk = p.cu_k[b + 1] - k_off;
+    if (p.seq_lens_k != nullptr) {
+      // keys gathered from a paged cache: sequence b's slot of max_pages * 16 tokens
+      k_off = b * p.max_pages * 16;
+      Lk = min(max(p.seq_lens_k[b], 0), p.max_pages * 16);
+    } else {
+      k_off = p.cu_k[b];
+      Lk = p.cu_k[b + 1] - k_off;
+    }
   }
   const int r0 = qt * BM;
   if (r0 >= Lq) return;
@@ -566,8 +572,9 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
       if (qrow[rb] < Lq) {
+        // the lane's 4 entries (offset hi * 4) of each 8-entry chunk of the row
 #pragma unroll
-        for (int c = 0; c < D / 8; c += 2)
+        for (int c = 0; c < D / 8; ++c)
           *reinterpret_cast<u32x2_t*>(oa[rb] + c * 8) = u32x2_t{0, 0};
         if (hi == 0 && p.lse != nullptr) *la[rb] = kNegInf;
       }
@@ -873,6 +880,32 @@ hipError_t launch32(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Copy of each sequence's pages of K and V into its slot of max_pages * 16 tokens in a
+// token-major workspace [S * max_pages * 16, Hkv, D]. A page of 16 tokens is one
+// contiguous block in the cache and in the workspace, so the copy streams whole pages
+// (nontemporal reads: the cache is read once). Workgroup (j, s) copies page j of sequence
+// s if the sequence has that many pages. Page ids are clamped to the cache.
+__global__ __launch_bounds__(256) void gather_kv_pages_kernel(const u32x4_t* __restrict__ kc,
+                                                              const u32x4_t* __restrict__ vc,
+                                                              const int32_t* __restrict__ bt,
+                                                              const int32_t* __restrict__ seq_lens,
+                                                              u32x4_t* __restrict__ wk, u32x4_t* __restrict__ wv,
+                                                              int max_pages, int num_pages, int page16) {
+  const int j = blockIdx.x, sq = blockIdx.y;
+  const int L = min(max(seq_lens[sq], 0), max_pages * 16);
+  if (j * 16 >= L) return;
+  const int page = min(max(bt[(int64_t)sq * max_pages + j], 0), num_pages - 1);
+  const u32x4_t* ks = kc + (int64_t)page * page16;
+  const u32x4_t* vs = vc + (int64_t)page * page16;
+  const int64_t dst = ((int64_t)sq * max_pages + j) * page16;
+  for (int i = threadIdx.x; i < page16; i += 256) {
+    const u32x4_t a = __builtin_nontemporal_load(ks + i);
+    const u32x4_t c = __builtin_nontemporal_load(vs + i);
+    wk[dst + i] = a;
+    wv[dst + i] = c;
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch16_paged(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = (int64_t)p.q_tiles * p.hq * p.batch;
@@ -885,6 +918,16 @@ hipError_t launch16_paged(const FwdParams& p, hipStream_t st) {
 }  // namespace
 
 int fwd_paged_block_rows() { return kNW16 * 32; }
+
+hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,
+                                  int num_pages, int page_bytes, hipStream_t st) {
+  hipLaunchKernelGGL(gather_kv_pages_kernel, dim3(max_pages, num_seqs), dim3(256), 0, st,
+                     static_cast<const u32x4_t*>(k_cache), static_cast<const u32x4_t*>(v_cache), block_table,
+                     seq_lens, static_cast<u32x4_t*>(ws_k), static_cast<u32x4_t*>(ws_v), max_pages, num_pages,
+                     page_bytes / 16);
+  return hipGetLastError();
+}
 
 // dtype: 1 = f16, 2 = bf16
 hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStream_t st) {

@@ -65,7 +65,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 PREFILL_KERNEL = "fwd_r2_kernel<true, 0>"
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
-CHUNKED_KERNEL = "fwd_mfma16_kernel<128, 8, 64, true, true>"
+CHUNKED_KERNEL = ("gather_kv_pages_kernel", "fwd_r2_kernel<true, 1>")
 
 
 def kernel_source_digest() -> str:
@@ -246,6 +246,10 @@ def main(argv=None):
               "bt": torch.from_numpy(cc.cache.block_table).to(dev),
               "cu": torch.from_numpy(cc.cu_seqlens_q).to(dev), "sl": torch.from_numpy(cc.seq_lens_k).to(dev)}
         ct["o"] = torch.empty_like(ct["q"])
+        ws = attn.fwd_paged_workspace_size(num_seqs=len(cc.seq_lens_k), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                           max_pages_per_seq=cc.cache.max_pages, num_pages=cc.cache.k_cache.shape[0],
+                                           dtype=torch.bfloat16)
+        ct["ws"] = torch.empty(ws, dtype=torch.uint8, device=dev)
         chk = (cc, ct, chunked_flops(cc))
         del cc.cache.k_cache, cc.cache.v_cache
 
@@ -264,10 +268,10 @@ def main(argv=None):
         attn.decode_paged(dt["q"], dt["k"], dt["v"], dt["bt"], dt["sl"], dc.max_seq_len, out=dt["o"],
                           workspace=dt["ws"])
 
-    def run_chunked():
+    def run_chunked(gather=True):
         cc, ct, _ = chk
         attn.fwd_paged(ct["q"], ct["k"], ct["v"], ct["bt"], ct["cu"], ct["sl"], cc.max_seqlen_q, causal=True,
-                       out=ct["o"])
+                       out=ct["o"], workspace=ct["ws"] if gather else None, gather=gather)
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
@@ -283,10 +287,11 @@ def main(argv=None):
             run_decode()
         if chk:
             run_chunked()
+            run_chunked(gather=False)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -304,6 +309,10 @@ def main(argv=None):
             ev[i][4].record(stream)
             run_chunked()
             ev[i][5].record(stream)
+            flush()
+            ev[i][6].record(stream)
+            run_chunked(gather=False)
+            ev[i][7].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -359,11 +368,17 @@ def main(argv=None):
         cms = [e[4].elapsed_time(e[5]) for e in ev]
         cavg = float(np.mean(cms))
         ctf = cflops / (cavg * 1e-3) / 1e12
+        dms_ = [e[6].elapsed_time(e[7]) for e in ev]
+        davg_ = float(np.mean(dms_))
         out["chunked_prefill"] = {"tflops": round(ctf, 2), "ms": round(cavg, 4), "flops_per_launch": cflops,
+                                  "route": "page copy into the workspace + ragged prefill kernel (both timed)",
                                   "keys_per_sequence": cc.seq_lens_k.tolist(),
                                   "roofline": {"bound": "mfma", "achieved": round(ctf, 2), "peak": PEAK_BF16_TFLOPS,
                                                "unit": "TFLOP/s", "frac": round(ctf / PEAK_BF16_TFLOPS, 4),
                                                "traffic": load_traffic(CHUNKED_KERNEL),
+                                               "kernel": "gather_kv_pages_kernel + fwd_r2_kernel<bf16, masked>"},
+                                  "in_place": {"tflops": round(cflops / (davg_ * 1e-3) / 1e12, 2),
+                                               "ms": round(davg_, 4),
                                                "kernel": "fwd_mfma16_kernel<128, 8, 64, bf16, paged>"}}
     out["cache_flush_before_each_launch"] = flush_buf is not None
 

@@ -147,14 +147,25 @@ typedef struct {
  *   o            [T, Hq, D] contiguous, dtype
  *   lse          nullable float32 [Hq, T], natural log; a row with no allowed key
  *                gets O = 0 and LSE = -inf
+ *   workspace    nullable device buffer, 256-byte aligned, of at least
+ *                attn_fwd_paged_workspace_size(args) bytes when that size is non-zero.
+ *                Given one (head_dim 128), the call first copies each sequence's pages
+ *                of K and V into the workspace (one slot of max_pages_per_seq * page_size
+ *                tokens per sequence) and then runs the ragged prefill kernel on the
+ *                copy, the faster route; without one, a single kernel reads the pages
+ *                in place. Both give the same mathematical result (rounding may differ).
  *
- * The kernel clamps page ids to [0, num_pages) and key counts to the table row, so
+ * The kernels clamp page ids to [0, num_pages) and key counts to the table row, so
  * out-of-range device indices give wrong values, never an access outside the cache.
  */
 attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t *args, const void *q, const void *k_cache,
                              const void *v_cache, const int32_t *block_table,
                              const int32_t *cu_seqlens_q, const int32_t *seq_lens_k, void *o,
-                             float *lse, void *stream);
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_fwd_paged can use for these args: 0 when there is no
+ * gathered route for them (head_dim 32 / 64) or on bad args. */
+size_t attn_fwd_paged_workspace_size(const attn_fwd_paged_args_t *args);
 
 /* ----------------------------------------------------------------- decode ---- */
 

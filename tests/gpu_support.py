@@ -72,8 +72,8 @@ def run_prefill(case, *, return_lse=True, out=None):
         kw.update(cu_seqlens_q=torch.from_numpy(case.cu_seqlens_q).cuda(),
                   cu_seqlens_k=torch.from_numpy(case.cu_seqlens_k).cuda(),
                   max_seqlen_q=case.seqlen_q, max_seqlen_k=case.seqlen_k)
-    if out is not None:
-        kw["out"] = out
+    # the output starts as NaN: an entry the kernels leave unwritten fails the comparison
+    kw["out"] = torch.full(q.shape, float("nan"), dtype=q.dtype, device=q.device) if out is None else out
     res = attn.fwd(q, k, v, **kw)
     torch.cuda.synchronize()
     if return_lse:
@@ -191,12 +191,15 @@ def paged_prefill_tensors(case):
                 seq_lens_k=torch.from_numpy(c.seq_lens).cuda())
 
 
-def run_paged_prefill(case, tensors=None):
+def run_paged_prefill(case, tensors=None, *, gather=True):
+    """gather=True: the gathered-key route where the library has one (head_dim 128);
+    gather=False: the kernel that reads the pages in place."""
     import attention_forward_03_amd as attn
     t = paged_prefill_tensors(case) if tensors is None else tensors
     o, lse = attn.fwd_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["cu_seqlens_q"],
                             t["seq_lens_k"], case.max_seqlen_q, causal=case.causal, window=case.window,
-                            softcap=case.softcap, return_lse=True)
+                            softcap=case.softcap, return_lse=True, gather=gather,
+                            out=torch.full(t["q"].shape, float("nan"), dtype=t["q"].dtype, device=t["q"].device))
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 

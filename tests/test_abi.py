@@ -129,7 +129,7 @@ def _paged_args(**kw):
 def test_fwd_paged_rejects_bad_arguments(kw, status):
     L = _lib.lib()
     a = _paged_args(**kw)
-    st = L.attn_fwd_paged(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    st = L.attn_fwd_paged(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None)
     assert st == status, L.attn_last_error_message()
     assert len(L.attn_last_error_message()) > 0
 
@@ -137,26 +137,40 @@ def test_fwd_paged_rejects_bad_arguments(kw, status):
 def test_fwd_paged_rejects_null_and_misaligned_pointers():
     L = _lib.lib()
     a = _paged_args()
-    assert L.attn_fwd_paged(None, *([FAKE] * 7), None, None) == _lib.ATTN_ERROR_INVALID_VALUE
+    assert L.attn_fwd_paged(None, *([FAKE] * 7), None, None, 0, None) == _lib.ATTN_ERROR_INVALID_VALUE
     for i in range(7):
         ptrs = [FAKE] * 7
         ptrs[i] = None
-        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None) == _lib.ATTN_ERROR_INVALID_VALUE, i
+        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None, 0, None) == _lib.ATTN_ERROR_INVALID_VALUE, i
     for i, bad in ((0, FAKE + 8), (1, FAKE + 8), (2, FAKE + 8), (6, FAKE + 8)):
         ptrs = [FAKE] * 7
         ptrs[i] = bad
-        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None) == _lib.ATTN_ERROR_NOT_SUPPORTED, i
+        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None, 0, None) == _lib.ATTN_ERROR_NOT_SUPPORTED, i
     for i in (3, 4, 5):
         ptrs = [FAKE] * 7
         ptrs[i] = FAKE + 2
-        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None) == _lib.ATTN_ERROR_INVALID_VALUE, i
-    assert L.attn_fwd_paged(ctypes.byref(a), *([FAKE] * 7), FAKE + 2, None) == _lib.ATTN_ERROR_INVALID_VALUE
+        assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, None, 0, None) == _lib.ATTN_ERROR_INVALID_VALUE, i
+    assert L.attn_fwd_paged(ctypes.byref(a), *([FAKE] * 7), FAKE + 2, None, 0, None) == _lib.ATTN_ERROR_INVALID_VALUE
 
 
 def test_fwd_paged_empty_chunks_are_a_no_op():
     L = _lib.lib()
     a = _paged_args(max_seqlen_q=0)
-    assert L.attn_fwd_paged(ctypes.byref(a), *([None] * 9)) == _lib.ATTN_SUCCESS
+    assert L.attn_fwd_paged(ctypes.byref(a), *([None] * 9), 0, None) == _lib.ATTN_SUCCESS
+
+
+def test_fwd_paged_workspace():
+    L = _lib.lib()
+    a = _paged_args()
+    need = L.attn_fwd_paged_workspace_size(ctypes.byref(a))
+    # K and V of 4 sequences x 64 pages x 16 tokens x 2 heads x 128 x bf16
+    assert need == 2 * 4 * 64 * 16 * 2 * 128 * 2
+    assert L.attn_fwd_paged_workspace_size(ctypes.byref(_paged_args(head_dim=64))) == 0
+    assert L.attn_fwd_paged_workspace_size(ctypes.byref(_paged_args(num_seqs=0))) == 0
+    ptrs = [FAKE] * 7
+    assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, FAKE, need - 1, None) == \
+        _lib.ATTN_ERROR_WORKSPACE_TOO_SMALL
+    assert L.attn_fwd_paged(ctypes.byref(a), *ptrs, None, FAKE + 16, need, None) == _lib.ATTN_ERROR_INVALID_VALUE
 
 
 def _dec_kw(**kw):

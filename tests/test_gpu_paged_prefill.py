@@ -26,9 +26,9 @@ def _case(dtype, d, hq, hkv, mask, seed, lens_q=LENS_Q, lens_k=LENS_K):
                                         head_dim=d, dtype=dtype, seed=seed, **mask)
 
 
-def _check(case, label):
-    note(f"[paged-prefill] {label}")
-    o, lse = run_paged_prefill(case)
+def _check(case, label, gather=True):
+    note(f"[paged-prefill] {label} gather={gather}")
+    o, lse = run_paged_prefill(case, gather=gather)
     ro, rl = oracle_paged_prefill(case)
     s = compare(widen(o, case.cache.q_dtype), ro, case.cache.q_dtype, f"{label} O")
     compare(lse.numpy(), rl, case.cache.q_dtype, f"{label} LSE", lse=True)
@@ -39,6 +39,23 @@ def _check(case, label):
 @pytest.mark.parametrize("mask", MASKS, ids=["causal", "full", "window", "softcap"])
 def test_small_bf16(d, mask):
     _check(_case("bf16", d, 8, 2, mask, seed=d), f"bf16 D={d} {mask}")
+
+
+@pytest.mark.parametrize("mask", MASKS, ids=["causal", "full", "window", "softcap"])
+def test_small_bf16_d128_pages_in_place(mask):
+    """head_dim 128 without a workspace: the kernel that reads the pages in place."""
+    _check(_case("bf16", 128, 8, 2, mask, seed=128), f"bf16 D=128 {mask}", gather=False)
+
+
+def test_routes_agree_and_gather_is_repeatable():
+    case = _case("bf16", 128, 8, 2, dict(causal=True, window=300), seed=129)
+    t = paged_prefill_tensors(case)
+    o_g, l_g = run_paged_prefill(case, t, gather=True)
+    o_d, l_d = run_paged_prefill(case, t, gather=False)
+    compare(widen(o_g, "bf16"), widen(o_d, "bf16"), "bf16", "gathered vs in-place O")
+    compare(l_g.numpy(), l_d.numpy(), "bf16", "gathered vs in-place LSE", lse=True)
+    o_g2, _ = run_paged_prefill(case, t, gather=True)
+    assert torch.equal(o_g.view(torch.int16), o_g2.view(torch.int16))
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -80,14 +97,15 @@ def test_equals_ragged_prefill_bitwise():
     assert torch.equal(l_p, l_r)
 
 
-def test_chunked_prefill_workload_sampled():
+@pytest.mark.parametrize("gather", [True, False], ids=["gathered", "in-place"])
+def test_chunked_prefill_workload_sampled(gather):
     """The workload the benchmark times (8 chunks of 2048 queries over contexts up to 14336
-    keys, Hq=32, Hkv=8, D=128, bf16), in the same launch; the oracle takes sampled rows of
+    keys, Hq=32, Hkv=8, D=128, bf16), in the same launches; the oracle takes sampled rows of
     three sequences, among them the first and last rows of each chunk."""
     case = workloads.config_chunked_prefill()
-    note(f"[paged-prefill] workload: keys {case.seq_lens_k.tolist()}")
+    note(f"[paged-prefill] workload: keys {case.seq_lens_k.tolist()} gather={gather}")
     t = paged_prefill_tensors(case)
-    o, lse = run_paged_prefill(case, t)
+    o, lse = run_paged_prefill(case, t, gather=gather)
     seqs = [0, 3, 7]
     rows = {s: np.unique(np.r_[0, 1, 255, 256, 1000, 2046, 2047]) for s in seqs}
     heads = np.array([0, 5, 31])

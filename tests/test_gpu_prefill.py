@@ -72,6 +72,27 @@ def test_fully_masked_rows_give_zero_and_neg_inf():
         assert np.isneginf(lse.numpy()[:, :, :60]).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_blocks_without_keys_write_whole_rows(dtype):
+    """D = 128: whole 256-row blocks with no allowed key (causal, Nq - Nk >= 256) and a
+    ragged sequence with no keys write O = 0 over every entry of their rows (the output
+    starts as NaN, so an entry left unwritten fails)."""
+    case = workloads.make_prefill(batch=1, num_q_heads=2, num_kv_heads=1, seqlen_q=600, seqlen_k=40,
+                                  head_dim=128, dtype=dtype, seed=6, causal=True)
+    out = torch.full(case.q.shape, float("nan"), dtype=case.q.dtype, device="cuda")
+    o, lse = run_prefill(case, out=out)
+    assert (widen(o, dtype)[:, :, :560] == 0).all()
+    assert np.isneginf(lse.numpy()[:, :, :560]).all()
+    check_prefill_full(case, f"keyless blocks {dtype}")
+    case = workloads.make_prefill_varlen(lengths_q=[300, 7, 20], lengths_k=[300, 0, 20], num_q_heads=2,
+                                         num_kv_heads=2, head_dim=128, dtype=dtype, seed=7, causal=False)
+    out = torch.full(case.q.shape, float("nan"), dtype=case.q.dtype, device="cuda")
+    o, lse = run_prefill(case, out=out)
+    assert (widen(o, dtype)[300:307] == 0).all()
+    assert np.isneginf(lse.numpy()[:, 300:307]).all()
+    check_prefill_full(case, f"ragged keyless sequence {dtype}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_ragged_batches(dtype):
     lengths = [1, 129, 300, 64, 0, 77]
