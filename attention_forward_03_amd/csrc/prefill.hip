@@ -31,6 +31,36 @@ struct RowRange {
   int fend, fbeg;  // keys every row of the wave sees:  [fbeg, fend)
 };
 
+// Work item of workgroup w: (query tile, query head, sequence). Workgroups are dealt to
+// the 8 XCDs round-robin (w % 8), and each XCD has its own L2. The unit of placement is a
+// (sequence, KV head) pair: all query tiles of all query heads that read one KV head run on
+// one XCD and share its L2 copy of K and V, and unit j goes to XCD j % 8, so every XCD
+// gets a slice of every sequence (a ragged or chunked batch stays balanced across XCDs).
+// When the unit count is not a multiple of 8 the work index is taken XCD-major instead.
+struct WorkItem {
+  int qt, h, b;
+};
+__device__ __forceinline__ WorkItem work_item(int w, int nblk, int q_tiles, int hq, int hkv, int batch) {
+  const int G = hq / hkv;
+  const int per = G * q_tiles;  // items per unit
+  const int units = batch * hkv;
+  int j, rem;
+  if ((units & 7) == 0) {
+    const int i = w >> 3;
+    j = (w & 7) + 8 * (i / per);
+    rem = i % per;
+  } else {
+    const int u = (nblk & 7) == 0 ? (w & 7) * (nblk >> 3) + (w >> 3) : w;
+    j = u / per;
+    rem = u % per;
+  }
+  WorkItem r;
+  r.b = j / hkv;
+  r.h = (j % hkv) * G + rem / q_tiles;
+  r.qt = rem % q_tiles;
+  return r;
+}
+
 __device__ __forceinline__ RowRange wave_key_range(const FwdParams& p, int w0, int Lk, int delta) {
   RowRange r;
   r.wend = p.causal ? min(Lk, w0 + 32 + delta) : Lk;
@@ -167,16 +197,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // XCD-aware work order: consecutive workgroup ids land on different XCDs, so the
-  // linear work index is taken XCD-major; the query tiles of one head then run on one
-  // XCD at the same time and share that XCD's L2 copy of the head's K and V.
-  const int nblk = gridDim.x;
-  int u = blockIdx.x;
-  if ((nblk & 7) == 0) u = (u & 7) * (nblk >> 3) + (u >> 3);
-  int qt = u % p.q_tiles;
-  const int h = (u / p.q_tiles) % p.hq;
-  const int b = u / (p.q_tiles * p.hq);
-  if (p.causal) qt = p.q_tiles - 1 - qt;  // longest rows first
+  const WorkItem wi = work_item(blockIdx.x, gridDim.x, p.q_tiles, p.hq, p.hkv, p.batch);
+  const int h = wi.h, b = wi.b;
+  const int qt = p.causal ? p.q_tiles - 1 - wi.qt : wi.qt;  // longest rows first
 
   int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
   if (PAGED || p.cu_q != nullptr) {
@@ -505,13 +528,9 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int nblk = gridDim.x;
-  int u = blockIdx.x;
-  if ((nblk & 7) == 0) u = (u & 7) * (nblk >> 3) + (u >> 3);
-  int qt = u % p.q_tiles;
-  const int h = (u / p.q_tiles) % p.hq;
-  const int b = u / (p.q_tiles * p.hq);
-  if (p.causal) qt = p.q_tiles - 1 - qt;
+  const WorkItem wi = work_item(blockIdx.x, gridDim.x, p.q_tiles, p.hq, p.hkv, p.batch);
+  const int h = wi.h, b = wi.b;
+  const int qt = p.causal ? p.q_tiles - 1 - wi.qt : wi.qt;
 
   int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
   if (p.cu_q != nullptr) {
