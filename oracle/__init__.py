@@ -27,14 +27,19 @@ defining them, and the readings taken here are:
 * grouped heads: query head h reads KV head floor(h / (Hq / Hkv));
 * a fully masked row gives O = 0 and LSE = -inf;
 * LSE is the natural-log log-sum-exp of the final (scaled, capped, masked)
-  scores.
+  scores;
+* attention sink ("attention-sink" in the same list): an optional logit sigma_h
+  per query head that joins every row's normalisation as a score with no value
+  (exp(sigma_h) is added to the denominator and to the LSE's sum); a row with no
+  allowed key then gives O = 0 and LSE = sigma_h.
 
 Function pins (see tests/test_oracle_*.py): brute-force scalar loops, the
 page's online recurrence, closed forms (identical keys, dominant key, N = 1,
 D = 1), invariants (shift, permutation, GQA = MHA, varlen = concatenation,
 paged = dense, chunked paged prefill = brute force with
 scalar page indexing and = decode at one query, page-permutation invariance,
-split/combine associativity, softcap and window limits) and
+split/combine associativity, the sink (brute force, one-key closed form, the
+rescaling identity O_sink = O e^LSE / (e^LSE + e^sigma), a negligible sink), softcap and window limits) and
 library special cases (torch's bf16 / fp16 / float8_e4m3fn conversions).
 """
 from .numerics import (bf16_bits_to_f64, f16_bits_to_f64, e4m3_code_table, e4m3_codes_to_f64,

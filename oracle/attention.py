@@ -11,6 +11,13 @@ head-sharing readings as stated in this package's docstring):
 5. O_i = (sum_j P_ij V_j) / l_i; LSE_i = m_i + ln l_i.
    A row with no allowed key gives O_i = 0, LSE_i = -inf.
 
+Attention sink (optional, one logit sigma_h per query head, natural-log units): a
+score that takes part in every row's normalisation but carries no value, so step 4
+takes m_i = max(max_j S_ij, sigma_h) and adds exp(sigma_h - m_i) to l_i. The
+Ask-Don't-Equip page names "attention-sink" among the masks of the feature surface it
+covers (section 研究动机) without defining it; this is the per-head sink logit of that
+feature surface. A row with no allowed key then gives O_i = 0, LSE_i = sigma_h.
+
 No blocking, fusion or reordering beyond what a library matmul does internally.
 """
 from __future__ import annotations
@@ -63,12 +70,14 @@ def attention_probs(q: np.ndarray, k: np.ndarray, *, scale: float, causal: bool 
 
 def sdpa_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, causal: bool = False,
               window: int = 0, softcap: float = 0.0, q_pos: Optional[np.ndarray] = None,
-              nq_total: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+              nq_total: Optional[int] = None, sink: Optional[np.ndarray] = None
+              ) -> Tuple[np.ndarray, np.ndarray]:
     """One sequence: q [Hq, Nq, D], k/v [Hkv, Nk, D] (float64) -> o [Hq, Nq, D], lse [Hq, Nq].
 
     ``q_pos`` gives the positions (0-based, within a query sequence of length
     ``nq_total``) of the supplied query rows, so that a sample of rows can be
     checked on its own; by default the rows are 0..Nq-1 of an Nq-row sequence.
+    ``sink`` [Hq]: the per-head sink logits (None: no sink).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -83,6 +92,9 @@ def sdpa_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, caus
     mask = _allowed(nq, nk, causal=causal, window=window, q_pos=q_pos, nq_total=nq_total)
     o = np.zeros((hq, nq, v.shape[2]))
     lse = np.full((hq, nq), -np.inf)
+    if sink is not None:
+        sink = np.asarray(sink, dtype=np.float64)
+        lse[:] = sink[:, None]  # the value of rows with no allowed key
     if nk == 0:
         return o, lse
     for h in range(hq):
@@ -92,6 +104,14 @@ def sdpa_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, caus
             s = softcap * np.tanh(s / softcap)
         if mask is not None:
             s = np.where(mask, s, -np.inf)
+        if sink is not None:
+            sg = float(sink[h])
+            m = np.maximum(s.max(axis=1), sg)
+            p = np.exp(s - m[:, None])
+            l = p.sum(axis=1) + np.exp(sg - m)
+            o[h] = (p @ v[g]) / l[:, None]
+            lse[h] = m + np.log(l)
+            continue
         m = s.max(axis=1)
         ok = np.isfinite(m)
         if not ok.all():
@@ -106,7 +126,7 @@ def sdpa_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, caus
 
 def prefill_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, causal: bool = False,
                   window: int = 0, softcap: float = 0.0, q_rows: Optional[np.ndarray] = None,
-                  heads: Optional[np.ndarray] = None):
+                  heads: Optional[np.ndarray] = None, sink: Optional[np.ndarray] = None):
     """Batched dense: q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] -> o [B, Hq', Nq', D], lse [B, Hq', Nq'].
 
     ``q_rows`` / ``heads`` restrict the output to a sample of query rows / query
@@ -124,7 +144,7 @@ def prefill_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, 
             g = h // group
             ob, lb = sdpa_fp64(q[b][h][rows][None], k[b][g][None], v[b][g][None], scale=scale,
                                causal=causal, window=window, softcap=softcap, q_pos=rows,
-                               nq_total=nq)
+                               nq_total=nq, sink=None if sink is None else np.asarray(sink)[[h]])
             o[b, n] = ob[0]
             lse[b, n] = lb[0]
     return o, lse
@@ -133,7 +153,7 @@ def prefill_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float, 
 def prefill_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: np.ndarray, cu_k: np.ndarray, *,
                    scale: float, causal: bool = True, window: int = 0, softcap: float = 0.0,
                    seqs: Optional[np.ndarray] = None, rows_per_seq: Optional[dict] = None,
-                   heads: Optional[np.ndarray] = None):
+                   heads: Optional[np.ndarray] = None, sink: Optional[np.ndarray] = None):
     """Ragged batch: q [T, Hq, D], k/v [Tk, Hkv, D] packed token-major by cu_seqlens.
 
     Sequences are independent; sequence b's queries attend to its own keys with
@@ -158,7 +178,8 @@ def prefill_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: np.ndarray
         for n, h in enumerate(heads):
             g = h // group
             ob, lb = sdpa_fp64(qb[n:n + 1], kb[g:g + 1], vb[g:g + 1], scale=scale, causal=causal,
-                               window=window, softcap=softcap, q_pos=rows, nq_total=q1 - q0)
+                               window=window, softcap=softcap, q_pos=rows, nq_total=q1 - q0,
+                               sink=None if sink is None else np.asarray(sink)[[h]])
             o[q0 + rows, h] = ob[0]
             lse[h, q0 + rows] = lb[0]
     return o, lse
@@ -176,7 +197,7 @@ def gather_pages(cache: np.ndarray, block_table_row: np.ndarray, seq_len: int,
 def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
                  seq_lens: np.ndarray, *, scale: float, k_scale: Optional[np.ndarray] = None,
                  v_scale: Optional[np.ndarray] = None, seqs: Optional[np.ndarray] = None,
-                 page_size: int = 16):
+                 page_size: int = 16, sink: Optional[np.ndarray] = None):
     """Single-token decode over a paged cache.
 
     q [S, Hq, D]; caches [P, page_size, Hkv, D] already widened to float64 (for
@@ -197,7 +218,7 @@ def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_
         if v_scale is not None:
             vl = vl * np.asarray(v_scale, dtype=np.float64)[None, :, None]
         ob, lb = sdpa_fp64(q[s][:, None, :], np.transpose(kl, (1, 0, 2)),
-                           np.transpose(vl, (1, 0, 2)), scale=scale)
+                           np.transpose(vl, (1, 0, 2)), scale=scale, sink=sink)
         o[n] = ob[:, 0]
         lse[n] = lb[:, 0]
     return o, lse
@@ -207,7 +228,7 @@ def prefill_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block
                   cu_q: np.ndarray, seq_lens_k: np.ndarray, *, scale: float, causal: bool = True,
                   window: int = 0, softcap: float = 0.0, seqs: Optional[np.ndarray] = None,
                   rows_per_seq: Optional[dict] = None, heads: Optional[np.ndarray] = None,
-                  page_size: int = 16):
+                  page_size: int = 16, sink: Optional[np.ndarray] = None):
     """Chunked prefill over a paged cache: sequence b's queries q[cu_q[b]:cu_q[b+1]]
     ([T, Hq, D] packed) are its last Nq_b positions and attend to its Nk_b =
     seq_lens_k[b] keys, which sit in the cache pages its block-table row names
@@ -227,7 +248,8 @@ def prefill_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block
     k = np.concatenate(parts_k, axis=0)
     v = np.concatenate(parts_v, axis=0)
     return prefill_varlen(q, k, v, np.asarray(cu_q), np.asarray(cu_k), scale=scale, causal=causal,
-                          window=window, softcap=softcap, seqs=seqs, rows_per_seq=rows_per_seq, heads=heads)
+                          window=window, softcap=softcap, seqs=seqs, rows_per_seq=rows_per_seq, heads=heads,
+                          sink=sink)
 
 
 def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray):

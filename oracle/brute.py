@@ -27,8 +27,10 @@ def _allowed(i: int, j: int, nq: int, nk: int, causal: bool, window: int) -> boo
 
 
 def brute_sdpa(q, k, v, *, scale: float, causal: bool = False, window: int = 0,
-               softcap: float = 0.0):
-    """q [Hq][Nq][D], k/v [Hkv][Nk][D] nested lists -> (o [Hq][Nq][D], lse [Hq][Nq])."""
+               softcap: float = 0.0, sink=None):
+    """q [Hq][Nq][D], k/v [Hkv][Nk][D] nested lists -> (o [Hq][Nq][D], lse [Hq][Nq]).
+    ``sink`` [Hq]: per-head sink logits, a valueless extra term of each row's
+    normalisation (None: none)."""
     hq, hkv = len(q), len(k)
     group = hq // hkv
     nq, nk = len(q[0]), len(k[0])
@@ -46,11 +48,15 @@ def brute_sdpa(q, k, v, *, scale: float, causal: bool = False, window: int = 0,
                 if softcap > 0:
                     s = softcap * math.tanh(s / softcap)
                 scores.append((j, s))
+            if sink is not None:
+                # the sink joins the normalisation as a valueless score (index -1)
+                scores.append((-1, float(sink[h])))
             if not scores:
                 continue
             m = max(s for _, s in scores)
             w = [(j, math.exp(s - m)) for j, s in scores]
             l = math.fsum(x for _, x in w)
+            w = [(j, x) for j, x in w if j >= 0]
             for d in range(dv):
                 o[h][i][d] = math.fsum(x * v[g][j][d] for j, x in w) / l
             lse[h][i] = m + math.log(l)

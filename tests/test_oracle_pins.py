@@ -416,3 +416,78 @@ def test_paged_prefill_sample_equals_full():
     np.testing.assert_array_equal(o2[rows, 1], o[rows, 1])
     np.testing.assert_array_equal(lse2[1, rows], lse[1, rows])
     assert np.isnan(o2[:16]).all() and np.isnan(o2[rows, 0]).all()
+
+
+# ------------------------------------------------------------------- attention sink ----
+
+@pytest.mark.parametrize("hq,hkv,nq,nk,d", [(2, 1, 5, 5, 3), (4, 2, 7, 3, 4), (2, 2, 1, 9, 2)])
+@pytest.mark.parametrize("causal,window,softcap", [(False, 0, 0.0), (True, 0, 0.0), (True, 2, 1.5)])
+def test_sink_brute_force(hq, hkv, nq, nk, d, causal, window, softcap):
+    q, k, v = _rand(hq, nq, d, scale=1.5), _rand(hkv, nk, d, scale=1.5), _rand(hkv, nk, d)
+    sink = _rand(hq, scale=2.0)
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.6, causal=causal, window=window, softcap=softcap, sink=sink)
+    ob, lb = brute.brute_sdpa(_tolist(q), _tolist(k), _tolist(v), scale=0.6, causal=causal, window=window,
+                              softcap=softcap, sink=_tolist(sink))
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lb), rtol=0, atol=1e-12)
+
+
+def test_sink_closed_forms():
+    # one key: O = v e^s / (e^s + e^sigma), LSE = ln(e^s + e^sigma)
+    q, k, v = np.array([[[0.3, -1.2]]]), np.array([[[2.0, 0.5]]]), np.array([[[1.5, -4.0]]])
+    s = (0.3 * 2.0 - 1.2 * 0.5) * 0.7
+    sigma = 0.25
+    o, lse = oracle.sdpa_fp64(q, k, v, scale=0.7, sink=np.array([sigma]))
+    w = math.exp(s) / (math.exp(s) + math.exp(sigma))
+    np.testing.assert_allclose(o[0, 0], [1.5 * w, -4.0 * w], rtol=1e-15)
+    assert abs(lse[0, 0] - math.log(math.exp(s) + math.exp(sigma))) < 1e-15
+    # a row with no allowed key: O = 0, LSE = sigma
+    q5, k2, v2 = _rand(1, 5, 3), _rand(1, 2, 3), _rand(1, 2, 3)
+    o, lse = oracle.sdpa_fp64(q5, k2, v2, scale=1.0, causal=True, sink=np.array([-0.5]))
+    assert (o[0, :3] == 0).all() and (lse[0, :3] == -0.5).all()
+    o, lse = oracle.sdpa_fp64(q5, k2[:, :0], v2[:, :0], scale=1.0, sink=np.array([1.25]))
+    assert (o == 0).all() and (lse == 1.25).all()
+
+
+def test_sink_rescales_the_sinkless_result():
+    # from the definition: O_sink = O * e^LSE / (e^LSE + e^sigma), LSE_sink = logaddexp(LSE, sigma);
+    # a sink far below every score changes nothing
+    q, k, v = _rand(4, 6, 5), _rand(2, 11, 5), _rand(2, 11, 5)
+    sink = np.array([0.0, 3.0, -2.0, 40.0])
+    o0, l0 = oracle.sdpa_fp64(q, k, v, scale=0.45, causal=True, window=4)
+    o1, l1 = oracle.sdpa_fp64(q, k, v, scale=0.45, causal=True, window=4, sink=sink)
+    f = 1.0 / (1.0 + np.exp(sink[:, None] - l0))
+    np.testing.assert_allclose(o1, o0 * f[..., None], rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(l1, np.logaddexp(l0, sink[:, None]), rtol=0, atol=1e-12)
+    o2, l2 = oracle.sdpa_fp64(q, k, v, scale=0.45, causal=True, window=4, sink=np.full(4, -800.0))
+    np.testing.assert_array_equal(o2, o0)
+    np.testing.assert_array_equal(l2, l0)
+
+
+def test_sink_passes_through_every_entry():
+    sink = np.array([0.5, -1.0, 2.0, 0.0])
+    case = make_decode(lengths=[5, 33], num_q_heads=4, num_kv_heads=2, head_dim=4, kv_dtype="bf16", seed=31,
+                       keep_logical=True)
+    kc, vc = (oracle.tensor_to_f64(t, "bf16") for t in (case.k_cache, case.v_cache))
+    q = oracle.tensor_to_f64(case.q, "bf16")
+    o, lse = oracle.decode_paged(q, kc, vc, case.block_table, case.seq_lens, scale=0.3, sink=sink)
+    for s in range(2):
+        kl = oracle.tensor_to_f64(case.k_logical[s], "bf16").transpose(1, 0, 2)
+        vl = oracle.tensor_to_f64(case.v_logical[s], "bf16").transpose(1, 0, 2)
+        ob, lb = brute.brute_sdpa(_tolist(q[s][:, None, :]), _tolist(kl), _tolist(vl), scale=0.3,
+                                  sink=_tolist(sink))
+        np.testing.assert_allclose(o[s], np.array(ob)[:, 0], atol=1e-12)
+        np.testing.assert_allclose(lse[s], np.array(lb)[:, 0], atol=1e-12)
+    # dense, sampled rows / heads, ragged and paged forms use the head's own sink
+    qd, kd, vd = _rand(1, 4, 9, 3), _rand(1, 2, 9, 3), _rand(1, 2, 9, 3)
+    o, lse = oracle.prefill_dense(qd, kd, vd, scale=0.5, causal=True, sink=sink)
+    o2, lse2 = oracle.prefill_dense(qd, kd, vd, scale=0.5, causal=True, sink=sink, q_rows=np.array([2, 8]),
+                                    heads=np.array([2]))
+    np.testing.assert_array_equal(o2[0, 0], o[0, 2, [2, 8]])
+    ob, lb = oracle.sdpa_fp64(qd[0], kd[0], vd[0], scale=0.5, causal=True, sink=sink)
+    np.testing.assert_allclose(o[0], ob, atol=1e-15)
+    cu = np.array([0, 9])
+    ov, lv = oracle.prefill_varlen(qd[0].transpose(1, 0, 2), kd[0].transpose(1, 0, 2),
+                                   vd[0].transpose(1, 0, 2), cu, cu, scale=0.5, causal=True, sink=sink)
+    np.testing.assert_allclose(ov.transpose(1, 0, 2), ob, atol=1e-15)
+    np.testing.assert_allclose(lv, lb, atol=1e-15)
