@@ -45,20 +45,28 @@ def _require_cuda(*ts):
             raise ValueError("tensors must be on the GPU")
 
 
+def _sinks_ptr(sinks: Optional[torch.Tensor], hq: int) -> Optional[int]:
+    if sinks is None:
+        return None
+    if sinks.dtype != torch.float32 or not sinks.is_contiguous() or sinks.shape != (hq,) or not sinks.is_cuda:
+        raise ValueError(f"sinks must be a contiguous float32 GPU tensor of shape ({hq},)")
+    return sinks.data_ptr()
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False, window: int = 0,
         softcap: float = 0.0, softmax_scale: float = 0.0, cu_seqlens_q: Optional[torch.Tensor] = None,
         cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
         max_seqlen_k: Optional[int] = None, return_lse: bool = False, out: Optional[torch.Tensor] = None,
-        lse_out: Optional[torch.Tensor] = None):
+        lse_out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None):
     """Fused attention forward.
 
     Dense: q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (any strides with D contiguous).
     Ragged: q [T, Hq, D], k/v [Tk, Hkv, D] with int32 cu_seqlens_q/k [B+1] on the
     GPU and host-side upper bounds max_seqlen_q/k.
     Returns o (like q), and lse (float32; dense [B, Hq, Nq], ragged [Hq, T]) if
-    return_lse.
+    return_lse. sinks: optional float32 [Hq] per-head sink logits (natural log).
     """
-    _require_cuda(q, k, v)
+    _require_cuda(q, k, v, sinks)
     if q.dtype not in (torch.float32, torch.float16, torch.bfloat16):
         raise AttnNotSupported(_lib.ATTN_ERROR_NOT_SUPPORTED, f"dtype {q.dtype} not supported")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -111,6 +119,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     a.window = int(window)
     a.softmax_scale = float(softmax_scale)
     a.softcap = float(softcap)
+    a.sinks = _sinks_ptr(sinks, a.num_q_heads)
     for name, st in (("q_stride", qs), ("k_stride", ks), ("v_stride", vs), ("o_stride", os_)):
         arr = getattr(a, name)
         for i in range(3):
@@ -125,7 +134,8 @@ def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
               cu_seqlens_q: torch.Tensor, seq_lens_k: torch.Tensor, max_seqlen_q: int, *, causal: bool = True,
               window: int = 0, softcap: float = 0.0, softmax_scale: float = 0.0, return_lse: bool = False,
               out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, gather: bool = True):
+              workspace: Optional[torch.Tensor] = None, gather: bool = True,
+              sinks: Optional[torch.Tensor] = None):
     """Chunked prefill over a paged KV cache.
 
     q [T, Hq, D] packed chunks (int32 cu_seqlens_q [S+1] on the GPU, max_seqlen_q a
@@ -138,7 +148,7 @@ def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     fwd_paged_workspace_size bytes, allocated here unless ``workspace`` is given);
     gather=False reads the pages in place.
     """
-    _require_cuda(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k)
+    _require_cuda(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, sinks)
     for t in (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k):
         if not t.is_contiguous():
             raise ValueError("paged prefill tensors must be contiguous")
@@ -162,6 +172,7 @@ def fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, blo
     a.window = int(window)
     a.softmax_scale = float(softmax_scale)
     a.softcap = float(softcap)
+    a.sinks = _sinks_ptr(sinks, a.num_q_heads)
     o = torch.empty_like(q) if out is None else out
     if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
         raise ValueError("out must match q")
@@ -204,7 +215,7 @@ def fwd_paged_workspace_size(*, num_seqs, num_q_heads, num_kv_heads, head_dim, m
 
 
 def _decode_args(*, num_seqs, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, max_seq_len,
-                 q_dtype, kv_dtype, softmax_scale=0.0, num_splits=0, page_size=16) -> _lib.DecodeArgs:
+                 q_dtype, kv_dtype, softmax_scale=0.0, num_splits=0, page_size=16, sinks=None) -> _lib.DecodeArgs:
     a = _lib.DecodeArgs()
     a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = num_seqs, num_q_heads, num_kv_heads, head_dim
     a.page_size = page_size
@@ -214,6 +225,7 @@ def _decode_args(*, num_seqs, num_q_heads, num_kv_heads, head_dim, max_pages_per
     a.kv_dtype = _DTYPES[kv_dtype] if isinstance(kv_dtype, torch.dtype) else int(kv_dtype)
     a.softmax_scale = float(softmax_scale)
     a.num_splits = int(num_splits)
+    a.sinks = sinks
     return a
 
 
@@ -234,7 +246,7 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                  seq_lens: torch.Tensor, max_seq_len: int, *, k_scale: Optional[torch.Tensor] = None,
                  v_scale: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, num_splits: int = 0,
                  return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
-                 out: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None):
     """Paged split-KV decode.
 
     q [S, Hq, D]; k_cache/v_cache [P, 16, Hkv, D] (bf16/f16, or float8_e4m3fn with
@@ -242,7 +254,7 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     [S]; max_seq_len a host-side bound of seq_lens. Returns o [S, Hq, D] (and lse
     [S, Hq] float32 if return_lse).
     """
-    _require_cuda(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale)
+    _require_cuda(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks)
     for t in (q, k_cache, v_cache, block_table, seq_lens):
         if not t.is_contiguous():
             raise ValueError("decode tensors must be contiguous")
@@ -262,7 +274,7 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     for sc in (k_scale, v_scale):
         if sc is not None and (sc.dtype != torch.float32 or not sc.is_contiguous()):
             raise ValueError("k_scale / v_scale must be contiguous float32")
-    a = _decode_args(**kw)
+    a = _decode_args(**kw, sinks=_sinks_ptr(sinks, hq))
     L = _lib.lib()
     need = int(L.attn_decode_paged_workspace_size(ctypes.byref(a)))
     if workspace is None:

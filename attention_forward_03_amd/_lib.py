@@ -42,6 +42,7 @@ class FwdArgs(ctypes.Structure):
         ("o_stride", ctypes.c_int64 * 3),
         ("cu_seqlens_q", ctypes.c_void_p),
         ("cu_seqlens_k", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -58,6 +59,7 @@ class DecodeArgs(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -76,6 +78,7 @@ class FwdPagedArgs(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("softcap", ctypes.c_float),
+        ("sinks", ctypes.c_void_p),
     ]
 
 

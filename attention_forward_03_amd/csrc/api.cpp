@@ -118,6 +118,7 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
     return fail(ATTN_ERROR_NOT_SUPPORTED, "q, k, v and o must be 16-byte aligned");
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(ATTN_ERROR_INVALID_VALUE, "lse must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(a->sinks) & 3u) return fail(ATTN_ERROR_INVALID_VALUE, "sinks must be 4-byte aligned");
   const int es = elem_size(a->dtype);
   attn_status_t st;
   if ((st = check_strides("q", a->q_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
@@ -158,6 +159,7 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
   }
   const int bm = attn::fwd_block_rows(a->dtype, a->head_dim);
   p.q_tiles = (a->seqlen_q + bm - 1) / bm;
+  p.sinks = a->sinks;
 
   hipError_t e = attn::launch_fwd(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
@@ -194,6 +196,7 @@ static attn_status_t check_fwd_paged_args(const attn_fwd_paged_args_t* a) {
     return fail(ATTN_ERROR_NOT_SUPPORTED, "num_kv_heads * head_dim must be below 2^24");
   if ((int64_t)a->num_q_heads * a->head_dim >= (int64_t)1 << 24)
     return fail(ATTN_ERROR_NOT_SUPPORTED, "num_q_heads * head_dim must be below 2^24");
+  if (reinterpret_cast<uintptr_t>(a->sinks) & 3u) return fail(ATTN_ERROR_INVALID_VALUE, "sinks must be 4-byte aligned");
   return ATTN_SUCCESS;
 }
 
@@ -270,6 +273,7 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, cons
   p.seq_lens_k = seq_lens_k;
   p.max_pages = a->max_pages_per_seq;
   p.num_pages = a->num_pages;
+  p.sinks = a->sinks;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -304,8 +308,8 @@ static attn_status_t check_decode_args(const attn_decode_args_t* a) {
   if (a->num_q_heads % a->num_kv_heads != 0)
     return fail(ATTN_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                 a->num_q_heads, a->num_kv_heads);
-  if (a->num_q_heads / a->num_kv_heads > 16)
-    return fail(ATTN_ERROR_NOT_SUPPORTED, "more than 16 query heads per KV head");
+  if (a->num_seqs > 0 && a->num_kv_heads > 0 && (int64_t)a->num_kv_heads * ((a->num_q_heads / a->num_kv_heads + 15) / 16) > 65535)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_kv_heads * ceil(group / 16) is limited to 65535");
   if (a->head_dim != 128) return fail(ATTN_ERROR_NOT_SUPPORTED, "decode supports head_dim 128 only");
   if (a->page_size != kPageSize) return fail(ATTN_ERROR_NOT_SUPPORTED, "page_size must be 16");
   if (a->max_pages_per_seq < 1) return fail(ATTN_ERROR_INVALID_VALUE, "max_pages_per_seq must be >= 1");
@@ -322,6 +326,7 @@ static attn_status_t check_decode_args(const attn_decode_args_t* a) {
     return fail(ATTN_ERROR_NOT_SUPPORTED, "num_seqs and num_kv_heads are limited to 65535");
   if (!(a->softmax_scale == a->softmax_scale) || isinf(a->softmax_scale))
     return fail(ATTN_ERROR_INVALID_VALUE, "softmax_scale must be finite");
+  if (reinterpret_cast<uintptr_t>(a->sinks) & 3u) return fail(ATTN_ERROR_INVALID_VALUE, "sinks must be 4-byte aligned");
   return ATTN_SUCCESS;
 }
 
@@ -400,8 +405,10 @@ attn_status_t attn_decode_paged(const attn_decode_args_t* a, const void* q, cons
   p.hq = a->num_q_heads;
   p.hkv = a->num_kv_heads;
   p.group = a->num_q_heads / a->num_kv_heads;
+  p.head_tiles = (p.group + 15) / 16;
   p.max_pages = a->max_pages_per_seq;
   p.split_len = split_len;
+  p.sinks = a->sinks;
   p.max_splits = max_splits;
   p.scale_log2 = (float)(resolve_scale(a->softmax_scale, a->head_dim) * kLog2eD);
   hipError_t e = attn::launch_decode(p, a->q_dtype, a->kv_dtype, static_cast<hipStream_t>(stream));

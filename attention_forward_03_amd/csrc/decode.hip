@@ -4,7 +4,8 @@
 //
 // Split kernel: one wave per (split, KV head g, sequence s). The G = Hq/Hkv query
 // heads that share KV head g are processed together, so every K/V byte is read
-// once. Work runs page by page (16 tokens = one page):
+// once; beyond 16 heads per KV head (MQA-like groups) the heads are taken 16 at a
+// time by adjacent workgroups, which read the same pages at about the same time. Work runs page by page (16 tokens = one page):
 //   scores  S^T[key][query] = K . Q^T on the 16x16x32 matrix core, K loaded straight
 //           from the page into the A operand (lane l: token slot l%16, 64 contiguous
 //           bytes of head_dim at 32*(l/16)); Q (zero beyond G) is the B operand;
@@ -111,27 +112,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #if ATTN_DECODE_HEAD_MAJOR
   // the KV heads of one split are adjacent workgroups: the slices of each physical page
   // that belong to different heads are fetched at about the same time
-  const int g = blockIdx.x;
+  const int gt = blockIdx.x;
   const int split = blockIdx.y;
 #else
   const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  const int gt = blockIdx.y;
 #endif
+  const int g = gt / p.head_tiles;                            // KV head
+  const int h0 = g * p.group + 16 * (gt % p.head_tiles);      // first query head of the tile
+  const int G = min(16, p.group - 16 * (gt % p.head_tiles));  // query heads in the tile
   const int s = blockIdx.z;
   const int lane = threadIdx.x;
-  const int col = lane & 15;   // query column (head g*G + col when col < G) / token slot
+  const int col = lane & 15;   // query column (head h0 + col when col < G) / token slot
   const int quad = lane >> 4;  // token slots 4*quad .. 4*quad+3 of the score tile
 
   const int L = p.seq_lens[s];
   const int t0 = split * p.split_len;
   if (t0 >= L) return;
   const int t1 = min(L, t0 + p.split_len);
-  const int G = p.group;
 
   // Q as the B operand of the score product: k-step ks, slot group quad <-> head_dim
   // 32*quad + 8*ks .. +7.
   u32x4_t qf[4];
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.hq + g * G + col) * kD + 32 * quad;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.hq + h0 + col) * kD + 32 * quad;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     qf[ks] = u32x4_t{0, 0, 0, 0};
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   float lt = l + xor_shuffle(l, 16);
   lt += xor_shuffle(lt, 32);
   if (col < G) {
-    const int h = g * G + col;
+    const int h = h0 + col;
     const int64_t slot = ((int64_t)s * p.hq + h) * p.max_splits + split;
     float* dst = p.part_o + slot * kD;
     const float inv = vsc / lt;
@@ -339,18 +342,20 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
   uint16_t* orow = static_cast<uint16_t*>(p.o) + ((int64_t)s * p.hq + h) * kD + 2 * lane;
   if (n <= 0) {
     *reinterpret_cast<uint32_t*>(orow) = 0u;
-    if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)s * p.hq + h] = kNegInf;
+    if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)s * p.hq + h] = p.sinks != nullptr ? p.sinks[h] : kNegInf;
     return;
   }
   const float* lse2 = p.part_lse + base;
+  // the attention sink (a per-head logit with no value) is one more term of the merge
+  const float sink2 = p.sinks != nullptr ? p.sinks[h] * kLog2e : kNegInf;
 
-  float mx = kNegInf;
+  float mx = sink2;
   for (int k = lane; k < n; k += 64) mx = fmaxf(mx, lse2[k]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, xor_shuffle(mx, off));
 
   f32x2_t acc = {0.0f, 0.0f};
-  float wsum = 0.0f;
+  float wsum = p.sinks != nullptr ? fast_exp2(sink2 - mx) : 0.0f;
   const float* po = p.part_o + base * kD + 2 * lane;
   for (int k = 0; k < n; ++k) {
     const float w = fast_exp2(lse2[k] - mx);
@@ -378,9 +383,9 @@ constexpr int kStages8 = ATTN_DECODE_STAGES_FP8;  // fp8 KV, 4 KiB per stage
 template <int KV, bool QBF16>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
 #if ATTN_DECODE_HEAD_MAJOR
-  dim3 grid(p.hkv, p.max_splits, p.num_seqs);
+  dim3 grid(p.hkv * p.head_tiles, p.max_splits, p.num_seqs);
 #else
-  dim3 grid(p.max_splits, p.hkv, p.num_seqs);
+  dim3 grid(p.max_splits, p.hkv * p.head_tiles, p.num_seqs);
 #endif
   constexpr int nst = KV == KV_FP8 ? kStages8 : kStages16;
   hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst>), grid, dim3(64), 0, st, p);

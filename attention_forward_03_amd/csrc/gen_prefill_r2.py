@@ -844,9 +844,26 @@ class Gen:
         e(f"v_add_f32 {v(LT)}, {v(T0)}, {v(T1)}")
         e(f"v_add_f32 {v(LT + 1)}, {v(T2)}, {v(T3)}")
         for rb in range(RB):
-            # 1/l (0 for a row with no allowed key)
+            # The sink (s52: the head's sink logit in log2 units, -inf for none) joins the
+            # denominator: M = max(MU, sink) (sink alone for a row with no allowed key),
+            # l' = l 2^(MU - M) + 2^(sink - M), O = o 2^(MU - M) / l', LSE = M + log2 l'.
+            # Without a sink M = MU, the factor is 2^0 = 1 and l' = l exactly.
+            e(f"v_mov_b32 {v(T3)}, {s(52)}")
+            e(f"v_max_f32 {v(T0)}, {v(T3)}, {v(MU + rb)}")
+            e(f"v_cmp_lt_f32 vcc, 0, {v(LT + rb)}")
+            e(f"v_cndmask_b32 {v(T0)}, {v(T3)}, {v(T0)}, vcc")
+            e(f"v_sub_f32 {v(T1)}, {v(MU + rb)}, {v(T0)}")
+            e(f"v_exp_f32 {v(T1)}, {v(T1)}")
+            e(f"v_sub_f32 {v(T2)}, {v(T3)}, {v(T0)}")
+            e(f"v_exp_f32 {v(T2)}, {v(T2)}")
+            e("s_nop 0")
+            e(f"v_cndmask_b32 {v(T1)}, 0, {v(T1)}, vcc")
+            e(f"v_fma_f32 {v(LT + rb)}, {v(LT + rb)}, {v(T1)}, {v(T2)}")
+            e(f"v_mov_b32 {v(MU + rb)}, {v(T0)}")
+            # factor / l' (0 for a row with no weight at all)
             e(f"v_rcp_f32 {v(INV + rb)}, {v(LT + rb)}")
             e("s_nop 0")
+            e(f"v_mul_f32 {v(INV + rb)}, {v(INV + rb)}, {v(T1)}")
             e(f"v_cmp_lt_f32 vcc, 0, {v(LT + rb)}")
             e(f"v_cndmask_b32 {v(INV + rb)}, 0, {v(INV + rb)}, vcc")
         for rb in range(RB):

@@ -32,6 +32,7 @@ struct FwdParams {
   const int32_t* block_table;
   const int32_t* seq_lens_k;
   int32_t max_pages, num_pages;
+  const float* sinks;   // per query head sink logit (natural log), or NULL
 };
 
 // One paged-decode launch (split kernel + combine kernel).
@@ -48,8 +49,10 @@ struct DecodeParams {
   void* o;
   float* lse;
   int32_t num_seqs, hq, hkv, group, max_pages;
+  int32_t head_tiles;   // ceil(group / 16): query-head tiles of 16 per KV head
   int32_t split_len, max_splits;
   float scale_log2;
+  const float* sinks;   // per query head sink logit (natural log), or NULL
 };
 
 // Block-rows of the prefill kernels for a given dtype/head_dim (the host needs it

@@ -70,6 +70,23 @@ __device__ __forceinline__ RowRange wave_key_range(const FwdParams& p, int w0, i
   return r;
 }
 
+// Final normalisation of a row whose probabilities 2^(s - m) over its keys sum to lt (m in
+// log2 units): 1 / denominator for O and the natural-log LSE. The attention sink (a per
+// query head logit that joins the denominator with no value) adds 2^(sink - M) at the
+// common reference M = max(m, sink). Without a sink a row with no key gets O = 0 and
+// LSE = -inf; with one, O = 0 and LSE = the sink.
+struct RowNorm {
+  float inv, lse;
+};
+__device__ __forceinline__ RowNorm row_norm(float lt, float m, const float* sinks, int h) {
+  if (sinks == nullptr) return {lt > 0.0f ? 1.0f / lt : 0.0f, lt > 0.0f ? (m + fast_log2(lt)) * kLn2 : kNegInf};
+  const float s2 = sinks[h] * kLog2e;
+  const float M = lt > 0.0f ? fmaxf(m, s2) : s2;
+  const float f = lt > 0.0f ? fast_exp2(m - M) : 0.0f;
+  const float l2 = lt * f + fast_exp2(s2 - M);
+  return {l2 > 0.0f ? f / l2 : 0.0f, l2 > 0.0f ? (M + fast_log2(l2)) * kLn2 : kNegInf};
+}
+
 // Softcap, mask and online-softmax update of one key tile for one lane's query row.
 // s[] holds raw dot products on entry and unnormalised probabilities on exit.
 template <int NKB>
@@ -456,8 +473,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   }
 
   if (!wave_live) return;
-  const float lt = pair_sum(l);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  const RowNorm nrm = row_norm(pair_sum(l), m, p.sinks, h);
+  const float inv = nrm.inv;
   if (qrow < Lq) {
     uint16_t* orow = og + qrow * os2;
 #pragma unroll
@@ -472,7 +489,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
     if (hi == 0 && p.lse != nullptr) {
       const int64_t idx = ragged ? (int64_t)h * p.cu_q[p.batch] + q_off + qrow
                                  : ((int64_t)b * p.hq + h) * p.nq + qrow;
-      p.lse[idx] = lt > 0.0f ? (m + fast_log2(lt)) * kLn2 : kNegInf;
+      p.lse[idx] = nrm.lse;
     }
   }
 }
@@ -587,7 +604,8 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
       la[rb] = p.lse + (ragged ? (int64_t)h * p.cu_q[p.batch] + q_off + qrow[rb]
                                : ((int64_t)b * p.hq + h) * p.nq + qrow[rb]);
   }
-  if (ntiles == 0) {  // no allowed key for any row: O = 0, LSE = -inf
+  if (ntiles == 0) {  // no allowed key for any row: O = 0, LSE = -inf (the sink with one)
+    const float lse0 = p.sinks != nullptr ? p.sinks[h] : kNegInf;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
       if (qrow[rb] < Lq) {
@@ -595,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
 #pragma unroll
         for (int c = 0; c < D / 8; ++c)
           *reinterpret_cast<u32x2_t*>(oa[rb] + c * 8) = u32x2_t{0, 0};
-        if (hi == 0 && p.lse != nullptr) *la[rb] = kNegInf;
+        if (hi == 0 && p.lse != nullptr) *la[rb] = lse0;
       }
     return;
   }
@@ -626,6 +644,7 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
   };
   const float sc = uni(MODE == 2 ? 1.0f : fmaxf(p.scale_log2, 1.17549435e-38f));  // > 0: its reciprocal is taken
   const float cap_in = uni(p.cap_in), cap_c = uni(p.cap_out);
+  const float sink2 = uni(p.sinks != nullptr ? p.sinks[h] * kLog2e : kNegInf);
   const int has_lse = uni((int)(p.lse != nullptr));
   const uint16_t* const kg_u = uni(kg);
   const uint16_t* const vg_u = uni(vg);
@@ -639,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
       "{v16}"(qrow[0]), "{v17}"(qrow[1]), "{v19}"(ld_k0), "{v20}"(ld_v0), "{v21}"(k_rd),                      \
       "{v22}"(v_rd), "{s[40:41]}"(kg_u), "{s[42:43]}"(vg_u), "{s44}"(ks2_u), "{s45}"(vs2_u), "{s46}"(Lk_u),   \
       "{s47}"(kbeg_u), "{s48}"(ntiles_u), "{s49}"(sc), "{s50}"(cap_in), "{s51}"(cap_c),                         \
-      "{s53}"(wave), "{s54}"(Lq_u), "{s55}"(has_lse), "{s56}"(lds_u), "{s57}"(wlo_u),             \
+      "{s52}"(sink2), "{s53}"(wave), "{s54}"(Lq_u), "{s55}"(has_lse), "{s56}"(lds_u), "{s57}"(wlo_u),             \
       "{s58}"(whi_u)
   if constexpr (BF16 && MODE == 0) {
     asm volatile(
@@ -837,8 +856,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f32_kernel(const FwdParams p) 
   }
 
   if (!wave_live) return;
-  const float lt = l + xor_shuffle(l, 32);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  const RowNorm nrm = row_norm(l + xor_shuffle(l, 32), m, p.sinks, h);
+  const float inv = nrm.inv;
   if (qrow < Lq) {
     float* orow = og + qrow * os2;
 #pragma unroll
@@ -856,7 +875,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f32_kernel(const FwdParams p) 
     if (hi == 0 && p.lse != nullptr) {
       const int64_t idx = ragged ? (int64_t)h * p.cu_q[p.batch] + q_off + qrow
                                  : ((int64_t)b * p.hq + h) * p.nq + qrow;
-      p.lse[idx] = lt > 0.0f ? (m + fast_log2(lt)) * kLn2 : kNegInf;
+      p.lse[idx] = nrm.lse;
     }
   }
 }

@@ -90,6 +90,13 @@ typedef struct {
    * mask offset is Nk_b - Nq_b. Every length must be <= seqlen_q / seqlen_k. */
   const int32_t *cu_seqlens_q;
   const int32_t *cu_seqlens_k;
+  /* Attention sink: NULL (none) or a device float32 [Hq] of per query head logits
+   * sigma_h (natural-log units). Each row's softmax denominator gains e^sigma_h, a
+   * score with no value: O = sum_j e^{s_j} V_j / (e^sigma_h + sum_j e^{s_j}) and
+   * LSE = ln(e^sigma_h + sum_j e^{s_j}); a row with no allowed key gets O = 0 and
+   * LSE = sigma_h. ("attention-sink" in the masks of the feature surface named by
+   * "Ask, Don't Equip", section 研究动机; the definition is the per-head sink logit.) */
+  const float *sinks;
 } attn_fwd_args_t;
 
 /*
@@ -124,6 +131,7 @@ typedef struct {
   int32_t window;            /* as for attn_fwd (requires causal) */
   float softmax_scale;       /* <= 0: 1/sqrt(D) as for attn_fwd */
   float softcap;             /* as for attn_fwd */
+  const float *sinks;        /* NULL or device float32 [Hq], as for attn_fwd */
 } attn_fwd_paged_args_t;
 
 /*
@@ -183,6 +191,7 @@ typedef struct {
   int32_t num_splits;        /* 0: the library plans the split length; n > 0: split_len =
                                 ceil(max_seq_len / n) rounded up to a whole page, capped at
                                 4096 tokens (the longest split the kernel handles) */
+  const float *sinks;        /* NULL or device float32 [Hq], as for attn_fwd */
 } attn_decode_args_t;
 
 /* Split plan: every sequence s is cut into ceil(seq_lens[s] / split_len)

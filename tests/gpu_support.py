@@ -64,10 +64,15 @@ def compare(got: np.ndarray, ref: np.ndarray, kind: str, what: str, lse: bool = 
 
 # ---------------------------------------------------------------------------- prefill ----
 
-def run_prefill(case, *, return_lse=True, out=None):
+def _dev_sinks(sinks):
+    return None if sinks is None else torch.as_tensor(np.asarray(sinks, dtype=np.float32)).cuda()
+
+
+def run_prefill(case, *, return_lse=True, out=None, sinks=None):
     import attention_forward_03_amd as attn
     q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
-    kw = dict(causal=case.causal, window=case.window, softcap=case.softcap, return_lse=return_lse)
+    kw = dict(causal=case.causal, window=case.window, softcap=case.softcap, return_lse=return_lse,
+              sinks=_dev_sinks(sinks))
     if case.varlen:
         kw.update(cu_seqlens_q=torch.from_numpy(case.cu_seqlens_q).cuda(),
                   cu_seqlens_k=torch.from_numpy(case.cu_seqlens_k).cuda(),
@@ -82,7 +87,7 @@ def run_prefill(case, *, return_lse=True, out=None):
     return res.cpu(), None
 
 
-def oracle_prefill(case, *, rows=None, heads=None, seqs=None):
+def oracle_prefill(case, *, rows=None, heads=None, seqs=None, sinks=None):
     """Oracle O/LSE for the case (a sample of rows / heads when given), float64."""
     q = oracle.tensor_to_f64(case.q, case.dtype)
     k = oracle.tensor_to_f64(case.k, case.dtype)
@@ -91,18 +96,23 @@ def oracle_prefill(case, *, rows=None, heads=None, seqs=None):
     if case.varlen:
         return oracle.prefill_varlen(q, k, v, case.cu_seqlens_q, case.cu_seqlens_k, scale=scale,
                                      causal=case.causal, window=case.window, softcap=case.softcap,
-                                     seqs=seqs, rows_per_seq=rows, heads=heads)
+                                     seqs=seqs, rows_per_seq=rows, heads=heads, sink=_f64(sinks))
     return oracle.prefill_dense(q, k, v, scale=scale, causal=case.causal, window=case.window,
-                                softcap=case.softcap, q_rows=rows, heads=heads)
+                                softcap=case.softcap, q_rows=rows, heads=heads, sink=_f64(sinks))
 
 
-def check_prefill_full(case, label: str) -> dict:
+def _f64(sinks):
+    """The sink logits as the kernels receive them (float32), widened."""
+    return None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
+
+
+def check_prefill_full(case, label: str, sinks=None) -> dict:
     """Every output of a small case against the oracle."""
     note(f"[prefill] {label}: B={case.batch} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
          f"Nq={case.seqlen_q} Nk={case.seqlen_k} D={case.head_dim} {case.dtype} causal={case.causal} "
          f"window={case.window} softcap={case.softcap} varlen={case.varlen}")
-    o, lse = run_prefill(case)
-    ro, rl = oracle_prefill(case)
+    o, lse = run_prefill(case, sinks=sinks)
+    ro, rl = oracle_prefill(case, sinks=sinks)
     s1 = compare(widen(o, case.dtype), ro, case.dtype, f"{label} O")
     s2 = compare(lse.numpy(), rl, case.dtype, f"{label} LSE", lse=True)
     return {**s1, "lse_max_abs": s2["max_abs"]}
@@ -150,17 +160,17 @@ def decode_tensors(case):
     return t
 
 
-def run_decode(case, tensors=None, *, num_splits=0):
+def run_decode(case, tensors=None, *, num_splits=0, sinks=None):
     import attention_forward_03_amd as attn
     t = decode_tensors(case) if tensors is None else tensors
     o, lse = attn.decode_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"],
                                case.max_seq_len, k_scale=t.get("k_scale"), v_scale=t.get("v_scale"),
-                               num_splits=num_splits, return_lse=True)
+                               num_splits=num_splits, return_lse=True, sinks=_dev_sinks(sinks))
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
 
-def oracle_decode(case, seqs=None):
+def oracle_decode(case, seqs=None, sinks=None):
     q = oracle.tensor_to_f64(case.q, case.q_dtype)
     seqs = np.arange(case.num_seqs) if seqs is None else np.asarray(seqs)
     # widen only the pages the sampled sequences use
@@ -174,7 +184,7 @@ def oracle_decode(case, seqs=None):
     bt = case.block_table.astype(np.int64).copy()
     sub_bt = np.where(bt >= 0, remap[bt], -1)
     return oracle.decode_paged(q, kc, vc, sub_bt, case.seq_lens, scale=oracle.default_scale(case.head_dim),
-                               k_scale=case.k_scale, v_scale=case.v_scale, seqs=seqs)
+                               k_scale=case.k_scale, v_scale=case.v_scale, seqs=seqs, sink=_f64(sinks))
 
 
 def decode_kind(case) -> str:
@@ -191,20 +201,20 @@ def paged_prefill_tensors(case):
                 seq_lens_k=torch.from_numpy(c.seq_lens).cuda())
 
 
-def run_paged_prefill(case, tensors=None, *, gather=True):
+def run_paged_prefill(case, tensors=None, *, gather=True, sinks=None):
     """gather=True: the gathered-key route where the library has one (head_dim 128);
     gather=False: the kernel that reads the pages in place."""
     import attention_forward_03_amd as attn
     t = paged_prefill_tensors(case) if tensors is None else tensors
     o, lse = attn.fwd_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["cu_seqlens_q"],
                             t["seq_lens_k"], case.max_seqlen_q, causal=case.causal, window=case.window,
-                            softcap=case.softcap, return_lse=True, gather=gather,
+                            softcap=case.softcap, return_lse=True, gather=gather, sinks=_dev_sinks(sinks),
                             out=torch.full(t["q"].shape, float("nan"), dtype=t["q"].dtype, device=t["q"].device))
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
 
-def oracle_paged_prefill(case, *, seqs=None, rows_per_seq=None, heads=None):
+def oracle_paged_prefill(case, *, seqs=None, rows_per_seq=None, heads=None, sinks=None):
     """Oracle O [T, Hq, D] / LSE [Hq, T] (float64) of a chunked-prefill case; only the pages
     of the sampled sequences are widened."""
     c = case.cache
@@ -223,4 +233,4 @@ def oracle_paged_prefill(case, *, seqs=None, rows_per_seq=None, heads=None):
                                 scale=oracle.default_scale(c.head_dim), causal=case.causal,
                                 window=case.window, softcap=case.softcap,
                                 seqs=None if seqs is None else list(sel), rows_per_seq=rows_per_seq,
-                                heads=heads)
+                                heads=heads, sink=_f64(sinks))

@@ -75,6 +75,7 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
     (dict(q_stride=(8192, 2048, 30)), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(k_stride=(8192, 2048, 16)), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(v_stride=(8192, -2048, 32)), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(sinks=FAKE + 2), _lib.ATTN_ERROR_INVALID_VALUE),
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     L = _lib.lib()
@@ -125,6 +126,7 @@ def _paged_args(**kw):
     (dict(causal=0, window=8), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(causal=3), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(softmax_scale=float("inf")), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(sinks=FAKE + 1), _lib.ATTN_ERROR_INVALID_VALUE),
 ])
 def test_fwd_paged_rejects_bad_arguments(kw, status):
     L = _lib.lib()
@@ -205,8 +207,9 @@ def test_decode_workspace_size():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=30), _lib.ATTN_ERROR_INVALID_VALUE),
-    (dict(num_q_heads=32, num_kv_heads=1), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(num_q_heads=65536 * 17, num_kv_heads=65536), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(head_dim=64), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(sinks=FAKE + 2), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(max_seq_len=40000), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(q_dtype=_lib.ATTN_F32), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(kv_dtype=_lib.ATTN_F16), _lib.ATTN_ERROR_NOT_SUPPORTED),
