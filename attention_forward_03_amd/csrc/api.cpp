@@ -44,6 +44,12 @@ int elem_size(int dtype) {
   }
 }
 
+// head dims with a prefill kernel: 16-bit inputs 32, 64, 96, 128, 192, 256; fp32 32, 64, 128
+bool head_dim_ok(int d, bool sixteen_bit) {
+  if (d == 32 || d == 64 || d == 128) return true;
+  return sixteen_bit && (d == 96 || d == 192 || d == 256);
+}
+
 float resolve_scale(float s, int head_dim) {
   return s > 0.0f ? s : (float)(1.0 / sqrt((double)head_dim));
 }
@@ -97,10 +103,11 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
                 a->num_q_heads, a->num_kv_heads);
   if (a->seqlen_q < 0 || a->seqlen_k < 0)
     return fail(ATTN_ERROR_INVALID_VALUE, "sequence lengths must be >= 0");
-  if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
-    return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of 32, 64, 128", a->head_dim);
   if (a->dtype != ATTN_F32 && a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
     return fail(ATTN_ERROR_NOT_SUPPORTED, "dtype %d is not F32, F16 or BF16", a->dtype);
+  if (!head_dim_ok(a->head_dim, a->dtype != ATTN_F32))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of %s", a->head_dim,
+                a->dtype != ATTN_F32 ? "32, 64, 96, 128, 192, 256" : "32, 64, 128");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERROR_INVALID_VALUE, "causal must be 0 or 1");
   if (a->window > 0 && !a->causal)
     return fail(ATTN_ERROR_INVALID_VALUE, "a sliding window requires causal = 1");
@@ -174,8 +181,8 @@ static attn_status_t check_fwd_paged_args(const attn_fwd_paged_args_t* a) {
   if (a->num_q_heads % a->num_kv_heads != 0)
     return fail(ATTN_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                 a->num_q_heads, a->num_kv_heads);
-  if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
-    return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of 32, 64, 128", a->head_dim);
+  if (!head_dim_ok(a->head_dim, true))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of 32, 64, 96, 128, 192, 256", a->head_dim);
   if (a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
     return fail(ATTN_ERROR_NOT_SUPPORTED, "dtype %d is not F16 or BF16", a->dtype);
   if (a->page_size != kPageSize) return fail(ATTN_ERROR_NOT_SUPPORTED, "page_size must be 16");
@@ -267,7 +274,7 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, cons
     p.cap_in = (float)(scale / (double)a->softcap);
     p.cap_out = (float)((double)a->softcap * kLog2eD);
   }
-  const int bm = attn::fwd_paged_block_rows();
+  const int bm = attn::fwd_paged_block_rows(a->head_dim);
   p.q_tiles = (a->max_seqlen_q + bm - 1) / bm;
   p.block_table = block_table;
   p.seq_lens_k = seq_lens_k;

@@ -62,7 +62,7 @@ int fwd_block_rows(int dtype, int head_dim);
 hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
 // chunked prefill over a paged cache (16-bit inputs)
 hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
-int fwd_paged_block_rows();
+int fwd_paged_block_rows(int head_dim);
 // page-by-page copy of K and V into per-sequence slots of max_pages * 16 tokens
 hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,

@@ -147,17 +147,25 @@ __device__ __forceinline__ float softmax_tile(const FwdParams& p, f32x16_t (&s)[
 //   consecutive head-dim entries of 4 keys, so every lane ends up with 4 keys of one
 //   head-dim entry: exactly the A operand of O^T = V^T . P^T, with no transposition on
 //   the way into LDS. A 4-key x 4-chunk read hits 16 distinct bank groups.
+// Head dims that are not a power of two (96, 192) use LDS rows of the next power of two
+// (128, 256): the extra chunks of a row are padding that no read touches.
 
 template <int D>
 struct Swizzle {
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  __device__ static __forceinline__ int k(int row, int c) { return c ^ ((row / (16 / CPR)) % CPR); }
+  __device__ static __forceinline__ int k(int row, int c) {
+    if constexpr (CPR >= 16) return c ^ (row & 15);
+    else return c ^ ((row / (16 / CPR)) % CPR);
+  }
   __device__ static __forceinline__ int v(int row, int c) {
-    if constexpr (D == 128) return c ^ ((row & 3) << 2);
+    if constexpr (D >= 128) return c ^ ((row & 3) << 2);
     else if constexpr (D == 64) return c ^ (((row >> 1) & 1) << 2);
     else return c;
   }
 };
+
+// LDS row width (elements) for head dim D
+constexpr int lds_row(int D) { return D <= 32 ? 32 : D <= 64 ? 64 : D <= 128 ? 128 : 256; }
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -189,24 +197,30 @@ constexpr float kRescaleSlack = 8.0f;
 // so each load reads inside a single page: its base is the page (a wave-uniform address)
 // and each lane adds its token slot. The page ids of a tile are read one tile ahead.
 template <int D, int NW, int BN, bool BF16, bool PAGED = false>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (D > 128 ? 1 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
-  constexpr int TILE = BN * D;  // elements per K or V tile
+  constexpr int DP = lds_row(D);  // LDS row width
+  constexpr int TILE = BN * DP;   // elements per K or V tile in LDS
   constexpr int NKB = BN / 32;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
   constexpr int NPS = BN / 16;
-  constexpr int CPR = D / 8;
-  constexpr int ROWS_PER_LOAD = 64 / CPR;
+  constexpr int CPR = D / 8;    // chunks of a row in memory
+  constexpr int CPRP = DP / 8;  // chunks of a row in LDS
+  constexpr int ROWS_PER_LOAD = 64 / CPRP;
   constexpr int LOADS = BN / ROWS_PER_LOAD;  // load instructions per tile (K or V)
   constexpr int LPW = (LOADS + NW - 1) / NW;  // per wave
   static_assert(BN % 32 == 0 && D % 32 == 0 && BN % ROWS_PER_LOAD == 0, "tile shape");
   static_assert(!PAGED || (BN % 16 == 0 && ROWS_PER_LOAD <= 16), "a paged load stays in one page");
-  using SW = Swizzle<D>;
+  using SW = Swizzle<DP>;
+  // the memory chunk held at LDS chunk position `slot` of a row; padding positions hold a
+  // copy of chunk 0 (loaded, never read)
+  auto src_k = [](int row, int slot) { const int c = SW::k(row, slot); return c < CPR ? c : 0; };
+  auto src_v = [](int row, int slot) { const int c = SW::v(row, slot); return c < CPR ? c : 0; };
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
-  uint16_t* const k_lds = smem;             // [2][BN][D]
-  uint16_t* const v_lds = smem + 2 * TILE;  // [2][BN][D]
+  uint16_t* const k_lds = smem;             // [2][BN][DP]
+  uint16_t* const v_lds = smem + 2 * TILE;  // [2][BN][DP]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -273,16 +287,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
 #pragma unroll
   for (int n = 0; n < LPW; ++n) {
     const int i = wave + n * NW;
-    const int row = i * ROWS_PER_LOAD + lane / CPR;
-    const int slot = lane % CPR;
+    const int row = i * ROWS_PER_LOAD + lane / CPRP;
+    const int slot = lane % CPRP;
     ld_row[n] = row;
-    ld_k[n] = row * ks2 + SW::k(row, slot) * 8;
-    ld_v[n] = row * vs2 + SW::v(row, slot) * 8;
+    ld_k[n] = row * ks2 + src_k(row, slot) * 8;
+    ld_v[n] = row * vs2 + src_v(row, slot) * 8;
   }
   // K reads: chunk 2*ks + hi of row kb*32 + l32 (the swizzle does not depend on kb)
   int rd_k[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+  for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * DP + SW::k(l32, 2 * ks + hi) * 8;
   // V transposing reads: rows t*16 + vrow (+8), head-dim block db
   const int grp = lane >> 4, gi = lane & 15;
   const int vrow = 4 * hi + (gi >> 2);
@@ -290,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
-    rd_v[db] = vrow * D + SW::v(vrow, c) * 8 + (gi & 1) * 4;
+    rd_v[db] = vrow * DP + SW::v(vrow, c) * 8 + (gi & 1) * 4;
   }
 
   // Direct-to-LDS loads of one K or V tile. In the tail tile, rows past the last key
@@ -320,8 +334,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
   int ld_col_k[LPW], ld_col_v[LPW];
 #pragma unroll
   for (int n = 0; n < LPW; ++n) {
-    ld_col_k[n] = SW::k(ld_row[n], lane % CPR) * 8;
-    ld_col_v[n] = SW::v(ld_row[n], lane % CPR) * 8;
+    ld_col_k[n] = src_k(ld_row[n], lane % CPRP) * 8;
+    ld_col_v[n] = src_v(ld_row[n], lane % CPRP) * 8;
   }
   auto page_ids = [&](int kt, int (&pg)[LPW]) __attribute__((always_inline)) {
 #pragma unroll
@@ -365,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[ks]);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * DP + rd_k[ks]);
         s[kb] = mfma32x32x16<BF16>(a, qf[ks], ks == 0 ? zero16 : s[kb]);
       }
   };
@@ -423,8 +437,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma16_kernel(const FwdParams 
     for (int t = 0; t < NPS; ++t)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(vl + t * 16 * D + rd_v[db]);
-        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * D + rd_v[db]);
+        const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + rd_v[db]);
+        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + rd_v[db]);
         o[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pf[t], o[db]);
       }
   };
@@ -888,6 +902,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f32_kernel(const FwdParams p) 
 #endif
 constexpr int kNW16 = ATTN_PREFILL_WAVES;  // waves per workgroup, 16-bit inputs
 constexpr int kBN16 = ATTN_PREFILL_KEYS;   // keys per tile, 16-bit inputs
+// head dims 192 and 256: 4 waves (one per SIMD, so each may hold the 96 or 128
+// accumulator registers of its 32-row output block, the Q fragments, the scores and the
+// fragments read ahead without spilling); 32-key tiles at 256
+constexpr int nw16(int D) { return D >= 192 ? 4 : kNW16; }
+constexpr int bn16(int D) { return D == 256 ? 32 : kBN16; }
 constexpr int kNW32 = 4;
 constexpr int kBN32 = 32;
 
@@ -905,10 +924,11 @@ hipError_t launch16(const FwdParams& p, hipStream_t st) {
       hipLaunchKernelGGL((fwd_r2_kernel<BF16, 0>), grid, block, 0, st, p);
     }
     return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((fwd_mfma16_kernel<D, nw16(D), bn16(D), BF16>), dim3((unsigned)blocks), dim3(nw16(D) * 64), 0,
+                       st, p);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((fwd_mfma16_kernel<D, kNW16, kBN16, BF16>), dim3((unsigned)blocks), dim3(kNW16 * 64), 0,
-                     st, p);
-  return hipGetLastError();
 }
 
 template <int D>
@@ -948,14 +968,14 @@ template <int D, bool BF16>
 hipError_t launch16_paged(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = (int64_t)p.q_tiles * p.hq * p.batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_mfma16_kernel<D, kNW16, kBN16, BF16, true>), dim3((unsigned)blocks), dim3(kNW16 * 64),
-                     0, st, p);
+  hipLaunchKernelGGL((fwd_mfma16_kernel<D, nw16(D), bn16(D), BF16, true>), dim3((unsigned)blocks),
+                     dim3(nw16(D) * 64), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int fwd_paged_block_rows() { return kNW16 * 32; }
+int fwd_paged_block_rows(int head_dim) { return nw16(head_dim) * 32; }
 
 hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,
@@ -972,16 +992,22 @@ hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStre
   switch (dtype * 1000 + head_dim) {
     case 1032: return launch16_paged<32, false>(p, st);
     case 1064: return launch16_paged<64, false>(p, st);
+    case 1096: return launch16_paged<96, false>(p, st);
     case 1128: return launch16_paged<128, false>(p, st);
+    case 1192: return launch16_paged<192, false>(p, st);
+    case 1256: return launch16_paged<256, false>(p, st);
     case 2032: return launch16_paged<32, true>(p, st);
     case 2064: return launch16_paged<64, true>(p, st);
+    case 2096: return launch16_paged<96, true>(p, st);
     case 2128: return launch16_paged<128, true>(p, st);
+    case 2192: return launch16_paged<192, true>(p, st);
+    case 2256: return launch16_paged<256, true>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-int fwd_block_rows(int dtype, int /*head_dim*/) {
-  return dtype == 0 ? kNW32 * 32 : kNW16 * 32;
+int fwd_block_rows(int dtype, int head_dim) {
+  return dtype == 0 ? kNW32 * 32 : head_dim == 128 ? 256 : nw16(head_dim) * 32;
 }
 
 // dtype: 0 = f32, 1 = f16, 2 = bf16 (attn_dtype_t values)
@@ -992,10 +1018,16 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t s
     case 128: return launch32<128>(p, st);
     case 1032: return launch16<32, false>(p, st);
     case 1064: return launch16<64, false>(p, st);
+    case 1096: return launch16<96, false>(p, st);
     case 1128: return launch16<128, false>(p, st);
+    case 1192: return launch16<192, false>(p, st);
+    case 1256: return launch16<256, false>(p, st);
     case 2032: return launch16<32, true>(p, st);
     case 2064: return launch16<64, true>(p, st);
+    case 2096: return launch16<96, true>(p, st);
     case 2128: return launch16<128, true>(p, st);
+    case 2192: return launch16<192, true>(p, st);
+    case 2256: return launch16<256, true>(p, st);
     default: return hipErrorInvalidValue;
   }
 }

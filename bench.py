@@ -134,6 +134,60 @@ def load_traffic(kernel_substr):
     return round(sum(tot)) if tot else None
 
 
+def _timed(torch, fn, flush, reps: int) -> float:
+    """Average duration (ms) of fn over reps launches, HIP events on the current stream
+    around each launch, caches flushed before each."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """Timings of the variants beside the main workloads: the 16-bit prefill at head dims
+    96 / 192 / 256 (causal B=2 H=16 N=4096 bf16), the headline prefill with a per-head
+    sink, and the decode workload with one KV head (MQA; bytes = the KV cache read once)."""
+    res = {}
+    for d in (96, 192, 256):
+        c = workloads.config_headdim(d)
+        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+        o = torch.empty_like(q)
+        ms = _timed(torch, lambda: attn.fwd(q, k, v, causal=True, out=o), flush, reps)
+        fl = 4.0 * d * c.num_q_heads * c.batch * allowed_pairs(c.seqlen_q, c.seqlen_k, True)
+        res[f"prefill_causal_B2_H16_N4096_D{d}"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                                                    "frac_of_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o
+    pc = workloads.config_headline()
+    q, k, v = pc.q.to(dev), pc.k.to(dev), pc.v.to(dev)
+    o = torch.empty_like(q)
+    sinks = torch.linspace(-2.0, 6.0, pc.num_q_heads, dtype=torch.float32, device=dev)
+    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, sinks=sinks), flush, reps)
+    fl = prefill_flops(pc.batch, pc.num_q_heads, pc.seqlen_q, pc.seqlen_k, pc.head_dim)
+    res["prefill_headline_with_sink"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+    del q, k, v, o
+    dc = workloads.config_decode("bf16", num_kv_heads=1)
+    t = dict(q=dc.q.to(dev), k=dc.k_cache.to(dev), v=dc.v_cache.to(dev), bt=torch.from_numpy(dc.block_table).to(dev),
+             sl=torch.from_numpy(dc.seq_lens).to(dev))
+    ws = torch.empty(attn.decode_workspace_size(num_seqs=dc.num_seqs, num_q_heads=32, num_kv_heads=1, head_dim=128,
+                                                max_pages_per_seq=dc.max_pages, max_seq_len=dc.max_seq_len,
+                                                q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    od = torch.empty_like(t["q"])
+    ms = _timed(torch, lambda: attn.decode_paged(t["q"], t["k"], t["v"], t["bt"], t["sl"], dc.max_seq_len, out=od,
+                                                 workspace=ws), flush, reps)
+    nb = decode_bytes(dc, kv_elt=2)
+    res["decode_mqa_64seq_Hq32_Hkv1"] = {"ms": round(ms, 4), "gbps": round(nb / ms / 1e6, 1),
+                                         "frac_of_peak": round(nb / ms / 1e6 / PEAK_HBM_GBPS, 4),
+                                         "bytes_per_launch": nb}
+    return res
+
+
 def random_bf16_words(seed: int, n_words: int) -> "np.ndarray":
     """n_words 32-bit words, each two bf16 values (truncated) of a standard normal draw."""
     x = np.random.default_rng(seed).standard_normal(2 * n_words).astype(np.float32)
@@ -189,6 +243,8 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true",
                     help="run only the decode (per-kernel counter passes; prints decode timing only)")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill over the paged cache")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the variant measurements (head dims 96/192/256, sink, MQA decode)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--no-flush", action="store_true",
@@ -381,6 +437,10 @@ def main(argv=None):
                                                "ms": round(davg_, 4),
                                                "kernel": "fwd_mfma16_kernel<128, 8, 64, bf16, paged>"}}
     out["cache_flush_before_each_launch"] = flush_buf is not None
+
+    # ------------------------------------------------------------ variants ----
+    if not args.no_variants and not args.no_prefill:
+        out["variants"] = measure_variants(attn, torch, workloads, dev, flush, args.steps)
 
     # ------------------------------------------------------- measured peaks ----
     if not args.no_probes:

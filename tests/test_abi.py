@@ -66,7 +66,10 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(num_q_heads=6, num_kv_heads=4), _lib.ATTN_ERROR_INVALID_VALUE),
-    (dict(head_dim=96), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(head_dim=96), _lib.ATTN_ERROR_NOT_SUPPORTED),           # fp32: 32, 64, 128 only
+    (dict(head_dim=96, dtype=_lib.ATTN_BF16, q_stride=(8192, 2048, 96), k_stride=(8192, 2048, 96),
+          v_stride=(8192, 2048, 96), o_stride=(8192, 2048, 96), batch=0), _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(head_dim=80, dtype=_lib.ATTN_BF16), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(dtype=_lib.ATTN_FP8_E4M3), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(window=16), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(causal=2), _lib.ATTN_ERROR_INVALID_VALUE),
@@ -116,7 +119,8 @@ def _paged_args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(num_seqs=0), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(num_q_heads=6, num_kv_heads=4), _lib.ATTN_ERROR_INVALID_VALUE),
-    (dict(head_dim=96), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(head_dim=80), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(head_dim=512), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(dtype=_lib.ATTN_F32), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(dtype=_lib.ATTN_FP8_E4M3), _lib.ATTN_ERROR_NOT_SUPPORTED),
     (dict(page_size=32), _lib.ATTN_ERROR_NOT_SUPPORTED),

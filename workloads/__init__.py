@@ -332,13 +332,14 @@ def decode_lengths(seed: int = 5, num_seqs: int = 64, lo: int = 512, hi: int = 3
 
 
 def config_decode(kv_dtype: str, seed: int = 5, num_seqs: int = 64,
-                  lengths: Optional[Sequence[int]] = None) -> DecodeCase:
-    """Split-KV paged decode: 64 sequences, Hq=32 Hkv=8 D=128, L ~ U[512, 32768]."""
+                  lengths: Optional[Sequence[int]] = None, num_kv_heads: int = 8) -> DecodeCase:
+    """Split-KV paged decode: 64 sequences, Hq=32 Hkv=8 D=128, L ~ U[512, 32768]
+    (num_kv_heads=1: the MQA form of the same workload)."""
     if lengths is None:
         lengths = decode_lengths(seed, num_seqs)
     child = np.random.SeedSequence(seed).spawn(2)[1]
     sub = int(np.random.Generator(np.random.PCG64(child)).integers(0, 2**63))
-    return make_decode(lengths=lengths, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    return make_decode(lengths=lengths, num_q_heads=32, num_kv_heads=num_kv_heads, head_dim=128,
                        q_dtype="bf16", kv_dtype=kv_dtype, seed=sub + (1 if kv_dtype != "bf16" else 0))
 
 
@@ -366,6 +367,13 @@ def config_chunked_prefill(seed: int = 6, num_seqs: int = 8, chunk: int = 2048,
     lq, lk = chunked_prefill_lengths(seed, num_seqs, chunk, max_context)
     return make_paged_prefill(lengths_q=lq, lengths_k=lk, num_q_heads=32, num_kv_heads=8,
                               head_dim=128, dtype="bf16", seed=seed)
+
+
+def config_headdim(head_dim: int, seed: int = 8) -> PrefillCase:
+    """Causal prefill bf16 B=2 H=16 N=4096 at the head dims without a dedicated workload
+    (96, 192, 256); Q, K, V iid N(0,1)."""
+    return make_prefill(batch=2, num_q_heads=16, num_kv_heads=16, seqlen_q=4096, head_dim=head_dim,
+                        dtype="bf16", seed=seed + head_dim, causal=True)
 
 
 def position_code(pos: np.ndarray, dim: int, base: int = 16, digits: int = 3) -> np.ndarray:
