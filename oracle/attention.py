@@ -194,6 +194,21 @@ def gather_pages(cache: np.ndarray, block_table_row: np.ndarray, seq_len: int,
     return cache[pages, t % page_size]
 
 
+def prefill_fp8(q_codes: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray, *, q_scale: float,
+                k_scale: float, v_scale: float, scale: float, causal: bool = False, window: int = 0,
+                softcap: float = 0.0, q_rows: Optional[np.ndarray] = None, heads: Optional[np.ndarray] = None,
+                sink: Optional[np.ndarray] = None):
+    """Dense prefill on fp8 (e4m3) inputs with per-tensor scales: the stored codes, already
+    widened to their float64 values, times q_scale / k_scale / v_scale are the Q, K, V of
+    the definition (fp8 inputs are a scenario axis of the Ask-Don't-Equip page, section
+    研究动机; the per-tensor scale is the reading taken). Layout and sampling as
+    prefill_dense.
+    """
+    return prefill_dense(np.asarray(q_codes) * float(q_scale), np.asarray(k_codes) * float(k_scale),
+                         np.asarray(v_codes) * float(v_scale), scale=scale, causal=causal, window=window,
+                         softcap=softcap, q_rows=q_rows, heads=heads, sink=sink)
+
+
 def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
                  seq_lens: np.ndarray, *, scale: float, k_scale: Optional[np.ndarray] = None,
                  v_scale: Optional[np.ndarray] = None, seqs: Optional[np.ndarray] = None,

@@ -491,3 +491,40 @@ def test_sink_passes_through_every_entry():
                                    vd[0].transpose(1, 0, 2), cu, cu, scale=0.5, causal=True, sink=sink)
     np.testing.assert_allclose(ov.transpose(1, 0, 2), ob, atol=1e-15)
     np.testing.assert_allclose(lv, lb, atol=1e-15)
+
+
+# ------------------------------------------------------------------ fp8 prefill ----
+
+def test_fp8_prefill_brute_force_on_decoded_codes():
+    from workloads import make_prefill_fp8
+    case = make_prefill_fp8(batch=1, num_q_heads=2, num_kv_heads=1, seqlen_q=5, seqlen_k=7, head_dim=4,
+                            seed=41, causal=True)
+    qc, kc, vc = (oracle.tensor_to_f64(t, "fp8_e4m3") for t in (case.q, case.k, case.v))
+    o, lse = oracle.prefill_fp8(qc, kc, vc, q_scale=case.q_scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                                scale=0.5, causal=True)
+    # decode the codes by the format's definition (sign, 4-bit exponent with bias 7, 3-bit mantissa)
+    def dec(code):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        x = m * 2.0 ** -9 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        return -x if s else x
+    bits = [t.view(torch.uint8).numpy() for t in (case.q, case.k, case.v)]
+    qv = [[[dec(int(c)) * case.q_scale for c in row] for row in bits[0][0, h]] for h in range(2)]
+    kv = [[[dec(int(c)) * case.k_scale for c in row] for row in bits[1][0, 0]]]
+    vv = [[[dec(int(c)) * case.v_scale for c in row] for row in bits[2][0, 0]]]
+    ob, lb = brute.brute_sdpa(qv, kv, vv, scale=0.5, causal=True)
+    np.testing.assert_allclose(o[0], np.array(ob), rtol=0, atol=1e-12)
+    fin = np.isfinite(np.array(lb))
+    np.testing.assert_allclose(lse[0][fin], np.array(lb)[fin], rtol=0, atol=1e-12)
+
+
+def test_fp8_prefill_scale_laws():
+    q, k, v = np.round(_rand(1, 2, 6, 3) * 8), np.round(_rand(1, 2, 9, 3) * 8), np.round(_rand(1, 2, 9, 3) * 8)
+    o1, l1 = oracle.prefill_fp8(q, k, v, q_scale=0.25, k_scale=0.5, v_scale=1.0, scale=0.3)
+    # the value scale multiplies O and leaves the LSE; the product of the Q and K scales and the
+    # softmax scale is all that reaches the scores
+    o2, l2 = oracle.prefill_fp8(q, k, v, q_scale=0.25, k_scale=0.5, v_scale=3.0, scale=0.3)
+    np.testing.assert_allclose(o2, 3.0 * o1, rtol=1e-14)
+    np.testing.assert_array_equal(l2, l1)
+    o3, l3 = oracle.prefill_fp8(q, k, v, q_scale=0.5, k_scale=1.0, v_scale=1.0, scale=0.075)
+    np.testing.assert_allclose(o3, o1, rtol=1e-13)
+    np.testing.assert_allclose(l3, l1, rtol=1e-13)

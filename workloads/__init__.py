@@ -369,6 +369,54 @@ def config_chunked_prefill(seed: int = 6, num_seqs: int = 8, chunk: int = 2048,
                               head_dim=128, dtype="bf16", seed=seed)
 
 
+@dataclasses.dataclass
+class Fp8PrefillCase:
+    """Dense prefill on fp8 e4m3 codes [B, H, N, D] (torch.float8_e4m3fn) with per-tensor
+    scales (value = code * scale); the output is bf16."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    q_scale: float
+    k_scale: float
+    v_scale: float
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    seqlen_q: int
+    seqlen_k: int
+    head_dim: int
+    causal: bool = False
+    window: int = 0
+    softcap: float = 0.0
+
+
+def make_prefill_fp8(*, batch: int, num_q_heads: int, num_kv_heads: int, seqlen_q: int,
+                     seqlen_k: Optional[int] = None, head_dim: int, seed, input_scale: float = 1.0,
+                     causal: bool = False, window: int = 0, softcap: float = 0.0) -> Fp8PrefillCase:
+    """Q, K, V drawn as make_prefill draws them, then stored as e4m3 codes of x / s with
+    one scale per tensor, s = max|x| / 448 (the codes span the format's range)."""
+    seqlen_k = seqlen_q if seqlen_k is None else seqlen_k
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for shape in ((batch, num_q_heads, seqlen_q, head_dim), (batch, num_kv_heads, seqlen_k, head_dim),
+                  (batch, num_kv_heads, seqlen_k, head_dim)):
+        x = _normal(rng, shape, input_scale)
+        sc = np.float32(max(float(np.abs(x).max()), 1e-30) / 448.0)
+        out.append((_cast(x / sc, "fp8_e4m3"), float(sc)))
+    (q, qs), (k, ks), (v, vs) = out
+    return Fp8PrefillCase(q=q, k=k, v=v, q_scale=qs, k_scale=ks, v_scale=vs, batch=batch,
+                          num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, seqlen_q=seqlen_q,
+                          seqlen_k=seqlen_k, head_dim=head_dim, causal=causal, window=window,
+                          softcap=softcap)
+
+
+def config_fp8_headline(seed: int = 9) -> Fp8PrefillCase:
+    """The headline shape (B=1 H=32 N=8192 D=128, dense, inputs 0.5 N(0,1)) on fp8 e4m3
+    inputs with per-tensor scales."""
+    return make_prefill_fp8(batch=1, num_q_heads=32, num_kv_heads=32, seqlen_q=8192, head_dim=128,
+                            seed=seed, input_scale=0.5)
+
+
 def config_headdim(head_dim: int, seed: int = 8) -> PrefillCase:
     """Causal prefill bf16 B=2 H=16 N=4096 at the head dims without a dedicated workload
     (96, 192, 256); Q, K, V iid N(0,1)."""
