@@ -57,7 +57,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         softcap: float = 0.0, softmax_scale: float = 0.0, cu_seqlens_q: Optional[torch.Tensor] = None,
         cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
         max_seqlen_k: Optional[int] = None, return_lse: bool = False, out: Optional[torch.Tensor] = None,
-        lse_out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None):
+        lse_out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
+        q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0):
     """Fused attention forward.
 
     Dense: q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (any strides with D contiguous).
@@ -65,10 +66,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     GPU and host-side upper bounds max_seqlen_q/k.
     Returns o (like q), and lse (float32; dense [B, Hq, Nq], ragged [Hq, T]) if
     return_lse. sinks: optional float32 [Hq] per-head sink logits (natural log).
+    float8_e4m3fn q/k/v (head_dim 128) take per-tensor scales q_scale / k_scale /
+    v_scale (value = code * scale) and give a bfloat16 o.
     """
     _require_cuda(q, k, v, sinks)
-    if q.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+    if q.dtype not in (torch.float32, torch.float16, torch.bfloat16, torch.float8_e4m3fn):
         raise AttnNotSupported(_lib.ATTN_ERROR_NOT_SUPPORTED, f"dtype {q.dtype} not supported")
+    out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share a dtype")
     ragged = cu_seqlens_q is not None
@@ -105,9 +109,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         raise ValueError("head_dim must be contiguous")
     if k.shape[-1] != a.head_dim or v.shape[-1] != a.head_dim:
         raise ValueError("q, k and v must share head_dim")
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
-    if o.shape != q.shape or o.dtype != q.dtype or o.stride(-1) != 1:
-        raise ValueError("out must match q's shape and dtype")
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device) if out is None else out
+    if o.shape != q.shape or o.dtype != out_dtype or o.stride(-1) != 1:
+        raise ValueError(f"out must have q's shape and dtype {out_dtype}")
     os_ = (0, o.stride(1), o.stride(0)) if ragged else (o.stride(0), o.stride(1), o.stride(2))
     lse = None
     if return_lse:
@@ -120,6 +124,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     a.softmax_scale = float(softmax_scale)
     a.softcap = float(softcap)
     a.sinks = _sinks_ptr(sinks, a.num_q_heads)
+    a.q_scale, a.k_scale, a.v_scale = float(q_scale), float(k_scale), float(v_scale)
     for name, st in (("q_stride", qs), ("k_stride", ks), ("v_stride", vs), ("o_stride", os_)):
         arr = getattr(a, name)
         for i in range(3):

@@ -43,6 +43,9 @@ class FwdArgs(ctypes.Structure):
         ("cu_seqlens_q", ctypes.c_void_p),
         ("cu_seqlens_k", ctypes.c_void_p),
         ("sinks", ctypes.c_void_p),
+        ("q_scale", ctypes.c_float),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 

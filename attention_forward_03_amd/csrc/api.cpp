@@ -103,11 +103,17 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
                 a->num_q_heads, a->num_kv_heads);
   if (a->seqlen_q < 0 || a->seqlen_k < 0)
     return fail(ATTN_ERROR_INVALID_VALUE, "sequence lengths must be >= 0");
-  if (a->dtype != ATTN_F32 && a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
-    return fail(ATTN_ERROR_NOT_SUPPORTED, "dtype %d is not F32, F16 or BF16", a->dtype);
-  if (!head_dim_ok(a->head_dim, a->dtype != ATTN_F32))
+  if (a->dtype != ATTN_F32 && a->dtype != ATTN_F16 && a->dtype != ATTN_BF16 && a->dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "dtype %d is not F32, F16, BF16 or FP8_E4M3", a->dtype);
+  const bool fp8 = a->dtype == ATTN_FP8_E4M3;
+  if (fp8 ? a->head_dim != 128 : !head_dim_ok(a->head_dim, a->dtype != ATTN_F32))
     return fail(ATTN_ERROR_NOT_SUPPORTED, "head_dim %d is not one of %s", a->head_dim,
-                a->dtype != ATTN_F32 ? "32, 64, 96, 128, 192, 256" : "32, 64, 128");
+                fp8 ? "128" : a->dtype != ATTN_F32 ? "32, 64, 96, 128, 192, 256" : "32, 64, 128");
+  if (fp8 && a->cu_seqlens_q != nullptr)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "fp8 inputs take dense batches only");
+  if (fp8 && !(a->q_scale > 0.0f && a->k_scale > 0.0f && a->v_scale > 0.0f && !isinf(a->q_scale) &&
+               !isinf(a->k_scale) && !isinf(a->v_scale)))
+    return fail(ATTN_ERROR_INVALID_VALUE, "fp8 inputs need finite q_scale, k_scale and v_scale > 0");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERROR_INVALID_VALUE, "causal must be 0 or 1");
   if (a->window > 0 && !a->causal)
     return fail(ATTN_ERROR_INVALID_VALUE, "a sliding window requires causal = 1");
@@ -131,7 +137,7 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
   if ((st = check_strides("q", a->q_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
   if ((st = check_strides("k", a->k_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
   if ((st = check_strides("v", a->v_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
-  if ((st = check_strides("o", a->o_stride, es, a->head_dim)) != ATTN_SUCCESS) return st;
+  if ((st = check_strides("o", a->o_stride, fp8 ? 2 : es, a->head_dim)) != ATTN_SUCCESS) return st;
 
   attn::FwdParams p{};
   p.q = q;
@@ -155,7 +161,10 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
   p.nk = a->seqlen_k;
   p.causal = a->causal;
   p.window = a->window > 0 ? a->window : 0;
-  const double scale = resolve_scale(a->softmax_scale, a->head_dim);
+  // fp8: the Q and K scales multiply the scores (folded into the exponent's scale), the V
+  // scale the output (folded into the normalisation)
+  const double scale = resolve_scale(a->softmax_scale, a->head_dim) *
+                       (fp8 ? (double)a->q_scale * (double)a->k_scale : 1.0);
   p.scale_log2 = (float)(scale * kLog2eD);
   if (a->softcap > 0.0f) {
     p.cap_in = (float)(scale / (double)a->softcap);
@@ -164,11 +173,13 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
     p.cap_in = 0.0f;
     p.cap_out = 0.0f;
   }
-  const int bm = attn::fwd_block_rows(a->dtype, a->head_dim);
+  p.o_scale = fp8 ? a->v_scale : 1.0f;
+  const int bm = fp8 ? attn::fwd_fp8_block_rows() : attn::fwd_block_rows(a->dtype, a->head_dim);
   p.q_tiles = (a->seqlen_q + bm - 1) / bm;
   p.sinks = a->sinks;
 
-  hipError_t e = attn::launch_fwd(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
+  hipError_t e = fp8 ? attn::launch_fwd_fp8(p, a->head_dim, static_cast<hipStream_t>(stream))
+                     : attn::launch_fwd(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

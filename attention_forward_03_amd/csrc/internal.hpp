@@ -33,6 +33,7 @@ struct FwdParams {
   const int32_t* seq_lens_k;
   int32_t max_pages, num_pages;
   const float* sinks;   // per query head sink logit (natural log), or NULL
+  float o_scale;        // fp8 inputs: the value scale, applied with the normalisation
 };
 
 // One paged-decode launch (split kernel + combine kernel).
@@ -63,6 +64,9 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t s
 // chunked prefill over a paged cache (16-bit inputs)
 hipError_t launch_fwd_paged(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
 int fwd_paged_block_rows(int head_dim);
+// fp8 e4m3 dense prefill (head_dim 128, bf16 output)
+int fwd_fp8_block_rows();
+hipError_t launch_fwd_fp8(const FwdParams& p, int head_dim, hipStream_t stream);
 // page-by-page copy of K and V into per-sequence slots of max_pages * 16 tokens
 hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,

@@ -28,6 +28,7 @@ import time
 import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2   # dense fp8 matrix cores: twice the 16-bit rate
 PEAK_HBM_GBPS = 8000.0
 
 
@@ -66,13 +67,15 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 PREFILL_KERNEL = "fwd_r2_kernel<true, 0>"
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
 CHUNKED_KERNEL = ("gather_kv_pages_kernel", "fwd_r2_kernel<true, 1>")
+FP8_KERNEL = "fwd_fp8_kernel"
 
 
 def kernel_source_digest() -> str:
     """Digest of the kernel sources: counter-derived traffic is only reported while it matches."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("prefill.hip", "gen_prefill_r2.py", "decode.hip", "common.hpp"):
+    for name in ("prefill.hip", "prefill_fp8.hip", "prefill_shared.hpp", "gen_prefill_r2.py", "decode.hip",
+                 "common.hpp"):
         with open(os.path.join(HERE, "attention_forward_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -243,6 +246,7 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true",
                     help="run only the decode (per-kernel counter passes; prints decode timing only)")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill over the paged cache")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 e4m3 prefill")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the variant measurements (head dims 96/192/256, sink, MQA decode)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -437,6 +441,22 @@ def main(argv=None):
                                                "ms": round(davg_, 4),
                                                "kernel": "fwd_mfma16_kernel<128, 8, 64, bf16, paged>"}}
     out["cache_flush_before_each_launch"] = flush_buf is not None
+
+    # ----------------------------------------------------------- fp8 prefill ----
+    if not args.no_fp8 and not args.no_prefill:
+        fc = workloads.config_fp8_headline()
+        fq, fk, fv = fc.q.to(dev), fc.k.to(dev), fc.v.to(dev)
+        fo = torch.empty(fq.shape, dtype=torch.bfloat16, device=dev)
+        fms = _timed(torch, lambda: attn.fwd(fq, fk, fv, out=fo, q_scale=fc.q_scale, k_scale=fc.k_scale,
+                                             v_scale=fc.v_scale), flush, args.steps)
+        ftf = flops / (fms * 1e-3) / 1e12
+        out["fp8_prefill"] = {"tflops": round(ftf, 2), "ms": round(fms, 4), "flops_per_launch": flops,
+                              "workload": "dense non-causal B=1 H=32 N=8192 D=128, Q/K/V fp8 e4m3 with "
+                                          "per-tensor scales, O bf16",
+                              "roofline": {"bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_FP8_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
+                                           "traffic": load_traffic(FP8_KERNEL), "kernel": "fwd_fp8_kernel"}}
+        del fq, fk, fv, fo
 
     # ------------------------------------------------------------ variants ----
     if not args.no_variants and not args.no_prefill:

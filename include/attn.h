@@ -69,8 +69,9 @@ typedef struct {
   int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
   int32_t seqlen_q;      /* dense: Nq; ragged: an upper bound of every sequence's query length */
   int32_t seqlen_k;      /* dense: Nk; ragged: an upper bound of every sequence's key length */
-  int32_t head_dim;      /* D in {32, 64, 128} */
-  int32_t dtype;         /* attn_dtype_t: ATTN_F32, ATTN_F16 or ATTN_BF16, shared by Q, K, V, O */
+  int32_t head_dim;      /* D: 32, 64, 128 (F32); 32, 64, 96, 128, 192, 256 (F16, BF16); 128 (FP8_E4M3) */
+  int32_t dtype;         /* attn_dtype_t: ATTN_F32, ATTN_F16 or ATTN_BF16, shared by Q, K, V, O;
+                            or ATTN_FP8_E4M3 for Q, K, V with O in BF16 (dense batches) */
   int32_t causal;        /* 0/1. Bottom-right aligned: key j allowed for query i iff j <= i + (Nk - Nq) */
   int32_t window;        /* <= 0: off. W > 0 (requires causal): also j > i + (Nk - Nq) - W,
                             i.e. the W most recent keys, the diagonal included */
@@ -97,6 +98,11 @@ typedef struct {
    * LSE = sigma_h. ("attention-sink" in the masks of the feature surface named by
    * "Ask, Don't Equip", section 研究动机; the definition is the per-head sink logit.) */
   const float *sinks;
+  /* FP8_E4M3 inputs only: one scale per tensor, value = code * scale (finite, > 0; ignored
+   * for the other dtypes). Q and K's scales multiply the scores, V's the output.
+   * (fp8 inputs: "Ask, Don't Equip", section 研究动机; the per-tensor scale is the
+   * reading taken.) */
+  float q_scale, k_scale, v_scale;
 } attn_fwd_args_t;
 
 /*
@@ -104,13 +110,15 @@ typedef struct {
  *
  *   q   [B, Hq, Nq, D] (or ragged [T, Hq, D]) in args->dtype
  *   k,v [B, Hkv, Nk, D] (or ragged [Tk, Hkv, D]) in args->dtype
- *   o   same layout as q (strides o_stride), written in args->dtype
+ *   o   same layout as q (strides o_stride), written in args->dtype (BF16 for FP8_E4M3
+ *       inputs; strides are in elements of each tensor's own type)
  *   lse nullable, float32, natural-log log-sum-exp of each row's final scores:
  *       dense [B, Hq, Nq] contiguous; ragged [Hq, T] contiguous.
  *       A row with no allowed key gets O = 0 and LSE = -inf.
  *
  * Accumulation is float32 throughout; Q K^T and P V run on the matrix cores
- * (bf16/f16 inputs: P is rounded to the input type before P V).
+ * (bf16/f16 inputs: P is rounded to the input type before P V; fp8 inputs: P is
+ * rounded to e4m3 and both products run on the fp8 matrix cores).
  */
 attn_status_t attn_fwd(const attn_fwd_args_t *args, const void *q, const void *k, const void *v,
                        void *o, float *lse, void *stream);

@@ -70,7 +70,11 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
     (dict(head_dim=96, dtype=_lib.ATTN_BF16, q_stride=(8192, 2048, 96), k_stride=(8192, 2048, 96),
           v_stride=(8192, 2048, 96), o_stride=(8192, 2048, 96), batch=0), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(head_dim=80, dtype=_lib.ATTN_BF16), _lib.ATTN_ERROR_NOT_SUPPORTED),
-    (dict(dtype=_lib.ATTN_FP8_E4M3), _lib.ATTN_ERROR_NOT_SUPPORTED),
+    (dict(dtype=_lib.ATTN_FP8_E4M3), _lib.ATTN_ERROR_NOT_SUPPORTED),             # head_dim 32
+    (dict(dtype=_lib.ATTN_FP8_E4M3, head_dim=128, q_scale=0.0, k_scale=1.0, v_scale=1.0),
+     _lib.ATTN_ERROR_INVALID_VALUE),
+    (dict(dtype=_lib.ATTN_FP8_E4M3, head_dim=128, q_scale=1.0, k_scale=float("inf"), v_scale=1.0),
+     _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(window=16), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(causal=2), _lib.ATTN_ERROR_INVALID_VALUE),
     (dict(seqlen_q=-1), _lib.ATTN_ERROR_INVALID_VALUE),
