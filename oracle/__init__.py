@@ -40,16 +40,20 @@ paged = dense, chunked paged prefill = brute force with
 scalar page indexing and = decode at one query, page-permutation invariance,
 split/combine associativity, the sink (brute force, one-key closed form, the
 rescaling identity O_sink = O e^LSE / (e^LSE + e^sigma), a negligible sink), the fp8
-prefill (brute force on codes decoded bit by bit, the scale laws), softcap and window limits) and
+prefill (brute force on codes decoded bit by bit, the scale laws), the backward (central
+finite differences of sum(dO * O), float64 autograd through a separately written forward,
+closed forms for one key and for identical keys), softcap and window limits) and
 library special cases (torch's bf16 / fp16 / float8_e4m3fn conversions).
 """
 from .numerics import (bf16_bits_to_f64, f16_bits_to_f64, e4m3_code_table, e4m3_codes_to_f64,
                        default_scale, tensor_to_f64)
 from .attention import (sdpa_fp64, prefill_dense, prefill_varlen, prefill_fp8, gather_pages, decode_paged,
-                        prefill_paged, combine_partials, attention_probs)
+                        prefill_paged, combine_partials, attention_probs, sdpa_backward_fp64,
+                        prefill_backward_dense)
 
 __all__ = [
     "bf16_bits_to_f64", "f16_bits_to_f64", "e4m3_code_table", "e4m3_codes_to_f64",
     "default_scale", "tensor_to_f64", "sdpa_fp64", "prefill_dense", "prefill_varlen", "prefill_fp8",
     "gather_pages", "decode_paged", "prefill_paged", "combine_partials", "attention_probs",
+    "sdpa_backward_fp64", "prefill_backward_dense",
 ]

@@ -285,3 +285,69 @@ def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
     coef = np.where(tot[None] > 0, w / np.where(tot > 0, tot, 1.0)[None], 0.0)
     o = (coef[..., None] * o_parts).sum(axis=0)
     return o, lse
+
+
+def sdpa_backward_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *, scale: float,
+                       causal: bool = False, window: int = 0, softcap: float = 0.0,
+                       sink: Optional[np.ndarray] = None):
+    """Gradients of the forward definition for one sequence: q [Hq, Nq, D], k/v [Hkv, Nk, D],
+    do = dL/dO [Hq, Nq, D] -> (dq, dk, dv) of the same shapes (float64).
+
+    The backward pass is named by the Ask-Don't-Equip page (section 局限与改进: forward
+    only, a backward pass as the next step) and not defined there; these are the
+    derivatives of the definition, by the chain rule on its steps:
+      S_raw = Q K^T, S = scale S_raw (or c tanh(scale S_raw / c)), P = softmax of the allowed
+      S (with the sink in the normalisation when given), O = P V;
+      dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(dO * O));
+      dS_raw = dS * scale (times 1 - tanh^2(scale S_raw / c) with a softcap);
+      dQ = dS_raw K; dK = dS_raw^T Q. Query heads sharing a KV head add their dK, dV.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    hq, nq, _ = q.shape
+    hkv, nk, _ = k.shape
+    group = hq // hkv
+    mask = _allowed(nq, nk, causal=causal, window=window, q_pos=np.arange(nq), nq_total=nq)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        g = h // group
+        s_raw = q[h] @ k[g].T
+        if softcap > 0:
+            t = np.tanh(s_raw * scale / softcap)
+            s = softcap * t
+        else:
+            s = s_raw * scale
+        if mask is not None:
+            s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1)
+        if sink is not None:
+            m = np.maximum(m, float(sink[h]))
+        ok = np.isfinite(m)
+        p = np.zeros_like(s)
+        p[ok] = np.exp(s[ok] - m[ok, None])
+        l = p.sum(axis=1)
+        if sink is not None:
+            l = l + np.exp(float(sink[h]) - m)
+        p[ok] /= l[ok, None]
+        o = p @ v[g]
+        dv[g] += p.T @ do[h]
+        dp = do[h] @ v[g].T
+        delta = (do[h] * o).sum(axis=1)
+        ds = p * (dp - delta[:, None])
+        ds_raw = ds * scale * ((1.0 - t * t) if softcap > 0 else 1.0)
+        dq[h] = ds_raw @ k[g]
+        dk[g] += ds_raw.T @ q[h]
+    return dq, dk, dv
+
+
+def prefill_backward_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *, scale: float,
+                           causal: bool = False, window: int = 0, softcap: float = 0.0,
+                           sink: Optional[np.ndarray] = None):
+    """Batched dense: q/do [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] -> (dq, dk, dv)."""
+    out = [sdpa_backward_fp64(q[b], k[b], v[b], do[b], scale=scale, causal=causal, window=window,
+                              softcap=softcap, sink=sink) for b in range(q.shape[0])]
+    return tuple(np.stack([o[i] for o in out]) for i in range(3))

@@ -528,3 +528,63 @@ def test_fp8_prefill_scale_laws():
     o3, l3 = oracle.prefill_fp8(q, k, v, q_scale=0.5, k_scale=1.0, v_scale=1.0, scale=0.075)
     np.testing.assert_allclose(o3, o1, rtol=1e-13)
     np.testing.assert_allclose(l3, l1, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------- backward ----
+
+def _loss(q, k, v, do, **kw):
+    o, _ = oracle.sdpa_fp64(q, k, v, **kw)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(causal=True), dict(causal=True, window=3), dict(softcap=1.5),
+                                dict(causal=True, sink=np.array([0.3, -1.0, 2.0, 0.0]))],
+                         ids=["full", "causal", "window", "softcap", "sink"])
+def test_backward_equals_finite_differences(kw):
+    # L = sum(dO * O): its gradients are the backward's outputs
+    q, k, v, do = _rand(4, 5, 3), _rand(2, 6, 3), _rand(2, 6, 3), _rand(4, 5, 3)
+    kw = dict(kw, scale=0.7)
+    dq, dk, dv = oracle.sdpa_backward_fp64(q, k, v, do, **kw)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = [xp if a is x else a for a in (q, k, v)]
+            argm = [xm if a is x else a for a in (q, k, v)]
+            num[idx] = (_loss(*args, do, **kw) - _loss(*argm, do, **kw)) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7)
+
+
+def test_backward_matches_autograd_of_a_separate_forward():
+    # torch float64 autograd through a forward written here (not the oracle's code)
+    tq, tk, tv, tdo = (torch.from_numpy(x).requires_grad_(True) for x in
+                       (_rand(4, 9, 5), _rand(2, 11, 5), _rand(2, 11, 5), _rand(4, 9, 5)))
+    scale, cap = 0.45, 2.0
+    kk, vv = tk.repeat_interleave(2, dim=0), tv.repeat_interleave(2, dim=0)
+    s = cap * torch.tanh(scale * (tq @ kk.transpose(1, 2)) / cap)
+    i = torch.arange(9)[:, None]
+    j = torch.arange(11)[None, :]
+    s = s.masked_fill(j > i + 2, float("-inf"))
+    o = torch.softmax(s, dim=-1) @ vv
+    (o * tdo).sum().backward()
+    dq, dk, dv = oracle.sdpa_backward_fp64(tq.detach().numpy(), tk.detach().numpy(), tv.detach().numpy(),
+                                           tdo.detach().numpy(), scale=scale, causal=True, softcap=cap)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_closed_forms():
+    # one key: O = v exactly, so dV = sum of dO and dQ = dK = 0
+    q, k, v, do = _rand(2, 3, 4), _rand(1, 1, 4), _rand(1, 1, 4), _rand(2, 3, 4)
+    dq, dk, dv = oracle.sdpa_backward_fp64(q, k, v, do, scale=0.5)
+    np.testing.assert_allclose(dv[0, 0], do.sum(axis=(0, 1)), atol=1e-14)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    # identical keys: uniform weights; dV_j = sum_i dO_i / Nk, dQ = 0
+    k3 = np.tile(k, (1, 5, 1))
+    dq, dk, dv = oracle.sdpa_backward_fp64(q, k3, _rand(1, 5, 4), do, scale=0.5)
+    np.testing.assert_allclose(dv[0], np.tile(do.sum(axis=(0, 1)) / 5, (5, 1)), atol=1e-14)
+    assert np.abs(dq).max() < 1e-13
