@@ -7,6 +7,7 @@ pointers. If the library is missing it raises: there is no CPU fallback.
 
     fwd(q, k, v, ...)            softmax(Q K^T * scale [+ mask]) V (prefill)
     fwd_paged(q, k_cache, ...)    chunked prefill over a paged cache
+    bwd(q, k, v, o, dout, lse)    gradients of fwd (dense batches)
     decode_paged(q, k_cache, ...) one query token per sequence over a paged cache
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, AttnInvalidValue, AttnNotSupported
 
-__all__ = ["fwd", "fwd_paged", "fwd_paged_workspace_size", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
+__all__ = ["fwd", "fwd_paged", "bwd", "fwd_paged_workspace_size", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
            "AttnError", "AttnInvalidValue", "AttnNotSupported"]
 
 _DTYPES = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
@@ -217,6 +218,44 @@ def fwd_paged_workspace_size(*, num_seqs, num_q_heads, num_kv_heads, head_dim, m
     a.dtype = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     a.causal = 1
     return int(_lib.lib().attn_fwd_paged_workspace_size(ctypes.byref(a)))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+        lse: torch.Tensor, *, causal: bool = False, window: int = 0, softcap: float = 0.0,
+        softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None):
+    """Gradients of fwd for dense batches: q, o, dout [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D]
+    (contiguous, bf16/f16); lse float32 [B, Hq, Nq] from fwd(..., return_lse=True).
+    Returns (dq, dk, dv)."""
+    _require_cuda(q, k, v, o, dout, lse)
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("backward tensors must be contiguous")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise AttnNotSupported(_lib.ATTN_ERROR_NOT_SUPPORTED, f"dtype {q.dtype} not supported")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout share a 16-bit dtype; lse is float32")
+    if q.dim() != 4 or k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B, Hq, Nq, D] and k, v [B, Hkv, Nk, D]")
+    if lse.shape != q.shape[:3]:
+        raise ValueError("lse must be [B, Hq, Nq]")
+    a = _lib.BwdArgs()
+    a.batch, a.num_q_heads, a.seqlen_q, a.head_dim = q.shape
+    a.num_kv_heads, a.seqlen_k = k.shape[1], k.shape[2]
+    a.dtype = _DTYPES[q.dtype]
+    a.causal = 1 if causal else 0
+    a.window = int(window)
+    a.softmax_scale = float(softmax_scale)
+    a.softcap = float(softcap)
+    L = _lib.lib()
+    need = int(L.attn_bwd_workspace_size(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    status = L.attn_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream_handle(q.device))
+    _lib.check(status)
+    return dq, dk, dv
 
 
 def _decode_args(*, num_seqs, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, max_seq_len,

@@ -18,7 +18,8 @@ ATTN_F16 = 1
 ATTN_BF16 = 2
 ATTN_FP8_E4M3 = 3
 
-EXPORTED = ("attn_fwd", "attn_fwd_paged", "attn_fwd_paged_workspace_size", "attn_decode_plan", "attn_decode_paged_workspace_size", "attn_decode_paged",
+EXPORTED = ("attn_fwd", "attn_fwd_paged", "attn_fwd_paged_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
+            "attn_decode_plan", "attn_decode_paged_workspace_size", "attn_decode_paged",
             "attn_probe_mfma", "attn_probe_hbm_read", "attn_flush_caches",
             "attn_status_string", "attn_last_error_message", "attn_abi_version")
 
@@ -85,6 +86,22 @@ class FwdPagedArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("seqlen_q", ctypes.c_int32),
+        ("seqlen_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+    ]
+
+
 _LIB = None
 
 
@@ -104,6 +121,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_paged.restype = ctypes.c_int
     L.attn_fwd_paged_workspace_size.argtypes = [ctypes.POINTER(FwdPagedArgs)]
     L.attn_fwd_paged_workspace_size.restype = ctypes.c_size_t
+    L.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs)] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]
+    L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+    L.attn_bwd_workspace_size.restype = ctypes.c_size_t
     L.attn_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int32),
                                    ctypes.POINTER(ctypes.c_int32)]
     L.attn_decode_plan.restype = ctypes.c_int

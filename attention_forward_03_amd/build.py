@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
-SOURCES = ("prefill.hip", "prefill_fp8.hip", "decode.hip", "probes.hip", "api.cpp")
+SOURCES = ("prefill.hip", "prefill_fp8.hip", "backward.hip", "decode.hip", "probes.hip", "api.cpp")
 ARCH = "gfx950"
 
 

@@ -319,6 +319,82 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, cons
   return ok();
 }
 
+static attn_status_t check_bwd_args(const attn_bwd_args_t* a) {
+  if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
+  if (a->batch < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(ATTN_ERROR_INVALID_VALUE, "batch, num_q_heads and num_kv_heads must be >= 1");
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(ATTN_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->seqlen_q < 0 || a->seqlen_k < 1)
+    return fail(ATTN_ERROR_INVALID_VALUE, "seqlen_q must be >= 0 and seqlen_k >= 1");
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "backward head_dim %d is not 64 or 128", a->head_dim);
+  if (a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "backward dtype %d is not F16 or BF16", a->dtype);
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  if (a->window > 0 && !a->causal)
+    return fail(ATTN_ERROR_INVALID_VALUE, "a sliding window requires causal = 1");
+  if (!(a->softcap == a->softcap) || !(a->softmax_scale == a->softmax_scale) || isinf(a->softcap) ||
+      isinf(a->softmax_scale))
+    return fail(ATTN_ERROR_INVALID_VALUE, "softcap and softmax_scale must be finite");
+  if (a->num_q_heads > 65535 || a->batch > 65535)
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "num_q_heads and batch are limited to 65535");
+  return ATTN_SUCCESS;
+}
+
+size_t attn_bwd_workspace_size(const attn_bwd_args_t* a) {
+  if (check_bwd_args(a) != ATTN_SUCCESS) return 0;
+  return (size_t)a->batch * a->num_q_heads * (size_t)a->seqlen_q * sizeof(float);
+}
+
+attn_status_t attn_bwd(const attn_bwd_args_t* a, const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  attn_status_t st = check_bwd_args(a);
+  if (st != ATTN_SUCCESS) return st;
+  if (a->seqlen_q == 0) return ok();
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+    return fail(ATTN_ERROR_INVALID_VALUE, "every tensor pointer and the workspace must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || !aligned16(lse))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "tensors, lse and workspace must be 16-byte aligned");
+  const size_t need = attn_bwd_workspace_size(a);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  attn::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  p.batch = a->batch;
+  p.hq = a->num_q_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.nq = a->seqlen_q;
+  p.nk = a->seqlen_k;
+  p.causal = a->causal;
+  p.window = a->window > 0 ? a->window : 0;
+  const double scale = resolve_scale(a->softmax_scale, a->head_dim);
+  p.scale = (float)scale;
+  p.scale_log2 = (float)(scale * kLog2eD);
+  if (a->softcap > 0.0f) {
+    p.cap_in = (float)(scale / (double)a->softcap);
+    p.cap_out = (float)((double)a->softcap * kLog2eD);
+  }
+  hipError_t e = attn::launch_bwd(p, a->dtype, a->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(ATTN_ERROR_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 static attn_status_t check_decode_args(const attn_decode_args_t* a) {
   if (a == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "args is NULL");
   if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)

@@ -1,0 +1,476 @@
+// Attention backward (dQ, dK, dV) for gfx950, 16-bit inputs, head_dim 64 or 128.
+//
+// The backward pass is named as the next step by "Ask, Don't Equip: Question-Driven Coding
+// Agents for Deep Kernel Optimization" (section 局限与改进) and not defined there; these
+// kernels compute the derivatives of the forward definition with the saved LSE, the
+// recomputation scheme that the online softmax of the page "Agent 帮我写 CUDA：一个
+// Softmax Attention 算子的开发全记录" (section 四) makes possible (P is rebuilt tile by
+// tile from S and the row LSE, never stored):
+//   P = exp(S - LSE)   dV = P^T dO   dP = dO V^T   dS = P (dP - Delta) * scale
+//   (times 1 - tanh^2 under a softcap)   dQ = dS K   dK = dS^T Q,   Delta = rowsum(dO O).
+// Three kernels:
+//   bwd_delta_kernel   Delta per query row (fp32);
+//   bwd_dkdv_kernel    a workgroup owns 128 keys of one KV head (4 waves of 32) and walks
+//                      the query tiles of every query head of its group, so dK and dV are
+//                      complete in registers (no atomics, deterministic);
+//   bwd_dq_kernel      a workgroup owns 128 query rows (4 waves of 32) and walks the key
+//                      tiles, like the forward.
+// Every product is a 32x32x16 matrix-core product with the layouts of the forward
+// kernels: results are kept transposed when that puts P or dS straight into a B operand
+// (dV^T = dO^T P, dK^T = Q^T dS, dQ^T = K^T dS^T), and the transposed A operands (dO^T,
+// Q^T, K^T) come from row-major LDS tiles through the transposing LDS read. Q, dO and K
+// tiles are read both by rows and transposed, so every tile takes the row-read swizzle
+// (Swizzle::k) and the transposing reads apply it to their own rows; it depends on the
+// row only through bits that a step of 16 rows leaves unchanged.
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.hpp"
+#include "prefill_shared.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kBwdNW = 4;  // waves per workgroup (one per SIMD: the accumulators are large)
+
+// ------------------------------------------------------------------------- Delta ----
+// One thread per query row: Delta = sum_d dO O in fp32 (both read as 16-bit).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over B * Hq * Nq
+  const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
+  if (row >= rows) return;
+  const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * D;
+  const uint16_t* d = static_cast<const uint16_t*>(p.dout) + row * D;
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4_t a = load_global<u32x4_t>(o + 8 * c);
+    const u32x4_t b = load_global<u32x4_t>(d + 8 * c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += lo16<BF16>(a[w]) * lo16<BF16>(b[w]) + hi16<BF16>(a[w]) * hi16<BF16>(b[w]);
+  }
+  p.delta[row] = acc;
+}
+
+// Direct-to-LDS load of one row-major tile of ROWS rows x D (16-bit) into LDS, swizzled
+// as Swizzle<D>; rows past `valid` re-read the last valid row (the masks zero them).
+template <int D, int ROWS>
+struct TileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPL = 64 / CPR;            // rows per load instruction
+  static constexpr int LOADS = ROWS / RPL;        // per tile
+  static constexpr int LPW = LOADS / kBwdNW;      // per wave
+  static_assert(LOADS % kBwdNW == 0, "tile loads split evenly over the waves");
+  int row[LPW], off[LPW];
+  __device__ void init(int wave, int lane, int stride) {
+    using SW = Swizzle<D>;
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      const int i = wave + n * kBwdNW;
+      row[n] = i * RPL + lane / CPR;
+      off[n] = row[n] * stride + SW::k(row[n], lane % CPR) * 8;
+    }
+  }
+  // rows r0 .. r0 + ROWS - 1 of `base`, of which those < valid exist
+  __device__ void load(const uint16_t* base, int stride, int r0, int valid, uint16_t* dst, int wave) const {
+    const uint16_t* g = base + (int64_t)r0 * stride;
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      const int i = wave + n * kBwdNW;
+      const int shift = r0 + row[n] < valid ? 0 : (valid - 1 - r0) - row[n];
+      load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
+    }
+  }
+};
+
+// --------------------------------------------------------------------- dK and dV ----
+// Wave w of the workgroup owns keys kb0 + 32 w .. +31. Per query tile of 32 rows (staged
+// in LDS with its dO rows; double-buffered):
+//   S = Q K^T          A = Q rows (LDS), B = K^T (the wave's keys, registers)
+//   P = 2^(S sc - LSE2)                                 lane: key column, 16 query rows
+//   dV^T += dO^T P     A = dO^T (transposing LDS read), B = P (16-bit)
+//   dP = dO V^T        A = dO rows (LDS), B = V^T (registers)
+//   dS = P (dP - Delta) scale [(1 - t^2)]
+//   dK^T += Q^T dS     A = Q^T (transposing LDS read), B = dS (16-bit)
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int BQ = 32;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int TILE = BQ * D;
+  using SW = Swizzle<D>;
+  using LD = TileLoader<D, BQ>;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+  uint16_t* const q_lds = smem;              // [2][BQ][D]
+  uint16_t* const do_lds = smem + 2 * TILE;  // [2][BQ][D]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int kb0 = blockIdx.x * (kBwdNW * 32);
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
+  const int key = kb0 + wave * 32 + l32;  // this lane's key column
+  const int kb1 = min(Lk, kb0 + kBwdNW * 32);
+
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.hkv + g) * Lk * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.hkv + g) * Lk * D;
+  // K^T and V^T as B operands: lane holds head-dim entries 16 ks + 8 hi .. +7 of its key
+  u32x4_t kf[NKS], vf[NKS];
+  {
+    const int kr = min(key, Lk - 1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = load_global<u32x4_t>(kg + (int64_t)kr * D + ks * 16 + hi * 8);
+      vf[ks] = load_global<u32x4_t>(vg + (int64_t)kr * D + ks * 16 + hi * 8);
+    }
+  }
+  // the query rows that see any key of the block
+  int q_lo = p.causal ? max(0, kb0 - delta) : 0;
+  int q_hi = p.window > 0 ? min(Lq, kb1 - 1 - delta + p.window) : Lq;
+  q_lo = (q_lo / BQ) * BQ;
+  const int nqt = q_hi > q_lo ? (q_hi - q_lo + BQ - 1) / BQ : 0;
+  const int G = p.group;
+  const int steps = nqt * G;  // (head, query tile) pairs, head-major
+
+  LD ld;
+  ld.init(wave, lane, D);
+  int rd_q[NKS];  // row l32, chunk 2 ks + hi
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) rd_q[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * hi + (gi >> 2);
+  int rd_t[2][NDB];  // transposing reads of rows t*16 + 8*half + vrow (add t*16*D)
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
+      const int row = 8 * hf + vrow;
+      rd_t[hf][db] = row * D + SW::k(row, c) * 8 + (gi & 1) * 4;
+    }
+
+  f32x16_t dv[NDB], dk[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[db][r] = dk[db][r] = 0.0f;
+  const f32x16_t zero16 = {};
+
+  auto head_of = [&](int st) { return g * G + st / max(nqt, 1); };
+  auto qt_of = [&](int st) { return q_lo + (st % max(nqt, 1)) * BQ; };
+  auto qbase = [&](int st, const void* t) {
+    return static_cast<const uint16_t*>(t) + ((int64_t)b * p.hq + head_of(st)) * Lq * D;
+  };
+  // LSE2 and Delta of this lane's 16 query rows of step st (rows q0 + 8 j + 4 hi + i)
+  f32x4_t lse_n[4], del_n[4];
+  auto row_stats = [&](int st, f32x4_t (&ls)[4], f32x4_t (&de)[4]) __attribute__((always_inline)) {
+    const int64_t base = ((int64_t)b * p.hq + head_of(st)) * Lq;
+    const int q0 = qt_of(st);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = q0 + 8 * j + 4 * hi;
+      if (r + 3 < Lq) {
+        ls[j] = load_global<f32x4_t>(p.lse + base + r);
+        de[j] = load_global<f32x4_t>(p.delta + base + r);
+      } else {  // the tail of the sequence: rows past the end read the last row (masked)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ls[j][i] = p.lse[base + min(r + i, Lq - 1)];
+          de[j][i] = p.delta[base + min(r + i, Lq - 1)];
+        }
+      }
+    }
+  };
+
+  settle_global_loads();
+  if (steps > 0) {
+    ld.load(qbase(0, p.q), D, qt_of(0), Lq, q_lds, wave);
+    ld.load(qbase(0, p.dout), D, qt_of(0), Lq, do_lds, wave);
+    row_stats(0, lse_n, del_n);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  auto step = [&](auto bufc, int st) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    const uint16_t* ql = q_lds + BUF * TILE;
+    const uint16_t* dl = do_lds + BUF * TILE;
+    f32x4_t lse[4], del[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lse[j] = lse_n[j];
+      del[j] = del_n[j];
+    }
+    if (st + 1 < steps) {
+      ld.load(qbase(st + 1, p.q), D, qt_of(st + 1), Lq, q_lds + (BUF ^ 1) * TILE, wave);
+      ld.load(qbase(st + 1, p.dout), D, qt_of(st + 1), Lq, do_lds + (BUF ^ 1) * TILE, wave);
+      row_stats(st + 1, lse_n, del_n);
+    }
+    const int q0 = qt_of(st);
+    // S = Q K^T
+    f32x16_t s = zero16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      s = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]), kf[ks], s);
+    // P (0 where the mask or the key range excludes the pair)
+    float t2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = q0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+      float x;
+      if (p.cap_out > 0.0f) {
+        const float t = tanh_via_exp2(s[r] * p.cap_in);
+        t2[r] = 1.0f - t * t;
+        x = p.cap_out * t;
+      } else {
+        t2[r] = 1.0f;
+        x = s[r] * p.scale_log2;
+      }
+      bool ok = key < Lk && qi < Lq;
+      if (p.causal) ok = ok && key <= qi + delta;
+      if (p.window > 0) ok = ok && key > qi + delta - p.window;
+      const float l2 = lse[r >> 2][r & 3] * kLog2e;
+      s[r] = (ok && l2 != kNegInf) ? fast_exp2(x - l2) : 0.0f;
+    }
+    // dV^T += dO^T P
+    u32x4_t pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      pb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
+                      pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t lo = lds_read_tr16(dl + t * 16 * D + rd_t[0][db]);
+        const u32x2_t up = lds_read_tr16(dl + t * 16 * D + rd_t[1][db]);
+        dv[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dv[db]);
+      }
+    // dP = dO V^T, then dS
+    f32x16_t dp = zero16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      dp = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]), vf[ks], dp);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - del[r >> 2][r & 3]) * (p.scale * t2[r]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      pb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
+                      pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
+    // dK^T += Q^T dS
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t lo = lds_read_tr16(ql + t * 16 * D + rd_t[0][db]);
+        const u32x2_t up = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
+        dk[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dk[db]);
+      }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  for (int st = 0; st < steps; st += 2) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < steps) step(std::integral_constant<int, 1>{}, st + 1);
+  }
+
+  if (key >= Lk) return;
+  // dK^T / dV^T: lane column = key, register r of block db = head-dim 32 db + 8 (r/4) + 4 hi + r%4
+  uint16_t* dkr = static_cast<uint16_t*>(p.dk) + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+  uint16_t* dvr = static_cast<uint16_t*>(p.dv) + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + g4 * 8 + hi * 4;
+      *reinterpret_cast<u32x2_t*>(dkr + d) = u32x2_t{pack2<BF16>(dk[db][g4 * 4 + 0], dk[db][g4 * 4 + 1]),
+                                                     pack2<BF16>(dk[db][g4 * 4 + 2], dk[db][g4 * 4 + 3])};
+      *reinterpret_cast<u32x2_t*>(dvr + d) = u32x2_t{pack2<BF16>(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]),
+                                                     pack2<BF16>(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3])};
+    }
+}
+
+// ---------------------------------------------------------------------------- dQ ----
+// Wave w owns query rows q0 + 32 w .. +31; key tiles of 64 (K and V in LDS, double-
+// buffered). Per tile:
+//   S^T = K Q^T        A = K rows (LDS), B = Q (registers)     lane: query column, keys
+//   P^T = 2^(S^T sc - LSE2)
+//   dP^T = V dO^T      A = V rows (LDS), B = dO (registers)
+//   dS^T = P^T (dP^T - Delta) scale [(1 - t^2)]
+//   dQ^T += K^T dS^T   A = K^T (transposing LDS read), B = dS^T (16-bit)
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int BN = 64;
+  constexpr int NKS = D / 16, NDB = D / 32, NKB = BN / 32, NPS = BN / 16;
+  constexpr int TILE = BN * D;
+  using SW = Swizzle<D>;
+  using LD = TileLoader<D, BN>;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+  uint16_t* const k_lds = smem;
+  uint16_t* const v_lds = smem + 2 * TILE;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int r0 = blockIdx.x * (kBwdNW * 32);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
+  const int hk = h / p.group;
+  const int qrow = r0 + wave * 32 + l32;
+  const bool row_ok = qrow < Lq;
+  const int qr = min(qrow, Lq - 1);
+
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.hkv + hk) * Lk * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.hkv + hk) * Lk * D;
+  const int64_t rowi = ((int64_t)b * p.hq + h) * Lq + qr;
+  u32x4_t qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = load_global<u32x4_t>(static_cast<const uint16_t*>(p.q) + rowi * D + ks * 16 + hi * 8);
+    df[ks] = load_global<u32x4_t>(static_cast<const uint16_t*>(p.dout) + rowi * D + ks * 16 + hi * 8);
+  }
+  const float lse2 = p.lse[rowi] * kLog2e;
+  const float dl = p.delta[rowi];
+  const float lse_use = (row_ok && lse2 != kNegInf) ? lse2 : __builtin_inff();  // P = 0 for such rows
+
+  // keys any row of the workgroup sees
+  const int r1 = min(Lq, r0 + kBwdNW * 32);
+  const int kend = p.causal ? min(Lk, r1 + delta) : Lk;
+  int kbeg = p.window > 0 ? max(0, r0 + delta - p.window + 1) : 0;
+  kbeg = (kbeg / BN) * BN;
+  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int key_lo = p.window > 0 ? qrow + delta - p.window + 1 : 0;
+  const int key_hi = p.causal ? min(Lk, qrow + delta + 1) : Lk;
+  const uint32_t key_n = (uint32_t)max(key_hi - key_lo, 0);
+
+  LD ld;
+  ld.init(wave, lane, D);
+  int rd_k[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * hi + (gi >> 2);
+  int rd_t[2][NDB];  // transposing reads of rows t*16 + 8*half + vrow (add t*16*D)
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
+      const int row = 8 * hf + vrow;
+      rd_t[hf][db] = row * D + SW::k(row, c) * 8 + (gi & 1) * 4;
+    }
+
+  f32x16_t dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
+  const f32x16_t zero16 = {};
+
+  settle_global_loads();
+  if (ntiles > 0) {
+    ld.load(kg, D, kbeg, Lk, k_lds, wave);
+    ld.load(vg, D, kbeg, Lk, v_lds, wave);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int kt = kbeg + it * BN;
+    if (it + 1 < ntiles) {
+      ld.load(kg, D, kt + BN, Lk, k_lds + (BUF ^ 1) * TILE, wave);
+      ld.load(vg, D, kt + BN, Lk, v_lds + (BUF ^ 1) * TILE, wave);
+    }
+    const uint16_t* kl = k_lds + BUF * TILE;
+    const uint16_t* vl = v_lds + BUF * TILE;
+    f32x16_t s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = zero16;
+      dp[kb] = zero16;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s[kb] = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[ks]), qf[ks], s[kb]);
+        dp[kb] = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(vl + kb * 32 * D + rd_k[ks]), df[ks], dp[kb]);
+      }
+    }
+    // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
+    const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x, t2 = 1.0f;
+        if (p.cap_out > 0.0f) {
+          const float t = tanh_via_exp2(s[kb][r] * p.cap_in);
+          t2 = 1.0f - t * t;
+          x = p.cap_out * t;
+        } else {
+          x = s[kb][r] * p.scale_log2;
+        }
+        const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
+        const float pr = ok ? fast_exp2(x - lse_use) : 0.0f;
+        s[kb][r] = pr * (dp[kb][r] - dl) * (p.scale * t2);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t = 0; t < NPS; ++t) {
+      const int kb = t >> 1, o8 = (t & 1) * 8;
+      const u32x4_t pb = {pack2<BF16>(s[kb][o8 + 0], s[kb][o8 + 1]), pack2<BF16>(s[kb][o8 + 2], s[kb][o8 + 3]),
+                          pack2<BF16>(s[kb][o8 + 4], s[kb][o8 + 5]), pack2<BF16>(s[kb][o8 + 6], s[kb][o8 + 7])};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t lo = lds_read_tr16(kl + t * 16 * D + rd_t[0][db]);
+        const u32x2_t up = lds_read_tr16(kl + t * 16 * D + rd_t[1][db]);
+        dq[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb, dq[db]);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  if (!row_ok) return;
+  uint16_t* dqr = static_cast<uint16_t*>(p.dq) + (((int64_t)b * p.hq + h) * Lq + qrow) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + g4 * 8 + hi * 4;
+      *reinterpret_cast<u32x2_t*>(dqr + d) = u32x2_t{pack2<BF16>(dq[db][g4 * 4 + 0], dq[db][g4 * 4 + 1]),
+                                                     pack2<BF16>(dq[db][g4 * 4 + 2], dq[db][g4 * 4 + 3])};
+    }
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
+  const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
+  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 gkv((p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32), p.hkv, p.batch);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), gkv, dim3(kBwdNW * 64), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 gq((p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32), p.hq, p.batch);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), gq, dim3(kBwdNW * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// dtype: 1 = f16, 2 = bf16
+hipError_t launch_bwd(const BwdParams& p, int dtype, int head_dim, hipStream_t st) {
+  switch (dtype * 1000 + head_dim) {
+    case 1064: return launch_bwd_t<64, false>(p, st);
+    case 1128: return launch_bwd_t<128, false>(p, st);
+    case 2064: return launch_bwd_t<64, true>(p, st);
+    case 2128: return launch_bwd_t<128, true>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

@@ -36,6 +36,26 @@ struct FwdParams {
   float o_scale;        // fp8 inputs: the value scale, applied with the normalisation
 };
 
+// One backward launch (dense, contiguous [B, H, N, D] tensors, 16-bit).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;     // [B, Hq, Nq], natural log, as the forward writes it
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;         // workspace [B, Hq, Nq]
+  int32_t batch, hq, hkv, group, nq, nk, causal, window;
+  float scale;          // softmax scale
+  float scale_log2;     // scale * log2(e)
+  float cap_in, cap_out;  // softcap as for the forward (cap_out = 0: off)
+};
+
+hipError_t launch_bwd(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
+
 // One paged-decode launch (split kernel + combine kernel).
 struct DecodeParams {
   const void* q;

@@ -79,5 +79,45 @@ __device__ __forceinline__ float pair_sum(float x) { return x + xor_shuffle(x, 3
 // same reference max is used for P, for l and for the final LSE.
 constexpr float kRescaleSlack = 8.0f;
 
+// ----------------------------------------------------------------- 16-bit inputs ----
+// K and V tiles live in LDS row-major with 16-byte chunks XOR-swizzled per row (no
+// padding), filled straight from global memory by direct-to-LDS loads: each load
+// instruction moves 64 lanes x 16 bytes into one contiguous 1 KiB LDS block, and the
+// swizzle is applied by choosing which global chunk each lane fetches.
+//   K reads (A operand of S^T): 16 consecutive rows at one chunk -> 16 bank groups.
+//   V reads use the transposing LDS read: in each 16-lane group, lane i receives element
+//   i%4 of the 4-element rows addressed by lanes i/4 + 4e (e = 0..3). Lanes address 4
+//   consecutive head-dim entries of 4 keys, so every lane ends up with 4 keys of one
+//   head-dim entry: exactly the A operand of O^T = V^T . P^T, with no transposition on
+//   the way into LDS. A 4-key x 4-chunk read hits 16 distinct bank groups.
+// Head dims that are not a power of two (96, 192) use LDS rows of the next power of two
+// (128, 256): the extra chunks of a row are padding that no read touches.
+
+template <int D>
+struct Swizzle {
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __device__ static __forceinline__ int k(int row, int c) {
+    if constexpr (CPR >= 16) return c ^ (row & 15);
+    else return c ^ ((row / (16 / CPR)) % CPR);
+  }
+  __device__ static __forceinline__ int v(int row, int c) {
+    if constexpr (D >= 128) return c ^ ((row & 3) << 2);
+    else if constexpr (D == 64) return c ^ (((row >> 1) & 1) << 2);
+    else return c;
+  }
+};
+
+// LDS row width (elements) for head dim D
+constexpr int lds_row(int D) { return D <= 32 ? 32 : D <= 64 ? 64 : D <= 128 ? 128 : 256; }
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+
 }  // namespace
 }  // namespace attn

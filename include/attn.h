@@ -12,6 +12,7 @@
  *   attn_fwd_paged     chunked prefill: a chunk of new query tokens per
  *                      sequence attends to that sequence's keys in the same
  *                      paged KV cache.
+ *   attn_bwd           the gradients of attn_fwd (dense batches).
  *
  * The operation is the softmax attention of the page "Agent 帮我写 CUDA：一个
  * Softmax Attention 算子的开发全记录" (section 二, reference baseline and the
@@ -182,6 +183,47 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t *args, const void *q, c
 /* Bytes of workspace attn_fwd_paged can use for these args: 0 when there is no
  * gathered route for them (head_dim 32 / 64) or on bad args. */
 size_t attn_fwd_paged_workspace_size(const attn_fwd_paged_args_t *args);
+
+/* ---------------------------------------------------------------- backward ---- */
+
+typedef struct {
+  int32_t batch;         /* B >= 1 */
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv, Hq % Hkv == 0 */
+  int32_t seqlen_q;      /* Nq >= 0 (0: nothing to do) */
+  int32_t seqlen_k;      /* Nk >= 1 */
+  int32_t head_dim;      /* D in {64, 128} */
+  int32_t dtype;         /* ATTN_F16 or ATTN_BF16, every tensor but lse */
+  int32_t causal;        /* as for attn_fwd */
+  int32_t window;        /* as for attn_fwd */
+  float softmax_scale;   /* as for attn_fwd */
+  float softcap;         /* as for attn_fwd */
+} attn_bwd_args_t;
+
+/* Bytes of workspace attn_bwd needs (0 on bad args): one float per query row. */
+size_t attn_bwd_workspace_size(const attn_bwd_args_t *args);
+
+/*
+ * attn_bwd - gradients of attn_fwd (dense batches): given dL/dO, writes dL/dQ, dL/dK,
+ * dL/dV. The backward pass is named as the next step by "Ask, Don't Equip" (section
+ * 局限与改进) and not defined there; these are the derivatives of the forward definition:
+ * with P rebuilt from the scores and the forward's LSE,
+ *   dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO O)) * scale (times 1 - tanh^2 of
+ *   the capped argument under a softcap), dQ = dS K, dK = dS^T Q,
+ * and query heads that share a KV head add their dK and dV. A forward with a sink gives
+ * an LSE that includes it, and the same formulas hold (the sink's own gradient is not
+ * computed).
+ *
+ *   q, o, dout, dq  [B, Hq, Nq, D] contiguous, dtype (o and lse from attn_fwd)
+ *   k, v, dk, dv    [B, Hkv, Nk, D] contiguous, dtype
+ *   lse             float32 [B, Hq, Nq], natural log, as attn_fwd writes it
+ *   workspace       device buffer of attn_bwd_workspace_size(args) bytes, 16-byte aligned
+ * Accumulation is float32; P and dS are rounded to dtype for their products. dk and dv
+ * are written whole (no accumulation into the caller's buffers).
+ */
+attn_status_t attn_bwd(const attn_bwd_args_t *args, const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse, void *dq, void *dk, void *dv, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* ----------------------------------------------------------------- decode ---- */
 

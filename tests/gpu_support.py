@@ -34,6 +34,10 @@ TOL = {
     # for the outer bound (2^-3 times the largest |v| of the test inputs, 13.5) and the
     # Frobenius bound.
     "fp8_prefill": dict(atol=1.7, rtol=0.0, fro=6e-2),
+    # gradients (16-bit inputs): sums whose terms can cancel, so the element check is the
+    # term-magnitude bound of tests/test_gpu_backward.py; this entry is the outer element
+    # bound and the Frobenius bound (the 16-bit one)
+    "grad": dict(atol=0.5, rtol=0.02, fro=1e-2),
 }
 
 

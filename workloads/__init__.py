@@ -417,6 +417,19 @@ def config_fp8_headline(seed: int = 9) -> Fp8PrefillCase:
                             seed=seed, input_scale=0.5)
 
 
+def make_grad_out(shape, *, dtype: str = "bf16", seed: int) -> torch.Tensor:
+    """dL/dO for the backward: iid N(0,1) in ``dtype``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _cast(_normal(rng, tuple(shape)), dtype)
+
+
+def config_backward(seed: int = 10) -> PrefillCase:
+    """Causal GQA bf16 prefill for the backward: B=1 Hq=32 Hkv=8 N=4096 D=128, inputs
+    N(0,1) (dL/dO from make_grad_out with seed + 1)."""
+    return make_prefill(batch=1, num_q_heads=32, num_kv_heads=8, seqlen_q=4096, head_dim=128, dtype="bf16",
+                        seed=seed, causal=True)
+
+
 def config_headdim(head_dim: int, seed: int = 8) -> PrefillCase:
     """Causal prefill bf16 B=2 H=16 N=4096 at the head dims without a dedicated workload
     (96, 192, 256); Q, K, V iid N(0,1)."""
