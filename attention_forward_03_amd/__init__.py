@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, AttnInvalidValue, AttnNotSupported
 
-__all__ = ["fwd", "fwd_paged", "bwd", "fwd_paged_workspace_size", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
+__all__ = ["fwd", "fwd_paged", "bwd", "bwd_workspace_size", "fwd_paged_workspace_size", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
            "AttnError", "AttnInvalidValue", "AttnNotSupported"]
 
 _DTYPES = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
@@ -218,6 +218,17 @@ def fwd_paged_workspace_size(*, num_seqs, num_q_heads, num_kv_heads, head_dim, m
     a.dtype = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     a.causal = 1
     return int(_lib.lib().attn_fwd_paged_workspace_size(ctypes.byref(a)))
+
+
+def bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False, window: int = 0) -> int:
+    """Bytes of workspace bwd needs for q [B, Hq, Nq, D] and k [B, Hkv, Nk, D]."""
+    a = _lib.BwdArgs()
+    a.batch, a.num_q_heads, a.seqlen_q, a.head_dim = q.shape
+    a.num_kv_heads, a.seqlen_k = k.shape[1], k.shape[2]
+    a.dtype = _DTYPES[q.dtype]
+    a.causal = 1 if causal else 0
+    a.window = int(window)
+    return int(_lib.lib().attn_bwd_workspace_size(ctypes.byref(a)))
 
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,

@@ -330,6 +330,8 @@ static attn_status_t check_bwd_args(const attn_bwd_args_t* a) {
     return fail(ATTN_ERROR_INVALID_VALUE, "seqlen_q must be >= 0 and seqlen_k >= 1");
   if (a->head_dim != 64 && a->head_dim != 128)
     return fail(ATTN_ERROR_NOT_SUPPORTED, "backward head_dim %d is not 64 or 128", a->head_dim);
+  if (a->seqlen_q > 65535 * 128 || a->seqlen_k > (1 << 24))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "backward sequence lengths are limited to 8388480 / 2^24");
   if (a->dtype != ATTN_F16 && a->dtype != ATTN_BF16)
     return fail(ATTN_ERROR_NOT_SUPPORTED, "backward dtype %d is not F16 or BF16", a->dtype);
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERROR_INVALID_VALUE, "causal must be 0 or 1");
@@ -343,9 +345,17 @@ static attn_status_t check_bwd_args(const attn_bwd_args_t* a) {
   return ATTN_SUCCESS;
 }
 
+// Delta [B, Hq, Nq] (rounded up to 256 bytes), then fp32 dK and dV [B, Hkv, Nk, D]
+static size_t bwd_delta_bytes(const attn_bwd_args_t* a) {
+  return ((size_t)a->batch * a->num_q_heads * (size_t)a->seqlen_q * sizeof(float) + 255) & ~(size_t)255;
+}
+
 size_t attn_bwd_workspace_size(const attn_bwd_args_t* a) {
   if (check_bwd_args(a) != ATTN_SUCCESS) return 0;
-  return (size_t)a->batch * a->num_q_heads * (size_t)a->seqlen_q * sizeof(float);
+  int chunks, steps;
+  attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, &chunks, &steps);
+  return bwd_delta_bytes(a) +
+         2 * (size_t)chunks * a->batch * a->num_kv_heads * (size_t)a->seqlen_k * a->head_dim * sizeof(float);
 }
 
 attn_status_t attn_bwd(const attn_bwd_args_t* a, const void* q, const void* k, const void* v, const void* o,
@@ -374,6 +384,9 @@ attn_status_t attn_bwd(const attn_bwd_args_t* a, const void* q, const void* k, c
   p.dk = dk;
   p.dv = dv;
   p.delta = static_cast<float*>(workspace);
+  attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, &p.chunks, &p.chunk_steps);
+  p.dk32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(a));
+  p.dv32 = p.dk32 + (size_t)p.chunks * a->batch * a->num_kv_heads * (size_t)a->seqlen_k * a->head_dim;
   p.batch = a->batch;
   p.hq = a->num_q_heads;
   p.hkv = a->num_kv_heads;

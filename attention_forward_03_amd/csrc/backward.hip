@@ -10,9 +10,13 @@
 //   (times 1 - tanh^2 under a softcap)   dQ = dS K   dK = dS^T Q,   Delta = rowsum(dO O).
 // Three kernels:
 //   bwd_delta_kernel   Delta per query row (fp32);
-//   bwd_dkdv_kernel    a workgroup owns 128 keys of one KV head (4 waves of 32) and walks
-//                      the query tiles of every query head of its group, so dK and dV are
-//                      complete in registers (no atomics, deterministic);
+//   bwd_dkdv_kernel    a workgroup owns 128 keys of one KV head (4 waves of 32) and one of
+//                      at most 4 equal chunks of the (query head of its group, query tile)
+//                      steps that reach them, so a causal problem (where early keys meet
+//                      far more queries than late ones) stays balanced; each chunk stores
+//                      its fp32 partial dK, dV in a slot of its own, and
+//                      bwd_convert_kernel adds a key's slots in a fixed order and rounds
+//                      to the output type (no atomics: the result is repeatable bit for bit);
 //   bwd_dq_kernel      a workgroup owns 128 query rows (4 waves of 32) and walks the key
 //                      tiles, like the forward.
 // Every product is a 32x32x16 matrix-core product with the layouts of the forward
@@ -31,7 +35,8 @@
 namespace attn {
 namespace {
 
-constexpr int kBwdNW = 4;  // waves per workgroup (one per SIMD: the accumulators are large)
+constexpr int kBwdNW = 4;   // waves per workgroup (one per SIMD: the accumulators are large)
+constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
 
 // ------------------------------------------------------------------------- Delta ----
 // One thread per query row: Delta = sum_d dO O in fp32 (both read as 16-bit).
@@ -96,7 +101,7 @@ struct TileLoader {
 //   dK^T += Q^T dS     A = Q^T (transposing LDS read), B = dS (16-bit)
 template <int D, bool BF16>
 __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int BQ = 32;
+  constexpr int BQ = kBwdBQ;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
   using SW = Swizzle<D>;
@@ -107,7 +112,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kb0 = blockIdx.x * (kBwdNW * 32);
+  const int kb0 = (blockIdx.x / p.chunks) * (kBwdNW * 32);
+  const int chunk = blockIdx.x % p.chunks;
   const int g = blockIdx.y, b = blockIdx.z;
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
   const int key = kb0 + wave * 32 + l32;  // this lane's key column
@@ -131,7 +137,16 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   q_lo = (q_lo / BQ) * BQ;
   const int nqt = q_hi > q_lo ? (q_hi - q_lo + BQ - 1) / BQ : 0;
   const int G = p.group;
-  const int steps = nqt * G;  // (head, query tile) pairs, head-major
+  const int all_steps = nqt * G;  // (head, query tile) pairs, head-major
+  const bool cap = p.cap_out > 0.0f;
+  // key - query offsets a pair may have: key <= query + delta (causal), key > query + delta -
+  // window (window), key < Lk; with key_rel = key - hi*4 the test is on u = key_rel - row
+  const int key_rel = key - hi * 4;
+  const int hi_u = key < Lk ? (p.causal ? delta + 1 : 0x40000000) : -0x40000000;
+  const int lo_u = p.window > 0 ? delta - p.window + 1 : -0x40000000;
+  const int st0 = chunk * p.chunk_steps;
+  if (st0 >= all_steps) return;  // (uniform over the workgroup)
+  const int steps = min(all_steps, st0 + p.chunk_steps);
 
   LD ld;
   ld.init(wave, lane, D);
@@ -184,11 +199,9 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   };
 
   settle_global_loads();
-  if (steps > 0) {
-    ld.load(qbase(0, p.q), D, qt_of(0), Lq, q_lds, wave);
-    ld.load(qbase(0, p.dout), D, qt_of(0), Lq, do_lds, wave);
-    row_stats(0, lse_n, del_n);
-  }
+  ld.load(qbase(st0, p.q), D, qt_of(st0), Lq, q_lds, wave);
+  ld.load(qbase(st0, p.dout), D, qt_of(st0), Lq, do_lds, wave);
+  row_stats(st0, lse_n, del_n);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -208,30 +221,40 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       row_stats(st + 1, lse_n, del_n);
     }
     const int q0 = qt_of(st);
-    // S = Q K^T
+    // S = Q K^T (the fragment reads issued ahead of the products)
     f32x16_t s = zero16;
+    {
+      u32x4_t qa[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      s = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]), kf[ks], s);
-    // P (0 where the mask or the key range excludes the pair)
+      for (int ks = 0; ks < NKS; ++ks) qa[ks] = *reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
+    }
+    // P (0 where the mask or the key range excludes the pair; a row without any allowed
+    // key, whose LSE is -inf, has every pair excluded)
     float t2[16];
+    if (cap) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = q0 + (r >> 2) * 8 + hi * 4 + (r & 3);
-      float x;
-      if (p.cap_out > 0.0f) {
+      for (int r = 0; r < 16; ++r) {
         const float t = tanh_via_exp2(s[r] * p.cap_in);
         t2[r] = 1.0f - t * t;
-        x = p.cap_out * t;
-      } else {
-        t2[r] = 1.0f;
-        x = s[r] * p.scale_log2;
+        s[r] = p.cap_out * t;
       }
-      bool ok = key < Lk && qi < Lq;
-      if (p.causal) ok = ok && key <= qi + delta;
-      if (p.window > 0) ok = ok && key > qi + delta - p.window;
-      const float l2 = lse[r >> 2][r & 3] * kLog2e;
-      s[r] = (ok && l2 != kNegInf) ? fast_exp2(x - l2) : 0.0f;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        t2[r] = 1.0f;
+        s[r] *= p.scale_log2;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // query q0 + (r/4)*8 + hi*4 + r%4 sees this lane's key iff u = key - (that query) lies in
+      // [lo_u, hi_u) (the causal / window offsets relative to the diagonal)
+      const int u = key_rel - q0 - ((r >> 2) * 8 + (r & 3));
+      const bool ok = (u < hi_u) & (u >= lo_u) & (q0 + (r >> 2) * 8 + hi * 4 + (r & 3) < Lq);
+      const float e = fast_exp2(s[r] - lse[r >> 2][r & 3] * kLog2e);
+      s[r] = ok ? e : 0.0f;
     }
     // dV^T += dO^T P
     u32x4_t pb[2];
@@ -249,9 +272,13 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       }
     // dP = dO V^T, then dS
     f32x16_t dp = zero16;
+    {
+      u32x4_t da[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      dp = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]), vf[ks], dp);
+      for (int ks = 0; ks < NKS; ++ks) da[ks] = *reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - del[r >> 2][r & 3]) * (p.scale * t2[r]);
 #pragma unroll
@@ -270,25 +297,57 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  for (int st = 0; st < steps; st += 2) {
+  for (int st = st0; st < steps; st += 2) {
     step(std::integral_constant<int, 0>{}, st);
     if (st + 1 < steps) step(std::integral_constant<int, 1>{}, st + 1);
   }
 
   if (key >= Lk) return;
   // dK^T / dV^T: lane column = key, register r of block db = head-dim 32 db + 8 (r/4) + 4 hi + r%4
-  uint16_t* dkr = static_cast<uint16_t*>(p.dk) + (((int64_t)b * p.hkv + g) * Lk + key) * D;
-  uint16_t* dvr = static_cast<uint16_t*>(p.dv) + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+  const int64_t slot = (int64_t)chunk * p.batch * p.hkv * Lk * D;
+  float* dkr = p.dk32 + slot + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+  float* dvr = p.dv32 + slot + (((int64_t)b * p.hkv + g) * Lk + key) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = db * 32 + g4 * 8 + hi * 4;
-      *reinterpret_cast<u32x2_t*>(dkr + d) = u32x2_t{pack2<BF16>(dk[db][g4 * 4 + 0], dk[db][g4 * 4 + 1]),
-                                                     pack2<BF16>(dk[db][g4 * 4 + 2], dk[db][g4 * 4 + 3])};
-      *reinterpret_cast<u32x2_t*>(dvr + d) = u32x2_t{pack2<BF16>(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]),
-                                                     pack2<BF16>(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3])};
+      *reinterpret_cast<f32x4_t*>(dkr + d) =
+          f32x4_t{dk[db][g4 * 4 + 0], dk[db][g4 * 4 + 1], dk[db][g4 * 4 + 2], dk[db][g4 * 4 + 3]};
+      *reinterpret_cast<f32x4_t*>(dvr + d) =
+          f32x4_t{dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1], dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]};
     }
+}
+
+// The number of dK / dV chunks that hold a partial for keys of block kb0 (the same range
+// arithmetic as bwd_dkdv_kernel).
+__device__ __forceinline__ int bwd_chunks_of(const BwdParams& p, int kb0) {
+  const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
+  const int kb1 = min(Lk, kb0 + kBwdNW * 32);
+  int q_lo = p.causal ? max(0, kb0 - delta) : 0;
+  const int q_hi = p.window > 0 ? min(Lq, kb1 - 1 - delta + p.window) : Lq;
+  q_lo = (q_lo / kBwdBQ) * kBwdBQ;
+  const int nqt = q_hi > q_lo ? (q_hi - q_lo + kBwdBQ - 1) / kBwdBQ : 0;
+  return min(p.chunks, (nqt * p.group + p.chunk_steps - 1) / p.chunk_steps);
+}
+
+// Sum of a key's partial dK / dV slots in chunk order -> the output type (4 entries per thread)
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_convert_kernel(const BwdParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nkv = (int64_t)p.batch * p.hkv * p.nk * D;
+  if (4 * i >= nkv) return;
+  const int key = (int)((4 * i / D) % p.nk);
+  const int n = bwd_chunks_of(p, (key / (kBwdNW * 32)) * (kBwdNW * 32));
+  f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f}, w = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < n; ++c) {
+    u += load_global<f32x4_t>(p.dk32 + c * nkv + 4 * i);
+    w += load_global<f32x4_t>(p.dv32 + c * nkv + 4 * i);
+  }
+  *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.dk) + 4 * i) =
+      u32x2_t{pack2<BF16>(u[0], u[1]), pack2<BF16>(u[2], u[3])};
+  *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.dv) + 4 * i) =
+      u32x2_t{pack2<BF16>(w[0], w[1]), pack2<BF16>(w[2], w[3])};
 }
 
 // ---------------------------------------------------------------------------- dQ ----
@@ -312,8 +371,10 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int r0 = blockIdx.x * (kBwdNW * 32);
-  const int h = blockIdx.y, b = blockIdx.z;
+  // every head's longest (causal) query tiles first: the grid is (head, tile, batch)
+  const int ntile = (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32);
+  const int r0 = (p.causal ? ntile - 1 - (int)blockIdx.y : (int)blockIdx.y) * (kBwdNW * 32);
+  const int h = blockIdx.x, b = blockIdx.z;
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
   const int hk = h / p.group;
   const int qrow = r0 + wave * 32 + l32;
@@ -342,6 +403,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
   const int key_lo = p.window > 0 ? qrow + delta - p.window + 1 : 0;
   const int key_hi = p.causal ? min(Lk, qrow + delta + 1) : Lk;
   const uint32_t key_n = (uint32_t)max(key_hi - key_lo, 0);
+  const bool cap = p.cap_out > 0.0f;
 
   LD ld;
   ld.init(wave, lane, D);
@@ -387,32 +449,42 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
     f32x16_t s[NKB], dp[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      u32x4_t ka[NKS], va[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        ka[ks] = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[ks]);
+        va[ks] = *reinterpret_cast<const u32x4_t*>(vl + kb * 32 * D + rd_k[ks]);
+      }
       s[kb] = zero16;
       dp[kb] = zero16;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s[kb] = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[ks]), qf[ks], s[kb]);
-        dp[kb] = mfma32x32x16<BF16>(*reinterpret_cast<const u32x4_t*>(vl + kb * 32 * D + rd_k[ks]), df[ks], dp[kb]);
+        s[kb] = mfma32x32x16<BF16>(ka[ks], qf[ks], s[kb]);
+        dp[kb] = mfma32x32x16<BF16>(va[ks], df[ks], dp[kb]);
       }
     }
     // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
     const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
+    if (cap) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x, t2 = 1.0f;
-        if (p.cap_out > 0.0f) {
+        for (int r = 0; r < 16; ++r) {
           const float t = tanh_via_exp2(s[kb][r] * p.cap_in);
-          t2 = 1.0f - t * t;
-          x = p.cap_out * t;
-        } else {
-          x = s[kb][r] * p.scale_log2;
+          const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
+          const float e = fast_exp2(p.cap_out * t - lse_use);
+          s[kb][r] = (ok ? e : 0.0f) * (dp[kb][r] - dl) * (p.scale * (1.0f - t * t));
         }
-        const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
-        const float pr = ok ? fast_exp2(x - lse_use) : 0.0f;
-        s[kb][r] = pr * (dp[kb][r] - dl) * (p.scale * t2);
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
+          const float e = fast_exp2(s[kb][r] * p.scale_log2 - lse_use);
+          s[kb][r] = (ok ? e : 0.0f) * (dp[kb][r] - dl) * p.scale;
+        }
+    }
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int t = 0; t < NPS; ++t) {
@@ -452,10 +524,13 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gkv((p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32), p.hkv, p.batch);
+  const int64_t nkv4 = (int64_t)p.batch * p.hkv * p.nk * D / 4;  // float4s per accumulator slot
+  const dim3 gkv((unsigned)((p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32) * p.chunks), p.hkv, p.batch);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), gkv, dim3(kBwdNW * 64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 gq((p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32), p.hq, p.batch);
+  hipLaunchKernelGGL((bwd_convert_kernel<D, BF16>), dim3((unsigned)((nkv4 + 255) / 256)), dim3(256), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 gq(p.hq, (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32), p.batch);
   hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), gq, dim3(kBwdNW * 64), 0, st, p);
   return hipGetLastError();
 }

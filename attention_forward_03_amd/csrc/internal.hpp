@@ -48,6 +48,9 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;         // workspace [B, Hq, Nq]
+  float* dk32;          // workspace [chunks][B, Hkv, Nk, D] fp32 partial dK, then dv32 alike
+  float* dv32;
+  int32_t chunk_steps, chunks;  // dK / dV work split, from bwd_plan
   int32_t batch, hq, hkv, group, nq, nk, causal, window;
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
@@ -55,6 +58,15 @@ struct BwdParams {
 };
 
 hipError_t launch_bwd(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
+
+// Split of the dK / dV work: the (query head, 32-row query tile) steps that reach a block
+// of keys, at most group * ceil(nq / 32), are cut into `chunks` (<= 4) runs of `steps`.
+inline void bwd_plan(int group, int nq, int* chunks, int* steps) {
+  const int max_steps = group * ((nq + 31) / 32);
+  *chunks = max_steps < 4 ? (max_steps > 0 ? max_steps : 1) : 4;
+  *steps = (max_steps + *chunks - 1) / *chunks;
+  if (*steps < 1) *steps = 1;
+}
 
 // One paged-decode launch (split kernel + combine kernel).
 struct DecodeParams {

@@ -68,14 +68,15 @@ PREFILL_KERNEL = "fwd_r2_kernel<true, 0>"
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
 CHUNKED_KERNEL = ("gather_kv_pages_kernel", "fwd_r2_kernel<true, 1>")
 FP8_KERNEL = "fwd_fp8_kernel"
+BWD_KERNELS = ("bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
 
 
 def kernel_source_digest() -> str:
     """Digest of the kernel sources: counter-derived traffic is only reported while it matches."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("prefill.hip", "prefill_fp8.hip", "prefill_shared.hpp", "gen_prefill_r2.py", "decode.hip",
-                 "common.hpp"):
+    for name in ("prefill.hip", "prefill_fp8.hip", "prefill_shared.hpp", "backward.hip", "gen_prefill_r2.py",
+                 "decode.hip", "common.hpp"):
         with open(os.path.join(HERE, "attention_forward_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -247,6 +248,7 @@ def main(argv=None):
                     help="run only the decode (per-kernel counter passes; prints decode timing only)")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill over the paged cache")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 e4m3 prefill")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the variant measurements (head dims 96/192/256, sink, MQA decode)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -457,6 +459,25 @@ def main(argv=None):
                                            "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
                                            "traffic": load_traffic(FP8_KERNEL), "kernel": "fwd_fp8_kernel"}}
         del fq, fk, fv, fo
+
+    # -------------------------------------------------------------- backward ----
+    if not args.no_bwd and not args.no_prefill:
+        bc = workloads.config_backward()
+        bq, bk, bv = bc.q.to(dev), bc.k.to(dev), bc.v.to(dev)
+        bdo = workloads.make_grad_out(bc.q.shape, seed=11).to(dev)
+        bo, blse = attn.fwd(bq, bk, bv, causal=True, return_lse=True)
+        bws = torch.empty(attn.bwd_workspace_size(bc.q, bc.k), dtype=torch.uint8, device=dev)
+        bms = _timed(torch, lambda: attn.bwd(bq, bk, bv, bo, bdo, blse, causal=True, workspace=bws), flush, args.steps)
+        # five products per allowed (query, key) pair against the forward's two: 2.5x its FLOPs
+        bfl = 2.5 * 4.0 * bc.head_dim * bc.num_q_heads * bc.batch * allowed_pairs(bc.seqlen_q, bc.seqlen_k, True)
+        btf = bfl / (bms * 1e-3) / 1e12
+        out["backward"] = {"tflops": round(btf, 2), "ms": round(bms, 4), "flops_per_launch": bfl,
+                           "workload": "causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16, dQ dK dV",
+                           "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                                        "traffic": load_traffic(BWD_KERNELS),
+                                        "kernels": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}}
+        del bq, bk, bv, bdo, bo, blse, bws
 
     # ------------------------------------------------------------ variants ----
     if not args.no_variants and not args.no_prefill:

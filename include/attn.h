@@ -200,7 +200,8 @@ typedef struct {
   float softcap;         /* as for attn_fwd */
 } attn_bwd_args_t;
 
-/* Bytes of workspace attn_bwd needs (0 on bad args): one float per query row. */
+/* Bytes of workspace attn_bwd needs (0 on bad args): one float per query row, then up to
+ * four float32 partial sums each of dK and dV (one per chunk of the queries). */
 size_t attn_bwd_workspace_size(const attn_bwd_args_t *args);
 
 /*
@@ -219,7 +220,8 @@ size_t attn_bwd_workspace_size(const attn_bwd_args_t *args);
  *   lse             float32 [B, Hq, Nq], natural log, as attn_fwd writes it
  *   workspace       device buffer of attn_bwd_workspace_size(args) bytes, 16-byte aligned
  * Accumulation is float32; P and dS are rounded to dtype for their products. dk and dv
- * are written whole (no accumulation into the caller's buffers).
+ * are written whole (no accumulation into the caller's buffers); the results are repeatable
+ * bit for bit.
  */
 attn_status_t attn_bwd(const attn_bwd_args_t *args, const void *q, const void *k, const void *v, const void *o,
                        const void *dout, const float *lse, void *dq, void *dk, void *dv, void *workspace,
