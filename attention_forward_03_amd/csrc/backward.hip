@@ -112,9 +112,22 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kb0 = (blockIdx.x / p.chunks) * (kBwdNW * 32);
-  const int chunk = blockIdx.x % p.chunks;
-  const int g = blockIdx.y, b = blockIdx.z;
+  // XCD placement as in the forward: the items of one (sequence, KV head) unit run on one
+  // XCD (workgroup w runs on XCD w % 8) and share its L2 copy of the unit's Q and dO
+  // (measured neutral here: the kernel waits on load latency, not on HBM)
+  const int per = p.kblocks * p.chunks;  // items per unit
+  const int w = blockIdx.x;
+  int unit, item;
+  if (((p.batch * p.hkv) & 7) == 0) {
+    unit = (w & 7) + 8 * ((w >> 3) / per);
+    item = (w >> 3) % per;
+  } else {
+    unit = w / per;
+    item = w % per;
+  }
+  const int g = unit % p.hkv, b = unit / p.hkv;
+  const int kb0 = (item / p.chunks) * (kBwdNW * 32);
+  const int chunk = item % p.chunks;
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
   const int key = kb0 + wave * 32 + l32;  // this lane's key column
   const int kb1 = min(Lk, kb0 + kBwdNW * 32);
@@ -371,7 +384,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  // every head's longest (causal) query tiles first: the grid is (head, tile, batch)
+  // every head's longest (causal) query tiles first: the grid is (head, tile, batch) (the
+  // forward's per-XCD placement measured 7% slower here)
   const int ntile = (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32);
   const int r0 = (p.causal ? ntile - 1 - (int)blockIdx.y : (int)blockIdx.y) * (kBwdNW * 32);
   const int h = blockIdx.x, b = blockIdx.z;
@@ -525,8 +539,11 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nkv4 = (int64_t)p.batch * p.hkv * p.nk * D / 4;  // float4s per accumulator slot
-  const dim3 gkv((unsigned)((p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32) * p.chunks), p.hkv, p.batch);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), gkv, dim3(kBwdNW * 64), 0, st, p);
+  BwdParams q = p;
+  q.kblocks = (p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32);
+  const int64_t nkv_items = (int64_t)q.kblocks * p.chunks * p.hkv * p.batch;
+  if (nkv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_convert_kernel<D, BF16>), dim3((unsigned)((nkv4 + 255) / 256)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;

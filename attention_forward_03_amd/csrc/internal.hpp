@@ -51,6 +51,7 @@ struct BwdParams {
   float* dk32;          // workspace [chunks][B, Hkv, Nk, D] fp32 partial dK, then dv32 alike
   float* dv32;
   int32_t chunk_steps, chunks;  // dK / dV work split, from bwd_plan
+  int32_t kblocks;              // 128-key blocks per (sequence, KV head), set by the launcher
   int32_t batch, hq, hkv, group, nq, nk, causal, window;
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
