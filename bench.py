@@ -71,6 +71,27 @@ FP8_KERNEL = "fwd_fp8_kernel"
 BWD_KERNELS = ("bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
 
 
+# the sources each kernel family is built from: counter-derived traffic of a kernel is
+# reported only while these files are unchanged since the counters were taken
+KERNEL_FILES = {
+    "fwd_r2_kernel": ("prefill.hip", "gen_prefill_r2.py", "prefill_shared.hpp", "common.hpp"),
+    "fwd_mfma16_kernel": ("prefill.hip", "prefill_shared.hpp", "common.hpp"),
+    "gather_kv_pages_kernel": ("prefill.hip", "common.hpp"),
+    "decode_": ("decode.hip", "common.hpp"),
+    "fwd_fp8_kernel": ("prefill_fp8.hip", "prefill_shared.hpp", "common.hpp"),
+    "bwd_": ("backward.hip", "prefill_shared.hpp", "common.hpp"),
+}
+
+
+def file_digests() -> dict:
+    import hashlib
+    out = {}
+    for name in sorted({f for fs in KERNEL_FILES.values() for f in fs}):
+        with open(os.path.join(HERE, "attention_forward_03_amd", "csrc", name), "rb") as f:
+            out[name] = hashlib.sha256(f.read()).hexdigest()[:16]
+    return out
+
+
 def kernel_source_digest() -> str:
     """Digest of the kernel sources: counter-derived traffic is only reported while it matches."""
     import hashlib
@@ -111,7 +132,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, out_path: 
     w_scale = known / (copy_w * 1024.0)
     fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
     write = {k: sum(v) / len(v) for k, v in write.items()}
-    res = {"source_digest": kernel_source_digest(), "fetch_scale": f_scale, "write_scale": w_scale,
+    res = {"source_digest": kernel_source_digest(), "file_digests": file_digests(),
+           "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_mib": copy_mib, "kernels": {}}
     for k in set(fetch) | set(write):
         if "copyBuffer" in k:
@@ -126,14 +148,19 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, out_path: 
 
 def load_traffic(kernel_substr):
     """Counter-measured HBM bytes per launch of the kernels whose name contains any of the
-    given substrings, or None when absent or taken on other kernel sources."""
+    given substrings, or None when absent or when any source file of those kernels has
+    changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("source_digest") != kernel_source_digest():
-        return None
     subs = (kernel_substr,) if isinstance(kernel_substr, str) else kernel_substr
+    then, now = t.get("file_digests", {}), file_digests()
+    for sub in subs:
+        fam = [k for k in KERNEL_FILES if k in sub]
+        files = KERNEL_FILES[fam[0]] if fam else tuple(now)
+        if any(then.get(f) != now[f] for f in files):
+            return None
     tot = [v["hbm_bytes"] for k, v in t["kernels"].items() if any(s in k for s in subs)]
     return round(sum(tot)) if tot else None
 
