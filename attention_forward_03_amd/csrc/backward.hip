@@ -59,6 +59,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
   p.delta[row] = acc;
 }
 
+// One direct-to-LDS load of 4 bytes per lane: lane l's dword from base + voff (bytes) to
+// LDS address lds_base + 4 l (the 4-byte form of load_lds16).
+__device__ __forceinline__ void load_lds4(const void* base, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory");
+}
+
 // Direct-to-LDS load of one row-major tile of ROWS rows x D (16-bit) into LDS, swizzled
 // as Swizzle<D>; rows past `valid` re-read the last valid row (the masks zero them).
 template <int D, int ROWS>
@@ -92,7 +100,8 @@ struct TileLoader {
 
 // --------------------------------------------------------------------- dK and dV ----
 // Wave w of the workgroup owns keys kb0 + 32 w .. +31. Per query tile of 32 rows (staged
-// in LDS with its dO rows; double-buffered):
+// in LDS with its dO rows, LSE and Delta; three buffers, loaded two steps ahead, because a
+// step's products are shorter than the latency of the next tile's loads):
 //   S = Q K^T          A = Q rows (LDS), B = K^T (the wave's keys, registers)
 //   P = 2^(S sc - LSE2)                                 lane: key column, 16 query rows
 //   dV^T += dO^T P     A = dO^T (transposing LDS read), B = P (16-bit)
@@ -104,11 +113,16 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   constexpr int BQ = kBwdBQ;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
+  constexpr int NBUF = 3;
   using SW = Swizzle<D>;
   using LD = TileLoader<D, BQ>;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
-  uint16_t* const q_lds = smem;              // [2][BQ][D]
-  uint16_t* const do_lds = smem + 2 * TILE;  // [2][BQ][D]
+  constexpr int NV = 2 * LD::LPW + 2;  // direct-to-LDS loads per wave per step
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
+  // per buffer: LSE then Delta, each [4 waves][64] floats (a wave loads rows 8 w .. 8 w + 7
+  // into the first 8 entries of its slot)
+  __shared__ __attribute__((aligned(1024))) float stats[NBUF * 2 * kBwdNW * 64];
+  uint16_t* const q_lds = smem;                 // [NBUF][BQ][D]
+  uint16_t* const do_lds = smem + NBUF * TILE;  // [NBUF][BQ][D]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -190,48 +204,40 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   auto qbase = [&](int st, const void* t) {
     return static_cast<const uint16_t*>(t) + ((int64_t)b * p.hq + head_of(st)) * Lq * D;
   };
-  // LSE2 and Delta of this lane's 16 query rows of step st (rows q0 + 8 j + 4 hi + i)
-  f32x4_t lse_n[4], del_n[4];
-  auto row_stats = [&](int st, f32x4_t (&ls)[4], f32x4_t (&de)[4]) __attribute__((always_inline)) {
-    const int64_t base = ((int64_t)b * p.hq + head_of(st)) * Lq;
+  // the loads of step st into buffer buf: Q and dO tiles, and LSE / Delta of rows
+  // q0 + 8 wave + lane % 8 (clamped to the sequence) into this wave's stats slots
+  auto issue = [&](int st, int buf) __attribute__((always_inline)) {
     const int q0 = qt_of(st);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = q0 + 8 * j + 4 * hi;
-      if (r + 3 < Lq) {
-        ls[j] = load_global<f32x4_t>(p.lse + base + r);
-        de[j] = load_global<f32x4_t>(p.delta + base + r);
-      } else {  // the tail of the sequence: rows past the end read the last row (masked)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ls[j][i] = p.lse[base + min(r + i, Lq - 1)];
-          de[j][i] = p.delta[base + min(r + i, Lq - 1)];
-        }
-      }
-    }
+    ld.load(qbase(st, p.q), D, q0, Lq, q_lds + buf * TILE, wave);
+    ld.load(qbase(st, p.dout), D, q0, Lq, do_lds + buf * TILE, wave);
+    const int64_t base = ((int64_t)b * p.hq + head_of(st)) * Lq;
+    const uint32_t voff = (uint32_t)min(q0 + 8 * wave + (lane & 7), Lq - 1) * 4u;
+    load_lds4(p.lse + base, voff, stats + ((buf * 2 + 0) * kBwdNW + wave) * 64);
+    load_lds4(p.delta + base, voff, stats + ((buf * 2 + 1) * kBwdNW + wave) * 64);
   };
 
   settle_global_loads();
-  ld.load(qbase(st0, p.q), D, qt_of(st0), Lq, q_lds, wave);
-  ld.load(qbase(st0, p.dout), D, qt_of(st0), Lq, do_lds, wave);
-  row_stats(st0, lse_n, del_n);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  issue(st0, 0);
+  if (st0 + 1 < steps) {
+    issue(st0 + 1, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
   auto step = [&](auto bufc, int st) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;
+    constexpr int BUF = decltype(bufc)::value;  // (st - st0) % NBUF
     const uint16_t* ql = q_lds + BUF * TILE;
     const uint16_t* dl = do_lds + BUF * TILE;
+    // buffer (BUF + 2) % NBUF was last read in step st - 1, which every wave has finished
+    if (st + 2 < steps) issue(st + 2, (BUF + 2) % NBUF);
+    // LSE and Delta of this lane's rows 8 j + 4 hi + i: loaded by wave j, entries 4 hi ..
     f32x4_t lse[4], del[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      lse[j] = lse_n[j];
-      del[j] = del_n[j];
-    }
-    if (st + 1 < steps) {
-      ld.load(qbase(st + 1, p.q), D, qt_of(st + 1), Lq, q_lds + (BUF ^ 1) * TILE, wave);
-      ld.load(qbase(st + 1, p.dout), D, qt_of(st + 1), Lq, do_lds + (BUF ^ 1) * TILE, wave);
-      row_stats(st + 1, lse_n, del_n);
+      lse[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 0) * kBwdNW + j) * 64 + 4 * hi);
+      del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
     }
     const int q0 = qt_of(st);
     // S = Q K^T (the fragment reads issued ahead of the products)
@@ -307,12 +313,18 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
         const u32x2_t up = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
         dk[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dk[db]);
       }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the loads of step st + 1 are complete once at most those of st + 2 remain
+    if (st + 2 < steps) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
   };
-  for (int st = st0; st < steps; st += 2) {
+  for (int st = st0; st < steps; st += NBUF) {
     step(std::integral_constant<int, 0>{}, st);
     if (st + 1 < steps) step(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < steps) step(std::integral_constant<int, 2>{}, st + 2);
   }
 
   if (key >= Lk) return;
