@@ -11,9 +11,8 @@
 //           bytes of head_dim at 32*(l/16)); Q (zero beyond G) is the B operand;
 //   softmax online-softmax update per query column (max over the 4 lanes that hold
 //           a column via two xor exchanges); alpha = 2^(m_old - m_new);
-//   values  O^T += V^T . P^T on the 16x16x4 fp32 matrix core: lane l loads 8
-//           head_dim entries of one token row (16 lanes cover a 256-byte row) and
-//           feeds entry c to product c, whose output row i is head_dim 8*i + c.
+//   values  O^T += V^T . P^T on the 16x16x16 16-bit matrix core, V^T read with the
+//           transposing LDS read (16- or 8-bit; fp8 codes widen exactly to 16 bits).
 // The split writes its normalised partial output and its log2-domain LSE to the
 // workspace. Combine kernel: one wave per (sequence, query head) merges the
 // ceil(L_s / split_len) partials: LSE = log sum_k 2^{lse_k}, O = sum_k
@@ -61,6 +60,12 @@ typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
   return __builtin_bit_cast(u32x2_t, v);
+}
+
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+__device__ __forceinline__ i32x2_t lds_read_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p));
 }
 
 // 16x16x16 matrix-core product on 16-bit inputs (4 per lane): lane l supplies row l%16 of
@@ -265,26 +270,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] * sl2 - m);
 
     if constexpr (KV == KV_FP8) {
-      l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      // O^T += V^T . P^T on the fp32 16x16x4 product: lane l reads 8 head_dim entries
-      // (8*col .. +7) of token slot 4*quad + r and feeds entry c to product c
+      // P packed to 16 bit as the B operand (keys 4*quad .. +3 of this lane's column); the
+      // row sum is taken over the same rounded values
+      const u32x2_t pb = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3])};
+      l += (lo16<QBF16>(pb[0]) + hi16<QBF16>(pb[0])) + (lo16<QBF16>(pb[1]) + hi16<QBF16>(pb[1]));
+      // O^T += V^T . P^T on the 16-bit 16x16x16 product. The 8-bit transposing read gives
+      // lane i of a 16-lane group byte i%8 of the 8-byte rows addressed by lanes i/8 + 2e:
+      // lane pair (2e, 2e+1) of quad q addresses key 4q + e%4 (each key twice), the even lane
+      // head_dim entries 16 db .. +7 and the odd lane 16 db + 8 .. +15, so the low dword of
+      // lane i holds keys 4q .. 4q+3 of head_dim 16 db + i, in the order P's registers hold
+      // them; the e4m3 codes widen exactly to 16 bits.
+      const int vkey = 4 * quad + ((col >> 1) & 3);
+      const int vpar = col & 1;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * quad + r;
-        const int c = col / 2;
-        const u32x2_t raw = *reinterpret_cast<const u32x2_t*>(vst + row * PL::ROW + PL::v_slot(row, c) * 16 + (col & 1) * 8);
-        float vf[8];
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false);
-          const f32x2_t b2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true);
-          vf[4 * w + 0] = a[0];
-          vf[4 * w + 1] = a[1];
-          vf[4 * w + 2] = b2[0];
-          vf[4 * w + 3] = b2[1];
-        }
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) o[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[c8], pr[r], o[c8], 0, 0, 0);
+      for (int db = 0; db < 8; ++db) {
+        const i32x2_t w = lds_read_tr8(vst + vkey * PL::ROW + PL::v_slot(vkey, db) * 16 + 8 * vpar);
+        const f32x2_t v01 = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], false);
+        const f32x2_t v23 = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], true);
+        const u32x2_t a = {pack2<QBF16>(v01[0], v01[1]), pack2<QBF16>(v23[0], v23[1])};
+        o[db] = mfma16x16x16<KBF16>(a, pb, o[db]);
       }
     } else {
       // P packed to 16 bit as the B operand (keys 4*quad .. +3 of this lane's column);
@@ -311,21 +315,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     const int64_t slot = ((int64_t)s * p.hq + h) * p.max_splits + split;
     float* dst = p.part_o + slot * kD;
     const float inv = vsc / lt;
-    if constexpr (KV == KV_FP8) {
-      // product c, row i holds head_dim 8*i + c: lane (col, quad) has 32*quad + 8*rr + c
+    // block db, row r holds head_dim 16*db + 4*quad + r
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        *reinterpret_cast<f32x4_t*>(dst + 32 * quad + 8 * rr) =
-            f32x4_t{o[0][rr] * inv, o[1][rr] * inv, o[2][rr] * inv, o[3][rr] * inv};
-        *reinterpret_cast<f32x4_t*>(dst + 32 * quad + 8 * rr + 4) =
-            f32x4_t{o[4][rr] * inv, o[5][rr] * inv, o[6][rr] * inv, o[7][rr] * inv};
-      }
-    } else {
-      // block db, row r holds head_dim 16*db + 4*quad + r
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-        *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * quad) = o[db] * inv;
-    }
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * quad) = o[db] * inv;
     if (quad == 0) p.part_lse[slot] = m + fast_log2(lt);
   }
 }

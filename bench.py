@@ -183,7 +183,8 @@ def _timed(torch, fn, flush, reps: int) -> float:
 def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
     """Timings of the variants beside the main workloads: the 16-bit prefill at head dims
     96 / 192 / 256 (causal B=2 H=16 N=4096 bf16), the headline prefill with a per-head
-    sink, and the decode workload with one KV head (MQA; bytes = the KV cache read once)."""
+    sink, the decode workload with fp8 e4m3 KV, and with one KV head (MQA); decode bytes =
+    the KV cache read once."""
     res = {}
     for d in (96, 192, 256):
         c = workloads.config_headdim(d)
@@ -202,6 +203,23 @@ def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
     fl = prefill_flops(pc.batch, pc.num_q_heads, pc.seqlen_q, pc.seqlen_k, pc.head_dim)
     res["prefill_headline_with_sink"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
     del q, k, v, o
+    dc8 = workloads.config_decode("fp8_e4m3")
+    t8 = dict(q=dc8.q.to(dev), k=dc8.k_cache.to(dev), v=dc8.v_cache.to(dev),
+              bt=torch.from_numpy(dc8.block_table).to(dev), sl=torch.from_numpy(dc8.seq_lens).to(dev),
+              ks=torch.from_numpy(dc8.k_scale).to(dev), vs=torch.from_numpy(dc8.v_scale).to(dev))
+    ws8 = torch.empty(attn.decode_workspace_size(num_seqs=dc8.num_seqs, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                                 max_pages_per_seq=dc8.max_pages, max_seq_len=dc8.max_seq_len,
+                                                 q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn),
+                      dtype=torch.uint8, device=dev)
+    o8 = torch.empty_like(t8["q"])
+    ms = _timed(torch, lambda: attn.decode_paged(t8["q"], t8["k"], t8["v"], t8["bt"], t8["sl"], dc8.max_seq_len,
+                                                 k_scale=t8["ks"], v_scale=t8["vs"], out=o8, workspace=ws8),
+                flush, reps)
+    nb = decode_bytes(dc8, kv_elt=1)
+    res["decode_fp8_kv_64seq_Hq32_Hkv8"] = {"ms": round(ms, 4), "gbps": round(nb / ms / 1e6, 1),
+                                            "frac_of_peak": round(nb / ms / 1e6 / PEAK_HBM_GBPS, 4),
+                                            "bytes_per_launch": nb}
+    del t8, ws8, o8, dc8
     dc = workloads.config_decode("bf16", num_kv_heads=1)
     t = dict(q=dc.q.to(dev), k=dc.k_cache.to(dev), v=dc.v_cache.to(dev), bt=torch.from_numpy(dc.block_table).to(dev),
              sl=torch.from_numpy(dc.seq_lens).to(dev))
