@@ -36,20 +36,35 @@ constexpr int kMaxSplitPages = 256;  // the host plans splits of at most 4096 to
 
 enum KvKind { KV_BF16 = 0, KV_F16 = 1, KV_FP8 = 2 };
 
-// Eight OCP e4m3 codes (two dwords) -> eight 16-bit values (a 128-bit operand of a
-// 16-bit product). Exact: every finite e4m3 value (|x| <= 448, smallest subnormal
-// 2^-9) is representable in both bf16 and f16.
+// Four OCP e4m3 codes (one dword, code 0 in the low byte) -> four 16-bit values in
+// two dwords, in the same order, by the packed scaled conversion at scale 1. Exact:
+// every finite e4m3 value (|x| <= 448, smallest subnormal 2^-9) is representable in
+// both bf16 and f16, and a unit scale leaves it unchanged.
 template <bool BF16>
-__device__ __forceinline__ u32x4_t fp8x8_to_16(u32x2_t codes) {
-  u32x4_t r;
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[w], false);
-    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[w], true);
-    r[2 * w] = pack2<BF16>(a[0], a[1]);
-    r[2 * w + 1] = pack2<BF16>(c[0], c[1]);
+__device__ __forceinline__ u32x2_t fp8x4_to_16(int codes) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+  u32x2_t r;
+  if constexpr (BF16) {
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
+    r[0] = __builtin_bit_cast(uint32_t, lo);
+    r[1] = __builtin_bit_cast(uint32_t, hi);
+  } else {
+    const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false);
+    const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, true);
+    r[0] = __builtin_bit_cast(uint32_t, lo);
+    r[1] = __builtin_bit_cast(uint32_t, hi);
   }
   return r;
+}
+
+// Eight codes (two dwords) -> eight 16-bit values (a 128-bit operand of a 16-bit product).
+template <bool BF16>
+__device__ __forceinline__ u32x4_t fp8x8_to_16(u32x2_t codes) {
+  const u32x2_t a = fp8x4_to_16<BF16>((int)codes[0]);
+  const u32x2_t b = fp8x4_to_16<BF16>((int)codes[1]);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
@@ -285,10 +300,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const i32x2_t w = lds_read_tr8(vst + vkey * PL::ROW + PL::v_slot(vkey, db) * 16 + 8 * vpar);
-        const f32x2_t v01 = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], false);
-        const f32x2_t v23 = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], true);
-        const u32x2_t a = {pack2<QBF16>(v01[0], v01[1]), pack2<QBF16>(v23[0], v23[1])};
-        o[db] = mfma16x16x16<KBF16>(a, pb, o[db]);
+        o[db] = mfma16x16x16<KBF16>(fp8x4_to_16<QBF16>(w[0]), pb, o[db]);
       }
     } else {
       // P packed to 16 bit as the B operand (keys 4*quad .. +3 of this lane's column);
