@@ -22,6 +22,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 SOURCES = ("prefill.hip", "prefill_fp8.hip", "backward.hip", "decode.hip", "probes.hip", "api.cpp")
 ARCH = "gfx950"
+# The compiler-built kernels take the VGPR form of the matrix-core instructions: their
+# accumulators live in ordinary vector registers, so the vector work on them (rescale,
+# masks, normalisation) needs no copies between the accumulation and vector register
+# files, and a kernel that fits in 256 registers runs two waves per SIMD. The D=128
+# prefill loop is inline asm either way; probes.hip keeps the default, so its measured
+# peaks stay comparable across builds.
+SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+                for src in ("prefill.hip", "prefill_fp8.hip", "backward.hip", "decode.hip")}
 
 
 def _hipcc() -> str:
@@ -55,7 +63,8 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *common_flags(), "-I", gen_dir, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *common_flags(), *SOURCE_FLAGS.get(src, []), "-I", gen_dir, *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -194,12 +194,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     const int e = pg0 + lane + 64 * c;
     btv[c] = (64 * c < pg1 - pg0 && e < pg1) ? bt[e] : 0;
   }
+  // Each register is read at the uniform lane first and the scalar results are selected:
+  // selecting among the registers before the read lets the compiler index the array
+  // dynamically, which puts it in scratch memory (a memory round trip per page).
   auto phys_page = [&](int idx) __attribute__((always_inline)) {  // idx = pg - pg0, uniform
-    int v = btv[0];
+    int v = __builtin_amdgcn_readlane(btv[0], idx & 63);
 #pragma unroll
-    for (int c = 1; c < kMaxSplitPages / 64; ++c)
-      if (idx >= 64 * c) v = btv[c];
-    return __builtin_amdgcn_readlane(v, idx & 63);
+    for (int c = 1; c < kMaxSplitPages / 64; ++c) {
+      const int w = __builtin_amdgcn_readlane(btv[c], idx & 63);
+      v = idx >= 64 * c ? w : v;
+    }
+    return v;
   };
   auto issue = [&](int pg) __attribute__((always_inline)) {
     uint8_t* st = ring + ((pg - pg0) % NST) * PL::STAGE;
