@@ -445,14 +445,27 @@ attn_status_t attn_decode_plan(const attn_decode_args_t* a, int32_t* split_len, 
     const int64_t per = ((int64_t)a->max_seq_len + a->num_splits - 1) / a->num_splits;
     len = (per + kPageSize - 1) / kPageSize * kPageSize;
   } else {
-#ifndef ATTN_DECODE_ITEMS
-#define ATTN_DECODE_ITEMS 8192
-#endif
-    // Aim at about ATTN_DECODE_ITEMS single-wave work items when lengths average half the
-    // maximum, keeping each split between 256 and 4096 tokens, rounded to a power of two.
-    const int64_t want = (int64_t)a->num_seqs * a->num_kv_heads * a->max_seq_len / (2 * ATTN_DECODE_ITEMS);
+    // Two aims, with the sequences' lengths taken as half the maximum on average:
+    // (1) about kDecodeItems single-wave work items (splits x KV heads), so short
+    //     splits keep a small batch busy: the shortest power of two reaching it;
+    // (2) partial results (fp32 O and LSE per query head, written, then read by the
+    //     combine) small next to the split's K/V bytes: at least 512 * G / kv_bytes
+    //     tokens for G query heads per KV head. This matters where many query heads
+    //     share a KV head (MQA: G = 32 makes 256-token splits move 25% extra bytes).
+    //     It is taken only while the split grid keeps at least kDecodeMinWaves waves
+    //     (head tiles of 16 query heads included).
+    constexpr int64_t kDecodeItems = 8192, kDecodeMinWaves = 256;
+    const int64_t seqs_heads = (int64_t)a->num_seqs * a->num_kv_heads;
+    const int64_t want = seqs_heads * a->max_seq_len / (2 * kDecodeItems);
     len = 256;
     while (len < want && len < kMaxSplitTokens) len *= 2;
+    const int64_t group = a->num_q_heads / a->num_kv_heads;
+    const int64_t tiles = (group + 15) / 16;
+    const int64_t kv_bytes = a->kv_dtype == ATTN_FP8_E4M3 ? 1 : 2;
+    const int64_t partial_len = 512 * group / kv_bytes;
+    while (len < partial_len && len < kMaxSplitTokens &&
+           seqs_heads * tiles * a->max_seq_len / (2 * (2 * len)) >= kDecodeMinWaves)
+      len *= 2;
   }
   if (len > kMaxSplitTokens) len = kMaxSplitTokens;  // the split kernel's page window
   const int64_t n = ((int64_t)a->max_seq_len + len - 1) / len;

@@ -10,7 +10,7 @@
 //           from the page into the A operand (lane l: token slot l%16, 64 contiguous
 //           bytes of head_dim at 32*(l/16)); Q (zero beyond G) is the B operand;
 //   softmax online-softmax update per query column (max over the 4 lanes that hold
-//           a column via two xor exchanges); alpha = 2^(m_old - m_new);
+//           a column via two lane swaps); alpha = 2^(m_old - m_new);
 //   values  O^T += V^T . P^T on the 16x16x16 16-bit matrix core, V^T read with the
 //           transposing LDS read (16- or 8-bit; fp8 codes widen exactly to 16 bits).
 // The split writes its normalised partial output and its log2-domain LSE to the
@@ -65,6 +65,23 @@ __device__ __forceinline__ u32x4_t fp8x8_to_16(u32x2_t codes) {
   const u32x2_t a = fp8x4_to_16<BF16>((int)codes[0]);
   const u32x2_t b = fp8x4_to_16<BF16>((int)codes[1]);
   return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// Maximum and sum over the four lanes col, col+16, col+32, col+48 (the lanes that hold one
+// query column of a 16x16 result) by the gfx950 lane-swap instructions, with no LDS round
+// trip: swapping the odd 16-lane rows of x with the even rows of a copy of x pairs lane l
+// with l^16, and swapping the upper 32 lanes with the lower 32 pairs l with l^32.
+__device__ __forceinline__ float max_over_column(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_column(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
@@ -271,8 +288,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       if (partial && tb + r >= t1) sc[r] = kNegInf;
       mx = fmaxf(mx, sc[r]);
     }
-    mx = fmaxf(mx, xor_shuffle(mx, 16));
-    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    mx = max_over_column(mx);
     // The reference max may trail the running max by up to 2^8; the accumulator is rescaled
     // only when a page would exceed that (every page holds at least one valid token, so
     // the new max is finite).
@@ -325,8 +341,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     }
   }
 
-  float lt = l + xor_shuffle(l, 16);
-  lt += xor_shuffle(lt, 32);
+  const float lt = sum_over_column(l);
   if (col < G) {
     const int h = h0 + col;
     const int64_t slot = ((int64_t)s * p.hq + h) * p.max_splits + split;
