@@ -180,6 +180,27 @@ def _timed(torch, fn, flush, reps: int) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+PEAK_F32_TFLOPS = 157.3  # fp32 matrix cores, dense
+
+
+def measure_sweep(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """The dense non-causal sweep B=2 H=8, N in {512, 1024, 2048, 4096} x D in {32, 64, 128},
+    fp32 and bf16 inputs (events around each launch, caches flushed before each): TFLOP/s
+    per point, 4*B*H*N^2*D per call, against the fp32 or bf16 matrix-core peak."""
+    res = {}
+    for dt, peak in (("f32", PEAK_F32_TFLOPS), ("bf16", PEAK_BF16_TFLOPS)):
+        for n in workloads.SWEEP_N:
+            for d in workloads.SWEEP_D:
+                c = workloads.config_sweep(n, d, dt)
+                q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+                o = torch.empty_like(q)
+                ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
+                tf = prefill_flops(c.batch, c.num_q_heads, n, n, d) / ms / 1e9
+                res[f"{dt}_N{n}_D{d}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
+                del q, k, v, o
+    return res
+
+
 def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
     """Timings of the variants beside the main workloads: the 16-bit prefill at head dims
     96 / 192 / 256 (causal B=2 H=16 N=4096 bf16), the headline prefill with a per-head
@@ -295,7 +316,8 @@ def main(argv=None):
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 e4m3 prefill")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the variant measurements (head dims 96/192/256, sink, MQA decode)")
+                    help="skip the variant measurements (head dims 96/192/256, sink, fp8-KV and MQA decode) "
+                         "and the dense (N, D) sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--no-flush", action="store_true",
@@ -527,6 +549,7 @@ def main(argv=None):
     # ------------------------------------------------------------ variants ----
     if not args.no_variants and not args.no_prefill:
         out["variants"] = measure_variants(attn, torch, workloads, dev, flush, args.steps)
+        out["sweep"] = measure_sweep(attn, torch, workloads, dev, flush, args.steps)
 
     # ------------------------------------------------------- measured peaks ----
     if not args.no_probes:
