@@ -87,7 +87,7 @@ __device__ __forceinline__ float softmax_tile(const FwdParams& p, f32x16_t (&s)[
 // so each load reads inside a single page: its base is the page (a wave-uniform address)
 // and each lane adds its token slot. The page ids of a tile are read one tile ahead.
 template <int D, int NW, int BN, bool BF16, bool PAGED = false>
-__global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
   constexpr int DP = lds_row(D);  // LDS row width
   constexpr int TILE = BN * DP;   // elements per K or V tile in LDS
@@ -792,12 +792,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f32_kernel(const FwdParams p) 
 #endif
 constexpr int kNW16 = ATTN_PREFILL_WAVES;  // waves per workgroup, 16-bit inputs
 constexpr int kBN16 = ATTN_PREFILL_KEYS;   // keys per tile, 16-bit inputs
-// head dims 192 and 256: 4 waves of 32 rows and 32-key tiles. At 192 the kernel fits
-// 256 registers, so two workgroups share a CU (two waves per SIMD: one wave's softmax
-// runs beside the other's products); at 256 the 128 accumulator registers of the output
-// block, the Q fragments and the scores need more, so one wave per SIMD holds them.
-constexpr int nw16(int D) { return D >= 192 ? 4 : kNW16; }
-constexpr int bn16(int D) { return D >= 192 ? 32 : kBN16; }
+// head dims 96, 192 and 256: 4 waves of 32 rows and 32-key tiles. At 96 three
+// workgroups share a CU (three waves per SIMD); at 192 the kernel fits in 256 registers,
+// so two do (two waves per SIMD: one wave's softmax runs beside another's products); at
+// 256 the 128 accumulator registers of the output block, the Q fragments and the scores
+// need more, so one wave per SIMD holds them.
+constexpr int nw16(int D) { return D >= 192 || D == 96 ? 4 : kNW16; }
+constexpr int bn16(int D) { return D >= 192 || D == 96 ? 32 : kBN16; }
 constexpr int kNW32 = 4;
 constexpr int kBN32 = 32;
 
