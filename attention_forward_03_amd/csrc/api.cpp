@@ -453,14 +453,14 @@ attn_status_t attn_decode_plan(const attn_decode_args_t* a, int32_t* split_len, 
     //     tokens for G query heads per KV head. This matters where many query heads
     //     share a KV head (MQA: G = 32 makes 256-token splits move 25% extra bytes).
     //     It is taken only while the split grid keeps at least kDecodeMinWaves waves
-    //     (head tiles of 16 query heads included).
-    constexpr int64_t kDecodeItems = 8192, kDecodeMinWaves = 256;
+    //     (a wave takes up to two head tiles of 16 query heads).
+    constexpr int64_t kDecodeItems = 8192, kDecodeMinWaves = 512;
     const int64_t seqs_heads = (int64_t)a->num_seqs * a->num_kv_heads;
     const int64_t want = seqs_heads * a->max_seq_len / (2 * kDecodeItems);
     len = 256;
     while (len < want && len < kMaxSplitTokens) len *= 2;
     const int64_t group = a->num_q_heads / a->num_kv_heads;
-    const int64_t tiles = (group + 15) / 16;
+    const int64_t tiles = group > 16 ? (group + 31) / 32 : 1;  // waves per KV head and split
     const int64_t kv_bytes = a->kv_dtype == ATTN_FP8_E4M3 ? 1 : 2;
     const int64_t partial_len = 512 * group / kv_bytes;
     while (len < partial_len && len < kMaxSplitTokens &&

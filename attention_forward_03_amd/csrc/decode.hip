@@ -4,8 +4,9 @@
 //
 // Split kernel: one wave per (split, KV head g, sequence s). The G = Hq/Hkv query
 // heads that share KV head g are processed together, so every K/V byte is read
-// once; beyond 16 heads per KV head (MQA-like groups) the heads are taken 16 at a
-// time by adjacent workgroups, which read the same pages at about the same time. Work runs page by page (16 tokens = one page):
+// once; beyond 16 heads per KV head (MQA-like groups) a wave takes two tiles of 16 query
+// heads, which share every K and V fragment read (more than 32 heads: adjacent workgroups
+// take further pairs of tiles). Work runs page by page (16 tokens = one page):
 //   scores  S^T[key][query] = K . Q^T on the 16x16x32 matrix core, K loaded straight
 //           from the page into the A operand (lane l: token slot l%16, 64 contiguous
 //           bytes of head_dim at 32*(l/16)); Q (zero beyond G) is the B operand;
@@ -139,7 +140,9 @@ struct PageLayout {
   }
 };
 
-template <int KV, bool QBF16, int NST>
+// HT: query-head tiles of 16 per wave (2 when a KV head has more than 16 query heads:
+// both tiles then share every K and V fragment read, and each page is streamed once).
+template <int KV, bool QBF16, int NST, int HT>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
   using PL = PageLayout<KV>;
   constexpr bool KBF16 = (KV == KV_FP8) ? QBF16 : (KV == KV_BF16);
@@ -155,12 +158,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int split = blockIdx.x;
   const int gt = blockIdx.y;
 #endif
-  const int g = gt / p.head_tiles;                            // KV head
-  const int h0 = g * p.group + 16 * (gt % p.head_tiles);      // first query head of the tile
-  const int G = min(16, p.group - 16 * (gt % p.head_tiles));  // query heads in the tile
+  const int wave_tiles = (p.head_tiles + HT - 1) / HT;
+  const int g = gt / wave_tiles;  // KV head
+  int h0[HT], G[HT];              // first query head and query heads of each tile (G may be 0)
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    const int tile = HT * (gt % wave_tiles) + t;
+    h0[t] = g * p.group + 16 * tile;
+    G[t] = max(0, min(16, p.group - 16 * tile));
+  }
   const int s = blockIdx.z;
   const int lane = threadIdx.x;
-  const int col = lane & 15;   // query column (head h0 + col when col < G) / token slot
+  const int col = lane & 15;   // query column (head h0[t] + col when col < G[t]) / token slot
   const int quad = lane >> 4;  // token slots 4*quad .. 4*quad+3 of the score tile
 
   const int L = p.seq_lens[s];
@@ -170,12 +179,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
   // Q as the B operand of the score product: k-step ks, slot group quad <-> head_dim
   // 32*quad + 8*ks .. +7.
-  u32x4_t qf[4];
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.hq + h0 + col) * kD + 32 * quad;
+  u32x4_t qf[HT][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    qf[ks] = u32x4_t{0, 0, 0, 0};
-    if (col < G) qf[ks] = load_global<u32x4_t>(qrow + 8 * ks);
+  for (int t = 0; t < HT; ++t) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.hq + h0[t] + col) * kD + 32 * quad;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[t][ks] = u32x4_t{0, 0, 0, 0};
+      if (col < G[t]) qf[t][ks] = load_global<u32x4_t>(qrow + 8 * ks);
+    }
   }
 
   const int64_t tok_bytes = (int64_t)p.hkv * PL::ROW;  // bytes between token slots
@@ -235,10 +247,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     }
   };
 
-  f32x4_t o[8];
+  f32x4_t o[HT][8];
+  float m[HT], l[HT];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = kNegInf, l = 0.0f;
+  for (int t = 0; t < HT; ++t) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[t][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m[t] = kNegInf;
+    l[t] = 0.0f;
+  }
 
   settle_global_loads();
 #pragma unroll
@@ -261,55 +278,70 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     const uint8_t* kst = ring + ((pg - pg0) % NST) * PL::STAGE;
     const uint8_t* vst = kst + PL::HALF;
 
-    // scores S^T[slot][query] = K . Q^T
-    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // scores S^T[slot][query] = K . Q^T, each K fragment feeding every tile
+    f32x4_t sc[HT];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (KV == KV_FP8) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // 16 codes = head_dim 32*quad + 16*j .. +15 of token slot `col`
         const int c = 2 * quad + j;
         const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kst + col * PL::ROW + PL::k_slot(col, c) * 16);
-        sc = mfma16x16x32<QBF16>(fp8x8_to_16<QBF16>(u32x2_t{raw[0], raw[1]}), qf[2 * j], sc);
-        sc = mfma16x16x32<QBF16>(fp8x8_to_16<QBF16>(u32x2_t{raw[2], raw[3]}), qf[2 * j + 1], sc);
+        const u32x4_t k0 = fp8x8_to_16<QBF16>(u32x2_t{raw[0], raw[1]});
+        const u32x4_t k1 = fp8x8_to_16<QBF16>(u32x2_t{raw[2], raw[3]});
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+          sc[t] = mfma16x16x32<QBF16>(k0, qf[t][2 * j], sc[t]);
+          sc[t] = mfma16x16x32<QBF16>(k1, qf[t][2 * j + 1], sc[t]);
+        }
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int c = 4 * quad + ks;
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kst + col * PL::ROW + PL::k_slot(col, c) * 16);
-        sc = mfma16x16x32<QBF16>(a, qf[ks], sc);
+#pragma unroll
+        for (int t = 0; t < HT; ++t) sc[t] = mfma16x16x32<QBF16>(a, qf[t][ks], sc[t]);
       }
     }
     const int tb = pg * kPage + 4 * quad;  // token of register r is tb + r
     const bool partial = (pg + 1) * kPage > t1;
-    float mx = kNegInf;
+    float pr[HT][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (partial && tb + r >= t1) sc[r] = kNegInf;
-      mx = fmaxf(mx, sc[r]);
+    for (int t = 0; t < HT; ++t) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (partial && tb + r >= t1) sc[t][r] = kNegInf;
+        mx = fmaxf(mx, sc[t][r]);
+      }
+      mx = max_over_column(mx);
+      // The reference max may trail the running max by up to 2^8; the accumulator is
+      // rescaled only when a page would exceed that (every page holds at least one valid
+      // token, so the new max is finite).
+      const float mxs = mx * sl2;
+      if (__any(mxs > m[t] + 8.0f)) {
+        const float m_new = fmaxf(m[t], mxs);
+        const float alpha = fast_exp2(m[t] - m_new);
+        l[t] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[t][c] *= alpha;
+        m[t] = m_new;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[t][r] = fast_exp2(sc[t][r] * sl2 - m[t]);
     }
-    mx = max_over_column(mx);
-    // The reference max may trail the running max by up to 2^8; the accumulator is rescaled
-    // only when a page would exceed that (every page holds at least one valid token, so
-    // the new max is finite).
-    const float mxs = mx * sl2;
-    if (__any(mxs > m + 8.0f)) {
-      const float m_new = fmaxf(m, mxs);
-      const float alpha = fast_exp2(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] *= alpha;
-      m = m_new;
-    }
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] * sl2 - m);
 
     if constexpr (KV == KV_FP8) {
       // P packed to 16 bit as the B operand (keys 4*quad .. +3 of this lane's column); the
       // row sum is taken over the same rounded values
-      const u32x2_t pb = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3])};
-      l += (lo16<QBF16>(pb[0]) + hi16<QBF16>(pb[0])) + (lo16<QBF16>(pb[1]) + hi16<QBF16>(pb[1]));
+      u32x2_t pb[HT];
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+        pb[t] = u32x2_t{pack2<QBF16>(pr[t][0], pr[t][1]), pack2<QBF16>(pr[t][2], pr[t][3])};
+        l[t] += (lo16<QBF16>(pb[t][0]) + hi16<QBF16>(pb[t][0])) + (lo16<QBF16>(pb[t][1]) + hi16<QBF16>(pb[t][1]));
+      }
       // O^T += V^T . P^T on the 16-bit 16x16x16 product. The 8-bit transposing read gives
       // lane i of a 16-lane group byte i%8 of the 8-byte rows addressed by lanes i/8 + 2e:
       // lane pair (2e, 2e+1) of quad q addresses key 4q + e%4 (each key twice), the even lane
@@ -321,13 +353,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const i32x2_t w = lds_read_tr8(vst + vkey * PL::ROW + PL::v_slot(vkey, db) * 16 + 8 * vpar);
-        o[db] = mfma16x16x16<KBF16>(fp8x4_to_16<QBF16>(w[0]), pb, o[db]);
+        const u32x2_t vw = fp8x4_to_16<QBF16>(w[0]);
+#pragma unroll
+        for (int t = 0; t < HT; ++t) o[t][db] = mfma16x16x16<KBF16>(vw, pb[t], o[t][db]);
       }
     } else {
       // P packed to 16 bit as the B operand (keys 4*quad .. +3 of this lane's column);
       // the row sum is taken over the same rounded values
-      const u32x2_t pb = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3])};
-      l += (lo16<QBF16>(pb[0]) + hi16<QBF16>(pb[0])) + (lo16<QBF16>(pb[1]) + hi16<QBF16>(pb[1]));
+      u32x2_t pb[HT];
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+        pb[t] = u32x2_t{pack2<QBF16>(pr[t][0], pr[t][1]), pack2<QBF16>(pr[t][2], pr[t][3])};
+        l[t] += (lo16<QBF16>(pb[t][0]) + hi16<QBF16>(pb[t][0])) + (lo16<QBF16>(pb[t][1]) + hi16<QBF16>(pb[t][1]));
+      }
       // O^T += V^T . P^T, 16 head_dim entries per product: the transposing read gives lane
       // l the 4 keys 4*quad .. +3 of head_dim 16*db + col
       const int vr = 4 * quad + (col >> 2);
@@ -336,22 +374,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       for (int db = 0; db < 8; ++db) {
         const int c = 2 * db + (vc2 >> 1);
         const u32x2_t a = lds_read_tr16(vst + vr * PL::ROW + PL::v_slot(vr, c) * 16 + (vc2 & 1) * 8);
-        o[db] = mfma16x16x16<KBF16>(a, pb, o[db]);
+#pragma unroll
+        for (int t = 0; t < HT; ++t) o[t][db] = mfma16x16x16<KBF16>(a, pb[t], o[t][db]);
       }
     }
   }
 
-  const float lt = sum_over_column(l);
-  if (col < G) {
-    const int h = h0 + col;
-    const int64_t slot = ((int64_t)s * p.hq + h) * p.max_splits + split;
-    float* dst = p.part_o + slot * kD;
-    const float inv = vsc / lt;
-    // block db, row r holds head_dim 16*db + 4*quad + r
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * quad) = o[db] * inv;
-    if (quad == 0) p.part_lse[slot] = m + fast_log2(lt);
+  for (int t = 0; t < HT; ++t) {
+    const float lt = sum_over_column(l[t]);
+    if (col < G[t]) {
+      const int h = h0[t] + col;
+      const int64_t slot = ((int64_t)s * p.hq + h) * p.max_splits + split;
+      float* dst = p.part_o + slot * kD;
+      const float inv = vsc / lt;
+      // block db, row r holds head_dim 16*db + 4*quad + r
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * quad) = o[t][db] * inv;
+      if (quad == 0) p.part_lse[slot] = m[t] + fast_log2(lt);
+    }
   }
 }
 
@@ -407,13 +449,18 @@ constexpr int kStages8 = ATTN_DECODE_STAGES_FP8;  // fp8 KV, 4 KiB per stage
 
 template <int KV, bool QBF16>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
+  const bool two = p.head_tiles >= 2;  // more than 16 query heads per KV head
+  const int wave_tiles = two ? (p.head_tiles + 1) / 2 : p.head_tiles;
 #if ATTN_DECODE_HEAD_MAJOR
-  dim3 grid(p.hkv * p.head_tiles, p.max_splits, p.num_seqs);
+  dim3 grid(p.hkv * wave_tiles, p.max_splits, p.num_seqs);
 #else
-  dim3 grid(p.max_splits, p.hkv * p.head_tiles, p.num_seqs);
+  dim3 grid(p.max_splits, p.hkv * wave_tiles, p.num_seqs);
 #endif
   constexpr int nst = KV == KV_FP8 ? kStages8 : kStages16;
-  hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst>), grid, dim3(64), 0, st, p);
+  if (two)
+    hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst, 2>), grid, dim3(64), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst, 1>), grid, dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<QBF16>), dim3(p.num_seqs * p.hq), dim3(64), 0, st, p);

@@ -200,12 +200,13 @@ def test_decode_plan_is_a_deterministic_integer_function():
     assert attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=1000, max_pages_per_seq=63)) == (256, 4)
     # many query heads per KV head: longer splits keep the partial results small next to
     # the K/V bytes (at least 512 * G / kv_bytes tokens) ...
-    assert attn.decode_plan(**_dec_kw(num_kv_heads=1)) == (4096, 8)
+    assert attn.decode_plan(**_dec_kw(num_kv_heads=1)) == (2048, 16)
     assert attn.decode_plan(**_dec_kw(num_kv_heads=2)) == (4096, 8)
     assert attn.decode_plan(**_dec_kw(kv_dtype=_lib.ATTN_FP8_E4M3)) == (2048, 16)
-    # ... while the grid keeps at least 256 waves
+    # ... while the grid keeps at least 512 waves (a wave takes two tiles of 16 query heads)
     assert attn.decode_plan(**_dec_kw(num_seqs=1, num_kv_heads=1)) == (256, 128)
-    assert attn.decode_plan(**_dec_kw(num_seqs=8, num_kv_heads=1)) == (1024, 32)
+    assert attn.decode_plan(**_dec_kw(num_seqs=8, num_kv_heads=1)) == (256, 128)
+    assert attn.decode_plan(**_dec_kw(num_seqs=32, num_kv_heads=1)) == (1024, 32)
     ln, n = attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=2_000_000, max_pages_per_seq=125000,
                                        num_splits=1000))
     assert ln == 2000 and n == 1000
