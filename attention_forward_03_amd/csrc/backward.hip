@@ -23,9 +23,9 @@
 // kernels: results are kept transposed when that puts P or dS straight into a B operand
 // (dV^T = dO^T P, dK^T = Q^T dS, dQ^T = K^T dS^T), and the transposed A operands (dO^T,
 // Q^T, K^T) come from row-major LDS tiles through the transposing LDS read. Q, dO and K
-// tiles are read both by rows and transposed, so every tile takes the row-read swizzle
-// (Swizzle::k) and the transposing reads apply it to their own rows; it depends on the
-// row only through bits that a step of 16 rows leaves unchanged.
+// tiles are read both by rows and transposed, so every tile takes one swizzle that suits
+// both (BwdSwizzle) and the transposing reads apply it to their own rows; it depends on
+// the row only through bits that a step of 16 rows leaves unchanged.
 #include <type_traits>
 
 #include "common.hpp"
@@ -34,6 +34,26 @@
 
 namespace attn {
 namespace {
+
+// Swizzle of the tiles read both by rows (16-byte chunks, 32 rows) and by the transposing
+// read (8 bytes of each of 8 rows x 4 chunks per instruction). At D = 128 (16 chunks per
+// row) the forward's row swizzle c ^ (row & 15) sends a transposing read to 8 of the 16
+// chunk positions: a 2-way bank conflict, and each 16-lane group of it (4 rows x 2
+// chunks) reaches only 4. XOR-ing the chunk with the row's low four bits rotated left by
+// one still maps a chunk column of 16 rows onto all 16 positions (row reads stay
+// conflict-free), and puts the 4 rows of a 16-lane group on bits 1 and 2 of the position
+// and the group's half of the wave on bit 3: 8 positions per group, 16 per instruction.
+template <int D>
+struct BwdSwizzle {
+  __device__ static __forceinline__ int k(int row, int c) {
+    if constexpr (D == 128) {
+      const int r = row & 15;
+      return c ^ (((r << 1) | (r >> 3)) & 15);
+    } else {
+      return Swizzle<D>::k(row, c);
+    }
+  }
+};
 
 constexpr int kBwdNW = 4;   // waves per workgroup (one per SIMD: the accumulators are large)
 constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
@@ -68,7 +88,7 @@ __device__ __forceinline__ void load_lds4(const void* base, uint32_t voff, const
 }
 
 // Direct-to-LDS load of one row-major tile of ROWS rows x D (16-bit) into LDS, swizzled
-// as Swizzle<D>; rows past `valid` re-read the last valid row (the masks zero them).
+// as BwdSwizzle<D>; rows past `valid` re-read the last valid row (the masks zero them).
 template <int D, int ROWS>
 struct TileLoader {
   static constexpr int CPR = D / 8;
@@ -78,7 +98,7 @@ struct TileLoader {
   static_assert(LOADS % kBwdNW == 0, "tile loads split evenly over the waves");
   int row[LPW], off[LPW];
   __device__ void init(int wave, int lane, int stride) {
-    using SW = Swizzle<D>;
+    using SW = BwdSwizzle<D>;
 #pragma unroll
     for (int n = 0; n < LPW; ++n) {
       const int i = wave + n * kBwdNW;
@@ -114,7 +134,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
   constexpr int NBUF = 3;
-  using SW = Swizzle<D>;
+  using SW = BwdSwizzle<D>;
   using LD = TileLoader<D, BQ>;
   constexpr int NV = 2 * LD::LPW + 2;  // direct-to-LDS loads per wave per step
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
@@ -388,7 +408,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
   constexpr int BN = 64;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BN / 32, NPS = BN / 16;
   constexpr int TILE = BN * D;
-  using SW = Swizzle<D>;
+  using SW = BwdSwizzle<D>;
   using LD = TileLoader<D, BN>;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
   uint16_t* const k_lds = smem;
