@@ -248,14 +248,18 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + i], sc, -m_use));
-        const int w = pack4_fp8(x[0], x[1], x[2], x[3]);
-        pf[4 * kb + q4] = w;
-        // the row sum takes the rounded values, so O is a weighted average of exactly the
-        // weights the product used (a dominant key then comes out exact)
-        const f32x2_t r01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        const f32x2_t r23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        l += (r01[0] + r01[1]) + (r23[0] + r23[1]);
+        pf[4 * kb + q4] = pack4_fp8(x[0], x[1], x[2], x[3]);
       }
+    {
+      // the row sum of the rounded P from the matrix core: an all-ones A operand (e4m3 1.0)
+      // puts the column sums of P^T (all 64 keys of the tile) in every row of the result;
+      // lanes l and l^32 hold the same query column and their sums are added at the end,
+      // so each takes half (exact)
+      const int one4 = 0x38383838;
+      const i32x8_t ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+      const f32x16_t ts = mfma_fp8(ones, pf, zero16);
+      l += 0.5f * ts[0];
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       i32x8_t a;
