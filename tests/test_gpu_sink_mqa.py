@@ -66,7 +66,9 @@ def test_chunked_prefill_sink(gather):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
-@pytest.mark.parametrize("heads", [(32, 1), (20, 1), (48, 2), (64, 4)])
+# (32, 1): one wave takes both 16-head tiles; (20, 1): its second tile holds 4 heads;
+# (48, 1): three tiles, so the second wave's second tile is empty; (64, 4): 16 heads, one tile
+@pytest.mark.parametrize("heads", [(32, 1), (20, 1), (48, 1), (48, 2), (64, 4)])
 def test_decode_many_heads_per_kv_head(kv, heads):
     hq, hkv = heads
     case = workloads.make_decode(lengths=[1, 17, 1000, 4099], num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
@@ -80,8 +82,9 @@ def test_decode_many_heads_per_kv_head(kv, heads):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
-def test_decode_sink(kv):
-    case = workloads.make_decode(lengths=[1, 33, 2000, 5000], num_q_heads=32, num_kv_heads=8, head_dim=128,
+@pytest.mark.parametrize("hkv", [8, 1], ids=["gqa", "mqa"])
+def test_decode_sink(kv, hkv):
+    case = workloads.make_decode(lengths=[1, 33, 2000, 5000], num_q_heads=32, num_kv_heads=hkv, head_dim=128,
                                  kv_dtype=kv, seed=21)
     sinks = _sinks(32, 22)
     for ns in (0, 1, 4):
