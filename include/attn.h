@@ -130,7 +130,7 @@ typedef struct {
   int32_t num_seqs;          /* S >= 1 */
   int32_t num_q_heads;       /* Hq */
   int32_t num_kv_heads;      /* Hkv, Hq % Hkv == 0 */
-  int32_t head_dim;          /* D in {32, 64, 128} */
+  int32_t head_dim;          /* D in {32, 64, 96, 128, 192, 256} */
   int32_t page_size;         /* tokens per page; must be 16 */
   int32_t max_pages_per_seq; /* row length of block_table */
   int32_t num_pages;         /* pages in each cache (rows of k_cache / v_cache) */
