@@ -181,7 +181,7 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t *args, const void *q, c
                              float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace attn_fwd_paged can use for these args: 0 when there is no
- * gathered route for them (head_dim 32 / 64) or on bad args. */
+ * gathered route for them (head_dim other than 128) or on bad args. */
 size_t attn_fwd_paged_workspace_size(const attn_fwd_paged_args_t *args);
 
 /* ---------------------------------------------------------------- backward ---- */
