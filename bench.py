@@ -201,6 +201,42 @@ def measure_sweep(attn, torch, workloads, dev, flush, reps: int) -> dict:
     return res
 
 
+def measure_gqa(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """The causal GQA prefill family B=4 Hq=32 Hkv=8 N=4096 D=128 bf16 (plain causal, window
+    1024, softcap 30, ragged lengths U[1024, 4096]) and the small fp32 case B=2 H=4 N=64 D=32
+    (events around each launch, caches flushed before each). TFLOP/s two ways: `nominal`
+    counts 4*B*Hq*N^2*D, halved for causal (ragged: per sequence); `exact` counts 4*D*Hq per
+    (query, key) pair the mask allows."""
+    res = {}
+    for var in workloads.GQA_VARIANTS:
+        c = workloads.config_gqa(var)
+        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+        kw = dict(causal=c.causal, window=c.window, softcap=c.softcap)
+        if c.varlen:
+            kw.update(cu_seqlens_q=torch.from_numpy(c.cu_seqlens_q).to(dev),
+                      cu_seqlens_k=torch.from_numpy(c.cu_seqlens_k).to(dev),
+                      max_seqlen_q=c.seqlen_q, max_seqlen_k=c.seqlen_k)
+            lens = np.diff(c.cu_seqlens_q).astype(np.int64)
+        else:
+            lens = np.full(c.batch, c.seqlen_q, dtype=np.int64)
+        o = torch.empty_like(q)
+        ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, **kw), flush, reps)
+        nominal = sum(4.0 * c.num_q_heads * int(n) * int(n) * c.head_dim / 2 for n in lens)
+        exact = sum(4.0 * c.head_dim * c.num_q_heads * allowed_pairs(int(n), int(n), True, c.window) for n in lens)
+        res[var] = {"ms": round(ms, 4), "tflops_nominal": round(nominal / ms / 1e9, 1),
+                    "tflops_exact": round(exact / ms / 1e9, 1),
+                    "frac_of_peak_exact": round(exact / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o
+    c = workloads.config_small_f32()
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    o = torch.empty_like(q)
+    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
+    fl = prefill_flops(c.batch, c.num_q_heads, c.seqlen_q, c.seqlen_k, c.head_dim)
+    res["small_f32_B2_H4_N64_D32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 3),
+                                      "note": "launch-bound (4.2 MFLOP)"}
+    return res
+
+
 def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
     """Timings of the variants beside the main workloads: the 16-bit prefill at head dims
     96 / 192 / 256 (causal B=2 H=16 N=4096 bf16), the headline prefill with a per-head
@@ -316,8 +352,8 @@ def main(argv=None):
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 e4m3 prefill")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the variant measurements (head dims 96/192/256, sink, fp8-KV and MQA decode) "
-                         "and the dense (N, D) sweep")
+                    help="skip the variant measurements (head dims 96/192/256, sink, fp8-KV and MQA decode), "
+                         "the dense (N, D) sweep and the causal GQA family")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--no-flush", action="store_true",
@@ -550,6 +586,7 @@ def main(argv=None):
     if not args.no_variants and not args.no_prefill:
         out["variants"] = measure_variants(attn, torch, workloads, dev, flush, args.steps)
         out["sweep"] = measure_sweep(attn, torch, workloads, dev, flush, args.steps)
+        out["gqa"] = measure_gqa(attn, torch, workloads, dev, flush, args.steps)
 
     # ------------------------------------------------------- measured peaks ----
     if not args.no_probes:
