@@ -454,7 +454,7 @@ attn_status_t attn_decode_plan(const attn_decode_args_t* a, int32_t* split_len, 
     //     share a KV head (MQA: G = 32 makes 256-token splits move 25% extra bytes).
     //     It is taken only while the split grid keeps at least kDecodeMinWaves waves
     //     (a wave takes up to two head tiles of 16 query heads).
-    constexpr int64_t kDecodeItems = 8192, kDecodeMinWaves = 512;
+    constexpr int64_t kDecodeItems = 8192, kDecodeMinWaves = 384;
     const int64_t seqs_heads = (int64_t)a->num_seqs * a->num_kv_heads;
     const int64_t want = seqs_heads * a->max_seq_len / (2 * kDecodeItems);
     len = 256;

@@ -203,10 +203,15 @@ def test_decode_plan_is_a_deterministic_integer_function():
     assert attn.decode_plan(**_dec_kw(num_kv_heads=1)) == (2048, 16)
     assert attn.decode_plan(**_dec_kw(num_kv_heads=2)) == (4096, 8)
     assert attn.decode_plan(**_dec_kw(kv_dtype=_lib.ATTN_FP8_E4M3)) == (2048, 16)
-    # ... while the grid keeps at least 512 waves (a wave takes two tiles of 16 query heads)
+    # ... while the grid keeps at least 384 waves (a wave takes two tiles of 16 query heads)
     assert attn.decode_plan(**_dec_kw(num_seqs=1, num_kv_heads=1)) == (256, 128)
     assert attn.decode_plan(**_dec_kw(num_seqs=8, num_kv_heads=1)) == (256, 128)
     assert attn.decode_plan(**_dec_kw(num_seqs=32, num_kv_heads=1)) == (1024, 32)
+    # the same choices when the longest sequence falls just short of a power of two (the
+    # decode workload's lengths: max 32567)
+    assert attn.decode_plan(**_dec_kw(num_kv_heads=1, max_seq_len=32567)) == (2048, 16)
+    assert attn.decode_plan(**_dec_kw(num_kv_heads=2, max_seq_len=32567)) == (4096, 8)
+    assert attn.decode_plan(**_dec_kw(max_seq_len=32567)) == (1024, 32)
     ln, n = attn.decode_plan(**_dec_kw(num_seqs=1, max_seq_len=2_000_000, max_pages_per_seq=125000,
                                        num_splits=1000))
     assert ln == 2000 and n == 1000
