@@ -113,12 +113,13 @@ def test_fp8_all_codes_decode_exactly():
         assert (np.abs(got[~nz]) < 1e-30).all()
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
-def test_full_decode_config_sampled(kv):
-    """64 sequences, L ~ U[512, 32768], Hq=32 Hkv=8 D=128: the GPU computes all, the oracle
-    checks the shortest, the longest and a few more sequences."""
-    case = workloads.config_decode(kv)
-    note(f"[decode] full {kv}: total tokens {int(case.seq_lens.sum())}")
+@pytest.mark.parametrize("kv,hkv", [("bf16", 8), ("fp8_e4m3", 8), ("bf16", 1)], ids=["bf16", "fp8_e4m3", "mqa_bf16"])
+def test_full_decode_config_sampled(kv, hkv):
+    """64 sequences, L ~ U[512, 32768], Hq=32 Hkv=8 D=128 (and the MQA form, Hkv=1, as the
+    bench times it): the GPU computes all, the oracle checks the shortest, the longest and a
+    few more sequences."""
+    case = workloads.config_decode(kv, num_kv_heads=hkv)
+    note(f"[decode] full {kv} Hkv={hkv}: total tokens {int(case.seq_lens.sum())}")
     o, lse = run_decode(case)
     order = np.argsort(case.seq_lens)
     seqs = np.unique(np.concatenate([order[:2], order[-2:], [7, 33]]))
