@@ -174,7 +174,8 @@ attn_status_t attn_fwd(const attn_fwd_args_t* a, const void* q, const void* k, c
     p.cap_out = 0.0f;
   }
   p.o_scale = fp8 ? a->v_scale : 1.0f;
-  const int bm = fp8 ? attn::fwd_fp8_block_rows() : attn::fwd_block_rows(a->dtype, a->head_dim);
+  const int bm = fp8 ? attn::fwd_fp8_block_rows()
+                     : attn::fwd_block_rows(a->dtype, a->head_dim, a->seqlen_q, (int64_t)a->batch * a->num_q_heads);
   p.q_tiles = (a->seqlen_q + bm - 1) / bm;
   p.sinks = a->sinks;
 
@@ -307,7 +308,7 @@ attn_status_t attn_fwd_paged(const attn_fwd_paged_args_t* a, const void* q, cons
       p.v = wv;
       p.ks[0] = p.vs[0] = 0;
       p.block_table = nullptr;
-      const int bm = attn::fwd_block_rows(a->dtype, a->head_dim);
+      const int bm = attn::fwd_block_rows(a->dtype, a->head_dim, a->max_seqlen_q, (int64_t)a->num_seqs * a->num_q_heads);
       p.q_tiles = (a->max_seqlen_q + bm - 1) / bm;
       e = attn::launch_fwd(p, a->dtype, a->head_dim, hs);
     }

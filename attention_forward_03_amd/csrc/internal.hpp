@@ -91,7 +91,8 @@ struct DecodeParams {
 
 // Block-rows of the prefill kernels for a given dtype/head_dim (the host needs it
 // to size the grid).
-int fwd_block_rows(int dtype, int head_dim);
+// query rows per workgroup of the dense / ragged prefill (units = sequences x query heads)
+int fwd_block_rows(int dtype, int head_dim, int64_t nq, int64_t units);
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, hipStream_t stream);
 // chunked prefill over a paged cache (16-bit inputs)
