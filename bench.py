@@ -165,11 +165,14 @@ def load_traffic(kernel_substr):
     return round(sum(tot)) if tot else None
 
 
-def _timed(torch, fn, flush, reps: int) -> float:
+def _timed(torch, fn, flush, reps: int, warmup: int = 3) -> float:
     """Average duration (ms) of fn over reps launches, HIP events on the current stream
-    around each launch, caches flushed before each."""
+    around each launch, caches flushed before each. A few flushed launches first: the
+    first ones after a different workload run measurably slower (clock and cache state)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    fn()
+    for _ in range(warmup):
+        flush()
+        fn()
     torch.cuda.synchronize()
     for a, b in ev:
         flush()
@@ -256,9 +259,13 @@ def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
     q, k, v = pc.q.to(dev), pc.k.to(dev), pc.v.to(dev)
     o = torch.empty_like(q)
     sinks = torch.linspace(-2.0, 6.0, pc.num_q_heads, dtype=torch.float32, device=dev)
-    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, sinks=sinks), flush, reps)
     fl = prefill_flops(pc.batch, pc.num_q_heads, pc.seqlen_q, pc.seqlen_k, pc.head_dim)
-    res["prefill_headline_with_sink"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+    # the same launch without the sink, timed right before it as a control (the variants
+    # run after the main workloads, at a different clock than the main prefill loop)
+    ms0 = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
+    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, sinks=sinks), flush, reps)
+    res["prefill_headline_with_sink"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                                         "control_without_sink_ms": round(ms0, 4)}
     del q, k, v, o
     dc8 = workloads.config_decode("fp8_e4m3")
     t8 = dict(q=dc8.q.to(dev), k=dc8.k_cache.to(dev), v=dc8.v_cache.to(dev),
