@@ -225,6 +225,22 @@ class Gen:
         self.emit(f"v_rcp_f32 {v(T2)}, {v(T2)}")
         self.emit("s_nop 0")
         self.emit(f"v_fma_f32 {v(dst)}, {v(T2)}, {v(VM2C)}, {v(CM + rr)}")
+    def softcap_filled(self, r, rr, fillers):
+        """softcap() of score register r in place, with independent instructions (callables
+        from fillers) in the slots after the exp2 and the reciprocal, whose results may not
+        be read by the next instruction; s_nop 0 where no filler is left."""
+        def gap():
+            if fillers:
+                fillers.pop(0)()
+            else:
+                self.emit("s_nop 0")
+        self.emit(f"v_exp_f32 {v(T2)}, {v(r)}")
+        gap()
+        self.emit(f"v_add_f32 {v(T2)}, 1.0, {v(T2)}")
+        self.emit(f"v_rcp_f32 {v(T2)}, {v(T2)}")
+        gap()
+        self.emit(f"v_fma_f32 {v(r)}, {v(T2)}, {v(VM2C)}, {v(CM + rr)}")
+
     def mask(self, src, dst, rr, e):
         """dst = src if key e of row block rr is allowed, else -inf (KBASE set)."""
         off = (e >> 2) * 8 + (e & 3)
@@ -417,15 +433,27 @@ class Gen:
                     # without the products of V, the scores of the last steps are younger
                     self.emit("s_nop 4")
                 # step g: mask score g (odd g: max of the pair); g+1: exp2; g+2: add to the
-                # row sum; 2u+3: pack pair u
-                self.mask_elem(sx, st, masked)
+                # row sum; 2u+3: pack pair u. With a softcap, the exp2 of score g-1 and the
+                # sum of g-2 (independent of score g) fill the two slots of the cap's chain.
+                fill = []
+                if not maxonly:
+                    if st >= 1:
+                        fill.append(lambda g=st - 1: self.exp_elem(sx, g))
+                    if st >= 2:
+                        fill.append(lambda g=st - 2: self.sum_elem(g))
+                if self.mode == 2:
+                    rr_, e_ = st // 16, st % 16
+                    reg = sx + 16 * rr_ + e_
+                    self.softcap_filled(reg, rr_, fill)
+                    if masked:
+                        self.mask(reg, reg, rr_, e_)
+                else:
+                    self.mask_elem(sx, st, masked)
                 if track and st % 2 == 1:
                     self.max_pair(sx, st // 2)
                 if not maxonly:
-                    if st >= 1:
-                        self.exp_elem(sx, st - 1)
-                    if st >= 2:
-                        self.sum_elem(st - 2)
+                    for f in fill:
+                        f()
                     if st >= 3 and st % 2 == 1:
                         self.cvt_pair(px, (st - 3) // 2)
                     if track and st == 16:
