@@ -114,12 +114,18 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, out_path: 
     import glob
 
     def per_kernel(d, counter):
-        vals = {}
+        """Values per kernel name, from the dispatches of its most frequent grid size (a
+        kernel that one measured workload launches is sometimes also launched once, on
+        another shape, by another part of the run)."""
+        by_grid = {}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(path)):
                 if r["Counter_Name"] == counter:
-                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
+                    by_grid.setdefault(r["Kernel_Name"], {}).setdefault(r["Grid_Size"], []).append(
+                        float(r["Counter_Value"]))
+        # the copy kernel keeps all its dispatches: the calibration copy is its largest one
+        return {k: (sum(g.values(), []) if "copyBuffer" in k else max(g.values(), key=len))
+                for k, g in by_grid.items()}
 
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
