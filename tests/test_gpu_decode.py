@@ -27,13 +27,17 @@ def test_small_decode(kv, heads):
     note(f"  stats {s}")
 
 
-def test_f16_decode():
-    case = workloads.make_decode(lengths=[3, 700, 33], num_q_heads=8, num_kv_heads=2, head_dim=128,
-                                 q_dtype="f16", kv_dtype="f16", seed=7)
+@pytest.mark.parametrize("kv,heads", [("f16", (8, 2)), ("fp8_e4m3", (8, 2)), ("fp8_e4m3", (32, 1)), ("f16", (32, 1))],
+                         ids=["f16", "fp8_kv", "fp8_kv_two_tiles", "f16_two_tiles"])
+def test_f16_decode(kv, heads):
+    """f16 queries, over f16 KV or over fp8 KV (codes widened to f16), with one head tile per
+    wave or two."""
+    case = workloads.make_decode(lengths=[3, 700, 33], num_q_heads=heads[0], num_kv_heads=heads[1], head_dim=128,
+                                 q_dtype="f16", kv_dtype=kv, seed=7)
     o, lse = run_decode(case)
     ro, rl = oracle_decode(case)
-    compare(widen(o, "f16"), ro, "f16", "decode f16 O")
-    compare(lse.numpy(), rl, "f16", "decode f16 LSE", lse=True)
+    compare(widen(o, "f16"), ro, decode_kind(case), f"decode f16 {kv} O")
+    compare(lse.numpy(), rl, decode_kind(case), f"decode f16 {kv} LSE", lse=True)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
