@@ -2,7 +2,10 @@
 // block-table KV cache, the key range of each sequence cut into splits that run in
 // separate workgroups, then merged by an LSE-weighted combine.
 //
-// Split kernel: one wave per (split, KV head g, sequence s). The G = Hq/Hkv query
+// Split kernel: one wave per (split, KV head g, sequence s); for fp8 KV with at most 16
+// query heads per KV head, the waves of up to 8 KV heads of one (split, sequence) form a
+// workgroup that loads whole pages contiguously into a shared LDS stage (the head-strided
+// row segments a lone wave reads cost 16% of the page stream's rate). The G = Hq/Hkv query
 // heads that share KV head g are processed together, so every K/V byte is read
 // once; beyond 16 heads per KV head (MQA-like groups) a wave takes two tiles of 16 query
 // heads, which share every K and V fragment read (more than 32 heads: adjacent workgroups
@@ -142,21 +145,33 @@ struct PageLayout {
 
 // HT: query-head tiles of 16 per wave (2 when a KV head has more than 16 query heads:
 // both tiles then share every K and V fragment read, and each page is streamed once).
-template <int KV, bool QBF16, int NST, int HT>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
+// CO: waves per workgroup. CO = 1: each wave streams its own KV head's rows of a page,
+// Hkv row segments of 128 or 256 bytes at a stride of Hkv rows. CO = Hkv > 1: the
+// workgroup holds the Hkv waves of one (split, sequence); wave w loads a contiguous
+// 1/Hkv slice of the whole page (K, then V) into a shared stage, which keeps the memory
+// stream sequential, and then reads its own head's rows from it (one barrier before
+// the stage is refilled, one after its loads land). The stage keeps the page's layout;
+// the 16-byte chunk slots are XOR-swizzled within each row as in the one-wave layout,
+// and for 8-bit KV the even/odd head pair is swapped on odd rows, so the 16 rows of one
+// head still cover all 16 bank groups.
+template <int KV, bool QBF16, int NST, int HT, int CO>
+__global__ __launch_bounds__(64 * CO) void decode_split_kernel(const DecodeParams p) {
   using PL = PageLayout<KV>;
   constexpr bool KBF16 = (KV == KV_FP8) ? QBF16 : (KV == KV_BF16);
   static_assert(KV == KV_FP8 || KBF16 == QBF16, "16-bit K must match the query type");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * PL::STAGE];
+  static_assert(CO == 1 || (HT == 1 && (KV != KV_FP8 || CO % 2 == 0)), "shared stages hold one tile per head");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * CO * PL::STAGE];
+  constexpr int RS = CO * PL::ROW;       // stage bytes between token rows
+  constexpr int KHALF = CO * PL::HALF;   // stage bytes of K (or V)
 
 #if ATTN_DECODE_HEAD_MAJOR
   // the KV heads of one split are adjacent workgroups: the slices of each physical page
   // that belong to different heads are fetched at about the same time
-  const int gt = blockIdx.x;
-  const int split = blockIdx.y;
+  const int gt = CO > 1 ? (int)(blockIdx.y * CO + (threadIdx.x >> 6)) : (int)blockIdx.x;
+  const int split = CO > 1 ? blockIdx.x : blockIdx.y;
 #else
   const int split = blockIdx.x;
-  const int gt = blockIdx.y;
+  const int gt = CO > 1 ? (int)(blockIdx.y * CO + (threadIdx.x >> 6)) : (int)blockIdx.y;
 #endif
   const int wave_tiles = (p.head_tiles + HT - 1) / HT;
   const int g = gt / wave_tiles;  // KV head
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     G[t] = max(0, min(16, p.group - 16 * tile));
   }
   const int s = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int col = lane & 15;   // query column (head h0[t] + col when col < G[t]) / token slot
   const int quad = lane >> 4;  // token slots 4*quad .. 4*quad+3 of the score tile
 
@@ -192,8 +207,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
   const int64_t tok_bytes = (int64_t)p.hkv * PL::ROW;  // bytes between token slots
   const int64_t page_bytes = kPage * tok_bytes;
-  const uint8_t* kc = static_cast<const uint8_t*>(p.k_cache) + (int64_t)g * PL::ROW;
-  const uint8_t* vc = static_cast<const uint8_t*>(p.v_cache) + (int64_t)g * PL::ROW;
+  // CO > 1: the workgroup's KV heads are g0 .. g0+CO-1, this wave's is g0 + wv
+  const int wv = CO > 1 ? (int)(threadIdx.x >> 6) : 0;
+  const int g0 = CO > 1 ? (int)blockIdx.y * CO : g;  // from the block index: wave-uniform
+  const uint8_t* kc = static_cast<const uint8_t*>(p.k_cache) + (int64_t)g0 * PL::ROW;
+  const uint8_t* vc = static_cast<const uint8_t*>(p.v_cache) + (int64_t)g0 * PL::ROW;
+  // stage offset of row r of this wave's head
+  auto row_at = [&](int r) __attribute__((always_inline)) {
+    const int h = CO == 1 ? 0 : (KV == KV_FP8 ? wv ^ (r & 1) : wv);
+    return r * RS + h * PL::ROW;
+  };
   const int32_t* bt = p.block_table + (int64_t)s * p.max_pages;
   float ksc = 1.0f, vsc = 1.0f;
   if constexpr (KV == KV_FP8) {
@@ -202,15 +225,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   }
   const float sl2 = p.scale_log2 * ksc;
 
-  // per-lane load pattern: load i of a half-page fills rows i*ROWS_PER_LOAD + lane/CPR
+  // per-lane load pattern: load i of a half-page fills stage bytes lds_blk(i) .. +1023,
+  // lane l the 16-byte slot l of it; the slot's token row, head and chunk give the
+  // global chunk it holds (the slot and head permutations are their own inverses)
   int ld_row[PL::LOADS], ld_k[PL::LOADS], ld_v[PL::LOADS];
 #pragma unroll
   for (int i = 0; i < PL::LOADS; ++i) {
-    const int row = i * PL::ROWS_PER_LOAD + lane / PL::CPR;
-    const int slot = lane % PL::CPR;
+    const int pos = (wv * PL::LOADS + i) * 64 + lane;  // 16-byte slot within the stage half
+    const int row = pos / (CO * PL::CPR);
+    const int hs = (pos / PL::CPR) % CO;
+    const int h = CO == 1 ? 0 : (KV == KV_FP8 ? hs ^ (row & 1) : hs);
+    const int slot = pos % PL::CPR;
     ld_row[i] = row;
-    ld_k[i] = row * (int)tok_bytes + PL::k_slot(row, slot) * 16;
-    ld_v[i] = row * (int)tok_bytes + PL::v_slot(row, slot) * 16;
+    ld_k[i] = row * (int)tok_bytes + h * PL::ROW + PL::k_slot(row, slot) * 16;
+    ld_v[i] = row * (int)tok_bytes + h * PL::ROW + PL::v_slot(row, slot) * 16;
   }
 
   const int pg0 = t0 / kPage;
@@ -236,14 +264,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     return v;
   };
   auto issue = [&](int pg) __attribute__((always_inline)) {
-    uint8_t* st = ring + ((pg - pg0) % NST) * PL::STAGE;
+    uint8_t* st = ring + ((pg - pg0) % NST) * CO * PL::STAGE + wv * PL::LOADS * 1024;
     const int64_t base = (int64_t)phys_page(pg - pg0) * page_bytes;
     const int valid = t1 - pg * kPage;  // rows past the end re-read the last valid row
 #pragma unroll
     for (int i = 0; i < PL::LOADS; ++i) {
       const int shift = valid >= kPage ? 0 : (min(ld_row[i], valid - 1) - ld_row[i]) * (int)tok_bytes;
       load_lds16_stream(kc + base, (uint32_t)(ld_k[i] + shift), st + i * 1024);
-      load_lds16_stream(vc + base, (uint32_t)(ld_v[i] + shift), st + PL::HALF + i * 1024);
+      load_lds16_stream(vc + base, (uint32_t)(ld_v[i] + shift), st + KHALF + i * 1024);
     }
   };
 
@@ -263,6 +291,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     if (pg0 + i < pg1) issue(pg0 + i);
 
   for (int pg = pg0; pg < pg1; ++pg) {
+    if constexpr (CO > 1 && NST >= 3) {
+      // one barrier per page: this wave's loads of page pg are done once at most those of
+      // the NST-2 later pages remain; after the barrier every wave's are, and every wave
+      // is done with page pg-1, whose stage the next issue refills
+      if (pg + NST - 2 < pg1) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PL::LOADS * (NST - 2)) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (pg + NST - 1 < pg1) issue(pg + NST - 1);
+    } else {
+    // every wave is done reading the stage the next issue refills
+    if constexpr (CO > 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (pg + NST - 1 < pg1) {
       issue(pg + NST - 1);
       // the loads of this page are complete once at most those of the NST-1 later pages
@@ -275,8 +317,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    const uint8_t* kst = ring + ((pg - pg0) % NST) * PL::STAGE;
-    const uint8_t* vst = kst + PL::HALF;
+    // every wave's loads of this page have landed
+    if constexpr (CO > 1) asm volatile("s_barrier" ::: "memory");
+    }
+    const uint8_t* kst = ring + ((pg - pg0) % NST) * CO * PL::STAGE;
+    const uint8_t* vst = kst + KHALF;
 
     // scores S^T[slot][query] = K . Q^T, each K fragment feeding every tile
     f32x4_t sc[HT];
@@ -287,7 +332,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       for (int j = 0; j < 2; ++j) {
         // 16 codes = head_dim 32*quad + 16*j .. +15 of token slot `col`
         const int c = 2 * quad + j;
-        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kst + col * PL::ROW + PL::k_slot(col, c) * 16);
+        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kst + row_at(col) + PL::k_slot(col, c) * 16);
         const u32x4_t k0 = fp8x8_to_16<QBF16>(u32x2_t{raw[0], raw[1]});
         const u32x4_t k1 = fp8x8_to_16<QBF16>(u32x2_t{raw[2], raw[3]});
 #pragma unroll
@@ -300,7 +345,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int c = 4 * quad + ks;
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kst + col * PL::ROW + PL::k_slot(col, c) * 16);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kst + row_at(col) + PL::k_slot(col, c) * 16);
 #pragma unroll
         for (int t = 0; t < HT; ++t) sc[t] = mfma16x16x32<QBF16>(a, qf[t][ks], sc[t]);
       }
@@ -352,7 +397,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       const int vpar = col & 1;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const i32x2_t w = lds_read_tr8(vst + vkey * PL::ROW + PL::v_slot(vkey, db) * 16 + 8 * vpar);
+        const i32x2_t w = lds_read_tr8(vst + row_at(vkey) + PL::v_slot(vkey, db) * 16 + 8 * vpar);
         const u32x2_t vw = fp8x4_to_16<QBF16>(w[0]);
 #pragma unroll
         for (int t = 0; t < HT; ++t) o[t][db] = mfma16x16x16<KBF16>(vw, pb[t], o[t][db]);
@@ -373,7 +418,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const int c = 2 * db + (vc2 >> 1);
-        const u32x2_t a = lds_read_tr16(vst + vr * PL::ROW + PL::v_slot(vr, c) * 16 + (vc2 & 1) * 8);
+        const u32x2_t a = lds_read_tr16(vst + row_at(vr) + PL::v_slot(vr, c) * 16 + (vc2 & 1) * 8);
 #pragma unroll
         for (int t = 0; t < HT; ++t) o[t][db] = mfma16x16x16<KBF16>(a, pb[t], o[t][db]);
       }
@@ -447,20 +492,54 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
 constexpr int kStages16 = ATTN_DECODE_STAGES;     // 16-bit KV, 8 KiB per stage
 constexpr int kStages8 = ATTN_DECODE_STAGES_FP8;  // fp8 KV, 4 KiB per stage
 
+#ifndef ATTN_DECODE_COOP
+#define ATTN_DECODE_COOP 1
+#endif
+// KV kinds whose split kernel runs as one workgroup of Hkv waves per (split, sequence)
+// (bit 0: fp8; bit 1: 16-bit) when Hkv is 2, 4 or 8 and a KV head has at most 16 query heads.
+constexpr int kCoopKinds = ATTN_DECODE_COOP;
+#ifndef ATTN_DECODE_COOP_WAVES
+#define ATTN_DECODE_COOP_WAVES 8
+#endif
+constexpr int kCoopWaves = ATTN_DECODE_COOP_WAVES;  // at most this many KV heads per workgroup
+#ifndef ATTN_DECODE_STAGES_COOP
+#define ATTN_DECODE_STAGES_COOP 2
+#endif
+constexpr int kStagesCoop = ATTN_DECODE_STAGES_COOP;  // whole-page stages per workgroup
+
+template <int KV, bool QBF16, int NST, int CO>
+hipError_t launch_coop(const DecodeParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, NST, 1, CO>), dim3(p.max_splits, p.hkv / CO, p.num_seqs), dim3(64 * CO),
+                     0, st, p);
+  return hipGetLastError();
+}
+
 template <int KV, bool QBF16>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const bool two = p.head_tiles >= 2;  // more than 16 query heads per KV head
   const int wave_tiles = two ? (p.head_tiles + 1) / 2 : p.head_tiles;
+  constexpr int nst = KV == KV_FP8 ? kStages8 : kStages16;
+  const int co = min(p.hkv & -p.hkv, kCoopWaves);  // a power of two that divides Hkv
+  const bool coop = (kCoopKinds & (KV == KV_FP8 ? 1 : 2)) && p.head_tiles == 1 && co >= 2;
+  if (coop) {
+    // a 16-bit page of 8 heads is 64 KiB: two stages fill most of the 160 KiB
+    constexpr int cst = KV == KV_FP8 ? kStagesCoop : 2;
+    const hipError_t e = co == 8   ? launch_coop<KV, QBF16, cst, 8>(p, st)
+                         : co == 4 ? launch_coop<KV, QBF16, cst, 4>(p, st)
+                                   : launch_coop<KV, QBF16, cst, 2>(p, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<QBF16>), dim3(p.num_seqs * p.hq), dim3(64), 0, st, p);
+    return hipGetLastError();
+  }
 #if ATTN_DECODE_HEAD_MAJOR
   dim3 grid(p.hkv * wave_tiles, p.max_splits, p.num_seqs);
 #else
   dim3 grid(p.max_splits, p.hkv * wave_tiles, p.num_seqs);
 #endif
-  constexpr int nst = KV == KV_FP8 ? kStages8 : kStages16;
   if (two)
-    hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst, 2>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst, 2, 1>), grid, dim3(64), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst, 1>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, nst, 1, 1>), grid, dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<QBF16>), dim3(p.num_seqs * p.hq), dim3(64), 0, st, p);
