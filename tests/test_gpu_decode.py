@@ -13,7 +13,9 @@ SMALL_LENGTHS = [1, 15, 16, 17, 100, 1000, 4099, 257]
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
-@pytest.mark.parametrize("heads", [(32, 8), (8, 8), (16, 1), (4, 2)])
+# (16, 16), (12, 12), (16, 4), (24, 6): fp8 workgroups of 8, 4, 4 and 2 KV-head waves that
+# cover part of the KV heads each (2, 3, 1 and 3 groups per split)
+@pytest.mark.parametrize("heads", [(32, 8), (8, 8), (16, 1), (4, 2), (16, 16), (12, 12), (16, 4), (24, 6)])
 def test_small_decode(kv, heads):
     hq, hkv = heads
     case = workloads.make_decode(lengths=SMALL_LENGTHS, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
