@@ -588,3 +588,69 @@ def test_backward_closed_forms():
     dq, dk, dv = oracle.sdpa_backward_fp64(q, k3, _rand(1, 5, 4), do, scale=0.5)
     np.testing.assert_allclose(dv[0], np.tile(do.sum(axis=(0, 1)) / 5, (5, 1)), atol=1e-14)
     assert np.abs(dq).max() < 1e-13
+
+
+# ------------------------------------------------- probabilities and batched backward ----
+
+@pytest.mark.parametrize("hq,hkv,nq,nk,d", [(2, 1, 5, 7, 3), (4, 2, 6, 6, 4), (3, 3, 4, 9, 2)])
+@pytest.mark.parametrize("causal,window,softcap", [(False, 0, 0.0), (True, 0, 0.0), (True, 2, 0.0),
+                                                   (False, 0, 1.5), (True, 3, 2.0)])
+def test_probabilities_equal_brute_force_weights(hq, hkv, nq, nk, d, causal, window, softcap):
+    # With V the Nk x Nk identity, row i of O = P V is row i of P itself, so the scalar
+    # brute force (math.fsum / math.exp loops) hands back the weight matrix entry by entry.
+    q, k = _rand(hq, nq, d, scale=1.5), _rand(hkv, nk, d, scale=1.5)
+    scale = oracle.default_scale(d)
+    eye = [np.eye(nk).tolist() for _ in range(hkv)]
+    ob, _ = brute.brute_sdpa(_tolist(q), _tolist(k), eye, scale=scale, causal=causal, window=window,
+                             softcap=softcap)
+    p = oracle.attention_probs(q, k, scale=scale, causal=causal, window=window, softcap=softcap)
+    np.testing.assert_allclose(p, np.array(ob), rtol=0, atol=1e-13)
+    # and P V is the definition's O for any V
+    v = _rand(hkv, nk, 5)
+    o, _ = oracle.sdpa_fp64(q, k, v, scale=scale, causal=causal, window=window, softcap=softcap)
+    group = hq // hkv
+    pv = np.stack([p[h] @ v[h // group] for h in range(hq)])
+    np.testing.assert_allclose(pv, o, rtol=0, atol=1e-12)
+
+
+def test_probabilities_of_two_keys_are_logistic():
+    # two keys: P_0 = 1 / (1 + exp(s_1 - s_0)) with s_j = c tanh(scale q.k_j / c)
+    q = np.array([[[1.0, 2.0]]])
+    k = np.array([[[0.5, -1.0], [2.0, 1.5]]])
+    for scale, cap in ((0.7, 0.0), (0.7, 1.25), (1.3, 0.5)):
+        raw = np.array([1.0 * 0.5 + 2.0 * -1.0, 1.0 * 2.0 + 2.0 * 1.5]) * scale
+        s = cap * np.tanh(raw / cap) if cap > 0 else raw
+        p0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+        p = oracle.attention_probs(q, k, scale=scale, softcap=cap)
+        np.testing.assert_allclose(p[0, 0], [p0, 1.0 - p0], rtol=0, atol=1e-15)
+
+
+def test_batched_backward_equals_per_batch_and_finite_differences():
+    # B = 2 with distinct inputs per batch entry, a sink and a causal mask: the batched
+    # wrapper must hand each entry its own q, k, v and dO.
+    b_, hq, hkv, n, d = 2, 4, 2, 5, 3
+    q, k, v, do = _rand(b_, hq, n, d), _rand(b_, hkv, n, d), _rand(b_, hkv, n, d), _rand(b_, hq, n, d)
+    sink = np.array([0.4, -0.8, 1.5, 0.0])
+    kw = dict(scale=0.6, causal=True, sink=sink)
+    dq, dk, dv = oracle.prefill_backward_dense(q, k, v, do, **kw)
+    for b in range(b_):
+        rq, rk, rv = oracle.sdpa_backward_fp64(q[b], k[b], v[b], do[b], **kw)
+        np.testing.assert_allclose(dq[b], rq, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(dk[b], rk, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(dv[b], rv, rtol=0, atol=1e-15)
+
+    # central differences of sum(dO * O) through the batched forward (prefill_dense)
+    def loss(qq, kk, vv):
+        o, _ = oracle.prefill_dense(qq, kk, vv, scale=0.6, causal=True, sink=sink)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            num[idx] = (loss(*[xp if a is x else a for a in (q, k, v)])
+                        - loss(*[xm if a is x else a for a in (q, k, v)])) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7)
