@@ -233,10 +233,13 @@ def bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
         lse: torch.Tensor, *, causal: bool = False, window: int = 0, softcap: float = 0.0,
-        softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None):
+        softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+        dq_out: Optional[torch.Tensor] = None, dk_out: Optional[torch.Tensor] = None,
+        dv_out: Optional[torch.Tensor] = None):
     """Gradients of fwd for dense batches: q, o, dout [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D]
     (contiguous, bf16/f16); lse float32 [B, Hq, Nq] from fwd(..., return_lse=True).
-    Returns (dq, dk, dv)."""
+    Returns (dq, dk, dv), written into dq_out / dk_out / dv_out when given (contiguous,
+    shapes and dtype of q, k, v)."""
     _require_cuda(q, k, v, o, dout, lse)
     for t in (q, k, v, o, dout, lse):
         if not t.is_contiguous():
@@ -261,7 +264,13 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout
     need = int(L.attn_bwd_workspace_size(ctypes.byref(a)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    grads = []
+    for given, like, name in ((dq_out, q, "dq_out"), (dk_out, k, "dk_out"), (dv_out, v, "dv_out")):
+        g = torch.empty_like(like) if given is None else given
+        if g.shape != like.shape or g.dtype != like.dtype or not g.is_contiguous() or g.device != like.device:
+            raise ValueError(f"{name} must be contiguous with the shape and dtype of its input")
+        grads.append(g)
+    dq, dk, dv = grads
     status = L.attn_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
                         _stream_handle(q.device))
@@ -301,13 +310,14 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                  seq_lens: torch.Tensor, max_seq_len: int, *, k_scale: Optional[torch.Tensor] = None,
                  v_scale: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, num_splits: int = 0,
                  return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
-                 out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                 sinks: Optional[torch.Tensor] = None):
     """Paged split-KV decode.
 
     q [S, Hq, D]; k_cache/v_cache [P, 16, Hkv, D] (bf16/f16, or float8_e4m3fn with
     float32 k_scale/v_scale [Hkv]); block_table int32 [S, max_pages]; seq_lens int32
     [S]; max_seq_len a host-side bound of seq_lens. Returns o [S, Hq, D] (and lse
-    [S, Hq] float32 if return_lse).
+    [S, Hq] float32 if return_lse), written into out / lse_out when given.
     """
     _require_cuda(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks)
     for t in (q, k_cache, v_cache, block_table, seq_lens):
@@ -337,7 +347,11 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     o = torch.empty_like(q) if out is None else out
     if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
         raise ValueError("out must match q")
-    lse = torch.empty((S, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = None
+    if return_lse:
+        lse = torch.empty((S, hq), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+        if lse.shape != (S, hq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse_out must be a contiguous float32 tensor of shape ({S}, {hq})")
     status = L.attn_decode_paged(ctypes.byref(a), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                  _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), _ptr(o), _ptr(lse),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),

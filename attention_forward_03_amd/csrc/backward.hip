@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
 __device__ __forceinline__ void load_lds4(const void* base, uint32_t voff, const void* lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Direct-to-LDS load of one row-major tile of ROWS rows x D (16-bit) into LDS, swizzled

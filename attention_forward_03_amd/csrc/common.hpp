@@ -92,12 +92,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // Written as inline asm: with the compiler builtin for this load, every later
 // transposing LDS read (ds_read_b64_tr_b16) is made to wait for all loads still in
 // flight, which would serialise the K/V prefetch with the P.V product. Completion is
-// awaited explicitly (s_waitcnt vmcnt) by the callers. M0 carries the LDS base and is
-// written only here (no compiler-generated code in these kernels uses M0).
+// awaited explicitly (s_waitcnt vmcnt) by the callers. M0 carries the LDS base; the
+// statement lists it as clobbered, so the compiler keeps no value of its own there.
 __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, const void* lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // The same load with the nontemporal hint: for data read once (the paged KV cache in
@@ -107,7 +107,7 @@ __device__ __forceinline__ void load_lds16_stream(const void* base, uint32_t vof
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base),
                "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Wait (visibly to the compiler) for this wave's ordinary global loads, so that the

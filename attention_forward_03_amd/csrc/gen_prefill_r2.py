@@ -944,9 +944,9 @@ def render(lines):
 def clobbers():
     regs = [f'"v{i}"' for i in range(24, NVGPR)] + [f'"a{i}"' for i in range(192)]
     regs += [f'"s{i}"' for i in range(NSGPR_LO, NSGPR_HI)]
-    # m0 and exec are written too (m0 for the LDS-DMA loads, exec around the row-masked
-    # stores, restored); nothing follows the statement in the kernel, so they are not listed
-    regs += ['"vcc"', '"scc"', '"memory"']
+    # m0 is written for the LDS-DMA loads; exec is written around the row-masked stores and
+    # restored before the statement ends
+    regs += ['"vcc"', '"scc"', '"m0"', '"memory"']
     return ", ".join(regs)
 
 

@@ -232,7 +232,8 @@ attn_status_t attn_bwd(const attn_bwd_args_t *args, const void *q, const void *k
 typedef struct {
   int32_t num_seqs;          /* S >= 1 */
   int32_t num_q_heads;       /* Hq */
-  int32_t num_kv_heads;      /* Hkv, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16 */
+  int32_t num_kv_heads;      /* Hkv, Hq % Hkv == 0 (any group size: more than 16 query heads per
+                                KV head take 16-head tiles in pairs); Hkv * ceil(Hq/Hkv / 16) <= 65535 */
   int32_t head_dim;          /* D == 128 */
   int32_t page_size;         /* tokens per page; must be 16 */
   int32_t max_pages_per_seq; /* row length of block_table */

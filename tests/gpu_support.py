@@ -75,6 +75,28 @@ def compare(got: np.ndarray, ref: np.ndarray, kind: str, what: str, lse: bool = 
     return stats
 
 
+# ------------------------------------------------------------------- poisoned outputs ----
+
+GUARD = 4096  # elements of NaN on each side of an output buffer
+
+
+class Guarded:
+    """An output tensor that starts as NaN, with NaN guard bands of GUARD elements on both
+    sides in the same allocation: an entry the kernels leave unwritten stays NaN (and fails
+    the comparison), and a write past either end changes a guard."""
+
+    def __init__(self, shape, dtype, device="cuda"):
+        n = int(np.prod(shape))
+        self.n = n
+        self.buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=dtype, device=device)
+        self.t = self.buf[GUARD:GUARD + n].view(shape)
+
+    def check_guards(self, what: str) -> None:
+        b = self.buf.detach().cpu().float()
+        lo, hi = b[:GUARD], b[GUARD + self.n:]
+        assert bool(torch.isnan(lo).all()) and bool(torch.isnan(hi).all()), f"{what}: a guard band was written"
+
+
 # ---------------------------------------------------------------------------- prefill ----
 
 def _dev_sinks(sinks):
@@ -90,8 +112,11 @@ def run_prefill(case, *, return_lse=True, out=None, sinks=None):
         kw.update(cu_seqlens_q=torch.from_numpy(case.cu_seqlens_q).cuda(),
                   cu_seqlens_k=torch.from_numpy(case.cu_seqlens_k).cuda(),
                   max_seqlen_q=case.seqlen_q, max_seqlen_k=case.seqlen_k)
-    # the output starts as NaN: an entry the kernels leave unwritten fails the comparison
+    # the outputs start as NaN: an entry the kernels leave unwritten fails the comparison
     kw["out"] = torch.full(q.shape, float("nan"), dtype=q.dtype, device=q.device) if out is None else out
+    if return_lse:
+        lse_shape = (q.shape[1], q.shape[0]) if case.varlen else tuple(q.shape[:3])
+        kw["lse_out"] = torch.full(lse_shape, float("nan"), dtype=torch.float32, device=q.device)
     res = attn.fwd(q, k, v, **kw)
     torch.cuda.synchronize()
     if return_lse:
@@ -176,10 +201,18 @@ def decode_tensors(case):
 def run_decode(case, tensors=None, *, num_splits=0, sinks=None):
     import attention_forward_03_amd as attn
     t = decode_tensors(case) if tensors is None else tensors
+    # O and LSE start as NaN inside NaN guard bands (the caching allocator would otherwise
+    # hand a call the previous call's block, and rows a plan left unwritten could pass)
+    go = Guarded(t["q"].shape, t["q"].dtype)
+    gl = Guarded((t["q"].shape[0], t["q"].shape[1]), torch.float32)
     o, lse = attn.decode_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"],
                                case.max_seq_len, k_scale=t.get("k_scale"), v_scale=t.get("v_scale"),
-                               num_splits=num_splits, return_lse=True, sinks=_dev_sinks(sinks))
+                               num_splits=num_splits, return_lse=True, sinks=_dev_sinks(sinks),
+                               out=go.t, lse_out=gl.t)
     torch.cuda.synchronize()
+    assert o.data_ptr() == go.t.data_ptr() and lse.data_ptr() == gl.t.data_ptr()
+    go.check_guards("decode O")
+    gl.check_guards("decode LSE")
     return o.cpu(), lse.cpu()
 
 

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_support import compare, note, widen
+from gpu_support import Guarded, compare, note, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -16,8 +16,13 @@ def _run(case, dout, sinks=None):
     q, k, v = case.q.cuda(), case.k.cuda(), case.v.cuda()
     kw = dict(causal=case.causal, window=case.window, softcap=case.softcap)
     o, lse = attn.fwd(q, k, v, return_lse=True, sinks=None if sinks is None else torch.as_tensor(sinks).cuda(), **kw)
-    dq, dk, dv = attn.bwd(q, k, v, o, dout.cuda(), lse, **kw)
+    # gradients start as NaN inside NaN guard bands: an entry left unwritten fails the
+    # comparison, a write past either end changes a guard
+    g = [Guarded(x.shape, x.dtype) for x in (q, k, v)]
+    dq, dk, dv = attn.bwd(q, k, v, o, dout.cuda(), lse, dq_out=g[0].t, dk_out=g[1].t, dv_out=g[2].t, **kw)
     torch.cuda.synchronize()
+    for name, gg in zip(("dQ", "dK", "dV"), g):
+        gg.check_guards(name)
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 

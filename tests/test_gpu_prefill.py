@@ -38,6 +38,18 @@ def test_dense_noncausal_shapes(dtype, d, shape):
     check_prefill_full(case, f"dense {dtype} D{d} {shape}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(2, 4, 2, 512, 512), (2, 4, 2, 1024, 1024), (1, 4, 2, 300, 512), (1, 2, 2, 1, 64)])
+def test_dense_no_mask_d128(dtype, shape):
+    """D = 128, dense, non-causal, no window or softcap, Nk a multiple of 64: the form of the
+    D = 128 kernel with no mask at all (whole key tiles, no per-row maxima), every output."""
+    b, hq, hkv, nq, nk = shape
+    case = workloads.make_prefill(batch=b, num_q_heads=hq, num_kv_heads=hkv, seqlen_q=nq, seqlen_k=nk,
+                                  head_dim=128, dtype=dtype, seed=zlib.crc32(repr(("nomask", dtype, shape)).encode()))
+    stats = check_prefill_full(case, f"no-mask {dtype} {shape}")
+    note(f"  stats {stats}")
+
+
 MASKS = [  # (causal, window, softcap)
     (True, 0, 0.0),
     (True, 1, 0.0),
@@ -161,6 +173,32 @@ def test_dominance_probe_selects_target_row_bit_exactly(dtype):
                 want = case.v[b, h // group][torch.from_numpy(np.asarray(targets)).long()]
                 got = o[b, h]
                 same = (got.view(torch.int16) == want.view(torch.int16)) if dtype != "f32" else (got == want)
+                assert bool(same.all()), f"{name}: b={b} h={h} first bad row {int((~same.all(1)).nonzero()[0])}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_dominance_probe_no_mask_redo(dtype):
+    """N = 512, dense and non-causal: the no-mask D = 128 kernel. Its rows take the max of
+    their first 32 keys as the softmax reference; a target later in the row scores at least
+    512 * scale * log2(e) = 65 log2 units above every key that shares fewer of its digits,
+    beyond the slack (15 for f16, 40 for bf16), so the pass runs again against the exact
+    row maxima. The output must still be the target's V row bit for bit."""
+    n = 512
+    rng = np.random.default_rng(8)
+    cases = {
+        "random": rng.integers(0, n, size=n),
+        "last": np.full(n, n - 1),
+        "late-half": rng.integers(n // 2, n, size=n),
+        "first": np.zeros(n, dtype=np.int64),  # inside the first sub-tile: no second pass
+    }
+    for name, targets in cases.items():
+        note(f"[probe] no-mask {dtype} {name}")
+        case, o = _probe(targets, dtype=dtype, n=n)
+        group = case.num_q_heads // case.num_kv_heads
+        for b in range(case.batch):
+            for h in range(case.num_q_heads):
+                want = case.v[b, h // group][torch.from_numpy(np.asarray(targets)).long()]
+                same = o[b, h].view(torch.int16) == want.view(torch.int16)
                 assert bool(same.all()), f"{name}: b={b} h={h} first bad row {int((~same.all(1)).nonzero()[0])}"
 
 
