@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, AttnInvalidValue, AttnNotSupported
 
-__all__ = ["fwd", "fwd_paged", "bwd", "bwd_workspace_size", "fwd_paged_workspace_size", "decode_paged", "decode_plan", "decode_workspace_size", "library_path",
+__all__ = ["fwd", "fwd_paged", "bwd", "bwd_workspace_size", "fwd_paged_workspace_size", "decode_paged", "decode_paged_noalloc", "decode_plan", "decode_workspace_size", "library_path",
            "AttnError", "AttnInvalidValue", "AttnNotSupported"]
 
 _DTYPES = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
@@ -358,6 +358,49 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                                  _stream_handle(q.device))
     _lib.check(status)
     return (o, lse) if return_lse else o
+
+
+DECODE_NOALLOC_MAX_WORKSPACE = 64 << 20  # bytes: ATTN_DECODE_NOALLOC_MAX_WORKSPACE of include/attn.h
+
+
+def decode_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, *, out: torch.Tensor, lse_out: Optional[torch.Tensor] = None,
+                         k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                         softmax_scale: float = 0.0, num_splits: int = 0, sinks: Optional[torch.Tensor] = None):
+    """decode_paged through attn_decode_paged_noalloc: no workspace, and the caller passes the
+    outputs (out [S, Hq, D] in q's dtype, optional lse_out float32 [S, Hq]), so the call
+    allocates nothing. The per-split partials go to the library's own per-GPU scratch array
+    (at most DECODE_NOALLOC_MAX_WORKSPACE bytes; calls that overlap on one GPU race)."""
+    _require_cuda(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, out, lse_out)
+    for t in (q, k_cache, v_cache, block_table, seq_lens, out):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must be [P, page, Hkv, D] of one dtype")
+    S, hq, d = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_table must be [S, max_pages] and seq_lens [S]")
+    if k_cache.shape[3] != d:
+        raise ValueError("head_dim mismatch between q and the caches")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse_out is not None and (lse_out.shape != (S, hq) or lse_out.dtype != torch.float32
+                                or not lse_out.is_contiguous()):
+        raise ValueError(f"lse_out must be a contiguous float32 tensor of shape ({S}, {hq})")
+    for sc in (k_scale, v_scale):
+        if sc is not None and (sc.dtype != torch.float32 or not sc.is_contiguous()):
+            raise ValueError("k_scale / v_scale must be contiguous float32")
+    a = _decode_args(num_seqs=S, num_q_heads=hq, num_kv_heads=k_cache.shape[2], head_dim=d,
+                     max_pages_per_seq=block_table.shape[1], max_seq_len=max_seq_len, q_dtype=q.dtype,
+                     kv_dtype=k_cache.dtype, softmax_scale=softmax_scale, num_splits=num_splits,
+                     page_size=k_cache.shape[1], sinks=_sinks_ptr(sinks, hq))
+    status = _lib.lib().attn_decode_paged_noalloc(ctypes.byref(a), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                  _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+                                                  _ptr(out), _ptr(lse_out), _stream_handle(q.device))
+    _lib.check(status)
+    return (out, lse_out) if lse_out is not None else out
 
 
 # ----------------------------------------------------------------- measurement ----

@@ -20,6 +20,7 @@ ATTN_FP8_E4M3 = 3
 
 EXPORTED = ("attn_fwd", "attn_fwd_paged", "attn_fwd_paged_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
             "attn_decode_plan", "attn_decode_paged_workspace_size", "attn_decode_paged",
+            "attn_decode_paged_noalloc",
             "attn_probe_mfma", "attn_probe_hbm_read", "attn_flush_caches",
             "attn_status_string", "attn_last_error_message", "attn_abi_version")
 
@@ -133,6 +134,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs)] + [ctypes.c_void_p] * 9 + \
         [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.attn_decode_paged.restype = ctypes.c_int
+    L.attn_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodeArgs)] + [ctypes.c_void_p] * 10
+    L.attn_decode_paged_noalloc.restype = ctypes.c_int
     L.attn_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
     L.attn_probe_mfma.restype = ctypes.c_int

@@ -12,6 +12,9 @@
 #include "../../include/attn.h"
 #include "internal.hpp"
 
+static_assert(ATTN_DECODE_NOALLOC_MAX_WORKSPACE == attn::kDecodeScratchBytes,
+              "the header states the scratch size the library is built with");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -484,6 +487,33 @@ size_t attn_decode_paged_workspace_size(const attn_decode_args_t* a) {
   return o_bytes + l_bytes;
 }
 
+// Checks of the decode call's tensors (not of the workspace), on the host.
+static attn_status_t check_decode_tensors(const attn_decode_args_t* a, const void* q, const void* k_cache,
+                                          const void* v_cache, const float* k_scale, const float* v_scale,
+                                          const int32_t* block_table, const int32_t* seq_lens, const void* o,
+                                          const float* lse) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || o == nullptr)
+    return fail(ATTN_ERROR_INVALID_VALUE, "q, k_cache, v_cache, block_table, seq_lens and o must be non-NULL");
+  const bool fp8 = a->kv_dtype == ATTN_FP8_E4M3;
+  if (fp8 && (k_scale == nullptr || v_scale == nullptr))
+    return fail(ATTN_ERROR_INVALID_VALUE, "fp8 KV needs k_scale and v_scale");
+  if (!fp8 && (k_scale != nullptr || v_scale != nullptr))
+    return fail(ATTN_ERROR_INVALID_VALUE, "k_scale / v_scale are only accepted with fp8 KV");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERROR_NOT_SUPPORTED, "q, caches and o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(ATTN_ERROR_INVALID_VALUE, "block_table, seq_lens and lse must be 4-byte aligned");
+  return ATTN_SUCCESS;
+}
+
+// The decode launch on a checked call with a workspace of at least the planned size.
+static attn_status_t decode_launch(const attn_decode_args_t* a, int32_t split_len, int32_t max_splits,
+                                   const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                   void* o, float* lse, void* workspace, void* stream);
+
 attn_status_t attn_decode_paged(const attn_decode_args_t* a, const void* q, const void* k_cache,
                                 const void* v_cache, const float* k_scale, const float* v_scale,
                                 const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
@@ -491,23 +521,44 @@ attn_status_t attn_decode_paged(const attn_decode_args_t* a, const void* q, cons
   int32_t split_len = 0, max_splits = 0;
   attn_status_t st = attn_decode_plan(a, &split_len, &max_splits);
   if (st != ATTN_SUCCESS) return st;
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
-      seq_lens == nullptr || o == nullptr || workspace == nullptr)
-    return fail(ATTN_ERROR_INVALID_VALUE,
-                "q, k_cache, v_cache, block_table, seq_lens, o and workspace must be non-NULL");
-  const bool fp8 = a->kv_dtype == ATTN_FP8_E4M3;
-  if (fp8 && (k_scale == nullptr || v_scale == nullptr))
-    return fail(ATTN_ERROR_INVALID_VALUE, "fp8 KV needs k_scale and v_scale");
-  if (!fp8 && (k_scale != nullptr || v_scale != nullptr))
-    return fail(ATTN_ERROR_INVALID_VALUE, "k_scale / v_scale are only accepted with fp8 KV");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
-    return fail(ATTN_ERROR_NOT_SUPPORTED, "q, caches, o and workspace must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
-      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-    return fail(ATTN_ERROR_INVALID_VALUE, "block_table, seq_lens and lse must be 4-byte aligned");
+  st = check_decode_tensors(a, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse);
+  if (st != ATTN_SUCCESS) return st;
+  if (workspace == nullptr) return fail(ATTN_ERROR_INVALID_VALUE, "workspace must be non-NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERROR_NOT_SUPPORTED, "workspace must be 16-byte aligned");
   const size_t need = attn_decode_paged_workspace_size(a);
   if (workspace_bytes < need)
     return fail(ATTN_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return decode_launch(a, split_len, max_splits, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o,
+                       lse, workspace, stream);
+}
+
+attn_status_t attn_decode_paged_noalloc(const attn_decode_args_t* a, const void* q, const void* k_cache,
+                                        const void* v_cache, const float* k_scale, const float* v_scale,
+                                        const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                        void* stream) {
+  int32_t split_len = 0, max_splits = 0;
+  attn_status_t st = attn_decode_plan(a, &split_len, &max_splits);
+  if (st != ATTN_SUCCESS) return st;
+  st = check_decode_tensors(a, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse);
+  if (st != ATTN_SUCCESS) return st;
+  const size_t need = attn_decode_paged_workspace_size(a);
+  if (need > attn::kDecodeScratchBytes)
+    return fail(ATTN_ERROR_WORKSPACE_TOO_SMALL,
+                "these arguments need %zu bytes of partial results; the built-in scratch holds %zu "
+                "(use attn_decode_paged with a workspace)",
+                need, (size_t)attn::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = attn::decode_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(ATTN_ERROR_LAUNCH_FAILED, "locating the decode scratch failed: %s", hipGetErrorString(e));
+  return decode_launch(a, split_len, max_splits, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o,
+                       lse, scratch, stream);
+}
+
+static attn_status_t decode_launch(const attn_decode_args_t* a, int32_t split_len, int32_t max_splits,
+                                   const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                   void* o, float* lse, void* workspace, void* stream) {
 
   attn::DecodeParams p{};
   p.q = q;

@@ -23,6 +23,7 @@
 // 2^{lse_k - LSE} O_k. Split-KV decode over a paged cache and the fp8 KV precision
 // are scenario axes of "Ask, Don't Equip: Question-Driven Coding Agents for Deep
 // Kernel Optimization", section 研究动机.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -547,6 +548,36 @@ hipError_t launch(const DecodeParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// Per-split partial results of the allocation-free decode entry point: a file-scope
+// device array, one copy per GPU, held until the process ends. Its name is only a
+// host-side stand-in for the symbol; kernels receive the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // q_dtype: 1 = f16, 2 = bf16; kv_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t st) {

@@ -106,6 +106,11 @@ hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, cons
                                   const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,
                                   int num_pages, int page_bytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t stream);
+// Bytes of the device scratch array behind attn_decode_paged_noalloc (per GPU): the
+// header's ATTN_DECODE_NOALLOC_MAX_WORKSPACE.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+// Device address of that array on the current device (looked up once per device).
+hipError_t decode_scratch(void** ptr);
 
 hipError_t launch_probe_mfma(const uint32_t* operands, int workgroups, int iters, int valu_mix, uint64_t* clocks,
                              float* sink, hipStream_t stream);

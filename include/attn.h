@@ -281,6 +281,32 @@ attn_status_t attn_decode_paged(const attn_decode_args_t *args, const void *q, c
                                 const int32_t *block_table, const int32_t *seq_lens, void *o,
                                 float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * attn_decode_paged_noalloc - attn_decode_paged for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, results and kernels, without the workspace. The
+ * per-split partial results go to a scratch array built into the library, one copy per
+ * GPU, which the process holds until it ends; no call allocates or frees anything.
+ *
+ *   Limit: attn_decode_paged_workspace_size(args) must not exceed
+ *          ATTN_DECODE_NOALLOC_MAX_WORKSPACE bytes (64 MiB); larger calls return
+ *          ATTN_ERROR_WORKSPACE_TOO_SMALL and enqueue nothing. The 64-sequence,
+ *          32768-token, Hq = 32 decode needs 34 MB.
+ *   Sharing: every call on one GPU uses that GPU's one scratch array, so calls that can
+ *          overlap on one GPU (on different streams, or from several host threads without
+ *          ordering) race and may return wrong results. Calls on one stream are ordered
+ *          and safe. The array keeps the last call's contents; nothing in it needs to
+ *          start at zero (every partial a call reads is written by the same call).
+ *   Set-up: the first call on a device looks up the array's address on that device
+ *          (the device current at the call) and keeps it; a failure there returns
+ *          ATTN_ERROR_LAUNCH_FAILED.
+ */
+#define ATTN_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+attn_status_t attn_decode_paged_noalloc(const attn_decode_args_t *args, const void *q, const void *k_cache,
+                                        const void *v_cache, const float *k_scale, const float *v_scale,
+                                        const int32_t *block_table, const int32_t *seq_lens, void *o,
+                                        float *lse, void *stream);
+
 /* ---------------------------------------------------------- measurement ---- */
 /*
  * Probes for the two figures a roofline needs, measured on this machine rather than

@@ -260,6 +260,32 @@ def test_decode_checks_scales_and_workspace():
     assert st == _lib.ATTN_ERROR_WORKSPACE_TOO_SMALL
 
 
+def test_decode_noalloc_checks_arguments_and_its_limit():
+    """The allocation-free decode rejects bad arguments, and calls whose partial results
+    exceed its built-in scratch, on the host before any HIP call."""
+    L = _lib.lib()
+    a = attn._decode_args(**_dec_kw(num_q_heads=30))
+    st = L.attn_decode_paged_noalloc(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None)
+    assert st == _lib.ATTN_ERROR_INVALID_VALUE
+    a = attn._decode_args(**_dec_kw())
+    st = L.attn_decode_paged_noalloc(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, None, None)
+    assert st == _lib.ATTN_ERROR_INVALID_VALUE  # no seq_lens
+    # 64 sequences of up to 32768 tokens, Hq = 32: 34 MB of partials, within the 64 MiB
+    assert attn.decode_workspace_size(**_dec_kw()) <= attn.DECODE_NOALLOC_MAX_WORKSPACE
+    big = _dec_kw(num_seqs=512)
+    assert attn.decode_workspace_size(**big) > attn.DECODE_NOALLOC_MAX_WORKSPACE
+    a = attn._decode_args(**big)
+    st = L.attn_decode_paged_noalloc(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None)
+    assert st == _lib.ATTN_ERROR_WORKSPACE_TOO_SMALL
+    assert b"scratch" in L.attn_last_error_message()
+
+
+def test_decode_noalloc_limit_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    m = re.search(r"#define ATTN_DECODE_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == attn.DECODE_NOALLOC_MAX_WORKSPACE
+
+
 @pytest.mark.parametrize("args", [
     (None, 256, 10, 0, FAKE, FAKE),          # no operands
     (FAKE, 0, 10, 0, FAKE, FAKE),            # no workgroups
