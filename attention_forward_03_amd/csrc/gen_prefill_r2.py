@@ -102,6 +102,19 @@ EP = KF                # 8 epilogue temporaries
 INV = KF + 8           # [rb]
 LT = KF + 10           # [rb]
 
+# Persistent form: one workgroup per CU runs its work items one after another. Items are
+# read from a table in LDS (one record of 16 dwords per item, written by the C++ code):
+#   0-1 Q base, 2-3 O base, 4-5 LSE base, 6-7 K base, 8-9 V base (byte addresses; Q and O
+#   at row 0 of the item's sequence, LSE at that row's entry, K and V at key 0 of the
+#   sequence), 10 first query row of the item within its sequence, 11 Lq, 12 Lk,
+#   13 first key tile start, 14 key tiles, 15 sink (log2 units).
+# Extra inputs: s30 items, s31 table address (LDS bytes), s32 window, s33 causal, s34 / s35
+# Q / O row strides (bytes), v249 = wave * 64 + lane % 32, v250 = lane / 32.
+REC = 64               # bytes of a record
+RECV = P_X             # 16 VGPRs the current record is read into (free between items)
+QNEXT = 192            # a[192:255]: the next item's Q fragments, raw, loaded while this one ends
+SK_ITEM, SK_FLAG = 96, 97   # item index; byte offset (0 / 4) of this item's redo-flag slot
+
 # SGPRs used by the stream
 SJ, SKT, ST, ST2, ST3 = 60, 61, 62, 63, 64
 SKROW, SVROW, SWB, SKT2, SATT, SUNM = 65, 66, 67, 68, 69, 70
@@ -130,9 +143,10 @@ def kbuf(c, h):
 
 
 class Gen:
-    def __init__(self, bf16, mode):
+    def __init__(self, bf16, mode, persistent=False):
         self.bf16 = bf16
         self.mode = mode
+        self.persistent = persistent
         # slack: P < 2^slack; fp16 probabilities must stay below 2^16
         self.slack_bits = "0x42200000" if bf16 else "0x41700000"   # 40 / 15
         self.sum_limit = "0x71800000" if bf16 else "0x47000000"    # 2^100 / 2^15
@@ -506,10 +520,16 @@ class Gen:
         self.thresholds()
         for rb in range(RB):
             self.emit(f"v_sub_f32 {v(DELTA + rb)}, {v(MU + rb)}, {v(MUOLD + rb)}")
+    def flag_addr(self, dst):
+        """LDS address of the redo flag (of this item's slot in the persistent form)."""
+        self.emit(f"v_mov_b32 {v(dst)}, {FLAG}")
+        self.emit(f"v_add_u32 {v(dst)}, {s(56)}, {v(dst)}")
+        if self.persistent:
+            self.emit(f"v_add_u32 {v(dst)}, {s(SK_FLAG)}, {v(dst)}")
+
     def set_flag(self):
         self.emit(f"v_mov_b32 {v(T0)}, 1")
-        self.emit(f"v_mov_b32 {v(T1)}, {FLAG}")
-        self.emit(f"v_add_u32 {v(T1)}, {s(56)}, {v(T1)}")
+        self.flag_addr(T1)
         self.emit(f"ds_write_b32 {v(T1)}, {v(T0)}")
         self.emit("s_waitcnt lgkmcnt(0)")
 
@@ -645,6 +665,10 @@ class Gen:
         qscale = v(VCAPK) if self.mode == 2 else s(49)
         for i in range(RB * NKS * 4):
             x = S_X + i
+            if self.persistent:
+                # the raw fragments arrived in a[QNEXT:]
+                x = T3
+                e(f"v_accvgpr_read_b32 {v(T3)}, {a(QNEXT + i)}")
             if self.bf16:
                 e(f"v_lshlrev_b32 {v(T0)}, 16, {v(x)}")
                 e(f"v_and_b32 {v(T1)}, 0xffff0000, {v(x)}")
@@ -658,25 +682,44 @@ class Gen:
             e(f"{cvt} {v(T2)}, {v(T0)}, {v(T1)}")
             e(f"v_accvgpr_write_b32 {a(128 + i)}, {v(T2)}")
 
-    def run_pass(self, exact, first=False):
-        tag = "x" if exact else "n"
-        self.emit(f"s_mov_b32 {s(SJ)}, 0")
-        self.emit(f"s_mov_b32 {s(SKT)}, {s(47)}")
-        # K(0) -> buffer 0, V(0) -> buffer 3, K(min(1, n-1)) -> buffer 1
+    def initial_loads(self):
+        """K(0) -> buffer 0, V(0) -> buffer 3, K(min(1, n-1)) -> buffer 1."""
         self.rsrc("k", 47)
         for n in range(4):
             self.load("k", n, 0)
-        if not exact:
-            self.rsrc("v", 47)
-            for n in range(4):
-                self.load("v", n, 3)
-            self.zero_v5()
-            for rb in range(RB):
-                self.emit(f"v_mov_b32 {v(LMX + rb)}, 0")
+        self.rsrc("v", 47)
+        for n in range(4):
+            self.load("v", n, 3)
         # the resource is read when a load issues: K(1) follows without a wait
         self.advance_rsrc("k")
         for n in range(4):
             self.load("k", n, 1)
+
+    def run_pass(self, exact, first=False):
+        tag = "x" if exact else "n"
+        self.emit(f"s_mov_b32 {s(SJ)}, 0")
+        self.emit(f"s_mov_b32 {s(SKT)}, {s(47)}")
+        if exact:
+            self.rsrc("k", 47)
+            for n in range(4):
+                self.load("k", n, 0)
+            self.advance_rsrc("k")
+            for n in range(4):
+                self.load("k", n, 1)
+        else:
+            if self.persistent:
+                # the first attempt finds its first tiles issued at the item change; a second
+                # attempt (after a redo) issues them here
+                pre = self.uniq("preloaded")
+                self.emit(f"s_cmp_eq_u32 {s(SATT)}, 0")
+                self.emit(f"s_cbranch_scc1 {pre}")
+                self.initial_loads()
+                self.emit(f"{pre}:")
+            else:
+                self.initial_loads()
+            self.zero_v5()
+            for rb in range(RB):
+                self.emit(f"v_mov_b32 {v(LMX + rb)}, 0")
         self.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
         if first:
             # the first attempt only: later ones find Q in the AGPRs already
@@ -747,6 +790,8 @@ class Gen:
                 if lbl is not None:
                     self.emit(f"{lbl}:")
                 self.lds = list(loop_state)
+                if self.persistent:
+                    self.q_prefetch_next()
                 self.phase(s_next=False, pv=True, soft=False, masked=False, track=False, maxonly=False,
                            kofs=None, vofs=kbuf(c, 1), knofs=None, vnofs=None, dma=None, sx=S_X, sy=S_Y,
                            px=P_X, py=P_Y, kt_sreg=SKT, tail=prev)
@@ -777,8 +822,129 @@ class Gen:
         self.lds = []
         self.gap()
 
-    # ------------------------------------------------------------------ whole stream
-    def build(self):
+    # ------------------------------------------------------------------ persistent form
+    def read_record(self, item_sreg):
+        """RECV = the 16 dwords of the record of item s[item_sreg]."""
+        e = self.emit
+        e(f"s_lshl_b32 {s(ST)}, {s(item_sreg)}, 6")
+        e(f"s_add_u32 {s(ST)}, {s(ST)}, {s(31)}")
+        e(f"v_mov_b32 {v(T0)}, {s(ST)}")
+        for i in range(4):
+            e(f"ds_read_b128 {v(RECV + 4 * i, 4)}, {v(T0)} offset:{16 * i}")
+        e("s_waitcnt lgkmcnt(0)")
+
+    def rec_scalars(self, pairs):
+        for dst, dw in pairs:
+            self.emit(f"v_readfirstlane_b32 {s(dst)}, {v(RECV + dw)}")
+        # an SGPR written by a vector instruction is read by memory instructions only after
+        # 5 wait states
+        self.emit("s_nop 4")
+
+    def q_prefetch_next(self):
+        """While this item's last products run: the raw Q fragments of the next item into
+        a[QNEXT:] (first attempt only; nothing after the last item)."""
+        e = self.emit
+        skip = self.uniq("noqnext")
+        e(f"s_cmp_lg_u32 {s(SATT)}, 0")
+        e(f"s_cbranch_scc1 {skip}")
+        e(f"s_add_u32 {s(ST2)}, {s(SK_ITEM)}, 1")
+        e(f"s_cmp_ge_u32 {s(ST2)}, {s(30)}")
+        e(f"s_cbranch_scc1 {skip}")
+        self.read_record(ST2)
+        # row of lane (rb, l32) = min(r0 + wave * 64 + 32 rb + l32, Lq - 1)
+        e(f"v_add_u32 {v(T3)}, {v(RECV + 10)}, {v(249)}")
+        e(f"v_add_u32 {v(T2)}, -1, {v(RECV + 11)}")
+        e(f"v_lshlrev_b32 {v(T1)}, 4, {v(250)}")
+        for rb in range(RB):
+            e(f"v_add_u32 {v(T0)}, {32 * rb}, {v(T3)}")
+            e(f"v_min_i32 {v(T0)}, {v(T0)}, {v(T2)}")
+            e(f"v_mov_b32 {v(2 * rb)}, {v(RECV)}")
+            e(f"v_mov_b32 {v(2 * rb + 1)}, {v(RECV + 1)}")
+            e(f"v_mad_u64_u32 {v(2 * rb, 2)}, {s(SPAIR, 2)}, {v(T0)}, {s(34)}, {v(2 * rb, 2)}")
+            e(f"v_add_co_u32 {v(2 * rb)}, vcc, {v(2 * rb)}, {v(T1)}")
+            e(f"v_addc_co_u32 {v(2 * rb + 1)}, vcc, 0, {v(2 * rb + 1)}, vcc")
+        for rb in range(RB):
+            for ks in range(NKS):
+                e(f"global_load_dwordx4 {a(QNEXT + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
+        e(f"{skip}:")
+
+    def item_kv(self):
+        """The record's K / V bases, Lk and first key into the stream's inputs."""
+        self.rec_scalars(((40, 6), (41, 7), (42, 8), (43, 9), (46, 12), (47, 13)))
+
+    def item_rest(self):
+        """Everything else of the item in RECV: Lq, tiles, sink, the wave's unmasked key range
+        and the per-lane rows, key ranges and O / LSE addresses (after the previous item's
+        epilogue, which reads the old ones)."""
+        e = self.emit
+        self.rec_scalars(((54, 11), (48, 14), (52, 15), (ST2, 10)))
+        # wave rows [w0, w0 + 64); delta = Lk - Lq
+        e(f"s_lshl_b32 {s(ST)}, {s(53)}, 6")
+        e(f"s_add_u32 {s(ST)}, {s(ST)}, {s(ST2)}")                 # w0
+        e(f"s_sub_i32 {s(ST3)}, {s(46)}, {s(54)}")                  # delta
+        # whi = causal ? max(0, min(Lk, w0 + delta + 1)) : Lk
+        e(f"s_add_i32 {s(58)}, {s(ST)}, {s(ST3)}")
+        e(f"s_add_i32 {s(58)}, {s(58)}, 1")
+        e(f"s_min_i32 {s(58)}, {s(58)}, {s(46)}")
+        e(f"s_max_i32 {s(58)}, {s(58)}, 0")
+        e(f"s_cmp_eq_u32 {s(33)}, 0")
+        e(f"s_cselect_b32 {s(58)}, {s(46)}, {s(58)}")
+        # wlo = window ? max(0, min(w0 + 63, Lq - 1) + delta - window + 1) : 0
+        e(f"s_add_i32 {s(57)}, {s(ST)}, 63")
+        e(f"s_add_i32 {s(SPAIR)}, {s(54)}, -1")
+        e(f"s_min_i32 {s(57)}, {s(57)}, {s(SPAIR)}")
+        e(f"s_add_i32 {s(57)}, {s(57)}, {s(ST3)}")
+        e(f"s_sub_i32 {s(57)}, {s(57)}, {s(32)}")
+        e(f"s_add_i32 {s(57)}, {s(57)}, 1")
+        e(f"s_max_i32 {s(57)}, {s(57)}, 0")
+        e(f"s_cmp_gt_i32 {s(32)}, 0")
+        e(f"s_cselect_b32 {s(57)}, {s(57)}, 0")
+        # per lane: key_lo = window ? row + delta - window + 1 : 0;
+        # key_hi = causal ? min(Lk, row + delta + 1) : Lk
+        e(f"s_sub_i32 {s(ST)}, {s(ST3)}, {s(32)}")
+        e(f"s_add_i32 {s(ST)}, {s(ST)}, 1")                          # delta - window + 1
+        e(f"s_add_i32 {s(ST3)}, {s(ST3)}, 1")                        # delta + 1
+        e(f"s_cmp_gt_i32 {s(32)}, 0")
+        e(f"s_cselect_b64 {s(SMASK, 2)}, -1, 0")
+        e(f"s_cmp_lg_u32 {s(33)}, 0")
+        e(f"s_cselect_b64 {s(SMASK2, 2)}, -1, 0")
+        e(f"v_add_u32 {v(16)}, {s(ST2)}, {v(249)}")
+        e(f"v_add_u32 {v(17)}, 32, {v(16)}")
+        for rb in range(RB):
+            q = v(16 + rb)
+            e(f"v_add_u32 {v(T0)}, {s(ST)}, {q}")
+            e(f"v_cndmask_b32_e64 {v(T0)}, 0, {v(T0)}, {s(SMASK, 2)}")   # key_lo
+            e(f"v_add_u32 {v(T1)}, {s(ST3)}, {q}")
+            e(f"v_min_i32 {v(T1)}, {s(46)}, {v(T1)}")
+            e(f"v_mov_b32 {v(T2)}, {s(46)}")
+            e(f"v_cndmask_b32_e64 {v(T1)}, {v(T2)}, {v(T1)}, {s(SMASK2, 2)}")  # key_hi
+            e(f"v_sub_u32 {v(T1)}, {v(T1)}, {v(T0)}")
+            e(f"v_max_i32 {v(14 + rb)}, 0, {v(T1)}")                    # key_n
+            e(f"v_lshlrev_b32 {v(T2)}, 2, {v(250)}")
+            e(f"v_sub_u32 {v(12 + rb)}, {v(T2)}, {v(T0)}")              # 4 hi - key_lo
+            # O row address: O base + row * O stride + 8 hi; LSE: LSE base + 4 row
+            e(f"v_mov_b32 {v(4 + 2 * rb)}, {v(RECV + 2)}")
+            e(f"v_mov_b32 {v(5 + 2 * rb)}, {v(RECV + 3)}")
+            e(f"v_mad_u64_u32 {v(4 + 2 * rb, 2)}, {s(SPAIR, 2)}, {q}, {s(35)}, {v(4 + 2 * rb, 2)}")
+            e(f"v_lshlrev_b32 {v(T2)}, 3, {v(250)}")
+            e(f"v_add_co_u32 {v(4 + 2 * rb)}, vcc, {v(4 + 2 * rb)}, {v(T2)}")
+            e(f"v_addc_co_u32 {v(5 + 2 * rb)}, vcc, 0, {v(5 + 2 * rb)}, vcc")
+            e(f"v_mov_b32 {v(8 + 2 * rb)}, {v(RECV + 4)}")
+            e(f"v_mov_b32 {v(9 + 2 * rb)}, {v(RECV + 5)}")
+            e(f"v_mad_u64_u32 {v(8 + 2 * rb, 2)}, {s(SPAIR, 2)}, {q}, 4, {v(8 + 2 * rb, 2)}")
+
+    def clear_flag(self):
+        """Wave 0 sets this item's redo-flag slot to 0 (before the pass's first barrier)."""
+        skip = self.uniq("noclear")
+        self.emit(f"s_cmp_lg_u32 {s(53)}, 0")
+        self.emit(f"s_cbranch_scc1 {skip}")
+        self.flag_addr(T1)
+        self.emit(f"ds_write_b32 {v(T1)}, {v(ZERO)}")
+        self.emit("s_waitcnt lgkmcnt(0)")
+        self.emit(f"{skip}:")
+
+    def setup(self):
+        """Constants of the stream: masks' -inf, softcap factors, LDS addresses, load offsets."""
         e = self.emit
         e(f"v_mov_b32 {v(VNINF)}, 0xff800000")
         e(f"v_mul_f32 {v(VM2C)}, -2.0, {s(51)}")
@@ -807,19 +973,11 @@ class Gen:
             e(f"v_add_u32 {v(VO + n)}, {s(ST3)}, {v(20)}")
         for r in range(ZERO, ZERO + 4):
             e(f"v_mov_b32 {v(r)}, 0")
-        # Q fragments (raw; scaled into AGPRs once the first pass's tile loads are issued)
-        for rb in range(RB):
-            for ks in range(NKS):
-                e(f"global_load_dwordx4 {v(S_X + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
-        # redo flag = 0 (wave 0), ordered before any write of 1 by the first barrier
-        skip = self.uniq("noinit")
-        e(f"s_cmp_lg_u32 {s(53)}, 0")
-        e(f"s_cbranch_scc1 {skip}")
-        e(f"v_mov_b32 {v(T1)}, {FLAG}")
-        e(f"v_add_u32 {v(T1)}, {s(56)}, {v(T1)}")
-        e(f"ds_write_b32 {v(T1)}, {v(ZERO)}")
-        e("s_waitcnt lgkmcnt(0)")
-        e(f"{skip}:")
+
+    def attempts(self):
+        """One item: the pass, and if its check tripped, the exact row maxima and the pass
+        again; ends with every wave past a barrier after the last pass."""
+        e = self.emit
         e(f"s_mov_b32 {s(SATT)}, 0")
         for rb in range(RB):
             e(f"v_mov_b32 {v(M + rb)}, {v(VNINF)}")
@@ -836,8 +994,7 @@ class Gen:
         e("s_barrier")
         e(f"s_cmp_lg_u32 {s(SATT)}, 0")
         e(f"s_cbranch_scc1 {done}")
-        e(f"v_mov_b32 {v(T1)}, {FLAG}")
-        e(f"v_add_u32 {v(T1)}, {s(56)}, {v(T1)}")
+        self.flag_addr(T1)
         e(f"ds_read_b32 {v(T0)}, {v(T1)}")
         e("s_waitcnt lgkmcnt(0)")
         e(f"v_readfirstlane_b32 {s(ST)}, {v(T0)}")
@@ -852,6 +1009,57 @@ class Gen:
         e("s_barrier")
         e("s_branch L_attempt_%=")
         e(f"{done}:")
+
+    def build_persistent(self):
+        e = self.emit
+        self.setup()
+        e(f"s_mov_b32 {s(SK_ITEM)}, 0")
+        e(f"s_mov_b32 {s(SK_FLAG)}, 0")
+        # item 0: Q (raw) into a[QNEXT:], its first tiles, its per-lane values
+        e(f"s_mov_b32 {s(SATT)}, 0")
+        e(f"s_sub_u32 {s(SK_ITEM)}, 0, 1")
+        self.q_prefetch_next()
+        e(f"s_mov_b32 {s(SK_ITEM)}, 0")
+        self.read_record(SK_ITEM)
+        self.item_kv()
+        self.initial_loads()
+        self.item_rest()
+        e("L_item_%=:")
+        self.clear_flag()
+        self.attempts()
+        # every wave is past the barrier after this item's last LDS read: the next item's
+        # first tiles go into the buffers now, ahead of this item's epilogue
+        last = self.uniq("lastitem")
+        e(f"s_add_u32 {s(ST2)}, {s(SK_ITEM)}, 1")
+        e(f"s_cmp_ge_u32 {s(ST2)}, {s(30)}")
+        e(f"s_cbranch_scc1 {last}")
+        self.read_record(ST2)
+        self.item_kv()
+        self.initial_loads()
+        e(f"{last}:")
+        self.epilogue()
+        e(f"s_add_u32 {s(SK_ITEM)}, {s(SK_ITEM)}, 1")
+        e(f"s_cmp_ge_u32 {s(SK_ITEM)}, {s(30)}")
+        e("s_cbranch_scc1 L_end_%=")
+        self.item_rest()
+        e(f"s_xor_b32 {s(SK_FLAG)}, {s(SK_FLAG)}, 4")
+        e("s_branch L_item_%=")
+        for blk in self.rare:
+            self.rare_block(*blk)
+        e("L_end_%=:")
+        return self.out
+
+    # ------------------------------------------------------------------ whole stream
+    def build(self):
+        e = self.emit
+        self.setup()
+        # Q fragments (raw; scaled into AGPRs once the first pass's tile loads are issued)
+        for rb in range(RB):
+            for ks in range(NKS):
+                e(f"global_load_dwordx4 {v(S_X + (rb * NKS + ks) * 4, 4)}, {v(2 * rb, 2)}, off offset:{ks * 32}")
+        # redo flag = 0 (wave 0), ordered before any write of 1 by the first barrier
+        self.clear_flag()
+        self.attempts()
         self.epilogue()
         e("s_branch L_end_%=")
         for blk in self.rare:
@@ -941,9 +1149,13 @@ def render(lines):
     return "\n".join('"' + ln + '\\n\\t"' for ln in lines) + "\n"
 
 
-def clobbers():
-    regs = [f'"v{i}"' for i in range(24, NVGPR)] + [f'"a{i}"' for i in range(192)]
+def clobbers(persistent=False):
+    regs = [f'"v{i}"' for i in range(24, NVGPR)] + [f'"a{i}"' for i in range(256 if persistent else 192)]
     regs += [f'"s{i}"' for i in range(NSGPR_LO, NSGPR_HI)]
+    if persistent:
+        # the item's own inputs are computed inside the statement from the item table
+        regs += [f'"v{i}"' for i in range(18)]
+        regs += [f'"s{i}"' for i in (40, 41, 42, 43, 46, 47, 48, 52, 54, 57, 58, SK_ITEM, SK_FLAG)]
     # m0 is written for the LDS-DMA loads; exec is written around the row-masked stores and
     # restored before the statement ends
     regs += ['"vcc"', '"scc"', '"m0"', '"memory"']
@@ -954,14 +1166,17 @@ def main(out_dir):
     os.makedirs(out_dir, exist_ok=True)
     for bf16 in (True, False):
         for mode in (0, 1, 2):
-            lines = Gen(bf16, mode).build()
-            name = f"prefill_r2_{'bf16' if bf16 else 'f16'}_m{mode}.inc"
-            with open(os.path.join(out_dir, name), "w") as f:
-                f.write(f"// generated by gen_prefill_r2.py: {len(lines)} lines\n")
-                f.write(render(lines))
+            for persistent in (False, True):
+                g = Gen(bf16, mode, persistent)
+                lines = g.build_persistent() if persistent else g.build()
+                name = f"prefill_r2{'p' if persistent else ''}_{'bf16' if bf16 else 'f16'}_m{mode}.inc"
+                with open(os.path.join(out_dir, name), "w") as f:
+                    f.write(f"// generated by gen_prefill_r2.py: {len(lines)} lines\n")
+                    f.write(render(lines))
     with open(os.path.join(out_dir, "prefill_r2_clobbers.inc"), "w") as f:
         f.write("// generated by gen_prefill_r2.py\n")
         f.write("#define ATTN_R2_CLOBBERS " + clobbers() + "\n")
+        f.write("#define ATTN_R2P_CLOBBERS " + clobbers(True) + "\n")
 
 
 if __name__ == "__main__":

@@ -592,6 +592,182 @@ __global__ __launch_bounds__(256, 1) void fwd_r2_kernel(const FwdParams p) {
 #undef ATTN_R2_INPUTS
 }
 
+// Persistent form of the same kernel: one workgroup per CU runs a list of work items one
+// after another inside the statement. Between items the next item's first K / V tiles are
+// issued before the current item's O is normalised and stored, and the next item's Q
+// fragments load into spare AGPRs while the current item's last P.V products run; the
+// per-item cost of a fresh workgroup (Q load, first tiles, dispatch) is thereby overlapped.
+// Workgroup w (on XCD w % 8) takes, in round j, item x + 8 p with x = w % 8 and p = j * n + c
+// (c = w / 8 of n = G / 8 workgroups per XCD) in even rounds, j * n + n - 1 - c in odd
+// ones: items keep the XCD placement of work_item(), and under a causal mask, where item
+// lengths fall with the item index inside a (sequence, KV head) unit, a workgroup's long
+// and short items alternate. Wave 0 writes the workgroup's item table into LDS (one
+// record per item, the layout gen_prefill_r2.py documents); items whose rows see no key
+// get O = 0 here and no record.
+constexpr int kMaxItemsPerWG = 64;
+
+struct ItemRec {
+  uint64_t q, o, lse, k, v;
+  int32_t r0, lq, lk, kbeg, ntiles;
+  float sink2;
+};
+static_assert(sizeof(ItemRec) == 64, "an item record is 16 dwords");
+
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(256, 1) void fwd_r2p_kernel(const FwdParams p, int total_items) {
+  constexpr int D = 128, BN = 64, RB = 2, NW = 4;
+  constexpr int BM = NW * 32 * RB;
+  constexpr int TILE = BN * D;
+  using SW = Swizzle<D>;
+  // K x3, V x3, two redo-flag slots (16 bytes), the item table, the items without keys
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[6 * TILE + 8 + 2 * kMaxItemsPerWG * 32];
+  ItemRec* const table = reinterpret_cast<ItemRec*>(smem + 6 * TILE + 8);
+  ItemRec* const empty = table + kMaxItemsPerWG;
+  __shared__ int n_items, n_empty;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const bool ragged = p.cu_q != nullptr;
+
+  if (wave == 0) {
+    const int G = gridDim.x, nloc = G >> 3, x = blockIdx.x & 7, c = blockIdx.x >> 3;
+    const int item = x + 8 * (lane * nloc + ((lane & 1) ? nloc - 1 - c : c));
+    ItemRec r{};
+    bool work = false, none = false;
+    if (item < total_items) {
+      const WorkItem wi = work_item(item, total_items, p.q_tiles, p.hq, p.hkv, p.batch);
+      const int h = wi.h, b = wi.b;
+      const int qt = p.causal ? p.q_tiles - 1 - wi.qt : wi.qt;
+      int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
+      if (ragged) {
+        q_off = p.cu_q[b];
+        Lq = p.cu_q[b + 1] - q_off;
+        if (p.seq_lens_k != nullptr) {
+          k_off = b * p.max_pages * 16;
+          Lk = min(max(p.seq_lens_k[b], 0), p.max_pages * 16);
+        } else {
+          k_off = p.cu_k[b];
+          Lk = p.cu_k[b + 1] - k_off;
+        }
+      }
+      const int r0 = qt * BM;
+      if (r0 < Lq) {
+        const int hk = h / p.group;
+        const int delta = Lk - Lq;
+        const int r1 = min(Lq, r0 + BM);
+        const int kend = p.causal ? min(Lk, r1 + delta) : Lk;
+        int kbeg = p.window > 0 ? max(0, r0 + delta - p.window + 1) : 0;
+        kbeg = (kbeg / BN) * BN;
+        const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+        const int64_t qe = (ragged ? 0 : (int64_t)b * p.qs[0]) + (int64_t)h * p.qs[1] + (int64_t)q_off * p.qs[2];
+        const int64_t oe = (ragged ? 0 : (int64_t)b * p.os[0]) + (int64_t)h * p.os[1] + (int64_t)q_off * p.os[2];
+        const int64_t ke = (ragged ? 0 : (int64_t)b * p.ks[0]) + (int64_t)hk * p.ks[1] + (int64_t)k_off * p.ks[2];
+        const int64_t ve = (ragged ? 0 : (int64_t)b * p.vs[0]) + (int64_t)hk * p.vs[1] + (int64_t)k_off * p.vs[2];
+        r.q = (uint64_t)(uintptr_t)p.q + 2 * (uint64_t)qe;
+        r.o = (uint64_t)(uintptr_t)p.o + 2 * (uint64_t)oe;
+        r.k = (uint64_t)(uintptr_t)p.k + 2 * (uint64_t)ke;
+        r.v = (uint64_t)(uintptr_t)p.v + 2 * (uint64_t)ve;
+        r.lse = p.lse == nullptr ? 0
+                                 : (uint64_t)(uintptr_t)(p.lse + (ragged ? (int64_t)h * p.cu_q[p.batch] + q_off
+                                                                         : ((int64_t)b * p.hq + h) * p.nq));
+        r.r0 = r0;
+        r.lq = Lq;
+        r.lk = Lk;
+        r.kbeg = kbeg;
+        r.ntiles = ntiles;
+        work = ntiles > 0;
+        none = ntiles == 0;
+        // the sink in log2 units, -inf for none (the epilogue's added terms are then exact
+        // no-ops); an item without keys keeps it in natural-log units: its LSE
+        const float sink = p.sinks != nullptr ? p.sinks[h] : kNegInf;
+        r.sink2 = none ? sink : sink * kLog2e;
+      }
+    }
+    const uint64_t wm = __ballot(work), nm = __ballot(none);
+    const uint64_t below = (1ull << lane) - 1ull;
+    if (work) table[__popcll(wm & below)] = r;
+    if (none) empty[__popcll(nm & below)] = r;
+    if (lane == 0) {
+      n_items = __popcll(wm);
+      n_empty = __popcll(nm);
+    }
+  }
+  __syncthreads();
+  // items whose rows see no key: O = 0, LSE = -inf (the sink with one); thread t owns row t
+  for (int e = 0; e < n_empty; ++e) {
+    const ItemRec r = empty[e];
+    const int row = r.r0 + tid;
+    if (row < r.lq) {
+      uint16_t* orow = reinterpret_cast<uint16_t*>((uintptr_t)r.o) + (int64_t)row * p.os[2];
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) *reinterpret_cast<u32x4_t*>(orow + c * 8) = u32x4_t{0, 0, 0, 0};
+      if (r.lse != 0) reinterpret_cast<float*>((uintptr_t)r.lse)[row] = r.sink2;
+    }
+  }
+  const int n = n_items;
+  if (n == 0) return;
+
+  const int ks2 = (int)p.ks[2], vs2 = (int)p.vs[2];
+  const int ld_row0 = wave * 4 + lane / 16;
+  const uint32_t ld_k0 = (uint32_t)(ld_row0 * ks2 + SW::k(ld_row0, lane % 16) * 8) * 2u;
+  const uint32_t ld_v0 = (uint32_t)(ld_row0 * vs2 + SW::v(ld_row0, lane % 16) * 8) * 2u;
+  const uint32_t k_rd = (uint32_t)(l32 * D + SW::k(l32, hi) * 8) * 2u;
+  const int grp = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * hi + (gi >> 2);
+  const uint32_t v_rd =
+      (uint32_t)(vrow * D + SW::v(vrow, (grp & 1) * 2 + ((gi & 3) >> 1)) * 8 + (gi & 1) * 4) * 2u;
+  const uint32_t lane_row = (uint32_t)(wave * 64 + l32);
+  const uint32_t lane_hi = (uint32_t)hi;
+  auto uni = [](auto x) __attribute__((always_inline)) {
+    return __builtin_bit_cast(decltype(x), __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, x)));
+  };
+  const float sc = uni(MODE == 2 ? 1.0f : fmaxf(p.scale_log2, 1.17549435e-38f));
+  const float cap_in = uni(p.cap_in), cap_c = uni(p.cap_out);
+  const int has_lse = uni((int)(p.lse != nullptr));
+  const int ks2_u = uni(ks2), vs2_u = uni(vs2);
+  const uint32_t lds_u = uni(lds0);
+  const int n_u = uni(n);
+  const uint32_t table_u = uni(lds0 + (uint32_t)((6 * TILE + 8) * 2));
+  const int win_u = uni(p.window), causal_u = uni(p.causal);
+  const int qrow_b = uni((int)(p.qs[2] * 2)), orow_b = uni((int)(p.os[2] * 2));
+
+#define ATTN_R2P_INPUTS                                                                                        \
+  "{v19}"(ld_k0), "{v20}"(ld_v0), "{v21}"(k_rd), "{v22}"(v_rd), "{v249}"(lane_row), "{v250}"(lane_hi),          \
+      "{s44}"(ks2_u), "{s45}"(vs2_u), "{s49}"(sc), "{s50}"(cap_in), "{s51}"(cap_c), "{s53}"(wave),             \
+      "{s55}"(has_lse), "{s56}"(lds_u), "{s30}"(n_u), "{s31}"(table_u), "{s32}"(win_u), "{s33}"(causal_u),     \
+      "{s34}"(qrow_b), "{s35}"(orow_b)
+  if constexpr (BF16 && MODE == 0) {
+    asm volatile(
+#include "prefill_r2p_bf16_m0.inc"
+        : : ATTN_R2P_INPUTS : ATTN_R2P_CLOBBERS);
+  } else if constexpr (BF16 && MODE == 1) {
+    asm volatile(
+#include "prefill_r2p_bf16_m1.inc"
+        : : ATTN_R2P_INPUTS : ATTN_R2P_CLOBBERS);
+  } else if constexpr (BF16) {
+    asm volatile(
+#include "prefill_r2p_bf16_m2.inc"
+        : : ATTN_R2P_INPUTS : ATTN_R2P_CLOBBERS);
+  } else if constexpr (MODE == 0) {
+    asm volatile(
+#include "prefill_r2p_f16_m0.inc"
+        : : ATTN_R2P_INPUTS : ATTN_R2P_CLOBBERS);
+  } else if constexpr (MODE == 1) {
+    asm volatile(
+#include "prefill_r2p_f16_m1.inc"
+        : : ATTN_R2P_INPUTS : ATTN_R2P_CLOBBERS);
+  } else {
+    asm volatile(
+#include "prefill_r2p_f16_m2.inc"
+        : : ATTN_R2P_INPUTS : ATTN_R2P_CLOBBERS);
+  }
+#undef ATTN_R2P_INPUTS
+}
+
 // ------------------------------------------------------------------ fp32 inputs ----
 // 32x32x2 fp32 matrix-core products. Q.K^T contracts over head_dim with lanes 0-31
 // taking the first half of D and lanes 32-63 the second; P.V contracts over keys in
@@ -811,11 +987,48 @@ bool small_grid16(int head_dim, int64_t nq, int64_t units) {
   return head_dim <= 64 && (nq + 255) / 256 * units < 256;
 }
 
+#ifndef ATTN_PREFILL_PERSISTENT
+#define ATTN_PREFILL_PERSISTENT 1
+#endif
+
+// Compute units of the current device (one persistent workgroup each).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <bool BF16>
+hipError_t launch_r2p(const FwdParams& p, int items, int grid, hipStream_t st) {
+  if (p.cap_out > 0.0f) {
+    hipLaunchKernelGGL((fwd_r2p_kernel<BF16, 2>), dim3(grid), dim3(256), 0, st, p, items);
+  } else if (p.causal || p.window > 0 || p.cu_q != nullptr || p.nk % 64 != 0) {
+    hipLaunchKernelGGL((fwd_r2p_kernel<BF16, 1>), dim3(grid), dim3(256), 0, st, p, items);
+  } else {
+    hipLaunchKernelGGL((fwd_r2p_kernel<BF16, 0>), dim3(grid), dim3(256), 0, st, p, items);
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch16(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = (int64_t)p.q_tiles * p.hq * p.batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if constexpr (D == 128) {
+    // dense batches with more items than compute units: the persistent form, one workgroup
+    // per CU (a multiple of 8, the XCD count), while each takes at most kMaxItemsPerWG items.
+    // Ragged batches keep one workgroup per item: their item lengths follow the sequence
+    // lengths, which the hardware's dispatch of workgroups to free CUs balances better than
+    // a fixed assignment (the ragged GQA workload ran 17% slower in the persistent form).
+    const int64_t cus = (int64_t)(device_cus() / 8 * 8);
+    if (ATTN_PREFILL_PERSISTENT && p.cu_q == nullptr && cus >= 8 && blocks > cus && blocks <= cus * kMaxItemsPerWG)
+      return launch_r2p<BF16>(p, (int)blocks, (int)cus, st);
     const dim3 grid((unsigned)blocks), block(256);
     if (p.cap_out > 0.0f) {
       hipLaunchKernelGGL((fwd_r2_kernel<BF16, 2>), grid, block, 0, st, p);
