@@ -64,7 +64,7 @@ def decode_bytes(case, kv_elt: int, q_elt: int = 2) -> float:
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
-PREFILL_KERNEL = "fwd_r2_kernel<true, 0>"
+PREFILL_KERNELS = ("fwd_r2p_kernel<true, 0>",)
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
 CHUNKED_KERNEL = ("gather_kv_pages_kernel", "fwd_r2_kernel<true, 1>")
 FP8_KERNEL = "fwd_fp8_kernel"
@@ -75,6 +75,7 @@ BWD_KERNELS = ("bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
 # reported only while these files are unchanged since the counters were taken
 KERNEL_FILES = {
     "fwd_r2_kernel": ("prefill.hip", "gen_prefill_r2.py", "prefill_shared.hpp", "common.hpp"),
+    "fwd_r2p_kernel": ("prefill.hip", "gen_prefill_r2.py", "prefill_shared.hpp", "common.hpp"),
     "fwd_mfma16_kernel": ("prefill.hip", "prefill_shared.hpp", "common.hpp"),
     "gather_kv_pages_kernel": ("prefill.hip", "common.hpp"),
     "decode_": ("decode.hip", "common.hpp"),
@@ -103,59 +104,55 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, out_path: str) -> dict:
-    """HBM traffic per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE).
-
-    Both counters are in KiB per dispatch. Each is scaled by what it reads for the plain
-    device copy of ``copy_mib`` MiB that the same run performs (the copy reads and writes
-    exactly that many bytes), which calibrates the counter to bytes.
-    """
+def _counter_rows(d, counter):
+    """Per kernel name: the values of `counter` of every dispatch in the rocprofv3 --pmc
+    output folder d, grouped by grid size."""
     import csv
     import glob
-
-    def per_kernel(d, counter):
-        """Values per kernel name, from the dispatches of its most frequent grid size (a
-        kernel that one measured workload launches is sometimes also launched once, on
-        another shape, by another part of the run)."""
-        by_grid = {}
-        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for r in csv.DictReader(open(path)):
+    by_grid = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
                     by_grid.setdefault(r["Kernel_Name"], {}).setdefault(r["Grid_Size"], []).append(
                         float(r["Counter_Value"]))
-        # the copy kernel keeps all its dispatches: the calibration copy is its largest one
-        return {k: (sum(g.values(), []) if "copyBuffer" in k else max(g.values(), key=len))
-                for k, g in by_grid.items()}
+    return by_grid
 
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
+
+def counter_traffic(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
+    """HBM traffic per launch from two rocprofv3 --pmc runs of one workload (FETCH_SIZE, then
+    WRITE_SIZE). Both counters are in KiB per dispatch. Each is scaled by what it reads for
+    the plain device copy of `copy_mib` MiB that the same run performs (the copy reads and
+    writes exactly that many bytes), which calibrates the counter to bytes. A kernel's value
+    is the mean over the dispatches of its most frequent grid size."""
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(write_dir, "WRITE_SIZE")
     known = copy_mib * (1 << 20)
     # the calibration copy is the largest copy dispatch of the run (small runtime copies
     # also appear under the same kernel name)
-    copy_f = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
-    copy_w = max(v for k, vs in write.items() if "copyBuffer" in k for v in vs)
+    copy_f = max(v for k, g in fetch.items() if "copyBuffer" in k for vs in g.values() for v in vs)
+    copy_w = max(v for k, g in write.items() if "copyBuffer" in k for vs in g.values() for v in vs)
     f_scale = known / (copy_f * 1024.0)
     w_scale = known / (copy_w * 1024.0)
-    fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
-    write = {k: sum(v) / len(v) for k, v in write.items()}
-    res = {"source_digest": kernel_source_digest(), "file_digests": file_digests(),
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "copy_mib": copy_mib, "kernels": {}}
+
+    def mean_main(g):
+        vs = max(g.values(), key=len)
+        return sum(vs) / len(vs)
+
+    res = {"fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for k in set(fetch) | set(write):
         if "copyBuffer" in k:
             continue
-        fb = fetch.get(k, 0.0) * 1024.0 * f_scale
-        wb = write.get(k, 0.0) * 1024.0 * w_scale
+        fb = mean_main(fetch[k]) * 1024.0 * f_scale if k in fetch else 0.0
+        wb = mean_main(write[k]) * 1024.0 * w_scale if k in write else 0.0
         res["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb}
-    with open(out_path, "w") as f:
-        json.dump(res, f, indent=1)
     return res
 
 
-def load_traffic(kernel_substr):
-    """Counter-measured HBM bytes per launch of the kernels whose name contains any of the
-    given substrings, or None when absent or when any source file of those kernels has
-    changed since the counters were taken."""
+def load_traffic(workload: str, kernel_substr):
+    """Counter-measured HBM bytes per launch of the kernels of `workload` whose name contains
+    any of the given substrings, or None when absent or when any source file of those
+    kernels has changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
@@ -167,14 +164,197 @@ def load_traffic(kernel_substr):
         files = KERNEL_FILES[fam[0]] if fam else tuple(now)
         if any(then.get(f) != now[f] for f in files):
             return None
-    tot = [v["hbm_bytes"] for k, v in t["kernels"].items() if any(s in k for s in subs)]
+    kern = t.get("workloads", {}).get(workload, {}).get("kernels", {})
+    tot = [v["hbm_bytes"] for k, v in kern.items() if any(s in k for s in subs)]
     return round(sum(tot)) if tot else None
 
 
-def _timed(torch, fn, flush, reps: int, warmup: int = 3) -> float:
-    """Average duration (ms) of fn over reps launches, HIP events on the current stream
-    around each launch, caches flushed before each. A few flushed launches first: the
-    first ones after a different workload run measurably slower (clock and cache state)."""
+# ---------------------------------------------------------------- profile summaries ----
+# One rocprofv3 folder set per workload (bench.py --only NAME): a kernel trace with --stats,
+# two counter passes for HBM traffic (FETCH_SIZE, WRITE_SIZE, with a calibration copy) and
+# one pass of SQ counters; plus the bench's own JSON line of an unprofiled run of the same
+# command. `--summarize-profiles ROOT NAME...` reads ROOT/NAME/{trace,fetch,write,sq} and
+# ROOT/NAME/{trace,plain}.json and writes profiles/<file>.md, and the workloads' traffic
+# into profiles/traffic.json.
+SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+               "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT")
+PROFILE_STEPS = {"trace": (5, 1), "counters": (2, 1)}  # (steps, warmup) of the profiled runs
+
+# name: (file, title, kernels of one call, how the work per call is found, unit, peak, algorithmic bytes)
+PROFILES = {
+    "prefill": ("prefill_fwd_r2p_bf16_B1_H32_N8192_D128", "fwd_r2p_kernel<bf16, no mask> (persistent) - dense "
+                "prefill B=1 H=32 N=8192 D=128 bf16", ("fwd_r2p_kernel<true, 0>",),
+                ("roofline", "flops_per_launch"), "TFLOP/s", PEAK_BF16_TFLOPS, 4 * 32 * 8192 * 128 * 2),
+    "decode": ("decode_paged_bf16_64seq_Hq32_Hkv8_D128", "decode_split_kernel<bf16> + decode_combine_kernel - paged "
+               "decode, 64 sequences, L ~ U[512, 32768], Hq=32 Hkv=8 D=128, bf16 KV",
+               ("decode_split_kernel", "decode_combine_kernel"), ("decode", "bytes_per_launch"), "GB/s",
+               PEAK_HBM_GBPS, None),
+    "decode_fp8": ("decode_paged_fp8_64seq_Hq32_Hkv8_D128", "decode_split_kernel<fp8, whole-page workgroups> + "
+                   "decode_combine_kernel - paged decode, 64 sequences, fp8 e4m3 KV",
+                   ("decode_split_kernel", "decode_combine_kernel"),
+                   ("decode_fp8_kv_64seq_Hq32_Hkv8", "bytes_per_launch"), "GB/s", PEAK_HBM_GBPS, None),
+    "decode_mqa": ("decode_paged_mqa_64seq_Hq32_Hkv1_D128", "decode_split_kernel<bf16, two head tiles> + "
+                   "decode_combine_kernel - paged decode, 64 sequences, Hq=32 Hkv=1 (MQA), bf16 KV",
+                   ("decode_split_kernel", "decode_combine_kernel"),
+                   ("decode_mqa_64seq_Hq32_Hkv1", "bytes_per_launch"), "GB/s", PEAK_HBM_GBPS, None),
+    "chunked": ("chunked_prefill_8x2048_Hq32_Hkv8_D128", "chunked prefill over the paged cache - 8 chunks x 2048 "
+                "queries, Hq=32 Hkv=8 D=128 bf16, causal (gathered route; the in-place route alongside)",
+                ("gather_kv_pages_kernel", "fwd_r2_kernel<true, 1>"), ("chunked_prefill", "flops_per_launch"),
+                "TFLOP/s", PEAK_BF16_TFLOPS, None),
+    "fp8_prefill": ("prefill_fwd_fp8_B1_H32_N8192_D128", "fwd_fp8_kernel - dense prefill B=1 H=32 N=8192 D=128, "
+                    "fp8 e4m3 Q/K/V", ("fwd_fp8_kernel",), ("fp8_prefill", "flops_per_launch"), "TFLOP/s",
+                    PEAK_FP8_TFLOPS, 3 * 32 * 8192 * 128 + 32 * 8192 * 128 * 2),
+    "backward": ("backward_causal_gqa_B1_Hq32_Hkv8_N4096_D128", "bwd_delta_kernel + bwd_dkdv_kernel + "
+                 "bwd_convert_kernel + bwd_dq_kernel - backward of causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16",
+                 ("bwd_",), ("backward", "flops_per_launch"), "TFLOP/s", PEAK_BF16_TFLOPS, None),
+    "gqa_causal": ("prefill_causal_gqa_B4_Hq32_Hkv8_N4096_D128", "fwd_r2p_kernel<bf16, masked> (persistent) - "
+                   "causal GQA prefill B=4 Hq=32 Hkv=8 N=4096 D=128 bf16",
+                   ("fwd_r2p_kernel<true, 1>",), ("gqa", "causal", "flops_exact_per_launch"), "TFLOP/s",
+                   PEAK_BF16_TFLOPS, None),
+}
+
+
+def _kernel_stats(d):
+    import csv
+    import glob
+    rows = {}
+    for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows[r["Name"]] = r
+    return rows
+
+
+def _json_line(path):
+    with open(path) as f:
+        return json.loads([ln for ln in f if ln.startswith("{")][-1])
+
+
+def _dig(d, keys):
+    for k in keys:
+        d = d[k]
+    return d
+
+
+def summarize_profiles(root: str, names, copy_mib: int = 1024) -> None:
+    import re
+    traffic = {"file_digests": file_digests(), "copy_mib": copy_mib, "workloads": {}}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            old = json.load(f)
+        if old.get("file_digests") == traffic["file_digests"]:
+            traffic["workloads"].update(old.get("workloads", {}))
+    for name in names:
+        fname, title, kernels, work_key, unit, peak, algo_bytes = PROFILES[name]
+        d = os.path.join(root, name)
+        stats = _kernel_stats(os.path.join(d, "trace"))
+        prof, plain = _json_line(os.path.join(d, "trace.json")), _json_line(os.path.join(d, "plain.json"))
+        work = float(_dig(plain, work_key))
+        tr = counter_traffic(os.path.join(d, "fetch"), os.path.join(d, "write"), copy_mib)
+        traffic["workloads"][name] = tr
+        sq = {}
+        for c in SQ_COUNTERS:
+            for k, g in _counter_rows(os.path.join(d, "sq"), c).items():
+                if any(s in k for s in kernels):
+                    vs = max(g.values(), key=len)
+                    sq.setdefault(k, {})[c] = round(sum(vs) / len(vs))
+        mine = {k: r for k, r in stats.items() if any(s in k for s in kernels)}
+        ns = sum(float(r["AverageNs"]) for r in mine.values())
+        rate = work / ns * (1e-3 if unit == "TFLOP/s" else 1.0)   # FLOP/ns -> TFLOP/s = 1e-3 x; B/ns = GB/s
+        short = {k: (re.search(r"::(\w+_kernel(?:<[^>]*>)?)\(", k) or [None, k])[1] for k in stats}
+        lines = [f"# {title}", "",
+                 f"Environment: one MI355X (gfx950), ROCm 7.2 rocprofv3. Kernel sources digest "
+                 f"`{kernel_source_digest()}`; per-file digests of the counter passes in `profiles/traffic.json`.",
+                 "", "Commands (from `/tmp` after `export TMPDIR=/tmp`; `$R` is the repository root; "
+                 "each a run of its own):", "", "```",
+                 f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/{name}/trace -o run "
+                 f"-- python3 $R/bench.py --only {name} --steps {PROFILE_STEPS['trace'][0]} "
+                 f"--warmup {PROFILE_STEPS['trace'][1]}",
+                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/{name}/fetch -o pmc -- "
+                 f"python3 $R/bench.py --only {name} --steps {PROFILE_STEPS['counters'][0]} "
+                 f"--warmup {PROFILE_STEPS['counters'][1]} --calib-copy-mib {copy_mib}",
+                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/{name}/write -o pmc -- "
+                 f"python3 $R/bench.py --only {name} --steps {PROFILE_STEPS['counters'][0]} "
+                 f"--warmup {PROFILE_STEPS['counters'][1]} --calib-copy-mib {copy_mib}",
+                 f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d $R/gpurun_out/prof/{name}/sq -o pmc "
+                 f"-- python3 $R/bench.py --only {name} --steps {PROFILE_STEPS['counters'][0]} "
+                 f"--warmup {PROFILE_STEPS['counters'][1]}",
+                 f"python3 $R/bench.py --only {name}    # unprofiled, same box",
+                 f"python3 $R/bench.py --summarize-profiles $R/gpurun_out/prof {name}   # writes this file", "```",
+                 "", "## Kernel trace (all dispatches of the traced run)", "",
+                 "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+        for k, r in sorted(stats.items(), key=lambda kv: -float(kv[1]["TotalDurationNs"])):
+            lines.append(f"| `{short[k]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                         f"{float(r['MaxNs']):.0f} |")
+        lines += ["", f"Algorithmic work per call: {work:.6g} {'FLOP' if unit == 'TFLOP/s' else 'bytes'} "
+                      f"(bench.py `{'.'.join(work_key)}`). Kernels of one call: "
+                      + ", ".join(f"`{short[k]}` {float(r['AverageNs']) / 1e3:.2f} us" for k, r in mine.items())
+                      + f", together {ns / 1e3:.2f} us -> **{rate:.1f} {unit}** at the rocprof averages "
+                        f"({100 * rate / peak:.1f}% of the {peak:g} {unit} peak).",
+                  "", f"bench.py (HIP events on the launch stream, caches flushed before each launch): unprofiled "
+                      f"run {_bench_rate(plain, name)}; in the traced run {_bench_rate(prof, name)}.",
+                  "", "## HBM traffic per call (FETCH_SIZE / WRITE_SIZE, calibrated)", "",
+                  f"Calibration: a {copy_mib} MiB device copy in each counter run; scale factors "
+                  f"x{tr['fetch_scale']:.3f} (fetch) and x{tr['write_scale']:.3f} (write).", "",
+                  "| kernel | fetched bytes | written bytes |", "|---|---|---|"]
+        tot = 0.0
+        for k, v in tr["kernels"].items():
+            if any(sname in k for sname in kernels):
+                lines.append(f"| `{short.get(k, k)}` | {v['fetch_bytes']:.4g} | {v['write_bytes']:.4g} |")
+                tot += v["hbm_bytes"]
+        ref = algo_bytes if algo_bytes is not None else (work if unit == "GB/s" else None)
+        lines.append("")
+        lines.append(f"Total {tot:.4g} bytes" + (f" against {ref:.4g} algorithmic (ratio {tot / ref:.3f})." if ref
+                                                 else "."))
+        lines += ["", "## SQ counters (mean per dispatch)", "", "```", json.dumps(
+            {short.get(k, k): v for k, v in sq.items()}, indent=1), "```", ""]
+        with open(os.path.join(HERE, "profiles", fname + ".md"), "w") as f:
+            f.write("\n".join(lines))
+        print(f"wrote profiles/{fname}.md: {rate:.1f} {unit}")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+
+
+def _bench_rate(j, name):
+    if name == "prefill":
+        return f"median {j['prefill_ms']['median']} ms = {j['value']} TFLOP/s (batch spread {j['prefill_ms']['batch_spread']})"
+    if name == "decode":
+        return f"median {j['decode']['ms']} ms = {j['decode']['gbps']} GB/s"
+    if name == "chunked":
+        c = j["chunked_prefill"]
+        return f"median {c['ms']} ms = {c['tflops']} TFLOP/s (in place: {c['in_place']['ms']} ms)"
+    if name in ("decode_fp8", "decode_mqa"):
+        r = j["decode_fp8_kv_64seq_Hq32_Hkv8" if name == "decode_fp8" else "decode_mqa_64seq_Hq32_Hkv1"]
+        return f"median {r['ms']} ms = {r['gbps']} GB/s"
+    if name in ("fp8_prefill", "backward"):
+        return f"median {j[name]['ms']} ms = {j[name]['tflops']} TFLOP/s"
+    if name.startswith("gqa_"):
+        r = j["gqa"][name[4:]]
+        return f"median {r['ms']} ms = {r['tflops_exact']} TFLOP/s over the allowed pairs"
+    return ""
+
+
+BATCHES = 4  # timed steps are split into this many consecutive batches
+
+
+def batch_stats(ms, batches: int = BATCHES) -> dict:
+    """Timing summary of consecutive launches: the median of each of `batches` consecutive
+    batches, the overall median, mean, min and max, and the spread between the batch
+    medians ((max - min) / overall median). The page that benchmarks FA3/FA4-class kernels
+    accepted runs whose batches agreed within 0.3%; the figures here use the overall median."""
+    a = np.asarray(ms, dtype=np.float64)
+    parts = np.array_split(a, max(1, min(batches, a.size)))
+    meds = [float(np.median(x)) for x in parts]
+    med = float(np.median(a))
+    return {"median": round(med, 4), "avg": round(float(a.mean()), 4), "min": round(float(a.min()), 4),
+            "max": round(float(a.max()), 4), "batch_medians": [round(m, 4) for m in meds],
+            "batch_spread": round((max(meds) - min(meds)) / med, 4) if med > 0 else 0.0}
+
+
+def _timed(torch, fn, flush, reps: int, warmup: int = 3) -> dict:
+    """batch_stats of fn over reps launches, HIP events on the current stream around each
+    launch, caches flushed before each. A few flushed launches first: the first ones after
+    a different workload run measurably slower (clock and cache state)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for _ in range(warmup):
         flush()
@@ -186,7 +366,7 @@ def _timed(torch, fn, flush, reps: int, warmup: int = 3) -> float:
         fn()
         b.record()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return batch_stats([a.elapsed_time(b) for a, b in ev])
 
 
 PEAK_F32_TFLOPS = 157.3  # fp32 matrix cores, dense
@@ -203,21 +383,23 @@ def measure_sweep(attn, torch, workloads, dev, flush, reps: int) -> dict:
                 c = workloads.config_sweep(n, d, dt)
                 q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
                 o = torch.empty_like(q)
-                ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
+                st = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
+                ms = st["median"]
                 tf = prefill_flops(c.batch, c.num_q_heads, n, n, d) / ms / 1e9
-                res[f"{dt}_N{n}_D{d}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
+                res[f"{dt}_N{n}_D{d}"] = {"ms": ms, "batch_spread": st["batch_spread"], "tflops": round(tf, 1),
+                                          "frac_of_peak": round(tf / peak, 4)}
                 del q, k, v, o
     return res
 
 
-def measure_gqa(attn, torch, workloads, dev, flush, reps: int) -> dict:
+def measure_gqa(attn, torch, workloads, dev, flush, reps: int, variants=None) -> dict:
     """The causal GQA prefill family B=4 Hq=32 Hkv=8 N=4096 D=128 bf16 (plain causal, window
     1024, softcap 30, ragged lengths U[1024, 4096]) and the small fp32 case B=2 H=4 N=64 D=32
     (events around each launch, caches flushed before each). TFLOP/s two ways: `nominal`
     counts 4*B*Hq*N^2*D, halved for causal (ragged: per sequence); `exact` counts 4*D*Hq per
     (query, key) pair the mask allows."""
     res = {}
-    for var in workloads.GQA_VARIANTS:
+    for var in (workloads.GQA_VARIANTS if variants is None else variants):
         c = workloads.config_gqa(var)
         q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
         kw = dict(causal=c.causal, window=c.window, softcap=c.softcap)
@@ -229,81 +411,94 @@ def measure_gqa(attn, torch, workloads, dev, flush, reps: int) -> dict:
         else:
             lens = np.full(c.batch, c.seqlen_q, dtype=np.int64)
         o = torch.empty_like(q)
-        ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, **kw), flush, reps)
+        st = _timed(torch, lambda: attn.fwd(q, k, v, out=o, **kw), flush, reps)
+        ms = st["median"]
         nominal = sum(4.0 * c.num_q_heads * int(n) * int(n) * c.head_dim / 2 for n in lens)
         exact = sum(4.0 * c.head_dim * c.num_q_heads * allowed_pairs(int(n), int(n), True, c.window) for n in lens)
-        res[var] = {"ms": round(ms, 4), "tflops_nominal": round(nominal / ms / 1e9, 1),
+        res[var] = {"ms": ms, "batch_spread": st["batch_spread"], "flops_exact_per_launch": exact,
+                    "tflops_nominal": round(nominal / ms / 1e9, 1),
                     "tflops_exact": round(exact / ms / 1e9, 1),
                     "frac_of_peak_exact": round(exact / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, o
-    c = workloads.config_small_f32()
-    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
-    o = torch.empty_like(q)
-    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
-    fl = prefill_flops(c.batch, c.num_q_heads, c.seqlen_q, c.seqlen_k, c.head_dim)
-    res["small_f32_B2_H4_N64_D32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 3),
-                                      "note": "launch-bound (4.2 MFLOP)"}
+    if variants is None:
+        c = workloads.config_small_f32()
+        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+        o = torch.empty_like(q)
+        ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)["median"]
+        fl = prefill_flops(c.batch, c.num_q_heads, c.seqlen_q, c.seqlen_k, c.head_dim)
+        res["small_f32_B2_H4_N64_D32"] = {"ms": ms, "tflops": round(fl / ms / 1e9, 3),
+                                          "note": "launch-bound (4.2 MFLOP)"}
     return res
 
 
-def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
-    """Timings of the variants beside the main workloads: the 16-bit prefill at head dims
-    96 / 192 / 256 (causal B=2 H=16 N=4096 bf16), the headline prefill with a per-head
-    sink, the decode workload with fp8 e4m3 KV, and with one KV head (MQA); decode bytes =
-    the KV cache read once."""
+def measure_headdims(attn, torch, workloads, dev, flush, reps: int, dims=(96, 192, 256)) -> dict:
+    """The 16-bit prefill at head dims 96 / 192 / 256 (causal B=2 H=16 N=4096 bf16)."""
     res = {}
-    for d in (96, 192, 256):
+    for d in dims:
         c = workloads.config_headdim(d)
         q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
         o = torch.empty_like(q)
-        ms = _timed(torch, lambda: attn.fwd(q, k, v, causal=True, out=o), flush, reps)
+        st = _timed(torch, lambda: attn.fwd(q, k, v, causal=True, out=o), flush, reps)
+        ms = st["median"]
         fl = 4.0 * d * c.num_q_heads * c.batch * allowed_pairs(c.seqlen_q, c.seqlen_k, True)
-        res[f"prefill_causal_B2_H16_N4096_D{d}"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+        res[f"prefill_causal_B2_H16_N4096_D{d}"] = {"ms": ms, "batch_spread": st["batch_spread"],
+                                                    "tflops": round(fl / ms / 1e9, 1),
                                                     "frac_of_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, o
+    return res
+
+
+def measure_sink(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """The headline prefill with a per-head sink, beside the same launch without one (timed
+    right before it as a control: the variants run after the main workloads, at a different
+    clock than the main prefill loop)."""
     pc = workloads.config_headline()
     q, k, v = pc.q.to(dev), pc.k.to(dev), pc.v.to(dev)
     o = torch.empty_like(q)
     sinks = torch.linspace(-2.0, 6.0, pc.num_q_heads, dtype=torch.float32, device=dev)
     fl = prefill_flops(pc.batch, pc.num_q_heads, pc.seqlen_q, pc.seqlen_k, pc.head_dim)
-    # the same launch without the sink, timed right before it as a control (the variants
-    # run after the main workloads, at a different clock than the main prefill loop)
-    ms0 = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)
-    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, sinks=sinks), flush, reps)
-    res["prefill_headline_with_sink"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-                                         "control_without_sink_ms": round(ms0, 4)}
-    del q, k, v, o
-    dc8 = workloads.config_decode("fp8_e4m3")
-    t8 = dict(q=dc8.q.to(dev), k=dc8.k_cache.to(dev), v=dc8.v_cache.to(dev),
-              bt=torch.from_numpy(dc8.block_table).to(dev), sl=torch.from_numpy(dc8.seq_lens).to(dev),
-              ks=torch.from_numpy(dc8.k_scale).to(dev), vs=torch.from_numpy(dc8.v_scale).to(dev))
-    ws8 = torch.empty(attn.decode_workspace_size(num_seqs=dc8.num_seqs, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                                                 max_pages_per_seq=dc8.max_pages, max_seq_len=dc8.max_seq_len,
-                                                 q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn),
-                      dtype=torch.uint8, device=dev)
-    o8 = torch.empty_like(t8["q"])
-    ms = _timed(torch, lambda: attn.decode_paged(t8["q"], t8["k"], t8["v"], t8["bt"], t8["sl"], dc8.max_seq_len,
-                                                 k_scale=t8["ks"], v_scale=t8["vs"], out=o8, workspace=ws8),
-                flush, reps)
-    nb = decode_bytes(dc8, kv_elt=1)
-    res["decode_fp8_kv_64seq_Hq32_Hkv8"] = {"ms": round(ms, 4), "gbps": round(nb / ms / 1e6, 1),
-                                            "frac_of_peak": round(nb / ms / 1e6 / PEAK_HBM_GBPS, 4),
-                                            "bytes_per_launch": nb}
-    del t8, ws8, o8, dc8
-    dc = workloads.config_decode("bf16", num_kv_heads=1)
+    ms0 = _timed(torch, lambda: attn.fwd(q, k, v, out=o), flush, reps)["median"]
+    ms = _timed(torch, lambda: attn.fwd(q, k, v, out=o, sinks=sinks), flush, reps)["median"]
+    return {"prefill_headline_with_sink": {"ms": ms, "tflops": round(fl / ms / 1e9, 1),
+                                           "control_without_sink_ms": ms0}}
+
+
+def measure_decode_variant(attn, torch, workloads, dev, flush, reps: int, kind: str) -> dict:
+    """The decode workload with fp8 e4m3 KV (kind "fp8"), or with one KV head (MQA, kind
+    "mqa"); decode bytes = the KV cache read once plus Q, O, block-table entries and lengths."""
+    if kind == "fp8":
+        dc = workloads.config_decode("fp8_e4m3")
+        kv_t, kv_elt, name = torch.float8_e4m3fn, 1, "decode_fp8_kv_64seq_Hq32_Hkv8"
+    else:
+        dc = workloads.config_decode("bf16", num_kv_heads=1)
+        kv_t, kv_elt, name = torch.bfloat16, 2, "decode_mqa_64seq_Hq32_Hkv1"
     t = dict(q=dc.q.to(dev), k=dc.k_cache.to(dev), v=dc.v_cache.to(dev), bt=torch.from_numpy(dc.block_table).to(dev),
              sl=torch.from_numpy(dc.seq_lens).to(dev))
-    ws = torch.empty(attn.decode_workspace_size(num_seqs=dc.num_seqs, num_q_heads=32, num_kv_heads=1, head_dim=128,
+    kw = {}
+    if kind == "fp8":
+        kw = dict(k_scale=torch.from_numpy(dc.k_scale).to(dev), v_scale=torch.from_numpy(dc.v_scale).to(dev))
+    ws = torch.empty(attn.decode_workspace_size(num_seqs=dc.num_seqs, num_q_heads=dc.num_q_heads,
+                                                num_kv_heads=dc.num_kv_heads, head_dim=128,
                                                 max_pages_per_seq=dc.max_pages, max_seq_len=dc.max_seq_len,
-                                                q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16),
+                                                q_dtype=torch.bfloat16, kv_dtype=kv_t),
                      dtype=torch.uint8, device=dev)
     od = torch.empty_like(t["q"])
-    ms = _timed(torch, lambda: attn.decode_paged(t["q"], t["k"], t["v"], t["bt"], t["sl"], dc.max_seq_len, out=od,
-                                                 workspace=ws), flush, reps)
-    nb = decode_bytes(dc, kv_elt=2)
-    res["decode_mqa_64seq_Hq32_Hkv1"] = {"ms": round(ms, 4), "gbps": round(nb / ms / 1e6, 1),
-                                         "frac_of_peak": round(nb / ms / 1e6 / PEAK_HBM_GBPS, 4),
-                                         "bytes_per_launch": nb}
+    st = _timed(torch, lambda: attn.decode_paged(t["q"], t["k"], t["v"], t["bt"], t["sl"], dc.max_seq_len, out=od,
+                                                 workspace=ws, **kw), flush, reps)
+    ms = st["median"]
+    nb = decode_bytes(dc, kv_elt=kv_elt)
+    return {name: {"ms": ms, "batch_spread": st["batch_spread"], "gbps": round(nb / ms / 1e6, 1),
+                   "frac_of_peak": round(nb / ms / 1e6 / PEAK_HBM_GBPS, 4), "bytes_per_launch": nb}}
+
+
+def measure_variants(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """Timings of the variants beside the main workloads: the 16-bit prefill at head dims
+    96 / 192 / 256, the headline prefill with a per-head sink, the decode workload with fp8
+    e4m3 KV, and with one KV head (MQA)."""
+    res = measure_headdims(attn, torch, workloads, dev, flush, reps)
+    res.update(measure_sink(attn, torch, workloads, dev, flush, reps))
+    res.update(measure_decode_variant(attn, torch, workloads, dev, flush, reps, "fp8"))
+    res.update(measure_decode_variant(attn, torch, workloads, dev, flush, reps, "mqa"))
     return res
 
 
@@ -353,14 +548,65 @@ def measure_peaks(attn, torch, dev) -> dict:
     return {"mfma_bf16_32x32x16_one_wave_per_simd": out, "hbm_read_nontemporal_gbps": round(gbps, 1)}
 
 
+ONLY_MAIN = ("prefill", "decode", "chunked")
+ONLY_EXTRA = ("fp8_prefill", "backward", "decode_fp8", "decode_mqa", "gqa_causal", "gqa_window", "gqa_softcap",
+              "gqa_ragged", "headdim96", "headdim192", "headdim256", "sink", "sweep")
+
+
+def cpu_description() -> dict:
+    """CPU model and the BLAS library numpy uses (the oracle's matrix products)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        deps = np.show_config(mode="dicts").get("Build Dependencies", {})
+        b = deps.get("blas", {})
+        blas = f"{b.get('name', 'unknown')} {b.get('version', '')}".strip()
+    except Exception:  # numpy without the dict form of its build configuration
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def cpu_baseline(pc, seconds: float) -> dict:
+    """The CPU oracle (float64 numpy, score matrix materialised) on whole heads of the headline
+    prefill until about `seconds` of CPU time, on this host's cores."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    scale = oracle.default_scale(pc.head_dim)
+    done, spent, per_head = 0, 0.0, []
+    while done < pc.num_q_heads and spent < seconds:
+        h = done
+        qh = oracle.tensor_to_f64(pc.q[0, h:h + 1], "bf16")
+        kh = oracle.tensor_to_f64(pc.k[0, h:h + 1], "bf16")
+        vh = oracle.tensor_to_f64(pc.v[0, h:h + 1], "bf16")
+        t = time.perf_counter()
+        oracle.sdpa_fp64(qh, kh, vh, scale=scale)
+        dt = time.perf_counter() - t
+        spent += dt
+        per_head.append(dt)
+        done += 1
+    tflops = prefill_flops(1, done, pc.seqlen_q, pc.seqlen_k, pc.head_dim) / spent / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of 32 heads of the same N=8192 D=128 prefill, float64 numpy, {spent:.1f} s "
+                      f"(median {float(np.median(per_head)):.3f} s per head)",
+            **cpu_description()}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-decode", action="store_true", help="time the prefill only")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="run only the decode (per-kernel counter passes; prints decode timing only)")
+    ap.add_argument("--only", choices=ONLY_MAIN + ONLY_EXTRA,
+                    help="time one workload alone (profiled runs: one workload per kernel name)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the paged decode in the main step")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked prefill over the paged cache")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 e4m3 prefill")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
@@ -374,15 +620,13 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc output folders "
-                         "(FETCH_SIZE, WRITE_SIZE) of runs made with --calib-copy-mib")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar=("ROOT", "NAME"),
+                    help="write profiles/<workload>.md and profiles/traffic.json from the rocprofv3 folders "
+                         "ROOT/NAME/{trace,fetch,write,sq} and ROOT/NAME/{trace,plain}.json of each NAME")
     args = ap.parse_args(argv)
 
-    if args.summarize_counters:
-        res = summarize_counters(*args.summarize_counters, copy_mib=args.calib_copy_mib or 1024,
-                                 out_path=TRAFFIC_FILE)
-        print(json.dumps(res, indent=1))
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles[0], args.summarize_profiles[1:], args.calib_copy_mib or 1024)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -396,6 +640,43 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    only = args.only
+    run_pre = only in (None, "prefill")
+    run_dec = only == "decode" or (only is None and not args.no_decode)
+    run_chk = only == "chunked" or (only is None and not args.no_chunked)
+
+    flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            attn.flush_caches(flush_buf)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if only in ONLY_EXTRA:
+        out = {"only": only, "steps": args.steps}
+        if only == "fp8_prefill":
+            out["fp8_prefill"] = measure_fp8_prefill(attn, torch, workloads, dev, flush, args.steps)
+        elif only == "backward":
+            out["backward"] = measure_backward(attn, torch, workloads, dev, flush, args.steps)
+        elif only in ("decode_fp8", "decode_mqa"):
+            out.update(measure_decode_variant(attn, torch, workloads, dev, flush, args.steps, only[7:]))
+        elif only.startswith("gqa_"):
+            out["gqa"] = measure_gqa(attn, torch, workloads, dev, flush, args.steps, variants=(only[4:],))
+        elif only.startswith("headdim"):
+            out.update(measure_headdims(attn, torch, workloads, dev, flush, args.steps, dims=(int(only[7:]),)))
+        elif only == "sink":
+            out.update(measure_sink(attn, torch, workloads, dev, flush, args.steps))
+        elif only == "sweep":
+            out["sweep"] = measure_sweep(attn, torch, workloads, dev, flush, args.steps)
+        print(json.dumps(out), flush=True)
+        return 0
 
     # ---------------------------------------------------------------- inputs ----
     pc = workloads.config_headline()
@@ -404,7 +685,7 @@ def main(argv=None):
     flops = prefill_flops(pc.batch, pc.num_q_heads, pc.seqlen_q, pc.seqlen_k, pc.head_dim)
 
     dec = None
-    if not args.no_decode:
+    if run_dec:
         dc = workloads.config_decode("bf16")
         dt = {"q": dc.q.to(dev), "k": dc.k_cache.to(dev), "v": dc.v_cache.to(dev),
               "bt": torch.from_numpy(dc.block_table).to(dev), "sl": torch.from_numpy(dc.seq_lens).to(dev)}
@@ -418,7 +699,7 @@ def main(argv=None):
         del dc.k_cache, dc.v_cache  # host copies no longer needed
 
     chk = None
-    if not args.no_chunked and not args.no_prefill:
+    if run_chk:
         cc = workloads.config_chunked_prefill()
         ct = {"q": cc.q.to(dev), "k": cc.cache.k_cache.to(dev), "v": cc.cache.v_cache.to(dev),
               "bt": torch.from_numpy(cc.cache.block_table).to(dev),
@@ -431,15 +712,8 @@ def main(argv=None):
         chk = (cc, ct, chunked_flops(cc))
         del cc.cache.k_cache, cc.cache.v_cache
 
-    flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
-    def flush():
-        if flush_buf is not None:
-            attn.flush_caches(flush_buf)
-
     def run_prefill():
-        if not args.no_prefill:
-            attn.fwd(q, k, v, out=o)
+        attn.fwd(q, k, v, out=o)
 
     def run_decode():
         dc, dt, _ = dec
@@ -451,16 +725,13 @@ def main(argv=None):
         attn.fwd_paged(ct["q"], ct["k"], ct["v"], ct["bt"], ct["cu"], ct["sl"], cc.max_seqlen_q, causal=True,
                        out=ct["o"], workspace=ct["ws"] if gather else None, gather=gather)
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-
     # ------------------------------------------------------------------- timing ----
+    # A step is one pass of the hot path: the headline prefill, the paged decode and the
+    # chunked prefill (both routes), each launch between its own pair of HIP events on the
+    # stream it runs on, the caches flushed before each.
     for _ in range(args.warmup):
-        run_prefill()
+        if run_pre:
+            run_prefill()
         if dec:
             run_decode()
         if chk:
@@ -473,10 +744,11 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        flush()
-        ev[i][0].record(stream)
-        run_prefill()
-        ev[i][1].record(stream)
+        if run_pre:
+            flush()
+            ev[i][0].record(stream)
+            run_prefill()
+            ev[i][1].record(stream)
         if dec:
             flush()
             ev[i][2].record(stream)
@@ -494,18 +766,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    if args.no_prefill:
-        if dec:
-            dms = [e[2].elapsed_time(e[3]) for e in ev]
-            print(json.dumps({"decode_ms": round(float(np.mean(dms)), 4),
-                              "decode_gbps": round(dec[2] / (float(np.mean(dms)) * 1e-3) / 1e9, 1)}))
-        return 0
-    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    pre_avg = float(np.mean(pre_ms))
-    tflops = flops / (pre_avg * 1e-3) / 1e12
     out = {
         "metric": "attn fwd TFLOP/s & % bf16 MFMA peak (N=8192,D=128); decode GB/s % HBM peak",
-        "value": round(tflops, 2),
+        "value": None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -516,98 +779,75 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, no weights)",
-        "config": {"workload": "dense non-causal attention fwd B=1 H=32 N=8192 D=128 bf16"
-                               + ("" if args.no_decode else
+        "config": {"workload": ("dense non-causal attention fwd B=1 H=32 N=8192 D=128 bf16" if run_pre else "")
+                               + ("" if dec is None else
                                   " + paged split-KV decode 64 seqs L~U[512,32768] Hq=32 Hkv=8 D=128 bf16 KV")
                                + ("" if chk is None else
                                   " + chunked prefill 8x2048 queries over U[0,14336] paged context, causal, "
                                   "Hq=32 Hkv=8 D=128 bf16"),
                    "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
-        "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4), "max": round(max(pre_ms), 4)},
+        "timing": f"per launch: HIP events on the launch stream, caches flushed before each; {args.steps} steps "
+                  f"in {min(BATCHES, args.steps)} consecutive batches; figures from the overall median",
         "kernel_source_digest": kernel_source_digest(),
     }
-    traffic = load_traffic(PREFILL_KERNEL)
-    out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                       "kernel": "fwd_r2_kernel<bf16, no mask>",
-                       "flops_per_launch": flops}
+    if only is not None:
+        out["only"] = only
+    tflops = None
+    if run_pre:
+        pst = batch_stats([e[0].elapsed_time(e[1]) for e in ev])
+        tflops = flops / (pst["median"] * 1e-3) / 1e12
+        out["value"] = round(tflops, 2)
+        out["prefill_ms"] = pst
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                           "traffic": load_traffic("prefill", PREFILL_KERNELS),
+                           "kernel": "fwd_r2p_kernel<bf16, no mask> (persistent: one workgroup per CU)",
+                           "flops_per_launch": flops}
     if dec:
         dc, _, nbytes = dec
-        dms = [e[2].elapsed_time(e[3]) for e in ev]
-        davg = float(np.mean(dms))
-        gbps = nbytes / (davg * 1e-3) / 1e9
-        out["decode"] = {"gbps": round(gbps, 1), "ms": round(davg, 4), "bytes_per_launch": nbytes,
+        dst_ = batch_stats([e[2].elapsed_time(e[3]) for e in ev])
+        gbps = nbytes / (dst_["median"] * 1e-3) / 1e9
+        out["decode"] = {"gbps": round(gbps, 1), "ms": dst_["median"], "timing": dst_, "bytes_per_launch": nbytes,
                          "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                                       "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                                      "traffic": load_traffic(DECODE_KERNELS),
+                                      "traffic": load_traffic("decode", DECODE_KERNELS),
                                       "kernels": "decode_split_kernel + decode_combine_kernel"}}
     if chk:
         cc, _, cflops = chk
-        cms = [e[4].elapsed_time(e[5]) for e in ev]
-        cavg = float(np.mean(cms))
-        ctf = cflops / (cavg * 1e-3) / 1e12
-        dms_ = [e[6].elapsed_time(e[7]) for e in ev]
-        davg_ = float(np.mean(dms_))
-        out["chunked_prefill"] = {"tflops": round(ctf, 2), "ms": round(cavg, 4), "flops_per_launch": cflops,
+        cst = batch_stats([e[4].elapsed_time(e[5]) for e in ev])
+        ctf = cflops / (cst["median"] * 1e-3) / 1e12
+        ist = batch_stats([e[6].elapsed_time(e[7]) for e in ev])
+        out["chunked_prefill"] = {"tflops": round(ctf, 2), "ms": cst["median"], "timing": cst,
+                                  "flops_per_launch": cflops,
                                   "route": "page copy into the workspace + ragged prefill kernel (both timed)",
                                   "keys_per_sequence": cc.seq_lens_k.tolist(),
                                   "roofline": {"bound": "mfma", "achieved": round(ctf, 2), "peak": PEAK_BF16_TFLOPS,
                                                "unit": "TFLOP/s", "frac": round(ctf / PEAK_BF16_TFLOPS, 4),
-                                               "traffic": load_traffic(CHUNKED_KERNEL),
+                                               "traffic": load_traffic("chunked", CHUNKED_KERNEL),
                                                "kernel": "gather_kv_pages_kernel + fwd_r2_kernel<bf16, masked>"},
-                                  "in_place": {"tflops": round(cflops / (davg_ * 1e-3) / 1e12, 2),
-                                               "ms": round(davg_, 4),
+                                  "in_place": {"tflops": round(cflops / (ist["median"] * 1e-3) / 1e12, 2),
+                                               "ms": ist["median"], "timing": ist,
                                                "kernel": "fwd_mfma16_kernel<128, 8, 64, bf16, paged>"}}
     out["cache_flush_before_each_launch"] = flush_buf is not None
 
-    # ----------------------------------------------------------- fp8 prefill ----
-    if not args.no_fp8 and not args.no_prefill:
-        fc = workloads.config_fp8_headline()
-        fq, fk, fv = fc.q.to(dev), fc.k.to(dev), fc.v.to(dev)
-        fo = torch.empty(fq.shape, dtype=torch.bfloat16, device=dev)
-        fms = _timed(torch, lambda: attn.fwd(fq, fk, fv, out=fo, q_scale=fc.q_scale, k_scale=fc.k_scale,
-                                             v_scale=fc.v_scale), flush, args.steps)
-        ftf = flops / (fms * 1e-3) / 1e12
-        out["fp8_prefill"] = {"tflops": round(ftf, 2), "ms": round(fms, 4), "flops_per_launch": flops,
-                              "workload": "dense non-causal B=1 H=32 N=8192 D=128, Q/K/V fp8 e4m3 with "
-                                          "per-tensor scales, O bf16",
-                              "roofline": {"bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_FP8_TFLOPS,
-                                           "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
-                                           "traffic": load_traffic(FP8_KERNEL), "kernel": "fwd_fp8_kernel"}}
-        del fq, fk, fv, fo
-
-    # -------------------------------------------------------------- backward ----
-    if not args.no_bwd and not args.no_prefill:
-        bc = workloads.config_backward()
-        bq, bk, bv = bc.q.to(dev), bc.k.to(dev), bc.v.to(dev)
-        bdo = workloads.make_grad_out(bc.q.shape, seed=11).to(dev)
-        bo, blse = attn.fwd(bq, bk, bv, causal=True, return_lse=True)
-        bws = torch.empty(attn.bwd_workspace_size(bc.q, bc.k), dtype=torch.uint8, device=dev)
-        bms = _timed(torch, lambda: attn.bwd(bq, bk, bv, bo, bdo, blse, causal=True, workspace=bws), flush, args.steps)
-        # five products per allowed (query, key) pair against the forward's two: 2.5x its FLOPs
-        bfl = 2.5 * 4.0 * bc.head_dim * bc.num_q_heads * bc.batch * allowed_pairs(bc.seqlen_q, bc.seqlen_k, True)
-        btf = bfl / (bms * 1e-3) / 1e12
-        out["backward"] = {"tflops": round(btf, 2), "ms": round(bms, 4), "flops_per_launch": bfl,
-                           "workload": "causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16, dQ dK dV",
-                           "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
-                                        "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
-                                        "traffic": load_traffic(BWD_KERNELS),
-                                        "kernels": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}}
-        del bq, bk, bv, bdo, bo, blse, bws
-
-    # ------------------------------------------------------------ variants ----
-    if not args.no_variants and not args.no_prefill:
-        out["variants"] = measure_variants(attn, torch, workloads, dev, flush, args.steps)
-        out["sweep"] = measure_sweep(attn, torch, workloads, dev, flush, args.steps)
-        out["gqa"] = measure_gqa(attn, torch, workloads, dev, flush, args.steps)
+    if only is None:
+        if not args.no_fp8:
+            out["fp8_prefill"] = measure_fp8_prefill(attn, torch, workloads, dev, flush, args.steps)
+        if not args.no_bwd:
+            out["backward"] = measure_backward(attn, torch, workloads, dev, flush, args.steps)
+        if not args.no_variants:
+            out["variants"] = measure_variants(attn, torch, workloads, dev, flush, args.steps)
+            out["sweep"] = measure_sweep(attn, torch, workloads, dev, flush, args.steps)
+            out["gqa"] = measure_gqa(attn, torch, workloads, dev, flush, args.steps)
 
     # ------------------------------------------------------- measured peaks ----
-    if not args.no_probes:
+    if only is None and not args.no_probes:
         peaks = measure_peaks(attn, torch, dev)
         out["measured_peaks"] = peaks
         mp = peaks["mfma_bf16_32x32x16_one_wave_per_simd"]["random_operands"]["tflops"]
-        out["roofline"]["measured_peak"] = mp
-        out["roofline"]["frac_of_measured"] = round(tflops / mp, 4)
+        if run_pre:
+            out["roofline"]["measured_peak"] = mp
+            out["roofline"]["frac_of_measured"] = round(tflops / mp, 4)
         if chk:
             out["chunked_prefill"]["roofline"]["measured_peak"] = mp
             out["chunked_prefill"]["roofline"]["frac_of_measured"] = round(out["chunked_prefill"]["tflops"] / mp, 4)
@@ -617,28 +857,49 @@ def main(argv=None):
             out["decode"]["roofline"]["frac_of_measured"] = round(out["decode"]["gbps"] / hp, 4)
 
     # ------------------------------------------------------------ CPU baseline ----
-    if not args.no_cpu:
-        import oracle
-        qh = oracle.tensor_to_f64(pc.q[0, :1], "bf16")
-        cores = len(os.sched_getaffinity(0))
-        scale = oracle.default_scale(pc.head_dim)
-        done, spent = 0, 0.0
-        while done < pc.num_q_heads and spent < args.cpu_seconds:
-            h = done
-            qh = oracle.tensor_to_f64(pc.q[0, h:h + 1], "bf16")
-            kh = oracle.tensor_to_f64(pc.k[0, h:h + 1], "bf16")
-            vh = oracle.tensor_to_f64(pc.v[0, h:h + 1], "bf16")
-            t = time.perf_counter()
-            oracle.sdpa_fp64(qh, kh, vh, scale=scale)
-            spent += time.perf_counter() - t
-            done += 1
-        cpu_tflops = prefill_flops(1, done, pc.seqlen_q, pc.seqlen_k, pc.head_dim) / spent / 1e12
-        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores,
-                               "kind": "oracle",
-                               "sample": f"{done} of 32 heads of the same N=8192 D=128 prefill, float64 numpy, "
-                                         f"{spent:.1f} s"}
+    if only is None and not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(pc, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measure_fp8_prefill(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """The fp8 e4m3 prefill at the headline shape (per-tensor scales, O bf16) against the
+    dense fp8 matrix-core peak."""
+    fc = workloads.config_fp8_headline()
+    fq, fk, fv = fc.q.to(dev), fc.k.to(dev), fc.v.to(dev)
+    fo = torch.empty(fq.shape, dtype=torch.bfloat16, device=dev)
+    st = _timed(torch, lambda: attn.fwd(fq, fk, fv, out=fo, q_scale=fc.q_scale, k_scale=fc.k_scale,
+                                        v_scale=fc.v_scale), flush, reps)
+    fms = st["median"]
+    flops = prefill_flops(fc.batch, fc.num_q_heads, fc.seqlen_q, fc.seqlen_k, fc.head_dim)
+    ftf = flops / (fms * 1e-3) / 1e12
+    return {"tflops": round(ftf, 2), "ms": fms, "timing": st, "flops_per_launch": flops,
+            "workload": "dense non-causal B=1 H=32 N=8192 D=128, Q/K/V fp8 e4m3 with per-tensor scales, O bf16",
+            "roofline": {"bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": load_traffic("fp8_prefill", FP8_KERNEL), "kernel": "fwd_fp8_kernel"}}
+
+
+def measure_backward(attn, torch, workloads, dev, flush, reps: int) -> dict:
+    """The backward of the causal GQA workload B=1 Hq=32 Hkv=8 N=4096 D=128 bf16 (events
+    around the launches of one call): five products per allowed (query, key) pair against
+    the forward's two, i.e. 2.5 x its FLOPs."""
+    bc = workloads.config_backward()
+    bq, bk, bv = bc.q.to(dev), bc.k.to(dev), bc.v.to(dev)
+    bdo = workloads.make_grad_out(bc.q.shape, seed=11).to(dev)
+    bo, blse = attn.fwd(bq, bk, bv, causal=True, return_lse=True)
+    bws = torch.empty(attn.bwd_workspace_size(bc.q, bc.k), dtype=torch.uint8, device=dev)
+    st = _timed(torch, lambda: attn.bwd(bq, bk, bv, bo, bdo, blse, causal=True, workspace=bws), flush, reps)
+    bms = st["median"]
+    bfl = 2.5 * 4.0 * bc.head_dim * bc.num_q_heads * bc.batch * allowed_pairs(bc.seqlen_q, bc.seqlen_k, True)
+    btf = bfl / (bms * 1e-3) / 1e12
+    return {"tflops": round(btf, 2), "ms": bms, "timing": st, "flops_per_launch": bfl,
+            "workload": "causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16, dQ dK dV",
+            "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic("backward", BWD_KERNELS),
+                         "kernels": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}}
 
 
 if __name__ == "__main__":
