@@ -59,24 +59,27 @@ constexpr int kBwdNW = 4;   // waves per workgroup (one per SIMD: the accumulato
 constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
 
 // ------------------------------------------------------------------------- Delta ----
-// One thread per query row: Delta = sum_d dO O in fp32 (both read as 16-bit).
+// Delta = sum_d dO O in fp32 (both read as 16-bit). D/8 consecutive lanes share a row, each
+// reading 16 bytes of it, so every load instruction of a wave covers 64 / (D/8) whole rows
+// of contiguous memory; the lanes of a row add their partial sums by lane exchanges.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over B * Hq * Nq
+  constexpr int LPR = D / 8;        // lanes per row
+  constexpr int RPB = 256 / LPR;    // rows per workgroup
   const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
-  if (row >= rows) return;
-  const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * D;
-  const uint16_t* d = static_cast<const uint16_t*>(p.dout) + row * D;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
   float acc = 0.0f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4_t a = load_global<u32x4_t>(o + 8 * c);
-    const u32x4_t b = load_global<u32x4_t>(d + 8 * c);
+  if (row < rows) {
+    const u32x4_t a = load_global<u32x4_t>(static_cast<const uint16_t*>(p.o) + row * D + 8 * c);
+    const u32x4_t b = load_global<u32x4_t>(static_cast<const uint16_t*>(p.dout) + row * D + 8 * c);
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       acc += lo16<BF16>(a[w]) * lo16<BF16>(b[w]) + hi16<BF16>(a[w]) * hi16<BF16>(b[w]);
   }
-  p.delta[row] = acc;
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += xor_shuffle(acc, off);
+  if (row < rows && c == 0) p.delta[row] = acc;
 }
 
 // One direct-to-LDS load of 4 bytes per lane: lane l's dword from base + voff (bytes) to
@@ -567,7 +570,9 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
 template <int D, bool BF16>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
-  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+  constexpr int kDeltaRows = 256 / (D / 8);  // rows per workgroup of bwd_delta_kernel
+  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + kDeltaRows - 1) / kDeltaRows)), dim3(256), 0,
+                     st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nkv4 = (int64_t)p.batch * p.hkv * p.nk * D / 4;  // float4s per accumulator slot
