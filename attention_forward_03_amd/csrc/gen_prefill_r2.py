@@ -20,7 +20,8 @@ Modes: 0 = no mask at all (every tile full, no causal / window / ragged tail); 1
 
 Schedule of a phase X(i) (one 32-key sub-tile): 32 steps, each with one matrix-core
 product (even steps S(i+1) = K Q^T, odd steps O^T += V^T P(i-1)^T) and a slice of the
-vector work on sub-tile i, software-pipelined so that no step waits on its own results:
+vector work on sub-tile i (emitted ahead of the step's LDS reads, wait and product),
+software-pipelined so that no step waits on its own results:
   step g: softcap / mask of score g (and, where row maxima are tracked, at odd g the max
   of the pair);   step g+1: FMA (scale, minus the reference) of score g;   step g+2:
   exp2 of score g;   step 2u+4: pack pair u to 16 bits;   steps 2u+4, 2u+5: add its two
@@ -390,6 +391,7 @@ class Gen:
         advance = list(advance)
         for st in range(NSTEP):
             is_s, idx, rb = st % 2 == 0, st // 4, (st // 2) % 2
+            mark0 = len(self.out)
             dma_now = None
             if dma is not None and st % DMA_EVERY == 0 and st // DMA_EVERY < 8:
                 n = st // DMA_EVERY
@@ -430,6 +432,7 @@ class Gen:
                 if vnofs is not None and rb == 0 and f >= 2 * NDB - PF:
                     g = f - (2 * NDB - PF)
                     self.read_v(vnofs, g, g, ("vn", g))
+            mark1 = len(self.out)
             if tail is not None:
                 self.tail_ops(st, tail)
             if soft:
@@ -477,6 +480,10 @@ class Gen:
                 for _ in range(per):
                     for line in advance.pop(0):
                         self.emit(line)
+            # The step's vector and scalar work goes ahead of its LDS reads, waits and
+            # product: the waits then come as late as they can, after work that does not
+            # need the fragments (0.9% fewer loop cycles, measured with timestamps).
+            self.out[mark0:] = self.out[mark1:] + self.out[mark0:mark1]
         assert not advance
         if soft and track and not maxonly:
             # any row max past its threshold (reference + slack, or a first unmasked key)?
