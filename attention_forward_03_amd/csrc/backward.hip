@@ -263,14 +263,22 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
     }
     const int q0 = qt_of(st);
-    // S = Q K^T (the fragment reads issued ahead of the products)
-    f32x16_t s = zero16;
+    // S = Q K^T and dP = dO V^T: two independent chains of products, interleaved so that
+    // each product's wait for its predecessor's result is covered by the other chain's
+    // (the fragment reads issued ahead of the products)
+    f32x16_t s = zero16, dp = zero16;
     {
-      u32x4_t qa[NKS];
+      u32x4_t qa[NKS], da[NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qa[ks] = *reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]);
+      for (int ks = 0; ks < NKS; ++ks) {
+        qa[ks] = *reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]);
+        da[ks] = *reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]);
+      }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
+        dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
+      }
     }
     // P (0 where the mask or the key range excludes the pair; a row without any allowed
     // key, whose LSE is -inf, has every pair excluded)
@@ -298,43 +306,29 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       const float e = fast_exp2(s[r] - lse[r >> 2][r & 3] * kLog2e);
       s[r] = ok ? e : 0.0f;
     }
-    // dV^T += dO^T P
-    u32x4_t pb[2];
+    // P and dS = P (dP - Delta) scale, packed to 16 bits as B operands
+    u32x4_t pb[2], sb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       pb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
                       pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(dl + t * 16 * D + rd_t[0][db]);
-        const u32x2_t up = lds_read_tr16(dl + t * 16 * D + rd_t[1][db]);
-        dv[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dv[db]);
-      }
-    // dP = dO V^T, then dS
-    f32x16_t dp = zero16;
-    {
-      u32x4_t da[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) da[ks] = *reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
-    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - del[r >> 2][r & 3]) * (p.scale * t2[r]);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      pb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
+      sb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
                       pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
-    // dK^T += Q^T dS
+    // dV^T += dO^T P and dK^T += Q^T dS, interleaved (independent accumulators)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(ql + t * 16 * D + rd_t[0][db]);
-        const u32x2_t up = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
-        dk[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dk[db]);
+        const u32x2_t vlo = lds_read_tr16(dl + t * 16 * D + rd_t[0][db]);
+        const u32x2_t vup = lds_read_tr16(dl + t * 16 * D + rd_t[1][db]);
+        const u32x2_t klo = lds_read_tr16(ql + t * 16 * D + rd_t[0][db]);
+        const u32x2_t kup = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
+        dv[db] = mfma32x32x16<BF16>(u32x4_t{vlo[0], vlo[1], vup[0], vup[1]}, pb[t], dv[db]);
+        dk[db] = mfma32x32x16<BF16>(u32x4_t{klo[0], klo[1], kup[0], kup[1]}, sb[t], dk[db]);
       }
     // the loads of step st + 1 are complete once at most those of st + 2 remain
     if (st + 2 < steps) {
