@@ -57,6 +57,7 @@ struct BwdSwizzle {
 
 constexpr int kBwdNW = 4;   // waves per workgroup (one per SIMD: the accumulators are large)
 constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
+static_assert(kBwdNW * 32 == kBwdKeyBlock, "a dK / dV workgroup owns one block of keys");
 
 // ------------------------------------------------------------------------- Delta ----
 // Delta = sum_d dO O in fp32 (both read as 16-bit). D/8 consecutive lanes share a row, each
@@ -121,6 +122,50 @@ struct TileLoader {
   }
 };
 
+// The query tiles (of kBwdBQ rows) that reach any key of the block starting at kb0: the
+// first tile's row and the count (causal: rows >= key - (Nk - Nq); window: rows < key + W
+// - (Nk - Nq), as the forward's mask).
+struct BwdQueryRange {
+  int q_lo, nqt;
+};
+__device__ __forceinline__ BwdQueryRange bwd_query_range(const BwdParams& p, int kb0) {
+  const int delta = p.nk - p.nq;
+  const int kb1 = min(p.nk, kb0 + kBwdNW * 32);
+  int q_lo = p.causal ? max(0, kb0 - delta) : 0;
+  const int q_hi = p.window > 0 ? min(p.nq, kb1 - 1 - delta + p.window) : p.nq;
+  q_lo = (q_lo / kBwdBQ) * kBwdBQ;
+  return {q_lo, q_hi > q_lo ? (q_hi - q_lo + kBwdBQ - 1) / kBwdBQ : 0};
+}
+
+// Steps (query head, query tile) of dK / dV item `item` (= key block * chunks + chunk).
+__device__ __forceinline__ int bwd_item_steps(const BwdParams& p, int item) {
+  const int all = bwd_query_range(p, (item / p.chunks) * (kBwdNW * 32)).nqt * p.group;
+  return min(max(all - (item % p.chunks) * p.chunk_steps, 0), p.chunk_steps);
+}
+
+// Run order of the dK / dV items of a unit (every unit has the same items): longest first,
+// so that the dispatcher, which starts workgroups in grid order as CUs free up, fills the
+// tail with short items (causal problems mix full chunks with short and empty ones). Item
+// i's place is the number of items with a larger key, plus those with an equal key and a
+// smaller index (a permutation, the same on every run); the key is the step count scaled
+// to 0..255. One thread per item; each workgroup first writes all keys into LDS.
+__global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t keys[kBwdOrderMax];
+  const int n = p.kblocks * p.chunks;
+  for (int i = threadIdx.x; i < n; i += 256)
+    keys[i] = (uint8_t)(bwd_item_steps(p, i) * 255 / p.chunk_steps);
+  __syncthreads();
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int ki = keys[i];
+  int place = 0;
+  for (int j = 0; j < n; ++j) {
+    const int kj = keys[j];
+    place += (kj > ki) | ((kj == ki) & (j < i));
+  }
+  p.order[place] = i;
+}
+
 // --------------------------------------------------------------------- dK and dV ----
 // Wave w of the workgroup owns keys kb0 + 32 w .. +31. Per query tile of 32 rows (staged
 // in LDS with its dO rows, LSE and Delta; three buffers, loaded two steps ahead, because a
@@ -149,25 +194,19 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  // XCD placement as in the forward: the items of one (sequence, KV head) unit run on one
-  // XCD (workgroup w runs on XCD w % 8) and share its L2 copy of the unit's Q and dO
-  // (measured neutral here: the kernel waits on load latency, not on HBM)
-  const int per = p.kblocks * p.chunks;  // items per unit
+  // Workgroup w runs place w / units of the run order for unit w % units (units = sequences
+  // x KV heads): the longest items of every unit come first. With a multiple of 8 units,
+  // all items of a unit run on one XCD (workgroup w runs on XCD w % 8) and share its L2
+  // copy of the unit's Q and dO.
+  const int units = p.batch * p.hkv;
   const int w = blockIdx.x;
-  int unit, item;
-  if (((p.batch * p.hkv) & 7) == 0) {
-    unit = (w & 7) + 8 * ((w >> 3) / per);
-    item = (w >> 3) % per;
-  } else {
-    unit = w / per;
-    item = w % per;
-  }
+  const int unit = w % units;
+  const int item = p.order != nullptr ? p.order[w / units] : w / units;
   const int g = unit % p.hkv, b = unit / p.hkv;
   const int kb0 = (item / p.chunks) * (kBwdNW * 32);
   const int chunk = item % p.chunks;
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
   const int key = kb0 + wave * 32 + l32;  // this lane's key column
-  const int kb1 = min(Lk, kb0 + kBwdNW * 32);
 
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.hkv + g) * Lk * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.hkv + g) * Lk * D;
@@ -182,10 +221,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     }
   }
   // the query rows that see any key of the block
-  int q_lo = p.causal ? max(0, kb0 - delta) : 0;
-  int q_hi = p.window > 0 ? min(Lq, kb1 - 1 - delta + p.window) : Lq;
-  q_lo = (q_lo / BQ) * BQ;
-  const int nqt = q_hi > q_lo ? (q_hi - q_lo + BQ - 1) / BQ : 0;
+  const BwdQueryRange qr = bwd_query_range(p, kb0);
+  const int q_lo = qr.q_lo, nqt = qr.nqt;
   const int G = p.group;
   const int all_steps = nqt * G;  // (head, query tile) pairs, head-major
   const bool cap = p.cap_out > 0.0f;
@@ -361,16 +398,10 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     }
 }
 
-// The number of dK / dV chunks that hold a partial for keys of block kb0 (the same range
-// arithmetic as bwd_dkdv_kernel).
+// The number of dK / dV chunks that hold a partial for keys of block kb0.
 __device__ __forceinline__ int bwd_chunks_of(const BwdParams& p, int kb0) {
-  const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
-  const int kb1 = min(Lk, kb0 + kBwdNW * 32);
-  int q_lo = p.causal ? max(0, kb0 - delta) : 0;
-  const int q_hi = p.window > 0 ? min(Lq, kb1 - 1 - delta + p.window) : Lq;
-  q_lo = (q_lo / kBwdBQ) * kBwdBQ;
-  const int nqt = q_hi > q_lo ? (q_hi - q_lo + kBwdBQ - 1) / kBwdBQ : 0;
-  return min(p.chunks, (nqt * p.group + p.chunk_steps - 1) / p.chunk_steps);
+  const int all = bwd_query_range(p, kb0).nqt * p.group;
+  return min(p.chunks, (all + p.chunk_steps - 1) / p.chunk_steps);
 }
 
 // Sum of a key's partial dK / dV slots in chunk order -> the output type (4 entries per thread)
@@ -574,6 +605,11 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   q.kblocks = (p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32);
   const int64_t nkv_items = (int64_t)q.kblocks * p.chunks * p.hkv * p.batch;
   if (nkv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (q.order != nullptr) {
+    const int n = q.kblocks * p.chunks;  // <= kBwdOrderMax (the table exists)
+    hipLaunchKernelGGL(bwd_order_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_convert_kernel<D, BF16>), dim3((unsigned)((nkv4 + 255) / 256)), dim3(256), 0, st, p);

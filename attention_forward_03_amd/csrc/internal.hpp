@@ -50,6 +50,8 @@ struct BwdParams {
   float* delta;         // workspace [B, Hq, Nq]
   float* dk32;          // workspace [chunks][B, Hkv, Nk, D] fp32 partial dK, then dv32 alike
   float* dv32;
+  int32_t* order;       // workspace [bwd_order_entries]: the (key block, chunk) items of a
+                        // unit, longest first; NULL: run them in index order
   int32_t chunk_steps, chunks;  // dK / dV work split, from bwd_plan
   int32_t kblocks;              // 128-key blocks per (sequence, KV head), set by the launcher
   int32_t batch, hq, hkv, group, nq, nk, causal, window;
@@ -67,6 +69,15 @@ inline void bwd_plan(int group, int nq, int* chunks, int* steps) {
   *chunks = max_steps < 4 ? (max_steps > 0 ? max_steps : 1) : 4;
   *steps = (max_steps + *chunks - 1) / *chunks;
   if (*steps < 1) *steps = 1;
+}
+
+// Entries of the dK / dV run-order table: one per (128-key block, chunk); 0 when the table
+// would exceed kBwdOrderMax entries (the items then run in index order).
+constexpr int kBwdKeyBlock = 128;
+constexpr int64_t kBwdOrderMax = 32768;
+inline int64_t bwd_order_entries(int nk, int chunks) {
+  const int64_t n = (int64_t)((nk + kBwdKeyBlock - 1) / kBwdKeyBlock) * chunks;
+  return n <= kBwdOrderMax ? n : 0;
 }
 
 // One paged-decode launch (split kernel + combine kernel).
