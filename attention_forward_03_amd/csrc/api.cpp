@@ -349,8 +349,9 @@ static attn_status_t check_bwd_args(const attn_bwd_args_t* a) {
   return ATTN_SUCCESS;
 }
 
-// Delta [B, Hq, Nq] (rounded up to 256 bytes), then fp32 dK and dV [chunks][B, Hkv, Nk, D]
-// (a multiple of 256 bytes), then the int32 run order of the dK / dV items
+// Delta [B, Hq, Nq] and LSE2 [B, Hq, Nq] (each rounded up to 256 bytes), then fp32 dK and
+// dV [chunks][B, Hkv, Nk, D] (a multiple of 256 bytes), then the int32 run order of the
+// dK / dV items
 static size_t bwd_delta_bytes(const attn_bwd_args_t* a) {
   return ((size_t)a->batch * a->num_q_heads * (size_t)a->seqlen_q * sizeof(float) + 255) & ~(size_t)255;
 }
@@ -363,7 +364,7 @@ size_t attn_bwd_workspace_size(const attn_bwd_args_t* a) {
   if (check_bwd_args(a) != ATTN_SUCCESS) return 0;
   int chunks, steps;
   attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, &chunks, &steps);
-  return bwd_delta_bytes(a) + bwd_partial_bytes(a, chunks) +
+  return 2 * bwd_delta_bytes(a) + bwd_partial_bytes(a, chunks) +
          (size_t)attn::bwd_order_entries(a->seqlen_k, chunks) * sizeof(int32_t);
 }
 
@@ -393,11 +394,12 @@ attn_status_t attn_bwd(const attn_bwd_args_t* a, const void* q, const void* k, c
   p.dk = dk;
   p.dv = dv;
   p.delta = static_cast<float*>(workspace);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(a));
   attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, &p.chunks, &p.chunk_steps);
-  p.dk32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(a));
+  p.dk32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * bwd_delta_bytes(a));
   p.dv32 = p.dk32 + (size_t)p.chunks * a->batch * a->num_kv_heads * (size_t)a->seqlen_k * a->head_dim;
   p.order = attn::bwd_order_entries(a->seqlen_k, p.chunks) > 0
-                ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_delta_bytes(a) +
+                ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 2 * bwd_delta_bytes(a) +
                                              bwd_partial_bytes(a, p.chunks))
                 : nullptr;
   p.batch = a->batch;

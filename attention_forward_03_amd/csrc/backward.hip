@@ -60,7 +60,7 @@ constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
 static_assert(kBwdNW * 32 == kBwdKeyBlock, "a dK / dV workgroup owns one block of keys");
 
 // ------------------------------------------------------------------------- Delta ----
-// Delta = sum_d dO O in fp32 (both read as 16-bit). D/8 consecutive lanes share a row, each
+// Delta = sum_d dO O in fp32 (both read as 16-bit), and LSE2 = LSE log2(e) of the row. D/8 consecutive lanes share a row, each
 // reading 16 bytes of it, so every load instruction of a wave covers 64 / (D/8) whole rows
 // of contiguous memory; the lanes of a row add their partial sums by lane exchanges.
 template <int D, bool BF16>
@@ -80,7 +80,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += xor_shuffle(acc, off);
-  if (row < rows && c == 0) p.delta[row] = acc;
+  if (row < rows && c == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // One direct-to-LDS load of 4 bytes per lane: lane l's dword from base + voff (bytes) to
@@ -167,32 +170,37 @@ __global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
 }
 
 // --------------------------------------------------------------------- dK and dV ----
-// Wave w of the workgroup owns keys kb0 + 32 w .. +31. Per query tile of 32 rows (staged
-// in LDS with its dO rows, LSE and Delta; three buffers, loaded two steps ahead, because a
-// step's products are shorter than the latency of the next tile's loads):
+// Wave w of the workgroup owns keys kb0 + 32 w .. +31 and sums their dK^T and dV^T over the
+// steps (query head, query tile of 32 rows) of its item. A step's Q and dO tiles and its
+// rows' LSE (base 2) and Delta are staged in LDS (four buffers, loaded three steps ahead):
 //   S = Q K^T          A = Q rows (LDS), B = K^T (the wave's keys, registers)
 //   P = 2^(S sc - LSE2)                                 lane: key column, 16 query rows
-//   dV^T += dO^T P     A = dO^T (transposing LDS read), B = P (16-bit)
 //   dP = dO V^T        A = dO rows (LDS), B = V^T (registers)
-//   dS = P (dP - Delta) scale [(1 - t^2)]
+//   dS = P (dP - Delta) [(1 - t^2)]      (the softmax scale multiplies dK once, at the end)
+//   dV^T += dO^T P     A = dO^T (transposing LDS read), B = P (16-bit)
 //   dK^T += Q^T dS     A = Q^T (transposing LDS read), B = dS (16-bit)
-template <int D, bool BF16>
+// The steps are software pipelined: step i computes S and dP of step i + 1 beside the
+// exponentials of its own P, then its dV products beside its dS, then its dK products, so
+// the matrix cores of the one wave per SIMD have independent work while the vector unit
+// runs. Only tiles that cut the mask or the sequence ends test pairs one by one.
+template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BQ = kBwdBQ;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   using SW = BwdSwizzle<D>;
   using LD = TileLoader<D, BQ>;
   constexpr int NV = 2 * LD::LPW + 2;  // direct-to-LDS loads per wave per step
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
-  // per buffer: LSE then Delta, each [4 waves][64] floats (a wave loads rows 8 w .. 8 w + 7
+  // per buffer: LSE2 then Delta, each [4 waves][64] floats (a wave loads rows 8 w .. 8 w + 7
   // into the first 8 entries of its slot)
   __shared__ __attribute__((aligned(1024))) float stats[NBUF * 2 * kBwdNW * 64];
   uint16_t* const q_lds = smem;                 // [NBUF][BQ][D]
   uint16_t* const do_lds = smem + NBUF * TILE;  // [NBUF][BQ][D]
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (wave is uniform over the wave; readfirstlane lets the compiler branch on it)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   // Workgroup w runs place w / units of the run order for unit w % units (units = sequences
   // x KV heads): the longest items of every unit come first. With a multiple of 8 units,
@@ -206,7 +214,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   const int kb0 = (item / p.chunks) * (kBwdNW * 32);
   const int chunk = item % p.chunks;
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
-  const int key = kb0 + wave * 32 + l32;  // this lane's key column
+  const int kw0 = kb0 + wave * 32;  // this wave's first key
+  const int key = kw0 + l32;        // this lane's key column
 
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.hkv + g) * Lk * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.hkv + g) * Lk * D;
@@ -225,7 +234,6 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   const int q_lo = qr.q_lo, nqt = qr.nqt;
   const int G = p.group;
   const int all_steps = nqt * G;  // (head, query tile) pairs, head-major
-  const bool cap = p.cap_out > 0.0f;
   // key - query offsets a pair may have: key <= query + delta (causal), key > query + delta -
   // window (window), key < Lk; with key_rel = key - hi*4 the test is on u = key_rel - row
   const int key_rel = key - hi * 4;
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   auto qbase = [&](int st, const void* t) {
     return static_cast<const uint16_t*>(t) + ((int64_t)b * p.hq + head_of(st)) * Lq * D;
   };
-  // the loads of step st into buffer buf: Q and dO tiles, and LSE / Delta of rows
+  // the loads of step st into buffer buf: Q and dO tiles, and LSE2 / Delta of rows
   // q0 + 8 wave + lane % 8 (clamped to the sequence) into this wave's stats slots
   auto issue = [&](int st, int buf) __attribute__((always_inline)) {
     const int q0 = qt_of(st);
@@ -272,27 +280,84 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     ld.load(qbase(st, p.dout), D, q0, Lq, do_lds + buf * TILE, wave);
     const int64_t base = ((int64_t)b * p.hq + head_of(st)) * Lq;
     const uint32_t voff = (uint32_t)min(q0 + 8 * wave + (lane & 7), Lq - 1) * 4u;
-    load_lds4(p.lse + base, voff, stats + ((buf * 2 + 0) * kBwdNW + wave) * 64);
+    load_lds4(p.lse2 + base, voff, stats + ((buf * 2 + 0) * kBwdNW + wave) * 64);
     load_lds4(p.delta + base, voff, stats + ((buf * 2 + 1) * kBwdNW + wave) * 64);
   };
+  // S and dP of the step staged in buffer buf
+  auto scores = [&](int buf, f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
+    const uint16_t* ql = q_lds + buf * TILE;
+    const uint16_t* dl = do_lds + buf * TILE;
+    u32x4_t qa[NKS], da[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qa[ks] = *reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]);
+      da[ks] = *reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]);
+    }
+    s = zero16;
+    dp = zero16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
+      dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
+    }
+  };
+  // P from the scores in place; t2 = 1 - t^2 of the softcap
+  auto probs = [&](f32x16_t& s, const f32x4_t (&lse)[4], float (&t2)[16], auto maskc, int q0)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(maskc)::value;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x;
+      if constexpr (CAP) {
+        const float t = tanh_via_exp2(s[r] * p.cap_in);
+        t2[r] = 1.0f - t * t;
+        x = fmaf(p.cap_out, t, -lse[r >> 2][r & 3]);
+      } else {
+        x = fmaf(s[r], p.scale_log2, -lse[r >> 2][r & 3]);
+      }
+      const float e = fast_exp2(x);
+      if constexpr (MASK) {
+        // query q0 + (r/4)*8 + hi*4 + r%4 sees this lane's key iff u = key - (that query)
+        // lies in [lo_u, hi_u) (the causal / window offsets relative to the diagonal)
+        const int u = key_rel - q0 - ((r >> 2) * 8 + (r & 3));
+        const bool ok = (u < hi_u) & (u >= lo_u) & (q0 + (r >> 2) * 8 + hi * 4 + (r & 3) < Lq);
+        s[r] = ok ? e : 0.0f;
+      } else {
+        s[r] = e;
+      }
+    }
+  };
+  // a step's tile of this wave needs the pair test unless every pair is allowed: all its
+  // rows and keys exist, its last key is at or before the first row's diagonal (causal),
+  // and its first key is inside the last row's window
+  auto masked_tile = [&](int q0) {
+    bool full = q0 + BQ <= Lq && kw0 + 32 <= Lk;
+    if (p.causal) full = full && kw0 + 31 <= q0 + delta;
+    if (p.window > 0) full = full && kw0 > q0 + BQ - 1 + delta - p.window;
+    return !full;
+  };
 
+  // the pipeline's start: steps st0 .. st0 + 2 in flight, S and dP of step st0
   settle_global_loads();
   issue(st0, 0);
-  if (st0 + 1 < steps) {
-    issue(st0 + 1, 1);
+  if (st0 + 1 < steps) issue(st0 + 1, 1);
+  if (st0 + 2 < steps) {
+    issue(st0 + 2, 2);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
+  f32x16_t s, dp;
+  scores(0, s, dp);
 
   auto step = [&](auto bufc, int st) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;  // (st - st0) % NBUF
     const uint16_t* ql = q_lds + BUF * TILE;
     const uint16_t* dl = do_lds + BUF * TILE;
-    // buffer (BUF + 2) % NBUF was last read in step st - 1, which every wave has finished
-    if (st + 2 < steps) issue(st + 2, (BUF + 2) % NBUF);
-    // LSE and Delta of this lane's rows 8 j + 4 hi + i: loaded by wave j, entries 4 hi ..
+    // buffer (BUF + 3) % NBUF was last read in step st - 1, which every wave has finished
+    if (st + 3 < steps) issue(st + 3, (BUF + 3) % NBUF);
+    // LSE2 and Delta of this lane's rows 8 j + 4 hi + i: loaded by wave j, entries 4 hi ..
     f32x4_t lse[4], del[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -300,75 +365,54 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
     }
     const int q0 = qt_of(st);
-    // S = Q K^T and dP = dO V^T: two independent chains of products, interleaved so that
-    // each product's wait for its predecessor's result is covered by the other chain's
-    // (the fragment reads issued ahead of the products)
-    f32x16_t s = zero16, dp = zero16;
-    {
-      u32x4_t qa[NKS], da[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        qa[ks] = *reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]);
-        da[ks] = *reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
-        dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
-      }
-    }
-    // P (0 where the mask or the key range excludes the pair; a row without any allowed
-    // key, whose LSE is -inf, has every pair excluded)
+    // S and dP of step st + 1 (buffer BUF + 1, complete since the end of step st - 1; after
+    // the last step they are computed from stale data and dropped) beside P of step st
+    f32x16_t sn, dpn;
     float t2[16];
-    if (cap) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float t = tanh_via_exp2(s[r] * p.cap_in);
-        t2[r] = 1.0f - t * t;
-        s[r] = p.cap_out * t;
-      }
+    if (masked_tile(q0)) {
+      scores((BUF + 1) % NBUF, sn, dpn);
+      probs(s, lse, t2, std::true_type{}, q0);
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        t2[r] = 1.0f;
-        s[r] *= p.scale_log2;
-      }
+      scores((BUF + 1) % NBUF, sn, dpn);
+      probs(s, lse, t2, std::false_type{}, q0);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // query q0 + (r/4)*8 + hi*4 + r%4 sees this lane's key iff u = key - (that query) lies in
-      // [lo_u, hi_u) (the causal / window offsets relative to the diagonal)
-      const int u = key_rel - q0 - ((r >> 2) * 8 + (r & 3));
-      const bool ok = (u < hi_u) & (u >= lo_u) & (q0 + (r >> 2) * 8 + hi * 4 + (r & 3) < Lq);
-      const float e = fast_exp2(s[r] - lse[r >> 2][r & 3] * kLog2e);
-      s[r] = ok ? e : 0.0f;
-    }
-    // P and dS = P (dP - Delta) scale, packed to 16 bits as B operands
+    // P and dS = P (dP - Delta) [(1 - t^2)], packed to 16 bits as B operands
     u32x4_t pb[2], sb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       pb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
                       pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - del[r >> 2][r & 3]) * (p.scale * t2[r]);
+    for (int r = 0; r < 16; ++r) {
+      float ds = s[r] * (dp[r] - del[r >> 2][r & 3]);
+      if constexpr (CAP) ds *= t2[r];
+      s[r] = ds;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       sb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
                       pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
-    // dV^T += dO^T P and dK^T += Q^T dS, interleaved (independent accumulators)
+    // dV^T += dO^T P, then dK^T += Q^T dS
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x2_t vlo = lds_read_tr16(dl + t * 16 * D + rd_t[0][db]);
-        const u32x2_t vup = lds_read_tr16(dl + t * 16 * D + rd_t[1][db]);
-        const u32x2_t klo = lds_read_tr16(ql + t * 16 * D + rd_t[0][db]);
-        const u32x2_t kup = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
-        dv[db] = mfma32x32x16<BF16>(u32x4_t{vlo[0], vlo[1], vup[0], vup[1]}, pb[t], dv[db]);
-        dk[db] = mfma32x32x16<BF16>(u32x4_t{klo[0], klo[1], kup[0], kup[1]}, sb[t], dk[db]);
+        const u32x2_t lo = lds_read_tr16(dl + t * 16 * D + rd_t[0][db]);
+        const u32x2_t up = lds_read_tr16(dl + t * 16 * D + rd_t[1][db]);
+        dv[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dv[db]);
       }
-    // the loads of step st + 1 are complete once at most those of st + 2 remain
-    if (st + 2 < steps) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t lo = lds_read_tr16(ql + t * 16 * D + rd_t[0][db]);
+        const u32x2_t up = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
+        dk[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, sb[t], dk[db]);
+      }
+    s = sn;
+    dp = dpn;
+    // buffer BUF + 2 (step st + 2) is complete once at most the loads of step st + 3 remain
+    if (st + 3 < steps) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -379,6 +423,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     step(std::integral_constant<int, 0>{}, st);
     if (st + 1 < steps) step(std::integral_constant<int, 1>{}, st + 1);
     if (st + 2 < steps) step(std::integral_constant<int, 2>{}, st + 2);
+    if (st + 3 < steps) step(std::integral_constant<int, 3>{}, st + 3);
   }
 
   if (key >= Lk) return;
@@ -386,13 +431,14 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   const int64_t slot = (int64_t)chunk * p.batch * p.hkv * Lk * D;
   float* dkr = p.dk32 + slot + (((int64_t)b * p.hkv + g) * Lk + key) * D;
   float* dvr = p.dv32 + slot + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+  const float sc = p.scale;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = db * 32 + g4 * 8 + hi * 4;
-      *reinterpret_cast<f32x4_t*>(dkr + d) =
-          f32x4_t{dk[db][g4 * 4 + 0], dk[db][g4 * 4 + 1], dk[db][g4 * 4 + 2], dk[db][g4 * 4 + 3]};
+      *reinterpret_cast<f32x4_t*>(dkr + d) = f32x4_t{dk[db][g4 * 4 + 0] * sc, dk[db][g4 * 4 + 1] * sc,
+                                                      dk[db][g4 * 4 + 2] * sc, dk[db][g4 * 4 + 3] * sc};
       *reinterpret_cast<f32x4_t*>(dvr + d) =
           f32x4_t{dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1], dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]};
     }
@@ -610,7 +656,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
     hipLaunchKernelGGL(bwd_order_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
+  if (p.cap_out > 0.0f)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, true>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, false>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_convert_kernel<D, BF16>), dim3((unsigned)((nkv4 + 255) / 256)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;

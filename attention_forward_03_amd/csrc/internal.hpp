@@ -48,6 +48,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;         // workspace [B, Hq, Nq]
+  float* lse2;          // workspace [B, Hq, Nq]: lse * log2(e)
   float* dk32;          // workspace [chunks][B, Hkv, Nk, D] fp32 partial dK, then dv32 alike
   float* dv32;
   int32_t* order;       // workspace [bwd_order_entries]: the (key block, chunk) items of a

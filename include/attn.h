@@ -200,7 +200,7 @@ typedef struct {
   float softcap;         /* as for attn_fwd */
 } attn_bwd_args_t;
 
-/* Bytes of workspace attn_bwd needs (0 on bad args): one float per query row, then up to
+/* Bytes of workspace attn_bwd needs (0 on bad args): two floats per query row, then up to
  * four float32 partial sums each of dK and dV (one per chunk of the queries), then one
  * int32 per (128-key block, chunk) for the order in which that work runs. */
 size_t attn_bwd_workspace_size(const attn_bwd_args_t *args);
