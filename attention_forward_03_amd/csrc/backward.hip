@@ -301,30 +301,25 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
     }
   };
-  // P from the scores in place; t2 = 1 - t^2 of the softcap
-  auto probs = [&](f32x16_t& s, const f32x4_t (&lse)[4], float (&t2)[16], auto maskc, int q0)
-      __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(maskc)::value;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x;
-      if constexpr (CAP) {
-        const float t = tanh_via_exp2(s[r] * p.cap_in);
-        t2[r] = 1.0f - t * t;
-        x = fmaf(p.cap_out, t, -lse[r >> 2][r & 3]);
-      } else {
-        x = fmaf(s[r], p.scale_log2, -lse[r >> 2][r & 3]);
-      }
-      const float e = fast_exp2(x);
-      if constexpr (MASK) {
-        // query q0 + (r/4)*8 + hi*4 + r%4 sees this lane's key iff u = key - (that query)
-        // lies in [lo_u, hi_u) (the causal / window offsets relative to the diagonal)
-        const int u = key_rel - q0 - ((r >> 2) * 8 + (r & 3));
-        const bool ok = (u < hi_u) & (u >= lo_u) & (q0 + (r >> 2) * 8 + hi * 4 + (r & 3) < Lq);
-        s[r] = ok ? e : 0.0f;
-      } else {
-        s[r] = e;
-      }
+  // P of score r of a step, and under a softcap its 1 - t^2
+  auto prob1 = [&](float sr, float lse2, float& t2r, auto maskc, int q0, int r) __attribute__((always_inline)) {
+    float x;
+    if constexpr (CAP) {
+      const float t = tanh_via_exp2(sr * p.cap_in);
+      t2r = 1.0f - t * t;
+      x = fmaf(p.cap_out, t, -lse2);
+    } else {
+      x = fmaf(sr, p.scale_log2, -lse2);
+    }
+    const float e = fast_exp2(x);
+    if constexpr (decltype(maskc)::value) {
+      // query q0 + (r/4)*8 + hi*4 + r%4 sees this lane's key iff u = key - (that query) lies
+      // in [lo_u, hi_u) (the causal / window offsets relative to the diagonal)
+      const int u = key_rel - q0 - ((r >> 2) * 8 + (r & 3));
+      const bool ok = (u < hi_u) & (u >= lo_u) & (q0 + (r >> 2) * 8 + hi * 4 + (r & 3) < Lq);
+      return ok ? e : 0.0f;
+    } else {
+      return e;
     }
   };
   // a step's tile of this wave needs the pair test unless every pair is allowed: all its
@@ -353,10 +348,23 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
 
   auto step = [&](auto bufc, int st) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;  // (st - st0) % NBUF
+    constexpr int NXT = (BUF + 1) % NBUF;
+    constexpr int NP = 2 * NKS;      // products of S and dP (phase 1)
+    constexpr int NT = 4 * NDB;      // products of dV and dK (phase 2)
+    constexpr int RA = 4;            // row fragments read ahead in phase 1
+    constexpr int E1 = 16 / NP;      // scores turned into P per phase-1 product
+    constexpr int E2 = 16 / (2 * NDB);  // dS entries per dV product
     const uint16_t* ql = q_lds + BUF * TILE;
     const uint16_t* dl = do_lds + BUF * TILE;
-    // buffer (BUF + 3) % NBUF was last read in step st - 1, which every wave has finished
-    if (st + 3 < steps) issue(st + 3, (BUF + 3) % NBUF);
+    // row fragment k of step st + 1 (buffer NXT, complete since the end of step st - 1;
+    // after the last step it is stale, and its products are dropped): k even feeds the S
+    // chain (Q rows), k odd the dP chain (dO rows)
+    auto row_frag = [&](int k) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4_t*>((k & 1 ? do_lds : q_lds) + NXT * TILE + rd_q[k >> 1]);
+    };
+    u32x4_t fr[RA + 1];
+#pragma unroll
+    for (int k = 0; k < RA; ++k) fr[k] = row_frag(k);
     // LSE2 and Delta of this lane's rows 8 j + 4 hi + i: loaded by wave j, entries 4 hi ..
     f32x4_t lse[4], del[4];
 #pragma unroll
@@ -364,53 +372,83 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       lse[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 0) * kBwdNW + j) * 64 + 4 * hi);
       del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
     }
+    // buffer (BUF + 3) % NBUF was last read in step st - 1, which every wave has finished
+    if (st + 3 < steps) issue(st + 3, (BUF + 3) % NBUF);
     const int q0 = qt_of(st);
-    // S and dP of step st + 1 (buffer BUF + 1, complete since the end of step st - 1; after
-    // the last step they are computed from stale data and dropped) beside P of step st
-    f32x16_t sn, dpn;
+    f32x16_t sn = zero16, dpn = zero16;
     float t2[16];
-    if (masked_tile(q0)) {
-      scores((BUF + 1) % NBUF, sn, dpn);
-      probs(s, lse, t2, std::true_type{}, q0);
-    } else {
-      scores((BUF + 1) % NBUF, sn, dpn);
-      probs(s, lse, t2, std::false_type{}, q0);
-    }
-    // P and dS = P (dP - Delta) [(1 - t^2)], packed to 16 bits as B operands
     u32x4_t pb[2], sb[2];
+    // phase 1: S and dP of step st + 1 beside P of step st. The program order is fixed by
+    // scheduling fences: per product, the read of a later fragment, the product, and a
+    // share of the exponentials, so that the wave issues vector work while the matrix
+    // core runs
+    auto phase1 = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      pb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
-                      pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
+      for (int k = 0; k < NP; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(k + RA);
+        if (k & 1)
+          dpn = mfma32x32x16<BF16>(fr[k % (RA + 1)], vf[k >> 1], dpn);
+        else
+          sn = mfma32x32x16<BF16>(fr[k % (RA + 1)], kf[k >> 1], sn);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float ds = s[r] * (dp[r] - del[r >> 2][r & 3]);
-      if constexpr (CAP) ds *= t2[r];
-      s[r] = ds;
+        for (int e = 0; e < E1; ++e) {
+          const int r = k * E1 + e;
+          s[r] = prob1(s[r], lse[r >> 2][r & 3], t2[r], maskc, q0, r);
+          if (r & 1) pb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (masked_tile(q0)) {
+      phase1(std::true_type{});
+    } else {
+      phase1(std::false_type{});
     }
+    // phase 2: dV^T += dO^T P beside dS = P (dP - Delta) [(1 - t^2)], then dK^T += Q^T dS.
+    // Product i takes its A operand from the ring slot that the transposing reads two
+    // products earlier filled.
+    auto tr_frag = [&](int i) __attribute__((always_inline)) {
+      const uint16_t* src = (i < 2 * NDB ? dl : ql) + ((i / NDB) & 1) * 16 * D;
+      const u32x2_t lo = lds_read_tr16(src + rd_t[0][i % NDB]);
+      const u32x2_t up = lds_read_tr16(src + rd_t[1][i % NDB]);
+      return u32x4_t{lo[0], lo[1], up[0], up[1]};
+    };
+    u32x4_t ring[3];
+    ring[0] = tr_frag(0);
+    ring[1] = tr_frag(1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      sb[t] = u32x4_t{pack2<BF16>(s[8 * t + 0], s[8 * t + 1]), pack2<BF16>(s[8 * t + 2], s[8 * t + 3]),
-                      pack2<BF16>(s[8 * t + 4], s[8 * t + 5]), pack2<BF16>(s[8 * t + 6], s[8 * t + 7])};
-    // dV^T += dO^T P, then dK^T += Q^T dS
+    for (int i = 0; i < NT; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < NT) ring[(i + 2) % 3] = tr_frag(i + 2);
+      const int db = i % NDB, t = (i / NDB) & 1;
+      if (i < 2 * NDB) {
+        dv[db] = mfma32x32x16<BF16>(ring[i % 3], pb[t], dv[db]);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int e = 0; e < E2; ++e) {
+          const int r = i * E2 + e;
+          float ds = s[r] * (dp[r] - del[r >> 2][r & 3]);
+          if constexpr (CAP) ds *= t2[r];
+          s[r] = ds;
+          if (r & 1) sb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
+        }
+      } else {
+        dk[db] = mfma32x32x16<BF16>(ring[i % 3], sb[t], dk[db]);
+        // S and dP of step st + 1 become the current ones (s and dp are free once dS is
+        // packed), a share beside each dK product
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(dl + t * 16 * D + rd_t[0][db]);
-        const u32x2_t up = lds_read_tr16(dl + t * 16 * D + rd_t[1][db]);
-        dv[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb[t], dv[db]);
+        for (int e = 0; e < E2; ++e) {
+          const int r = (i - 2 * NDB) * E2 + e;
+          s[r] = sn[r];
+          dp[r] = dpn[r];
+        }
       }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(ql + t * 16 * D + rd_t[0][db]);
-        const u32x2_t up = lds_read_tr16(ql + t * 16 * D + rd_t[1][db]);
-        dk[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, sb[t], dk[db]);
-      }
-    s = sn;
-    dp = dpn;
+      if (i + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // buffer BUF + 2 (step st + 2) is complete once at most the loads of step st + 3 remain
     if (st + 3 < steps) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
