@@ -94,6 +94,22 @@ __device__ __forceinline__ void load_lds4(const void* base, uint32_t voff, const
                : "memory", "m0");
 }
 
+// x, opaque to the optimiser (kept in a register of its own, not folded into addresses)
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Direct-to-LDS loads (16 and 4 bytes per lane) to a wave-uniform LDS byte address.
+__device__ __forceinline__ void load_lds16_at(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds4_at(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
 // Direct-to-LDS load of one row-major tile of ROWS rows x D (16-bit) into LDS, swizzled
 // as BwdSwizzle<D>; rows past `valid` re-read the last valid row (the masks zero them).
 template <int D, int ROWS>
@@ -172,7 +188,7 @@ __global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
 // --------------------------------------------------------------------- dK and dV ----
 // Wave w of the workgroup owns keys kb0 + 32 w .. +31 and sums their dK^T and dV^T over the
 // steps (query head, query tile of 32 rows) of its item. A step's Q and dO tiles and its
-// rows' LSE (base 2) and Delta are staged in LDS (four buffers, loaded three steps ahead):
+// rows' LSE (base 2) and Delta are staged in LDS:
 //   S = Q K^T          A = Q rows (LDS), B = K^T (the wave's keys, registers)
 //   P = 2^(S sc - LSE2)                                 lane: key column, 16 query rows
 //   dP = dO V^T        A = dO rows (LDS), B = V^T (registers)
@@ -182,22 +198,30 @@ __global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
 // The steps are software pipelined: step i computes S and dP of step i + 1 beside the
 // exponentials of its own P, then its dV products beside its dS, then its dK products, so
 // the matrix cores of the one wave per SIMD have independent work while the vector unit
-// runs. Only tiles that cut the mask or the sequence ends test pairs one by one.
+// runs. Only tiles that cut the mask or the sequence ends test pairs one by one. The
+// workgroup meets at a barrier once per two steps; eight staging buffers let the loads of
+// a pair of steps start two pairs ahead.
 template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BQ = kBwdBQ;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
-  constexpr int NBUF = 4;
+  constexpr int NBUF = 8;
   using SW = BwdSwizzle<D>;
-  using LD = TileLoader<D, BQ>;
-  constexpr int NV = 2 * LD::LPW + 2;  // direct-to-LDS loads per wave per step
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;             // rows per load instruction
+  constexpr int LPW = BQ / RPL / kBwdNW;    // tile load instructions per wave
+  static_assert(BQ % (RPL * kBwdNW) == 0, "tile loads split evenly over the waves");
+  constexpr int NV = 2 * LPW + 2;           // direct-to-LDS loads per wave per step
+  // buffer i: the Q tile at element 2 i TILE, the dO tile at 2 i TILE + TILE (each [BQ][D])
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
   // per buffer: LSE2 then Delta, each [4 waves][64] floats (a wave loads rows 8 w .. 8 w + 7
   // into the first 8 entries of its slot)
   __shared__ __attribute__((aligned(1024))) float stats[NBUF * 2 * kBwdNW * 64];
-  uint16_t* const q_lds = smem;                 // [NBUF][BQ][D]
-  uint16_t* const do_lds = smem + NBUF * TILE;  // [NBUF][BQ][D]
+  // LDS reads take a buffer's offset as the instruction's immediate, which reaches 64 KB:
+  // buffers from HB on are read from lane offsets 64 KB higher
+  constexpr int HB = 32768 / (2 * TILE);
+  static_assert(HB * 2 * TILE == 32768 || NBUF * 2 * TILE <= 32768, "buffers split at 64 KB");
 
   // (wave is uniform over the wave; readfirstlane lets the compiler branch on it)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -243,14 +267,15 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   if (st0 >= all_steps) return;  // (uniform over the workgroup)
   const int steps = min(all_steps, st0 + p.chunk_steps);
 
-  LD ld;
-  ld.init(wave, lane, D);
-  int rd_q[NKS];  // row l32, chunk 2 ks + hi
+  int rd_q[NKS], rd_q_hi[NKS];  // row l32, chunk 2 ks + hi
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) rd_q[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+  for (int ks = 0; ks < NKS; ++ks) {
+    rd_q[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+    rd_q_hi[ks] = opaque_int(rd_q[ks] + 32768);
+  }
   const int grp = lane >> 4, gi = lane & 15;
   const int vrow = 4 * hi + (gi >> 2);
-  int rd_t[2][NDB];  // transposing reads of rows t*16 + 8*half + vrow (add t*16*D)
+  int rd_t[2][NDB], rd_t_hi[2][NDB];  // transposing reads of rows t*16 + 8*half + vrow (add t*16*D)
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -258,6 +283,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
       const int row = 8 * hf + vrow;
       rd_t[hf][db] = row * D + SW::k(row, c) * 8 + (gi & 1) * 4;
+      rd_t_hi[hf][db] = opaque_int(rd_t[hf][db] + 32768);
     }
 
   f32x16_t dv[NDB], dk[NDB];
@@ -267,40 +293,64 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     for (int r = 0; r < 16; ++r) dv[db][r] = dk[db][r] = 0.0f;
   const f32x16_t zero16 = {};
 
-  auto head_of = [&](int st) { return g * G + st / max(nqt, 1); };
-  auto qt_of = [&](int st) { return q_lo + (st % max(nqt, 1)) * BQ; };
-  auto qbase = [&](int st, const void* t) {
-    return static_cast<const uint16_t*>(t) + ((int64_t)b * p.hq + head_of(st)) * Lq * D;
-  };
-  // the loads of step st into buffer buf: Q and dO tiles, and LSE2 / Delta of rows
-  // q0 + 8 wave + lane % 8 (clamped to the sequence) into this wave's stats slots
-  auto issue = [&](int st, int buf) __attribute__((always_inline)) {
-    const int q0 = qt_of(st);
-    ld.load(qbase(st, p.q), D, q0, Lq, q_lds + buf * TILE, wave);
-    ld.load(qbase(st, p.dout), D, q0, Lq, do_lds + buf * TILE, wave);
-    const int64_t base = ((int64_t)b * p.hq + head_of(st)) * Lq;
-    const uint32_t voff = (uint32_t)min(q0 + 8 * wave + (lane & 7), Lq - 1) * 4u;
-    load_lds4(p.lse2 + base, voff, stats + ((buf * 2 + 0) * kBwdNW + wave) * 64);
-    load_lds4(p.delta + base, voff, stats + ((buf * 2 + 1) * kBwdNW + wave) * 64);
-  };
-  // S and dP of the step staged in buffer buf
-  auto scores = [&](int buf, f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
-    const uint16_t* ql = q_lds + buf * TILE;
-    const uint16_t* dl = do_lds + buf * TILE;
-    u32x4_t qa[NKS], da[NKS];
+  // ---- loads. Tile load n of this wave moves rows RPL (wave + n kBwdNW) .. + RPL - 1 of a
+  // tile: lane l takes 16 bytes of row RPL (wave + n kBwdNW) + l / CPR into the swizzled
+  // LDS tile at byte 1024 (wave + n kBwdNW) + 16 l.
+  const uint32_t lds_q = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+  const uint32_t lds_do = lds_q + (uint32_t)(TILE * 2);
+  const uint32_t lds_st = (uint32_t)(uintptr_t)(const lds_void_t*)stats;
+  int trow[LPW];      // tile row of load n
+  uint32_t toff[LPW]; // its byte offset in global memory from the tile's first row
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qa[ks] = *reinterpret_cast<const u32x4_t*>(ql + rd_q[ks]);
-      da[ks] = *reinterpret_cast<const u32x4_t*>(dl + rd_q[ks]);
-    }
-    s = zero16;
-    dp = zero16;
+  for (int n = 0; n < LPW; ++n) {
+    trow[n] = RPL * (wave + n * kBwdNW) + lane / CPR;
+    toff[n] = (uint32_t)(trow[n] * D + SW::k(trow[n], lane % CPR) * 8) * 2u;
+  }
+  // The loads of the steps run in order: the head and first row of the next one to load
+  int ld_head = g * G + st0 / max(nqt, 1), ld_q0 = q_lo + (st0 % max(nqt, 1)) * BQ;
+  auto load_next = [&](int buf) __attribute__((always_inline)) {
+    const int64_t row0 = ((int64_t)b * p.hq + ld_head) * Lq;
+    const uint16_t* qt = static_cast<const uint16_t*>(p.q) + (row0 + ld_q0) * D;
+    const uint16_t* dt = static_cast<const uint16_t*>(p.dout) + (row0 + ld_q0) * D;
+    const uint32_t lq = lds_q + (uint32_t)(buf * 4 * TILE), ld = lds_do + (uint32_t)(buf * 4 * TILE);
+    if (ld_q0 + BQ <= Lq) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
-      dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
+      for (int n = 0; n < LPW; ++n) {
+        load_lds16_at(qt, toff[n], lq + 1024u * (uint32_t)(wave + n * kBwdNW));
+        load_lds16_at(dt, toff[n], ld + 1024u * (uint32_t)(wave + n * kBwdNW));
+      }
+    } else {
+      // rows past the sequence end re-read its last row (the pair test zeroes them)
+#pragma unroll
+      for (int n = 0; n < LPW; ++n) {
+        const int shift = ld_q0 + trow[n] < Lq ? 0 : (Lq - 1 - ld_q0) - trow[n];
+        const uint32_t off = toff[n] + (uint32_t)(shift * D * 2);
+        load_lds16_at(qt, off, lq + 1024u * (uint32_t)(wave + n * kBwdNW));
+        load_lds16_at(dt, off, ld + 1024u * (uint32_t)(wave + n * kBwdNW));
+      }
+    }
+    const uint32_t voff = (uint32_t)min(ld_q0 + 8 * wave + (lane & 7), Lq - 1) * 4u;
+    load_lds4_at(p.lse2 + row0, voff, lds_st + (uint32_t)((((buf * 2 + 0) * kBwdNW + wave) * 64) * 4));
+    load_lds4_at(p.delta + row0, voff, lds_st + (uint32_t)((((buf * 2 + 1) * kBwdNW + wave) * 64) * 4));
+    ld_q0 += BQ;
+    if (ld_q0 >= q_lo + nqt * BQ) {
+      ld_q0 = q_lo;
+      ++ld_head;
     }
   };
+  // waits until at most n steps' loads remain in flight (n <= 3)
+  auto wait_loads = [&](int n) __attribute__((always_inline)) {
+    if (n >= 3) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NV) : "memory");
+    } else if (n == 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NV) : "memory");
+    } else if (n == 1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+
   // P of score r of a step, and under a softcap its 1 - t^2
   auto prob1 = [&](float sr, float lse2, float& t2r, auto maskc, int q0, int r) __attribute__((always_inline)) {
     float x;
@@ -332,35 +382,47 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     return !full;
   };
 
-  // the pipeline's start: steps st0 .. st0 + 2 in flight, S and dP of step st0
+  // the pipeline's start: steps st0 .. st0 + 5 in flight; S and dP of step st0 once steps
+  // st0 .. st0 + 2 have arrived
   settle_global_loads();
-  issue(st0, 0);
-  if (st0 + 1 < steps) issue(st0 + 1, 1);
-  if (st0 + 2 < steps) {
-    issue(st0 + 2, 2);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  const int first = min(steps - st0, 6);
+  for (int i = 0; i < first; ++i) load_next(i);
+  wait_loads(first - 3);
   __syncthreads();
-  f32x16_t s, dp;
-  scores(0, s, dp);
+  f32x16_t s = zero16, dp = zero16;
+  {
+    u32x4_t qa[NKS], da[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qa[ks] = *reinterpret_cast<const u32x4_t*>(smem + rd_q[ks]);
+      da[ks] = *reinterpret_cast<const u32x4_t*>(smem + TILE + rd_q[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
+      dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
+    }
+  }
+  int cur_head_t = st0 % max(nqt, 1);  // query tile index of the step being computed
 
-  auto step = [&](auto bufc, int st) __attribute__((always_inline)) {
+  // one step (buffer BUF): phase 1 and phase 2
+  auto step = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;  // (st - st0) % NBUF
     constexpr int NXT = (BUF + 1) % NBUF;
     constexpr int NP = 2 * NKS;      // products of S and dP (phase 1)
     constexpr int NT = 4 * NDB;      // products of dV and dK (phase 2)
     constexpr int RA = 4;            // row fragments read ahead in phase 1
     constexpr int E1 = 16 / NP;      // scores turned into P per phase-1 product
-    constexpr int E2 = 16 / (2 * NDB);  // dS entries per dV product
-    const uint16_t* ql = q_lds + BUF * TILE;
-    const uint16_t* dl = do_lds + BUF * TILE;
-    // row fragment k of step st + 1 (buffer NXT, complete since the end of step st - 1;
-    // after the last step it is stale, and its products are dropped): k even feeds the S
-    // chain (Q rows), k odd the dP chain (dO rows)
+    constexpr int E2 = 16 / (2 * NDB);  // dS entries per dV product (and S, dP copies per dK one)
+    // element offsets of this step's Q tile (from rd_*[] for buffers below HB, rd_*_hi[] above)
+    constexpr int QO = (BUF < HB ? BUF : BUF - HB) * 2 * TILE;
+    constexpr int QN = (NXT < HB ? NXT : NXT - HB) * 2 * TILE;
+    // row fragment k of step st + 1 (buffer NXT, complete since the end of the previous
+    // pair of steps; after the last step it is stale, and its products are dropped): k even
+    // feeds the S chain (Q rows), k odd the dP chain (dO rows)
     auto row_frag = [&](int k) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4_t*>((k & 1 ? do_lds : q_lds) + NXT * TILE + rd_q[k >> 1]);
+      return *reinterpret_cast<const u32x4_t*>(smem + (NXT < HB ? rd_q[k >> 1] : rd_q_hi[k >> 1]) + QN +
+                                               (k & 1 ? TILE : 0));
     };
     u32x4_t fr[RA + 1];
 #pragma unroll
@@ -372,9 +434,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       lse[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 0) * kBwdNW + j) * 64 + 4 * hi);
       del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
     }
-    // buffer (BUF + 3) % NBUF was last read in step st - 1, which every wave has finished
-    if (st + 3 < steps) issue(st + 3, (BUF + 3) % NBUF);
-    const int q0 = qt_of(st);
+    const int q0 = q_lo + cur_head_t * BQ;
+    if (++cur_head_t == nqt) cur_head_t = 0;
     f32x16_t sn = zero16, dpn = zero16;
     float t2[16];
     u32x4_t pb[2], sb[2];
@@ -411,9 +472,11 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     // Product i takes its A operand from the ring slot that the transposing reads two
     // products earlier filled.
     auto tr_frag = [&](int i) __attribute__((always_inline)) {
-      const uint16_t* src = (i < 2 * NDB ? dl : ql) + ((i / NDB) & 1) * 16 * D;
-      const u32x2_t lo = lds_read_tr16(src + rd_t[0][i % NDB]);
-      const u32x2_t up = lds_read_tr16(src + rd_t[1][i % NDB]);
+      const int off = QO + (i < 2 * NDB ? TILE : 0) + ((i / NDB) & 1) * 16 * D;
+      const int b0 = BUF < HB ? rd_t[0][i % NDB] : rd_t_hi[0][i % NDB];
+      const int b1 = BUF < HB ? rd_t[1][i % NDB] : rd_t_hi[1][i % NDB];
+      const u32x2_t lo = lds_read_tr16(smem + b0 + off);
+      const u32x2_t up = lds_read_tr16(smem + b1 + off);
       return u32x4_t{lo[0], lo[1], up[0], up[1]};
     };
     u32x4_t ring[3];
@@ -449,19 +512,24 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // buffer BUF + 2 (step st + 2) is complete once at most the loads of step st + 3 remain
-    if (st + 3 < steps) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+  };
+  // a pair of steps (st, st + 1) in buffers B0, B0 + 1: the loads of st + 6 and st + 7 go
+  // into the buffers of the previous pair (which every wave has finished); at the end the
+  // steps up to st + 4 must have arrived, so those of st + 5 .. st + 7 may stay in flight
+  auto pair = [&](auto b0c, int st) __attribute__((always_inline)) {
+    constexpr int B0 = decltype(b0c)::value;
+    if (st + 6 < steps) load_next((B0 + 6) % NBUF);
+    if (st + 7 < steps) load_next((B0 + 7) % NBUF);
+    step(std::integral_constant<int, B0>{});
+    if (st + 1 < steps) step(std::integral_constant<int, (B0 + 1) % NBUF>{});
+    wait_loads(steps - (st + 5));
     __syncthreads();
   };
   for (int st = st0; st < steps; st += NBUF) {
-    step(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < steps) step(std::integral_constant<int, 1>{}, st + 1);
-    if (st + 2 < steps) step(std::integral_constant<int, 2>{}, st + 2);
-    if (st + 3 < steps) step(std::integral_constant<int, 3>{}, st + 3);
+    pair(std::integral_constant<int, 0>{}, st);
+    if (st + 2 < steps) pair(std::integral_constant<int, 2>{}, st + 2);
+    if (st + 4 < steps) pair(std::integral_constant<int, 4>{}, st + 4);
+    if (st + 6 < steps) pair(std::integral_constant<int, 6>{}, st + 6);
   }
 
   if (key >= Lk) return;
