@@ -576,25 +576,36 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------- dQ ----
-// Wave w owns query rows q0 + 32 w .. +31; key tiles of 64 (K and V in LDS, double-
-// buffered). Per tile:
+// Wave w owns query rows r0 + 32 w .. +31 and walks the key tiles of 64 (K and V staged in
+// LDS, four buffers loaded three tiles ahead). Per tile:
 //   S^T = K Q^T        A = K rows (LDS), B = Q (registers)     lane: query column, keys
 //   P^T = 2^(S^T sc - LSE2)
 //   dP^T = V dO^T      A = V rows (LDS), B = dO (registers)
-//   dS^T = P^T (dP^T - Delta) scale [(1 - t^2)]
+//   dS^T = P^T (dP^T - Delta) [(1 - t^2)]   (the softmax scale multiplies dQ at the end)
 //   dQ^T += K^T dS^T   A = K^T (transposing LDS read), B = dS^T (16-bit)
-template <int D, bool BF16>
+// Pipelined like the dK / dV kernel: tile i computes S and dP of tile i + 1 beside its own
+// exponentials, then its dQ products beside its dS; only tiles that cut the mask test
+// pairs one by one.
+template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams p) {
   constexpr int BN = 64;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BN / 32, NPS = BN / 16;
   constexpr int TILE = BN * D;
+  constexpr int NBUF = 4;
   using SW = BwdSwizzle<D>;
-  using LD = TileLoader<D, BN>;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
-  uint16_t* const k_lds = smem;
-  uint16_t* const v_lds = smem + 2 * TILE;
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;           // rows per load instruction
+  constexpr int LPW = BN / RPL / kBwdNW;  // tile load instructions per wave
+  static_assert(BN % (RPL * kBwdNW) == 0, "tile loads split evenly over the waves");
+  constexpr int NV = 2 * LPW;             // direct-to-LDS loads per wave per tile
+  // buffer i: the K tile at element 2 i TILE, the V tile at 2 i TILE + TILE (each [BN][D])
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
+  // LDS reads take a buffer's offset as the instruction's immediate (at most 64 KB): buffers
+  // from HB on are read from lane offsets 64 KB higher
+  constexpr int HB = 32768 / (2 * TILE) < NBUF ? 32768 / (2 * TILE) : NBUF;
+  static_assert(HB == NBUF || HB * 2 * TILE == 32768, "buffers split at 64 KB");
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   // every head's longest (causal) query tiles first: the grid is (head, tile, batch) (the
   // forward's per-XCD placement measured 7% slower here)
@@ -603,7 +614,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
   const int h = blockIdx.x, b = blockIdx.z;
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
   const int hk = h / p.group;
-  const int qrow = r0 + wave * 32 + l32;
+  const int qw0 = r0 + wave * 32;  // this wave's first query row
+  const int qrow = qw0 + l32;
   const bool row_ok = qrow < Lq;
   const int qr = min(qrow, Lq - 1);
 
@@ -616,7 +628,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
     qf[ks] = load_global<u32x4_t>(static_cast<const uint16_t*>(p.q) + rowi * D + ks * 16 + hi * 8);
     df[ks] = load_global<u32x4_t>(static_cast<const uint16_t*>(p.dout) + rowi * D + ks * 16 + hi * 8);
   }
-  const float lse2 = p.lse[rowi] * kLog2e;
+  const float lse2 = p.lse2[rowi];
   const float dl = p.delta[rowi];
   const float lse_use = (row_ok && lse2 != kNegInf) ? lse2 : __builtin_inff();  // P = 0 for such rows
 
@@ -629,16 +641,21 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
   const int key_lo = p.window > 0 ? qrow + delta - p.window + 1 : 0;
   const int key_hi = p.causal ? min(Lk, qrow + delta + 1) : Lk;
   const uint32_t key_n = (uint32_t)max(key_hi - key_lo, 0);
-  const bool cap = p.cap_out > 0.0f;
+  // a tile needs the pair test unless every key of it is allowed for every row of the wave
+  // (rows past the sequence end have P = 0 through lse_use)
+  const int full_hi = p.causal ? min(Lk, qw0 + delta + 1) : Lk;         // keys below it: all rows
+  const int full_lo = p.window > 0 ? qw0 + 31 + delta - p.window + 1 : 0;  // keys from it: all rows
+  auto masked_tile = [&](int kt) { return !(kt + BN <= full_hi && kt >= full_lo); };
 
-  LD ld;
-  ld.init(wave, lane, D);
-  int rd_k[NKS];
+  int rd_k[NKS], rd_k_hi[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+  for (int ks = 0; ks < NKS; ++ks) {
+    rd_k[ks] = l32 * D + SW::k(l32, 2 * ks + hi) * 8;
+    rd_k_hi[ks] = opaque_int(rd_k[ks] + 32768);
+  }
   const int grp = lane >> 4, gi = lane & 15;
   const int vrow = 4 * hi + (gi >> 2);
-  int rd_t[2][NDB];  // transposing reads of rows t*16 + 8*half + vrow (add t*16*D)
+  int rd_t[2][NDB], rd_t_hi[2][NDB];  // transposing reads of rows t*16 + 8*half + vrow (add t*16*D)
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -646,6 +663,7 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
       const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
       const int row = 8 * hf + vrow;
       rd_t[hf][db] = row * D + SW::k(row, c) * 8 + (gi & 1) * 4;
+      rd_t_hi[hf][db] = opaque_int(rd_t[hf][db] + 32768);
     }
 
   f32x16_t dq[NDB];
@@ -655,92 +673,208 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
   const f32x16_t zero16 = {};
 
-  settle_global_loads();
-  if (ntiles > 0) {
-    ld.load(kg, D, kbeg, Lk, k_lds, wave);
-    ld.load(vg, D, kbeg, Lk, v_lds, wave);
+  // ---- loads: tile load n of this wave moves rows RPL (wave + n kBwdNW) .. + RPL - 1 of a
+  // tile into the swizzled LDS tile at byte 1024 (wave + n kBwdNW) + 16 lane
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+  int trow[LPW];
+  uint32_t toff[LPW];
+#pragma unroll
+  for (int n = 0; n < LPW; ++n) {
+    trow[n] = RPL * (wave + n * kBwdNW) + lane / CPR;
+    toff[n] = (uint32_t)(trow[n] * D + SW::k(trow[n], lane % CPR) * 8) * 2u;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto load_tile = [&](int it, int buf) __attribute__((always_inline)) {
+    const int kt = kbeg + it * BN;
+    const uint16_t* kt_g = kg + (int64_t)kt * D;
+    const uint16_t* vt_g = vg + (int64_t)kt * D;
+    const uint32_t lk = lds_k + (uint32_t)(buf * 4 * TILE), lv = lk + (uint32_t)(2 * TILE);
+    if (kt + BN <= Lk) {
+#pragma unroll
+      for (int n = 0; n < LPW; ++n) {
+        load_lds16_at(kt_g, toff[n], lk + 1024u * (uint32_t)(wave + n * kBwdNW));
+        load_lds16_at(vt_g, toff[n], lv + 1024u * (uint32_t)(wave + n * kBwdNW));
+      }
+    } else {
+      // rows past the sequence end re-read its last row (the pair test zeroes them)
+#pragma unroll
+      for (int n = 0; n < LPW; ++n) {
+        const int shift = kt + trow[n] < Lk ? 0 : (Lk - 1 - kt) - trow[n];
+        const uint32_t off = toff[n] + (uint32_t)(shift * D * 2);
+        load_lds16_at(kt_g, off, lk + 1024u * (uint32_t)(wave + n * kBwdNW));
+        load_lds16_at(vt_g, off, lv + 1024u * (uint32_t)(wave + n * kBwdNW));
+      }
+    }
+  };
+
+  // P^T of score r of block kb of a tile (key kt + 32 kb + (r/4)*8 + hi*4 + r%4), and
+  // under a softcap dS^T directly
+  auto prob1 = [&](float sr, float dpr, auto maskc, uint32_t base, int kb, int r) __attribute__((always_inline)) {
+    float e;
+    if constexpr (CAP) {
+      const float t = tanh_via_exp2(sr * p.cap_in);
+      e = fast_exp2(fmaf(p.cap_out, t, -lse_use));
+      e *= (dpr - dl) * (1.0f - t * t);
+    } else {
+      e = fast_exp2(fmaf(sr, p.scale_log2, -lse_use));
+    }
+    if constexpr (decltype(maskc)::value) {
+      // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
+      const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
+      e = ok ? e : 0.0f;
+    }
+    return e;
+  };
+
+  // the pipeline's start: tiles 0 .. 2 in flight; S^T and dP^T of tile 0 once 0 and 1 arrived
+  settle_global_loads();
+  for (int i = 0; i < min(ntiles, 3); ++i) load_tile(i, i);
+  if (ntiles > 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
+  f32x16_t s[NKB], dp[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s[kb] = zero16;
+    dp[kb] = zero16;
+  }
+  if (ntiles > 0) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * D + rd_k[ks]);
+        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(smem + TILE + kb * 32 * D + rd_k[ks]);
+        s[kb] = mfma32x32x16<BF16>(ka, qf[ks], s[kb]);
+        dp[kb] = mfma32x32x16<BF16>(va, df[ks], dp[kb]);
+      }
+  }
 
   auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;
+    constexpr int BUF = decltype(bufc)::value;  // it % NBUF
+    constexpr int NXT = (BUF + 1) % NBUF;
+    constexpr int NP = 2 * NKS * NKB;  // products of S^T and dP^T (phase 1)
+    constexpr int NT = NPS * NDB;      // products of dQ^T (phase 2)
+    constexpr int RA = 4;              // row fragments read ahead in phase 1
+    constexpr int E1 = 16 * NKB / NP;  // scores turned into P per phase-1 product
+    constexpr int KO = (BUF < HB ? BUF : BUF - HB) * 2 * TILE;
+    constexpr int KN = (NXT < HB ? NXT : NXT - HB) * 2 * TILE;
     const int kt = kbeg + it * BN;
-    if (it + 1 < ntiles) {
-      ld.load(kg, D, kt + BN, Lk, k_lds + (BUF ^ 1) * TILE, wave);
-      ld.load(vg, D, kt + BN, Lk, v_lds + (BUF ^ 1) * TILE, wave);
-    }
-    const uint16_t* kl = k_lds + BUF * TILE;
-    const uint16_t* vl = v_lds + BUF * TILE;
-    f32x16_t s[NKB], dp[NKB];
+    // buffer (BUF + 3) % NBUF was last read in tile it - 1, which every wave has finished
+    if (it + 3 < ntiles) load_tile(it + 3, (BUF + 3) % NBUF);
+    // row fragment k of tile it + 1 (buffer NXT, complete since the end of tile it - 1;
+    // stale after the last tile, its products then dropped): block kb = k / (2 NKS), even k
+    // feed the S^T chain (K rows), odd k the dP^T chain (V rows)
+    auto row_frag = [&](int k) __attribute__((always_inline)) {
+      const int kb = k / (2 * NKS), ks = (k % (2 * NKS)) >> 1;
+      return *reinterpret_cast<const u32x4_t*>(smem + (NXT < HB ? rd_k[ks] : rd_k_hi[ks]) + KN +
+                                               (k & 1 ? TILE : 0) + kb * 32 * D);
+    };
+    u32x4_t fr[RA + 1];
+#pragma unroll
+    for (int k = 0; k < RA; ++k) fr[k] = row_frag(k);
+    const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
+    f32x16_t sn[NKB], dpn[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      u32x4_t ka[NKS], va[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        ka[ks] = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[ks]);
-        va[ks] = *reinterpret_cast<const u32x4_t*>(vl + kb * 32 * D + rd_k[ks]);
-      }
-      s[kb] = zero16;
-      dp[kb] = zero16;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s[kb] = mfma32x32x16<BF16>(ka[ks], qf[ks], s[kb]);
-        dp[kb] = mfma32x32x16<BF16>(va[ks], df[ks], dp[kb]);
-      }
+      sn[kb] = zero16;
+      dpn[kb] = zero16;
     }
-    // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
-    const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
-    if (cap) {
+    // phase 1: S^T and dP^T of tile it + 1 beside P^T of tile it (program order fixed per
+    // product by scheduling fences)
+    auto phase1 = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int k = 0; k < NP; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(k + RA);
+        const int kb = k / (2 * NKS), ks = (k % (2 * NKS)) >> 1;
+        if (k & 1)
+          dpn[kb] = mfma32x32x16<BF16>(fr[k % (RA + 1)], df[ks], dpn[kb]);
+        else
+          sn[kb] = mfma32x32x16<BF16>(fr[k % (RA + 1)], qf[ks], sn[kb]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float t = tanh_via_exp2(s[kb][r] * p.cap_in);
-          const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
-          const float e = fast_exp2(p.cap_out * t - lse_use);
-          s[kb][r] = (ok ? e : 0.0f) * (dp[kb][r] - dl) * (p.scale * (1.0f - t * t));
+        for (int e = 0; e < E1; ++e) {
+          const int x = k * E1 + e, xb = x >> 4, xr = x & 15;
+          s[xb][xr] = prob1(s[xb][xr], dp[xb][xr], maskc, base, xb, xr);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (masked_tile(kt)) {
+      phase1(std::true_type{});
     } else {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
-          const float e = fast_exp2(s[kb][r] * p.scale_log2 - lse_use);
-          s[kb][r] = (ok ? e : 0.0f) * (dp[kb][r] - dl) * p.scale;
-        }
+      phase1(std::false_type{});
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int t = 0; t < NPS; ++t) {
+    // phase 2: dQ^T += K^T dS^T over the tile's four 16-key steps t; the dS of step t + 1
+    // is computed and packed beside the products of step t
+    auto ds_pack = [&](int t) __attribute__((always_inline)) {
       const int kb = t >> 1, o8 = (t & 1) * 8;
-      const u32x4_t pb = {pack2<BF16>(s[kb][o8 + 0], s[kb][o8 + 1]), pack2<BF16>(s[kb][o8 + 2], s[kb][o8 + 3]),
-                          pack2<BF16>(s[kb][o8 + 4], s[kb][o8 + 5]), pack2<BF16>(s[kb][o8 + 6], s[kb][o8 + 7])};
+      if constexpr (!CAP) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(kl + t * 16 * D + rd_t[0][db]);
-        const u32x2_t up = lds_read_tr16(kl + t * 16 * D + rd_t[1][db]);
-        dq[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pb, dq[db]);
+        for (int j = 0; j < 8; ++j) s[kb][o8 + j] = s[kb][o8 + j] * (dp[kb][o8 + j] - dl);
       }
+      return u32x4_t{pack2<BF16>(s[kb][o8 + 0], s[kb][o8 + 1]), pack2<BF16>(s[kb][o8 + 2], s[kb][o8 + 3]),
+                     pack2<BF16>(s[kb][o8 + 4], s[kb][o8 + 5]), pack2<BF16>(s[kb][o8 + 6], s[kb][o8 + 7])};
+    };
+    auto tr_frag = [&](int i) __attribute__((always_inline)) {
+      const int t = i / NDB, db = i % NDB;
+      const int off = KO + t * 16 * D;
+      const int b0 = BUF < HB ? rd_t[0][db] : rd_t_hi[0][db];
+      const int b1 = BUF < HB ? rd_t[1][db] : rd_t_hi[1][db];
+      const u32x2_t lo = lds_read_tr16(smem + b0 + off);
+      const u32x2_t up = lds_read_tr16(smem + b1 + off);
+      return u32x4_t{lo[0], lo[1], up[0], up[1]};
+    };
+    u32x4_t ring[3], pbs[NPS];
+    ring[0] = tr_frag(0);
+    ring[1] = tr_frag(1);
+    pbs[0] = ds_pack(0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < NT) ring[(i + 2) % 3] = tr_frag(i + 2);
+      const int t = i / NDB, db = i % NDB;
+      dq[db] = mfma32x32x16<BF16>(ring[i % 3], pbs[t], dq[db]);
+      if (db == NDB - 1 && t + 1 < NPS) pbs[t + 1] = ds_pack(t + 1);
+      if (i + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = sn[kb];
+      dp[kb] = dpn[kb];
+    }
+    // tile it + 2 is complete once at most the loads of tile it + 3 remain
+    if (it + 3 < ntiles) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = 0; it < ntiles; it += NBUF) {
     tile(std::integral_constant<int, 0>{}, it);
     if (it + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 < ntiles) tile(std::integral_constant<int, 2>{}, it + 2);
+    if (it + 3 < ntiles) tile(std::integral_constant<int, 3>{}, it + 3);
   }
 
   if (!row_ok) return;
   uint16_t* dqr = static_cast<uint16_t*>(p.dq) + (((int64_t)b * p.hq + h) * Lq + qrow) * D;
+  const float sc = p.scale;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = db * 32 + g4 * 8 + hi * 4;
-      *reinterpret_cast<u32x2_t*>(dqr + d) = u32x2_t{pack2<BF16>(dq[db][g4 * 4 + 0], dq[db][g4 * 4 + 1]),
-                                                     pack2<BF16>(dq[db][g4 * 4 + 2], dq[db][g4 * 4 + 3])};
+      *reinterpret_cast<u32x2_t*>(dqr + d) =
+          u32x2_t{pack2<BF16>(dq[db][g4 * 4 + 0] * sc, dq[db][g4 * 4 + 1] * sc),
+                  pack2<BF16>(dq[db][g4 * 4 + 2] * sc, dq[db][g4 * 4 + 3] * sc)};
     }
 }
 
@@ -770,7 +904,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_convert_kernel<D, BF16>), dim3((unsigned)((nkv4 + 255) / 256)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 gq(p.hq, (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32), p.batch);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), gq, dim3(kBwdNW * 64), 0, st, p);
+  if (p.cap_out > 0.0f)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, true>), gq, dim3(kBwdNW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, false>), gq, dim3(kBwdNW * 64), 0, st, p);
   return hipGetLastError();
 }
 
