@@ -48,7 +48,7 @@ struct BwdSwizzle {
   __device__ static __forceinline__ int k(int row, int c) {
     if constexpr (D == 128) {
       const int r = row & 15;
-      return c ^ (((r << 1) | (r >> 3)) & 15);
+      return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
     } else {
       return Swizzle<D>::k(row, c);
     }
@@ -351,17 +351,19 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     }
   };
 
-  // P of score r of a step, and under a softcap its 1 - t^2
-  auto prob1 = [&](float sr, float lse2, float& t2r, auto maskc, int q0, int r) __attribute__((always_inline)) {
-    float x;
+  // P of score r of a step in two stages: the exponent (and under a softcap 1 - t^2), then
+  // the power of two with the pair test
+  auto prob_a = [&](float sr, float lse2, float& t2r) __attribute__((always_inline)) {
     if constexpr (CAP) {
       const float t = tanh_via_exp2(sr * p.cap_in);
       t2r = 1.0f - t * t;
-      x = fmaf(p.cap_out, t, -lse2);
+      return fmaf(p.cap_out, t, -lse2);
     } else {
-      x = fmaf(sr, p.scale_log2, -lse2);
+      return fmaf(sr, p.scale_log2, -lse2);
     }
-    const float e = fast_exp2(x);
+  };
+  auto prob_b = [&](float xe, auto maskc, int q0, int r) __attribute__((always_inline)) {
+    const float e = fast_exp2(xe);
     if constexpr (decltype(maskc)::value) {
       // query q0 + (r/4)*8 + hi*4 + r%4 sees this lane's key iff u = key - (that query) lies
       // in [lo_u, hi_u) (the causal / window offsets relative to the diagonal)
@@ -441,25 +443,41 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     u32x4_t pb[2], sb[2];
     // phase 1: S and dP of step st + 1 beside P of step st. The program order is fixed by
     // scheduling fences: per product, the read of a later fragment, the product, and a
-    // share of the exponentials, so that the wave issues vector work while the matrix
-    // core runs
+    // share of the vector work, so that the wave issues it while the matrix core runs. The
+    // vector work is skewed over the products (exponents of product k's scores, powers of
+    // product k - 1's, packing of product k - 2's), so no instruction waits on the one
+    // before it.
     auto phase1 = [&](auto maskc) __attribute__((always_inline)) {
+      float xe[16];
 #pragma unroll
-      for (int k = 0; k < NP; ++k) {
+      for (int k = 0; k < NP + 2; ++k) {
         __builtin_amdgcn_sched_barrier(0);
-        if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(k + RA);
-        if (k & 1)
-          dpn = mfma32x32x16<BF16>(fr[k % (RA + 1)], vf[k >> 1], dpn);
-        else
-          sn = mfma32x32x16<BF16>(fr[k % (RA + 1)], kf[k >> 1], sn);
+        if (k < NP) {
+          if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(k + RA);
+          if (k & 1)
+            dpn = mfma32x32x16<BF16>(fr[k % (RA + 1)], vf[k >> 1], dpn);
+          else
+            sn = mfma32x32x16<BF16>(fr[k % (RA + 1)], kf[k >> 1], sn);
+        }
 #pragma unroll
         for (int e = 0; e < E1; ++e) {
-          const int r = k * E1 + e;
-          s[r] = prob1(s[r], lse[r >> 2][r & 3], t2[r], maskc, q0, r);
-          if (r & 1) pb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
+          if (k < NP) {
+            const int r = k * E1 + e;
+            xe[r] = prob_a(s[r], lse[r >> 2][r & 3], t2[r]);
+          }
+          if (k >= 1 && k - 1 < NP) {
+            const int r = (k - 1) * E1 + e;
+            s[r] = prob_b(xe[r], maskc, q0, r);
+          }
+          if (k >= 2) {
+            const int r = (k - 2) * E1 + e;
+            if (r & 1) pb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
+          }
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k < NP) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -487,31 +505,37 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       __builtin_amdgcn_sched_barrier(0);
       if (i + 2 < NT) ring[(i + 2) % 3] = tr_frag(i + 2);
       const int db = i % NDB, t = (i / NDB) & 1;
-      if (i < 2 * NDB) {
-        dv[db] = mfma32x32x16<BF16>(ring[i % 3], pb[t], dv[db]);
+      // dS skewed like phase 1: dP - Delta of product i's share, the product with P (and
+      // 1 - t^2) of product i - 1's, packing of product i - 2's
 #pragma unroll
-        for (int e = 0; e < E2; ++e) {
+      for (int e = 0; e < E2; ++e) {
+        if (i < 2 * NDB) {
           const int r = i * E2 + e;
-          float ds = s[r] * (dp[r] - del[r >> 2][r & 3]);
+          dp[r] = dp[r] - del[r >> 2][r & 3];
+        }
+        if (i >= 1 && i - 1 < 2 * NDB) {
+          const int r = (i - 1) * E2 + e;
+          float ds = s[r] * dp[r];
           if constexpr (CAP) ds *= t2[r];
           s[r] = ds;
+        }
+        if (i >= 2 && i - 2 < 2 * NDB) {
+          const int r = (i - 2) * E2 + e;
           if (r & 1) sb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
         }
+      }
+      if (i < 2 * NDB) {
+        dv[db] = mfma32x32x16<BF16>(ring[i % 3], pb[t], dv[db]);
       } else {
         dk[db] = mfma32x32x16<BF16>(ring[i % 3], sb[t], dk[db]);
-        // S and dP of step st + 1 become the current ones (s and dp are free once dS is
-        // packed), a share beside each dK product
-#pragma unroll
-        for (int e = 0; e < E2; ++e) {
-          const int r = (i - 2 * NDB) * E2 + e;
-          s[r] = sn[r];
-          dp[r] = dpn[r];
-        }
       }
       if (i + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // S and dP of step st + 1 become the current ones
+    s = sn;
+    dp = dpn;
   };
   // a pair of steps (st, st + 1) in buffers B0, B0 + 1: the loads of st + 6 and st + 7 go
   // into the buffers of the previous pair (which every wave has finished); at the end the
