@@ -384,111 +384,124 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
     return !full;
   };
 
-  // the pipeline's start: steps st0 .. st0 + 5 in flight; S and dP of step st0 once steps
-  // st0 .. st0 + 2 have arrived
+  // the pipeline's start: steps st0 .. st0 + 5 in flight. Step st0's S and dP, and its P,
+  // once steps st0 .. st0 + 3 have arrived
   settle_global_loads();
   const int first = min(steps - st0, 6);
   for (int i = 0; i < first; ++i) load_next(i);
-  wait_loads(first - 3);
+  wait_loads(first - 4);
   __syncthreads();
-  f32x16_t s = zero16, dp = zero16;
+  constexpr int NP = 2 * NKS;         // products of S and dP (phase X)
+  constexpr int NT = 4 * NDB;         // products of dV and dK (phase Y)
+  constexpr int RA = 4;               // row fragments read ahead
+  constexpr int E1 = 16 / NP;         // dS entries per phase-X product
+  constexpr int E2 = 16 / NT;         // P entries per phase-Y product
+  int cur_head_t = st0 % max(nqt, 1);  // query tile index of the step being computed
+  auto tile_q0 = [&](int t) { return q_lo + t * BQ; };
+  f32x16_t s = zero16, dp = zero16;  // P and dP of the current step (fp32)
+  u32x4_t pb[2];                     // its P as 16-bit B operands
+  float t2[16];                      // its 1 - t^2 (softcap)
   {
     u32x4_t qa[NKS], da[NKS];
+    f32x4_t lse[4];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       qa[ks] = *reinterpret_cast<const u32x4_t*>(smem + rd_q[ks]);
       da[ks] = *reinterpret_cast<const u32x4_t*>(smem + TILE + rd_q[ks]);
     }
 #pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lse[j] = *reinterpret_cast<const f32x4_t*>(stats + (0 * kBwdNW + j) * 64 + 4 * hi);
+#pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       s = mfma32x32x16<BF16>(qa[ks], kf[ks], s);
       dp = mfma32x32x16<BF16>(da[ks], vf[ks], dp);
     }
+    const int q0 = tile_q0(cur_head_t);
+    const bool masked = masked_tile(q0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float xe = prob_a(s[r], lse[r >> 2][r & 3], t2[r]);
+      s[r] = masked ? prob_b(xe, std::true_type{}, q0, r) : prob_b(xe, std::false_type{}, q0, r);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pb[t][j] = pack2<BF16>(s[8 * t + 2 * j], s[8 * t + 2 * j + 1]);
   }
-  int cur_head_t = st0 % max(nqt, 1);  // query tile index of the step being computed
+  // row fragment k of the step staged in buffer buf: k even feeds the S chain (Q rows), k
+  // odd the dP chain (dO rows)
+  auto row_frag = [&](int buf, int k) __attribute__((always_inline)) {
+    const int qo = (buf < HB ? buf : buf - HB) * 2 * TILE;
+    return *reinterpret_cast<const u32x4_t*>(smem + (buf < HB ? rd_q[k >> 1] : rd_q_hi[k >> 1]) + qo +
+                                             (k & 1 ? TILE : 0));
+  };
+  u32x4_t fr[RA + 1];
+#pragma unroll
+  for (int k = 0; k < RA; ++k) fr[k] = row_frag(1 % NBUF, k);
 
-  // one step (buffer BUF): phase 1 and phase 2
+  // One step (buffer BUF). Phase X: the S and dP products of step st + 1 (buffer BUF + 1)
+  // beside dS of step st. Phase Y: the dV and dK products of step st beside P of step st + 1.
+  // The program order is fixed per product by scheduling fences: each product comes with
+  // the LDS reads of a later one and a share of the vector work, skewed over the products
+  // so that no instruction waits on the one before it. The row fragments of the next step's
+  // phase X are read at the end of phase Y (buffer BUF + 2, which the barriers have made
+  // complete), and the transposing reads of phase Y at the end of phase X.
   auto step = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;  // (st - st0) % NBUF
     constexpr int NXT = (BUF + 1) % NBUF;
-    constexpr int NP = 2 * NKS;      // products of S and dP (phase 1)
-    constexpr int NT = 4 * NDB;      // products of dV and dK (phase 2)
-    constexpr int RA = 4;            // row fragments read ahead in phase 1
-    constexpr int E1 = 16 / NP;      // scores turned into P per phase-1 product
-    constexpr int E2 = 16 / (2 * NDB);  // dS entries per dV product (and S, dP copies per dK one)
-    // element offsets of this step's Q tile (from rd_*[] for buffers below HB, rd_*_hi[] above)
     constexpr int QO = (BUF < HB ? BUF : BUF - HB) * 2 * TILE;
-    constexpr int QN = (NXT < HB ? NXT : NXT - HB) * 2 * TILE;
-    // row fragment k of step st + 1 (buffer NXT, complete since the end of the previous
-    // pair of steps; after the last step it is stale, and its products are dropped): k even
-    // feeds the S chain (Q rows), k odd the dP chain (dO rows)
-    auto row_frag = [&](int k) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4_t*>(smem + (NXT < HB ? rd_q[k >> 1] : rd_q_hi[k >> 1]) + QN +
-                                               (k & 1 ? TILE : 0));
-    };
-    u32x4_t fr[RA + 1];
-#pragma unroll
-    for (int k = 0; k < RA; ++k) fr[k] = row_frag(k);
-    // LSE2 and Delta of this lane's rows 8 j + 4 hi + i: loaded by wave j, entries 4 hi ..
-    f32x4_t lse[4], del[4];
+    // Delta of this step's rows and LSE2 of the next step's: lane rows
+    // 8 j + 4 hi + i, loaded by wave j into entries 4 hi ..
+    f32x4_t del[4], lsn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      lse[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 0) * kBwdNW + j) * 64 + 4 * hi);
       del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
+      lsn[j] = *reinterpret_cast<const f32x4_t*>(stats + ((NXT * 2 + 0) * kBwdNW + j) * 64 + 4 * hi);
     }
-    const int q0 = q_lo + cur_head_t * BQ;
     if (++cur_head_t == nqt) cur_head_t = 0;
+    const int q0n = tile_q0(cur_head_t);  // the next step's first row
     f32x16_t sn = zero16, dpn = zero16;
-    float t2[16];
-    u32x4_t pb[2], sb[2];
-    // phase 1: S and dP of step st + 1 beside P of step st. The program order is fixed by
-    // scheduling fences: per product, the read of a later fragment, the product, and a
-    // share of the vector work, so that the wave issues it while the matrix core runs. The
-    // vector work is skewed over the products (exponents of product k's scores, powers of
-    // product k - 1's, packing of product k - 2's), so no instruction waits on the one
-    // before it.
-    auto phase1 = [&](auto maskc) __attribute__((always_inline)) {
-      float xe[16];
+    u32x4_t sb[2], pbn[2];
+    float t2n[16];
+    // ---- phase X
 #pragma unroll
-      for (int k = 0; k < NP + 2; ++k) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (k < NP) {
-          if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(k + RA);
-          if (k & 1)
-            dpn = mfma32x32x16<BF16>(fr[k % (RA + 1)], vf[k >> 1], dpn);
-          else
-            sn = mfma32x32x16<BF16>(fr[k % (RA + 1)], kf[k >> 1], sn);
-        }
+    for (int k = 0; k < NP + 2; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (k < NP) {
+        if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(NXT, k + RA);
+        if (k & 1)
+          dpn = mfma32x32x16<BF16>(fr[k % (RA + 1)], vf[k >> 1], dpn);
+        else
+          sn = mfma32x32x16<BF16>(fr[k % (RA + 1)], kf[k >> 1], sn);
+      }
+      // dS = P (dP - Delta) [(1 - t^2)]: dP - Delta of product k's share, the product of
+      // k - 1's, packing of k - 2's
 #pragma unroll
-        for (int e = 0; e < E1; ++e) {
-          if (k < NP) {
-            const int r = k * E1 + e;
-            xe[r] = prob_a(s[r], lse[r >> 2][r & 3], t2[r]);
-          }
-          if (k >= 1 && k - 1 < NP) {
-            const int r = (k - 1) * E1 + e;
-            s[r] = prob_b(xe[r], maskc, q0, r);
-          }
-          if (k >= 2) {
-            const int r = (k - 2) * E1 + e;
-            if (r & 1) pb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
-          }
-        }
+      for (int e = 0; e < E1; ++e) {
         if (k < NP) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          const int r = k * E1 + e;
+          dp[r] = dp[r] - del[r >> 2][r & 3];
+        }
+        if (k >= 1 && k - 1 < NP) {
+          const int r = (k - 1) * E1 + e;
+          float ds = s[r] * dp[r];
+          if constexpr (CAP) ds *= t2[r];
+          s[r] = ds;
+        }
+        if (k >= 2) {
+          const int r = (k - 2) * E1 + e;
+          if (r & 1) sb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (masked_tile(q0)) {
-      phase1(std::true_type{});
-    } else {
-      phase1(std::false_type{});
+      if (k < NP) {
+        if (k + RA < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
-    // phase 2: dV^T += dO^T P beside dS = P (dP - Delta) [(1 - t^2)], then dK^T += Q^T dS.
-    // Product i takes its A operand from the ring slot that the transposing reads two
-    // products earlier filled.
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase Y: product i takes its A operand from the ring slot that the transposing
+    // reads two products earlier filled; P of step st + 1 without the pair test
     auto tr_frag = [&](int i) __attribute__((always_inline)) {
       const int off = QO + (i < 2 * NDB ? TILE : 0) + ((i / NDB) & 1) * 16 * D;
       const int b0 = BUF < HB ? rd_t[0][i % NDB] : rd_t_hi[0][i % NDB];
@@ -497,56 +510,82 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
       const u32x2_t up = lds_read_tr16(smem + b1 + off);
       return u32x4_t{lo[0], lo[1], up[0], up[1]};
     };
-    u32x4_t ring[3];
-    ring[0] = tr_frag(0);
-    ring[1] = tr_frag(1);
+    {
+      float xe[16];
+      u32x4_t ring[3];
+      ring[0] = tr_frag(0);
+      ring[1] = tr_frag(1);
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
+      for (int i = 0; i < NT + 2; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < NT) {
+          if (i + 2 < NT) ring[(i + 2) % 3] = tr_frag(i + 2);
+          const int db = i % NDB, t = (i / NDB) & 1;
+          if (i < 2 * NDB)
+            dv[db] = mfma32x32x16<BF16>(ring[i % 3], pb[t], dv[db]);
+          else
+            dk[db] = mfma32x32x16<BF16>(ring[i % 3], sb[t], dk[db]);
+        }
+        // P of step st + 1: its dP taken over and the exponent of product i's share, the
+        // power of i - 1's, packing of i - 2's
+#pragma unroll
+        for (int e = 0; e < E2; ++e) {
+          if (i < NT) {
+            const int r = i * E2 + e;
+            dp[r] = dpn[r];
+            xe[r] = prob_a(sn[r], lsn[r >> 2][r & 3], t2n[r]);
+          }
+          if (i >= 1 && i - 1 < NT) {
+            const int r = (i - 1) * E2 + e;
+            s[r] = prob_b(xe[r], std::false_type{}, q0n, r);
+          }
+          if (i >= 2) {
+            const int r = (i - 2) * E2 + e;
+            if (r & 1) pbn[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
+          }
+        }
+        if (i < NT) {
+          if (i + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < NT) ring[(i + 2) % 3] = tr_frag(i + 2);
-      const int db = i % NDB, t = (i / NDB) & 1;
-      // dS skewed like phase 1: dP - Delta of product i's share, the product with P (and
-      // 1 - t^2) of product i - 1's, packing of product i - 2's
-#pragma unroll
-      for (int e = 0; e < E2; ++e) {
-        if (i < 2 * NDB) {
-          const int r = i * E2 + e;
-          dp[r] = dp[r] - del[r >> 2][r & 3];
-        }
-        if (i >= 1 && i - 1 < 2 * NDB) {
-          const int r = (i - 1) * E2 + e;
-          float ds = s[r] * dp[r];
-          if constexpr (CAP) ds *= t2[r];
-          s[r] = ds;
-        }
-        if (i >= 2 && i - 2 < 2 * NDB) {
-          const int r = (i - 2) * E2 + e;
-          if (r & 1) sb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
-        }
-      }
-      if (i < 2 * NDB) {
-        dv[db] = mfma32x32x16<BF16>(ring[i % 3], pb[t], dv[db]);
-      } else {
-        dk[db] = mfma32x32x16<BF16>(ring[i % 3], sb[t], dk[db]);
-      }
-      if (i + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // S and dP of step st + 1 become the current ones
-    s = sn;
-    dp = dpn;
+    // a next tile that cuts the mask: its excluded pairs set to 0 after the fact (their
+    // powers may be inf; the selection drops them)
+    if (masked_tile(q0n)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int u = key_rel - q0n - ((r >> 2) * 8 + (r & 3));
+        const bool ok = (u < hi_u) & (u >= lo_u) & (q0n + (r >> 2) * 8 + hi * 4 + (r & 3) < Lq);
+        s[r] = ok ? s[r] : 0.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pbn[t][j] = pack2<BF16>(s[8 * t + 2 * j], s[8 * t + 2 * j + 1]);
+    }
+    pb[0] = pbn[0];
+    pb[1] = pbn[1];
+    if constexpr (CAP) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t2[r] = t2n[r];
+    }
+    // row fragments of the next step's phase X (buffer BUF + 2)
+#pragma unroll
+    for (int k = 0; k < RA; ++k) fr[k] = row_frag((BUF + 2) % NBUF, k);
   };
   // a pair of steps (st, st + 1) in buffers B0, B0 + 1: the loads of st + 6 and st + 7 go
   // into the buffers of the previous pair (which every wave has finished); at the end the
-  // steps up to st + 4 must have arrived, so those of st + 5 .. st + 7 may stay in flight
+  // steps up to st + 5 must have arrived (the next pair reads buffers up to its first step
+  // + 3), so those of st + 6 and st + 7 may stay in flight
   auto pair = [&](auto b0c, int st) __attribute__((always_inline)) {
     constexpr int B0 = decltype(b0c)::value;
     if (st + 6 < steps) load_next((B0 + 6) % NBUF);
     if (st + 7 < steps) load_next((B0 + 7) % NBUF);
     step(std::integral_constant<int, B0>{});
     if (st + 1 < steps) step(std::integral_constant<int, (B0 + 1) % NBUF>{});
-    wait_loads(steps - (st + 5));
+    wait_loads(min(2, steps - (st + 6)));
     __syncthreads();
   };
   for (int st = st0; st < steps; st += NBUF) {
