@@ -8,17 +8,19 @@
 // tile from S and the row LSE, never stored):
 //   P = exp(S - LSE)   dV = P^T dO   dP = dO V^T   dS = P (dP - Delta) * scale
 //   (times 1 - tanh^2 under a softcap)   dQ = dS K   dK = dS^T Q,   Delta = rowsum(dO O).
-// Three kernels:
-//   bwd_delta_kernel   Delta per query row (fp32);
-//   bwd_dkdv_kernel    a workgroup owns 128 keys of one KV head (4 waves of 32) and one of
+// Three launches:
+//   bwd_delta_kernel   -Delta and LSE log2(e) per query row (fp32); extra workgroups build
+//                      the run order of the dK / dV items (longest first);
+//   bwd_main_kernel    the dK / dV items, then the dQ items:
+//     dK / dV item     a workgroup owns 128 keys of one KV head (4 waves of 32) and one of
 //                      at most 4 equal chunks of the (query head of its group, query tile)
 //                      steps that reach them, so a causal problem (where early keys meet
 //                      far more queries than late ones) stays balanced; each chunk stores
-//                      its fp32 partial dK, dV in a slot of its own, and
-//                      bwd_convert_kernel adds a key's slots in a fixed order and rounds
-//                      to the output type (no atomics: the result is repeatable bit for bit);
-//   bwd_dq_kernel      a workgroup owns 128 query rows (4 waves of 32) and walks the key
-//                      tiles, like the forward.
+//                      its fp32 partial dK, dV in a slot of its own;
+//     dQ item          a workgroup owns 128 query rows (4 waves of 32) and walks the key
+//                      tiles, like the forward;
+//   bwd_convert_kernel adds a key's slots in a fixed order and rounds to the output type
+//                      (no atomics: the result is repeatable bit for bit).
 // Every product is a 32x32x16 matrix-core product with the layouts of the forward
 // kernels: results are kept transposed when that puts P or dS straight into a B operand
 // (dV^T = dO^T P, dK^T = Q^T dS, dQ^T = K^T dS^T), and the transposed A operands (dO^T,
@@ -58,33 +60,6 @@ struct BwdSwizzle {
 constexpr int kBwdNW = 4;   // waves per workgroup (one per SIMD: the accumulators are large)
 constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
 static_assert(kBwdNW * 32 == kBwdKeyBlock, "a dK / dV workgroup owns one block of keys");
-
-// ------------------------------------------------------------------------- Delta ----
-// Delta = sum_d dO O in fp32 (both read as 16-bit), and LSE2 = LSE log2(e) of the row. D/8 consecutive lanes share a row, each
-// reading 16 bytes of it, so every load instruction of a wave covers 64 / (D/8) whole rows
-// of contiguous memory; the lanes of a row add their partial sums by lane exchanges.
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
-  constexpr int LPR = D / 8;        // lanes per row
-  constexpr int RPB = 256 / LPR;    // rows per workgroup
-  const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
-  float acc = 0.0f;
-  if (row < rows) {
-    const u32x4_t a = load_global<u32x4_t>(static_cast<const uint16_t*>(p.o) + row * D + 8 * c);
-    const u32x4_t b = load_global<u32x4_t>(static_cast<const uint16_t*>(p.dout) + row * D + 8 * c);
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      acc += lo16<BF16>(a[w]) * lo16<BF16>(b[w]) + hi16<BF16>(a[w]) * hi16<BF16>(b[w]);
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += xor_shuffle(acc, off);
-  if (row < rows && c == 0) {
-    p.delta[row] = acc;
-    p.lse2[row] = p.lse[row] * kLog2e;
-  }
-}
 
 // One direct-to-LDS load of 4 bytes per lane: lane l's dword from base + voff (bytes) to
 // LDS address lds_base + 4 l (the 4-byte form of load_lds16).
@@ -167,14 +142,14 @@ __device__ __forceinline__ int bwd_item_steps(const BwdParams& p, int item) {
 // tail with short items (causal problems mix full chunks with short and empty ones). Item
 // i's place is the number of items with a larger key, plus those with an equal key and a
 // smaller index (a permutation, the same on every run); the key is the step count scaled
-// to 0..255. One thread per item; each workgroup first writes all keys into LDS.
-__global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t keys[kBwdOrderMax];
+// to 0..255. One thread per item; each workgroup first writes all keys into LDS. Runs in
+// the extra workgroups ob of the Delta kernel.
+__device__ __forceinline__ void bwd_order_block(const BwdParams& p, int ob, uint8_t* keys) {
   const int n = p.kblocks * p.chunks;
   for (int i = threadIdx.x; i < n; i += 256)
     keys[i] = (uint8_t)(bwd_item_steps(p, i) * 255 / p.chunk_steps);
   __syncthreads();
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = ob * 256 + threadIdx.x;
   if (i >= n) return;
   const int ki = keys[i];
   int place = 0;
@@ -183,6 +158,39 @@ __global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
     place += (kj > ki) | ((kj == ki) & (j < i));
   }
   p.order[place] = i;
+}
+
+// ------------------------------------------------------------------------- Delta ----
+// Delta = sum_d dO O in fp32 (both read as 16-bit), and LSE2 = LSE log2(e) of the row. D/8 consecutive lanes share a row, each
+// reading 16 bytes of it, so every load instruction of a wave covers 64 / (D/8) whole rows
+// of contiguous memory; the lanes of a row add their partial sums by lane exchanges.
+// Workgroups from delta_blocks on build the dK / dV run order instead.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p, int delta_blocks) {
+  constexpr int LPR = D / 8;        // lanes per row
+  constexpr int RPB = 256 / LPR;    // rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t keys[kBwdOrderMax];
+  if ((int)blockIdx.x >= delta_blocks) {
+    bwd_order_block(p, (int)blockIdx.x - delta_blocks, keys);
+    return;
+  }
+  const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4_t a = load_global<u32x4_t>(static_cast<const uint16_t*>(p.o) + row * D + 8 * c);
+    const u32x4_t b = load_global<u32x4_t>(static_cast<const uint16_t*>(p.dout) + row * D + 8 * c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += lo16<BF16>(a[w]) * lo16<BF16>(b[w]) + hi16<BF16>(a[w]) * hi16<BF16>(b[w]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += xor_shuffle(acc, off);
+  if (row < rows && c == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // --------------------------------------------------------------------- dK and dV ----
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(256) void bwd_order_kernel(const BwdParams p) {
 // workgroup meets at a barrier once per two steps; eight staging buffers let the loads of
 // a pair of steps start two pairs ahead.
 template <int D, bool BF16, bool CAP>
-__global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParams p) {
+__device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_t* smem, float* stats) {
   constexpr int BQ = kBwdBQ;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
@@ -213,11 +221,9 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   constexpr int LPW = BQ / RPL / kBwdNW;    // tile load instructions per wave
   static_assert(BQ % (RPL * kBwdNW) == 0, "tile loads split evenly over the waves");
   constexpr int NV = 2 * LPW + 2;           // direct-to-LDS loads per wave per step
-  // buffer i: the Q tile at element 2 i TILE, the dO tile at 2 i TILE + TILE (each [BQ][D])
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
-  // per buffer: LSE2 then Delta, each [4 waves][64] floats (a wave loads rows 8 w .. 8 w + 7
-  // into the first 8 entries of its slot)
-  __shared__ __attribute__((aligned(1024))) float stats[NBUF * 2 * kBwdNW * 64];
+  // LDS: smem holds buffer i's Q tile at element 2 i TILE and its dO tile at 2 i TILE + TILE
+  // (each [BQ][D]); stats, per buffer, LSE2 then Delta, each [4 waves][64] floats (a wave
+  // loads rows 8 w .. 8 w + 7 into the first 8 entries of its slot)
   // LDS reads take a buffer's offset as the instruction's immediate, which reaches 64 KB:
   // buffers from HB on are read from lane offsets 64 KB higher
   constexpr int HB = 32768 / (2 * TILE);
@@ -231,7 +237,6 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dkdv_kernel(const BwdParam
   // all items of a unit run on one XCD (workgroup w runs on XCD w % 8) and share its L2
   // copy of the unit's Q and dO.
   const int units = p.batch * p.hkv;
-  const int w = blockIdx.x;
   const int unit = w % units;
   const int item = p.order != nullptr ? p.order[w / units] : w / units;
   const int g = unit % p.hkv, b = unit / p.hkv;
@@ -650,7 +655,7 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const BwdParams p) {
 // exponentials, then its dQ products beside its dS; only tiles that cut the mask test
 // pairs one by one.
 template <int D, bool BF16, bool CAP>
-__global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams p) {
+__device__ __forceinline__ void bwd_dq_item(const BwdParams& p, int h, int yt, int b, uint16_t* smem) {
   constexpr int BN = 64;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BN / 32, NPS = BN / 16;
   constexpr int TILE = BN * D;
@@ -661,8 +666,8 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
   constexpr int LPW = BN / RPL / kBwdNW;  // tile load instructions per wave
   static_assert(BN % (RPL * kBwdNW) == 0, "tile loads split evenly over the waves");
   constexpr int NV = 2 * LPW;             // direct-to-LDS loads per wave per tile
-  // buffer i: the K tile at element 2 i TILE, the V tile at 2 i TILE + TILE (each [BN][D])
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * NBUF * TILE];
+  // LDS: buffer i holds the K tile at element 2 i TILE, the V tile at 2 i TILE + TILE (each
+  // [BN][D])
   // LDS reads take a buffer's offset as the instruction's immediate (at most 64 KB): buffers
   // from HB on are read from lane offsets 64 KB higher
   constexpr int HB = 32768 / (2 * TILE) < NBUF ? 32768 / (2 * TILE) : NBUF;
@@ -670,11 +675,10 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  // every head's longest (causal) query tiles first: the grid is (head, tile, batch) (the
-  // forward's per-XCD placement measured 7% slower here)
+  // every head's longest (causal) query tiles first: items run head-fastest, then tile, then
+  // sequence (the forward's per-XCD placement measured 7% slower here)
   const int ntile = (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32);
-  const int r0 = (p.causal ? ntile - 1 - (int)blockIdx.y : (int)blockIdx.y) * (kBwdNW * 32);
-  const int h = blockIdx.x, b = blockIdx.z;
+  const int r0 = (p.causal ? ntile - 1 - yt : yt) * (kBwdNW * 32);
   const int Lq = p.nq, Lk = p.nk, delta = Lk - Lq;
   const int hk = h / p.group;
   const int qw0 = r0 + wave * 32;  // this wave's first query row
@@ -941,36 +945,55 @@ __global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_dq_kernel(const BwdParams 
     }
 }
 
+// ------------------------------------------------------------------------ main ----
+// One launch runs the dK / dV items (longest first) and then the dQ items: the dQ items
+// start on the CUs that the dK / dV tail frees. Both kinds use one LDS allocation.
+template <int D>
+struct BwdLds {
+  static constexpr int kv_tiles = 2 * 8 * kBwdBQ * D * 2;      // bytes: 8 Q and dO buffers
+  static constexpr int kv = kv_tiles + 8 * 2 * kBwdNW * 64 * 4;  // and their LSE2 / Delta
+  static constexpr int dq = 2 * 4 * 64 * D * 2;                // 4 K and V buffers
+  static constexpr int bytes = kv > dq ? kv : dq;
+};
+
+template <int D, bool BF16, bool CAP>
+__global__ __launch_bounds__(kBwdNW * 64, 1) void bwd_main_kernel(const BwdParams p, int kv_items) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[BwdLds<D>::bytes];
+  const int w = blockIdx.x;
+  if (w < kv_items) {
+    bwd_dkdv_item<D, BF16, CAP>(p, w, reinterpret_cast<uint16_t*>(lds),
+                                reinterpret_cast<float*>(lds + BwdLds<D>::kv_tiles));
+  } else {
+    const int j = w - kv_items;
+    const int ntile = (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32);
+    bwd_dq_item<D, BF16, CAP>(p, j % p.hq, (j / p.hq) % ntile, j / (p.hq * ntile), reinterpret_cast<uint16_t*>(lds));
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const int64_t rows = (int64_t)p.batch * p.hq * p.nq;
   constexpr int kDeltaRows = 256 / (D / 8);  // rows per workgroup of bwd_delta_kernel
-  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + kDeltaRows - 1) / kDeltaRows)), dim3(256), 0,
-                     st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t nkv4 = (int64_t)p.batch * p.hkv * p.nk * D / 4;  // float4s per accumulator slot
   BwdParams q = p;
   q.kblocks = (p.nk + kBwdNW * 32 - 1) / (kBwdNW * 32);
-  const int64_t nkv_items = (int64_t)q.kblocks * p.chunks * p.hkv * p.batch;
-  if (nkv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (q.order != nullptr) {
-    const int n = q.kblocks * p.chunks;  // <= kBwdOrderMax (the table exists)
-    hipLaunchKernelGGL(bwd_order_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  const int64_t kv_items = (int64_t)q.kblocks * p.chunks * p.hkv * p.batch;
+  const int64_t dq_items = (int64_t)p.hq * ((p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32)) * p.batch;
+  const int64_t delta_blocks = (rows + kDeltaRows - 1) / kDeltaRows;
+  const int64_t order_blocks = q.order != nullptr ? ((int64_t)q.kblocks * p.chunks + 255) / 256 : 0;
+  if (kv_items + dq_items > 0x7fffffff || delta_blocks + order_blocks > 0x7fffffff)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)(delta_blocks + order_blocks)), dim3(256), 0, st, q,
+                     (int)delta_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(kv_items + dq_items));
   if (p.cap_out > 0.0f)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, true>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
+    hipLaunchKernelGGL((bwd_main_kernel<D, BF16, true>), grid, dim3(kBwdNW * 64), 0, st, q, (int)kv_items);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, false>), dim3((unsigned)nkv_items), dim3(kBwdNW * 64), 0, st, q);
+    hipLaunchKernelGGL((bwd_main_kernel<D, BF16, false>), grid, dim3(kBwdNW * 64), 0, st, q, (int)kv_items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nkv4 = (int64_t)p.batch * p.hkv * p.nk * D / 4;  // float4s per accumulator slot
   hipLaunchKernelGGL((bwd_convert_kernel<D, BF16>), dim3((unsigned)((nkv4 + 255) / 256)), dim3(256), 0, st, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 gq(p.hq, (p.nq + kBwdNW * 32 - 1) / (kBwdNW * 32), p.batch);
-  if (p.cap_out > 0.0f)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, true>), gq, dim3(kBwdNW * 64), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, false>), gq, dim3(kBwdNW * 64), 0, st, p);
   return hipGetLastError();
 }
 

@@ -68,7 +68,7 @@ PREFILL_KERNELS = ("fwd_r2p_kernel<true, 0>",)
 DECODE_KERNELS = ("decode_split_kernel", "decode_combine_kernel")
 CHUNKED_KERNEL = ("gather_kv_pages_kernel", "fwd_r2_kernel<true, 1>")
 FP8_KERNEL = "fwd_fp8_kernel"
-BWD_KERNELS = ("bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
+BWD_KERNELS = ("bwd_delta_kernel", "bwd_main_kernel", "bwd_convert_kernel")
 
 
 # the sources each kernel family is built from: counter-derived traffic of a kernel is
@@ -204,8 +204,8 @@ PROFILES = {
     "fp8_prefill": ("prefill_fwd_fp8_B1_H32_N8192_D128", "fwd_fp8_kernel - dense prefill B=1 H=32 N=8192 D=128, "
                     "fp8 e4m3 Q/K/V", ("fwd_fp8_kernel",), ("fp8_prefill", "flops_per_launch"), "TFLOP/s",
                     PEAK_FP8_TFLOPS, 3 * 32 * 8192 * 128 + 32 * 8192 * 128 * 2),
-    "backward": ("backward_causal_gqa_B1_Hq32_Hkv8_N4096_D128", "bwd_delta_kernel + bwd_dkdv_kernel + "
-                 "bwd_convert_kernel + bwd_dq_kernel - backward of causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16",
+    "backward": ("backward_causal_gqa_B1_Hq32_Hkv8_N4096_D128", "bwd_delta_kernel + bwd_main_kernel (dK/dV and dQ "
+                 "items) + bwd_convert_kernel - backward of causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16",
                  ("bwd_",), ("backward", "flops_per_launch"), "TFLOP/s", PEAK_BF16_TFLOPS, None),
     "gqa_causal": ("prefill_causal_gqa_B4_Hq32_Hkv8_N4096_D128", "fwd_r2p_kernel<bf16, masked> (persistent) - "
                    "causal GQA prefill B=4 Hq=32 Hkv=8 N=4096 D=128 bf16",
@@ -899,7 +899,7 @@ def measure_backward(attn, torch, workloads, dev, flush, reps: int) -> dict:
             "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
                          "traffic": load_traffic("backward", BWD_KERNELS),
-                         "kernels": "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}}
+                         "kernels": "bwd_delta_kernel + bwd_main_kernel + bwd_convert_kernel"}}
 
 
 if __name__ == "__main__":
