@@ -360,12 +360,12 @@ static size_t bwd_partial_bytes(const attn_bwd_args_t* a, int chunks) {
   return 2 * (size_t)chunks * a->batch * a->num_kv_heads * (size_t)a->seqlen_k * a->head_dim * sizeof(float);
 }
 
+// Sized for the largest split (kBwdMaxChunks), whatever the mask: the same buffer serves a
+// causal and a full call of the same shapes.
 size_t attn_bwd_workspace_size(const attn_bwd_args_t* a) {
   if (check_bwd_args(a) != ATTN_SUCCESS) return 0;
-  int chunks, steps;
-  attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, &chunks, &steps);
-  return 2 * bwd_delta_bytes(a) + bwd_partial_bytes(a, chunks) +
-         (size_t)attn::bwd_order_entries(a->seqlen_k, chunks) * sizeof(int32_t);
+  return 2 * bwd_delta_bytes(a) + bwd_partial_bytes(a, attn::kBwdMaxChunks) +
+         (size_t)attn::bwd_order_entries(a->seqlen_k, attn::kBwdMaxChunks) * sizeof(int32_t);
 }
 
 attn_status_t attn_bwd(const attn_bwd_args_t* a, const void* q, const void* k, const void* v, const void* o,
@@ -395,12 +395,13 @@ attn_status_t attn_bwd(const attn_bwd_args_t* a, const void* q, const void* k, c
   p.dv = dv;
   p.delta = static_cast<float*>(workspace);
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(a));
-  attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, &p.chunks, &p.chunk_steps);
+  attn::bwd_plan(a->num_q_heads / a->num_kv_heads, a->seqlen_q, a->seqlen_k, a->causal, a->window > 0 ? a->window : 0,
+                 a->batch * a->num_kv_heads, &p.chunks, &p.chunk_steps);
   p.dk32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * bwd_delta_bytes(a));
   p.dv32 = p.dk32 + (size_t)p.chunks * a->batch * a->num_kv_heads * (size_t)a->seqlen_k * a->head_dim;
   p.order = attn::bwd_order_entries(a->seqlen_k, p.chunks) > 0
                 ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 2 * bwd_delta_bytes(a) +
-                                             bwd_partial_bytes(a, p.chunks))
+                                             bwd_partial_bytes(a, attn::kBwdMaxChunks))
                 : nullptr;
   p.batch = a->batch;
   p.hq = a->num_q_heads;

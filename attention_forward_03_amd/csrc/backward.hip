@@ -58,7 +58,7 @@ struct BwdSwizzle {
 };
 
 constexpr int kBwdNW = 4;   // waves per workgroup (one per SIMD: the accumulators are large)
-constexpr int kBwdBQ = 32;  // query rows per step of the dK / dV kernel
+constexpr int kBwdBQ = kBwdQueryTile;  // query rows per step of the dK / dV items
 static_assert(kBwdNW * 32 == kBwdKeyBlock, "a dK / dV workgroup owns one block of keys");
 
 // One direct-to-LDS load of 4 bytes per lane: lane l's dword from base + voff (bytes) to

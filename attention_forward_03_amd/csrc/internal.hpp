@@ -63,18 +63,40 @@ struct BwdParams {
 
 hipError_t launch_bwd(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
 
-// Split of the dK / dV work: the (query head, 32-row query tile) steps that reach a block
-// of keys, at most group * ceil(nq / 32), are cut into `chunks` (<= 4) runs of `steps`.
-inline void bwd_plan(int group, int nq, int* chunks, int* steps) {
-  const int max_steps = group * ((nq + 31) / 32);
-  *chunks = max_steps < 4 ? (max_steps > 0 ? max_steps : 1) : 4;
-  *steps = (max_steps + *chunks - 1) / *chunks;
+// Split of the dK / dV work. A workgroup owns a block of kBwdKeyBlock keys and walks the
+// (query head of its group, kBwdQueryTile-row query tile) steps that reach them; those steps,
+// at most group * ceil(nq / kBwdQueryTile) per block, are cut into `chunks` (<= kBwdMaxChunks) runs of
+// `steps`, each a work item with an fp32 partial dK / dV of its own. Items are kept no
+// longer than one CU's share of all the steps (kBwdPlanCUs CUs), so that the longest-first
+// order balances them (with the dQ items that follow in the same launch), and split no
+// further: every extra chunk costs a partial written and summed.
+constexpr int kBwdKeyBlock = 128;
+constexpr int kBwdQueryTile = 32;
+constexpr int kBwdPlanCUs = 256;
+constexpr int kBwdMaxChunks = 4;
+inline void bwd_plan(int group, int nq, int nk, int causal, int window, int units, int* chunks, int* steps) {
+  const int max_steps = group * ((nq + kBwdQueryTile - 1) / kBwdQueryTile);
+  // all steps of one unit (the query-tile range of each key block, as the kernels count it)
+  int64_t total = 0;
+  const int delta = nk - nq;
+  for (int kb0 = 0; kb0 < nk; kb0 += kBwdKeyBlock) {
+    const int kb1 = nk < kb0 + kBwdKeyBlock ? nk : kb0 + kBwdKeyBlock;
+    int q_lo = causal ? (kb0 - delta > 0 ? kb0 - delta : 0) : 0;
+    const int q_hi = window > 0 ? (nq < kb1 - 1 - delta + window ? nq : kb1 - 1 - delta + window) : nq;
+    q_lo = (q_lo / kBwdQueryTile) * kBwdQueryTile;
+    if (q_hi > q_lo) total += (int64_t)((q_hi - q_lo + kBwdQueryTile - 1) / kBwdQueryTile) * group;
+  }
+  total *= units;
+  int c = total > 0 ? (int)(((int64_t)max_steps * kBwdPlanCUs + total - 1) / total) : 1;
+  c = c < 1 ? 1 : (c > kBwdMaxChunks ? kBwdMaxChunks : c);
+  if (c > max_steps) c = max_steps > 0 ? max_steps : 1;
+  *chunks = c;
+  *steps = (max_steps + c - 1) / c;
   if (*steps < 1) *steps = 1;
 }
 
 // Entries of the dK / dV run-order table: one per (128-key block, chunk); 0 when the table
 // would exceed kBwdOrderMax entries (the items then run in index order).
-constexpr int kBwdKeyBlock = 128;
 constexpr int64_t kBwdOrderMax = 32768;
 inline int64_t bwd_order_entries(int nk, int chunks) {
   const int64_t n = (int64_t)((nk + kBwdKeyBlock - 1) / kBwdKeyBlock) * chunks;

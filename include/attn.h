@@ -200,9 +200,10 @@ typedef struct {
   float softcap;         /* as for attn_fwd */
 } attn_bwd_args_t;
 
-/* Bytes of workspace attn_bwd needs (0 on bad args): two floats per query row, then up to
- * four float32 partial sums each of dK and dV (one per chunk of the queries), then one
- * int32 per (128-key block, chunk) for the order in which that work runs. */
+/* Bytes of workspace attn_bwd needs (0 on bad args): two floats per query row, then room
+ * for four float32 partial sums each of dK and dV (one per chunk of the queries; a call
+ * uses one to four chunks), then one int32 per 128-key block and chunk for the order in
+ * which that work runs. The size does not depend on causal, window or softcap. */
 size_t attn_bwd_workspace_size(const attn_bwd_args_t *args);
 
 /*

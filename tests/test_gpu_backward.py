@@ -119,6 +119,19 @@ def test_gqa_group_of_eight_and_sink():
     _check(case, "Hq=8 Hkv=1 sink", sinks=np.linspace(-1.0, 4.0, 8).astype(np.float32), seed=6)
 
 
+@pytest.mark.parametrize("batch,heads,seqlen,chunks", [(4, 16, 512, 1), (2, 16, 384, 3)], ids=["one_chunk", "three_chunks"])
+def test_split_of_the_key_blocks(batch, heads, seqlen, chunks):
+    """The dK / dV work of a key block runs as one to four chunks, chosen so that a chunk is
+    no longer than one CU's share of all the steps (256 CUs): with units x key blocks = 256
+    (full mask) the split is 1 chunk, with 96 it is 3 (4 and 2 are covered by the other
+    cases: the small shapes and the benchmark's shape)."""
+    units, kblocks = batch * heads, (seqlen + 127) // 128
+    assert -(-256 // (units * kblocks)) == chunks
+    case = workloads.make_prefill(batch=batch, num_q_heads=2 * heads, num_kv_heads=heads, seqlen_q=seqlen,
+                                  head_dim=64, dtype="bf16", seed=65 + chunks)
+    _check(case, f"{chunks} chunk(s)", seed=8 + chunks)
+
+
 def test_deterministic():
     """dQ, dK and dV are repeatable bit for bit (the chunked dK / dV partials are summed in a
     fixed order); the query length gives several chunks per key block."""
