@@ -131,6 +131,13 @@ __device__ __forceinline__ BwdQueryRange bwd_query_range(const BwdParams& p, int
   return {q_lo, q_hi > q_lo ? (q_hi - q_lo + kBwdBQ - 1) / kBwdBQ : 0};
 }
 
+// The number of dK / dV chunks that hold a partial for keys of block kb0 (one: the
+// item writes dK and dV in the output type itself).
+__device__ __forceinline__ int bwd_chunks_of(const BwdParams& p, int kb0) {
+  const int all = bwd_query_range(p, kb0).nqt * p.group;
+  return min(p.chunks, (all + p.chunk_steps - 1) / p.chunk_steps);
+}
+
 // Steps (query head, query tile) of dK / dV item `item` (= key block * chunks + chunk).
 __device__ __forceinline__ int bwd_item_steps(const BwdParams& p, int item) {
   const int all = bwd_query_range(p, (item / p.chunks) * (kBwdNW * 32)).nqt * p.group;
@@ -390,11 +397,12 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
   };
 
   // the pipeline's start: steps st0 .. st0 + 5 in flight. Step st0's S and dP, and its P,
-  // once steps st0 .. st0 + 3 have arrived
-  settle_global_loads();
+  // once steps st0 .. st0 + 3 have arrived (the wait for them also covers the K and V
+  // fragments, loaded first)
   const int first = min(steps - st0, 6);
-  for (int i = 0; i < first; ++i) load_next(i);
-  wait_loads(first - 4);
+  for (int i = 0; i < min(first, 4); ++i) load_next(i);
+  settle_global_loads();
+  for (int i = 4; i < first; ++i) load_next(i);
   __syncthreads();
   constexpr int NP = 2 * NKS;         // products of S and dP (phase X)
   constexpr int NT = 4 * NDB;         // products of dV and dK (phase Y)
@@ -602,10 +610,25 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
 
   if (key >= Lk) return;
   // dK^T / dV^T: lane column = key, register r of block db = head-dim 32 db + 8 (r/4) + 4 hi + r%4
+  const float sc = p.scale;
+  if (bwd_chunks_of(p, kb0) == 1) {
+    uint16_t* dkr = static_cast<uint16_t*>(p.dk) + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+    uint16_t* dvr = static_cast<uint16_t*>(p.dv) + (((int64_t)b * p.hkv + g) * Lk + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hi * 4;
+        *reinterpret_cast<u32x2_t*>(dkr + d) = u32x2_t{pack2<BF16>(dk[db][g4 * 4 + 0] * sc, dk[db][g4 * 4 + 1] * sc),
+                                                       pack2<BF16>(dk[db][g4 * 4 + 2] * sc, dk[db][g4 * 4 + 3] * sc)};
+        *reinterpret_cast<u32x2_t*>(dvr + d) = u32x2_t{pack2<BF16>(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]),
+                                                       pack2<BF16>(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3])};
+      }
+    return;
+  }
   const int64_t slot = (int64_t)chunk * p.batch * p.hkv * Lk * D;
   float* dkr = p.dk32 + slot + (((int64_t)b * p.hkv + g) * Lk + key) * D;
   float* dvr = p.dv32 + slot + (((int64_t)b * p.hkv + g) * Lk + key) * D;
-  const float sc = p.scale;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -618,13 +641,9 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
     }
 }
 
-// The number of dK / dV chunks that hold a partial for keys of block kb0.
-__device__ __forceinline__ int bwd_chunks_of(const BwdParams& p, int kb0) {
-  const int all = bwd_query_range(p, kb0).nqt * p.group;
-  return min(p.chunks, (all + p.chunk_steps - 1) / p.chunk_steps);
-}
 
-// Sum of a key's partial dK / dV slots in chunk order -> the output type (4 entries per thread)
+// Sum of a key's partial dK / dV slots in chunk order -> the output type (4 entries per
+// thread), for key blocks of two or more chunks
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const BwdParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -632,6 +651,7 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const BwdParams p) {
   if (4 * i >= nkv) return;
   const int key = (int)((4 * i / D) % p.nk);
   const int n = bwd_chunks_of(p, (key / (kBwdNW * 32)) * (kBwdNW * 32));
+  if (n == 1) return;  // written by its dK / dV item (none: zero)
   f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f}, w = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int c = 0; c < n; ++c) {
     u += load_global<f32x4_t>(p.dk32 + c * nkv + 4 * i);
@@ -793,13 +813,10 @@ __device__ __forceinline__ void bwd_dq_item(const BwdParams& p, int h, int yt, i
   };
 
   // the pipeline's start: tiles 0 .. 2 in flight; S^T and dP^T of tile 0 once 0 and 1 arrived
+  // (the wait for them also covers the row's Q, dO, LSE2 and Delta, loaded first)
+  for (int i = 0; i < min(ntiles, 2); ++i) load_tile(i, i);
   settle_global_loads();
-  for (int i = 0; i < min(ntiles, 3); ++i) load_tile(i, i);
-  if (ntiles > 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  if (ntiles > 2) load_tile(2, 2);
   __syncthreads();
   f32x16_t s[NKB], dp[NKB];
 #pragma unroll
