@@ -176,7 +176,8 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p, int delta_blocks) {
   constexpr int LPR = D / 8;        // lanes per row
   constexpr int RPB = 256 / LPR;    // rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t keys[kBwdOrderMax];
+  // the order's keys, one byte per item (the launch sizes this LDS to the item count)
+  extern __shared__ __attribute__((aligned(16))) uint8_t keys[];
   if ((int)blockIdx.x >= delta_blocks) {
     bwd_order_block(p, (int)blockIdx.x - delta_blocks, keys);
     return;
@@ -999,8 +1000,9 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const int64_t order_blocks = q.order != nullptr ? ((int64_t)q.kblocks * p.chunks + 255) / 256 : 0;
   if (kv_items + dq_items > 0x7fffffff || delta_blocks + order_blocks > 0x7fffffff)
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)(delta_blocks + order_blocks)), dim3(256), 0, st, q,
-                     (int)delta_blocks);
+  const size_t keys_bytes = q.order != nullptr ? (((size_t)q.kblocks * p.chunks + 15) & ~(size_t)15) : 0;
+  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)(delta_blocks + order_blocks)), dim3(256), keys_bytes,
+                     st, q, (int)delta_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(kv_items + dq_items));
