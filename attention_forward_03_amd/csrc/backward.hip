@@ -201,6 +201,28 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p, int d
   }
 }
 
+// 32x32x16 products written out, with the accumulator in VGPRs and the B operand in AGPRs
+// (the compiler would give a product's result an AGPR, which the vector work cannot read,
+// and copy it out score by score). Each starts with the two wait states that a vector-ALU
+// write of an operand needs before a matrix product reads it; the results are read by
+// other instructions only a phase later, beyond the 12 wait states of that hazard, and a
+// chain's next product takes its predecessor's result as srcC, which is forwarded (a host
+// test checks every distance in the compiled kernels).
+template <bool BF16>
+__device__ __forceinline__ void mfma_v_first(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  if constexpr (BF16)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+template <bool BF16>
+__device__ __forceinline__ void mfma_v_acc(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  if constexpr (BF16)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
 // --------------------------------------------------------------------- dK and dV ----
 // Wave w of the workgroup owns keys kb0 + 32 w .. +31 and sums their dK^T and dV^T over the
 // steps (query head, query tile of 32 rows) of its item. A step's Q and dO tiles and its
@@ -475,7 +497,7 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
     }
     if (++cur_head_t == nqt) cur_head_t = 0;
     const int q0n = tile_q0(cur_head_t);  // the next step's first row
-    f32x16_t sn = zero16, dpn = zero16;
+    f32x16_t sn, dpn;
     u32x4_t sb[2], pbn[2];
     float t2n[16];
     // ---- phase X
@@ -484,10 +506,12 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
       __builtin_amdgcn_sched_barrier(0);
       if (k < NP) {
         if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(NXT, k + RA);
-        if (k & 1)
-          dpn = mfma32x32x16<BF16>(fr[k % (RA + 1)], vf[k >> 1], dpn);
+        f32x16_t& acc = k & 1 ? dpn : sn;
+        const u32x4_t& kv = k & 1 ? vf[k >> 1] : kf[k >> 1];
+        if (k < 2)
+          mfma_v_first<BF16>(acc, fr[k % (RA + 1)], kv);
         else
-          sn = mfma32x32x16<BF16>(fr[k % (RA + 1)], kf[k >> 1], sn);
+          mfma_v_acc<BF16>(acc, fr[k % (RA + 1)], kv);
       }
       // dS = P (dP - Delta) [(1 - t^2)]: dP - Delta of product k's share, the product of
       // k - 1's, packing of k - 2's
@@ -508,10 +532,7 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
           if (r & 1) sb[r >> 3][(r & 7) >> 1] = pack2<BF16>(s[r - 1], s[r]);
         }
       }
-      if (k < NP) {
-        if (k + RA < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
+      if (k < NP && k + RA < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase Y: product i takes its A operand from the ring slot that the transposing

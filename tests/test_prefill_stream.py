@@ -1,6 +1,7 @@
 """Host-side checks of the generated prefill instruction stream (no GPU): the hazard
 checker is pinned on planted violations, the generated text keeps its register contract,
-and the compiled gfx950 kernels keep every wait-state distance."""
+and the compiled gfx950 kernels (the generated prefill, and the backward with its
+written-out matrix products) keep every wait-state distance."""
 import os
 import re
 import shutil
@@ -123,5 +124,23 @@ def test_compiled_kernels_keep_the_wait_states(tmp_path):
     assert len(names) == 6
     for n in names:
         ins, labels = hz.parse(funcs[n])
+        bad = hz.check(ins, labels)
+        assert not bad, (n, bad[:3])
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_compiled_backward_keeps_the_wait_states(tmp_path):
+    out = tmp_path / "backward.s"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-x", "hip", "-S", "--offload-device-only", os.path.join(CSRC, "backward.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    funcs = hz.functions(out.read_text())
+    names = [n for n in funcs if "bwd_main_kernel" in n]
+    assert len(names) == 8
+    for n in names:
+        ins, labels = hz.parse(funcs[n])
+        assert sum(op.startswith("v_mfma") for op, _, _ in ins) > 0
         bad = hz.check(ins, labels)
         assert not bad, (n, bad[:3])
