@@ -815,9 +815,8 @@ __device__ __forceinline__ void bwd_dq_item(const BwdParams& p, int h, int yt, i
     }
   };
 
-  // P^T of score r of block kb of a tile (key kt + 32 kb + (r/4)*8 + hi*4 + r%4), and
-  // under a softcap dS^T directly
-  auto prob1 = [&](float sr, float dpr, auto maskc, uint32_t base, int kb, int r) __attribute__((always_inline)) {
+  // P^T of a score of a tile (without the pair test), and under a softcap dS^T directly
+  auto prob1 = [&](float sr, float dpr) __attribute__((always_inline)) {
     float e;
     if constexpr (CAP) {
       const float t = tanh_via_exp2(sr * p.cap_in);
@@ -825,11 +824,6 @@ __device__ __forceinline__ void bwd_dq_item(const BwdParams& p, int h, int yt, i
       e *= (dpr - dl) * (1.0f - t * t);
     } else {
       e = fast_exp2(fmaf(sr, p.scale_log2, -lse_use));
-    }
-    if constexpr (decltype(maskc)::value) {
-      // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
-      const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
-      e = ok ? e : 0.0f;
     }
     return e;
   };
@@ -883,37 +877,40 @@ __device__ __forceinline__ void bwd_dq_item(const BwdParams& p, int h, int yt, i
     for (int k = 0; k < RA; ++k) fr[k] = row_frag(k);
     const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
     f32x16_t sn[NKB], dpn[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sn[kb] = zero16;
-      dpn[kb] = zero16;
-    }
     // phase 1: S^T and dP^T of tile it + 1 beside P^T of tile it (program order fixed per
     // product by scheduling fences)
-    auto phase1 = [&](auto maskc) __attribute__((always_inline)) {
+    {
 #pragma unroll
       for (int k = 0; k < NP; ++k) {
         __builtin_amdgcn_sched_barrier(0);
         if (k + RA < NP) fr[(k + RA) % (RA + 1)] = row_frag(k + RA);
         const int kb = k / (2 * NKS), ks = (k % (2 * NKS)) >> 1;
-        if (k & 1)
-          dpn[kb] = mfma32x32x16<BF16>(fr[k % (RA + 1)], df[ks], dpn[kb]);
+        f32x16_t& acc = k & 1 ? dpn[kb] : sn[kb];
+        const u32x4_t& bq = k & 1 ? df[ks] : qf[ks];
+        if (ks == 0)
+          mfma_v_first<BF16>(acc, fr[k % (RA + 1)], bq);
         else
-          sn[kb] = mfma32x32x16<BF16>(fr[k % (RA + 1)], qf[ks], sn[kb]);
+          mfma_v_acc<BF16>(acc, fr[k % (RA + 1)], bq);
 #pragma unroll
         for (int e = 0; e < E1; ++e) {
           const int x = k * E1 + e, xb = x >> 4, xr = x & 15;
-          s[xb][xr] = prob1(s[xb][xr], dp[xb][xr], maskc, base, xb, xr);
+          s[xb][xr] = prob1(s[xb][xr], dp[xb][xr]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k + RA < NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-    };
+    }
+    // a tile that cuts the mask: its excluded pairs set to 0 after the fact (a select, so an
+    // inf power is dropped). Key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in
+    // [key_lo, key_lo + key_n)
     if (masked_tile(kt)) {
-      phase1(std::true_type{});
-    } else {
-      phase1(std::false_type{});
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) < key_n;
+          s[kb][r] = ok ? s[kb][r] : 0.0f;
+        }
     }
     // phase 2: dQ^T += K^T dS^T over the tile's four 16-key steps t; the dS of step t + 1
     // is computed and packed beside the products of step t
@@ -945,7 +942,18 @@ __device__ __forceinline__ void bwd_dq_item(const BwdParams& p, int h, int yt, i
       if (i + 2 < NT) ring[(i + 2) % 3] = tr_frag(i + 2);
       const int t = i / NDB, db = i % NDB;
       dq[db] = mfma32x32x16<BF16>(ring[i % 3], pbs[t], dq[db]);
-      if (db == NDB - 1 && t + 1 < NPS) pbs[t + 1] = ds_pack(t + 1);
+      // dS of step t + 1, a share beside each product of step t, packed beside the last
+      if (t + 1 < NPS) {
+        const int kb = (t + 1) >> 1, o8 = ((t + 1) & 1) * 8;
+        if constexpr (!CAP) {
+#pragma unroll
+          for (int j = db * (8 / NDB); j < (db + 1) * (8 / NDB); ++j)
+            s[kb][o8 + j] = s[kb][o8 + j] * (dp[kb][o8 + j] - dl);
+        }
+        if (db == NDB - 1)
+          pbs[t + 1] = u32x4_t{pack2<BF16>(s[kb][o8 + 0], s[kb][o8 + 1]), pack2<BF16>(s[kb][o8 + 2], s[kb][o8 + 3]),
+                               pack2<BF16>(s[kb][o8 + 4], s[kb][o8 + 5]), pack2<BF16>(s[kb][o8 + 6], s[kb][o8 + 7])};
+      }
       if (i + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
