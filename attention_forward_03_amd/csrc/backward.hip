@@ -203,24 +203,25 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p, int d
 
 // 32x32x16 products written out, with the accumulator in VGPRs and the B operand in AGPRs
 // (the compiler would give a product's result an AGPR, which the vector work cannot read,
-// and copy it out score by score). Each starts with the two wait states that a vector-ALU
-// write of an operand needs before a matrix product reads it; the results are read by
-// other instructions only a phase later, beyond the 12 wait states of that hazard, and a
-// chain's next product takes its predecessor's result as srcC, which is forwarded (a host
-// test checks every distance in the compiled kernels).
+// and copy it out score by score). The compiler does not see these as matrix products, so
+// it keeps no wait states for them: their A operands come from LDS reads and their B
+// operands from AGPRs written once per item (no vector-ALU write just before), their
+// results are read by other instructions only a phase later (beyond the 12 wait states
+// of that hazard), and a chain's next product takes its predecessor's result as srcC,
+// which is forwarded. A host test checks every such distance in the compiled kernels.
 template <bool BF16>
 __device__ __forceinline__ void mfma_v_first(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
   if constexpr (BF16)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
 template <bool BF16>
 __device__ __forceinline__ void mfma_v_acc(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
   if constexpr (BF16)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 // --------------------------------------------------------------------- dK and dV ----
