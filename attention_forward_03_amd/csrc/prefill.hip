@@ -264,14 +264,25 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
     const int kt = kbeg + it * BN;
     return wave_live && kt < rr.wend && kt + BN > rr.wbeg;
   };
+  // S^T = K Q^T: product j = (kb, ks) takes its K fragment from a ring that the reads four
+  // products ahead fill (program order fixed by scheduling fences, so the fragments of a
+  // whole tile are never held at once)
   auto scores = [&](const uint16_t* kl) __attribute__((always_inline)) {
+    constexpr int NS = NKB * NKS, RA = 4;
+    auto frag = [&](int j) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4_t*>(kl + (j / NKS) * 32 * DP + rd_k[j % NKS]);
+    };
+    u32x4_t ring[RA + 1];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int j = 0; j < RA && j < NS; ++j) ring[j] = frag(j);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * DP + rd_k[ks]);
-        s[kb] = mfma32x32x16<BF16>(a, qf[ks], ks == 0 ? zero16 : s[kb]);
-      }
+    for (int j = 0; j < NS; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + RA < NS) ring[(j + RA) % (RA + 1)] = frag(j + RA);
+      const int kb = j / NKS, ks = j % NKS;
+      s[kb] = mfma32x32x16<BF16>(ring[j % (RA + 1)], qf[ks], ks == 0 ? zero16 : s[kb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   // softcap / mask / online-softmax update of tile `it` (in s), then O^T += V^T . P^T
   auto softmax_pv = [&](int it, const uint16_t* vl) __attribute__((always_inline)) {
@@ -323,14 +334,25 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
       // row sum in fp32 adds: a packed dot product would hold the matrix core up
       l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     }
+    // O^T += V^T P^T: product j = (t, db) takes its V fragment from a ring that the
+    // transposing reads two products ahead fill
+    constexpr int NV = NPS * NDB;
+    auto vfrag = [&](int j) __attribute__((always_inline)) {
+      const int t = j / NDB, db = j % NDB;
+      const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + rd_v[db]);
+      const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + rd_v[db]);
+      return u32x4_t{lo[0], lo[1], up[0], up[1]};
+    };
+    u32x4_t vr[3];
+    vr[0] = vfrag(0);
+    if (NV > 1) vr[1] = vfrag(1);
 #pragma unroll
-    for (int t = 0; t < NPS; ++t)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + rd_v[db]);
-        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + rd_v[db]);
-        o[db] = mfma32x32x16<BF16>(u32x4_t{lo[0], lo[1], up[0], up[1]}, pf[t], o[db]);
-      }
+    for (int j = 0; j < NV; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 2 < NV) vr[(j + 2) % 3] = vfrag(j + 2);
+      o[j % NDB] = mfma32x32x16<BF16>(vr[j % 3], pf[j / NDB], o[j % NDB]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
