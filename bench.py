@@ -158,13 +158,14 @@ def load_traffic(workload: str, kernel_substr):
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     subs = (kernel_substr,) if isinstance(kernel_substr, str) else kernel_substr
-    then, now = t.get("file_digests", {}), file_digests()
+    entry = t.get("workloads", {}).get(workload, {})
+    then, now = entry.get("file_digests", {}), file_digests()
     for sub in subs:
         fam = [k for k in KERNEL_FILES if k in sub]
         files = KERNEL_FILES[fam[0]] if fam else tuple(now)
         if any(then.get(f) != now[f] for f in files):
             return None
-    kern = t.get("workloads", {}).get(workload, {}).get("kernels", {})
+    kern = entry.get("kernels", {})
     tot = [v["hbm_bytes"] for k, v in kern.items() if any(s in k for s in subs)]
     return round(sum(tot)) if tot else None
 
@@ -207,6 +208,10 @@ PROFILES = {
     "backward": ("backward_causal_gqa_B1_Hq32_Hkv8_N4096_D128", "bwd_delta_kernel + bwd_main_kernel (dK/dV and dQ "
                  "items) + bwd_convert_kernel - backward of causal GQA B=1 Hq=32 Hkv=8 N=4096 D=128 bf16",
                  ("bwd_",), ("backward", "flops_per_launch"), "TFLOP/s", PEAK_BF16_TFLOPS, None),
+    **{f"headdim{d}": (f"prefill_mfma16_causal_B2_H16_N4096_D{d}", f"fwd_mfma16_kernel<{d}, bf16> - causal "
+                        f"prefill B=2 H=16 N=4096 D={d} bf16", ("fwd_mfma16_kernel",),
+                        (f"prefill_causal_B2_H16_N4096_D{d}", "flops_per_launch"), "TFLOP/s", PEAK_BF16_TFLOPS,
+                        4 * 2 * 16 * 4096 * d * 2) for d in (96, 192, 256)},
     "gqa_causal": ("prefill_causal_gqa_B4_Hq32_Hkv8_N4096_D128", "fwd_r2p_kernel<bf16, masked> (persistent) - "
                    "causal GQA prefill B=4 Hq=32 Hkv=8 N=4096 D=128 bf16",
                    ("fwd_r2p_kernel<true, 1>",), ("gqa", "causal", "flops_exact_per_launch"), "TFLOP/s",
@@ -238,12 +243,13 @@ def _dig(d, keys):
 
 def summarize_profiles(root: str, names, copy_mib: int = 1024) -> None:
     import re
-    traffic = {"file_digests": file_digests(), "copy_mib": copy_mib, "workloads": {}}
+    # each workload's entry carries the source digests of its own counter runs, so that
+    # re-profiling one workload leaves the others' entries as valid as they were
+    traffic = {"copy_mib": copy_mib, "workloads": {}}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             old = json.load(f)
-        if old.get("file_digests") == traffic["file_digests"]:
-            traffic["workloads"].update(old.get("workloads", {}))
+        traffic["workloads"].update({k: v for k, v in old.get("workloads", {}).items() if "file_digests" in v})
     for name in names:
         fname, title, kernels, work_key, unit, peak, algo_bytes = PROFILES[name]
         d = os.path.join(root, name)
@@ -251,6 +257,7 @@ def summarize_profiles(root: str, names, copy_mib: int = 1024) -> None:
         prof, plain = _json_line(os.path.join(d, "trace.json")), _json_line(os.path.join(d, "plain.json"))
         work = float(_dig(plain, work_key))
         tr = counter_traffic(os.path.join(d, "fetch"), os.path.join(d, "write"), copy_mib)
+        tr["file_digests"] = file_digests()
         traffic["workloads"][name] = tr
         sq = {}
         for c in SQ_COUNTERS:
@@ -264,7 +271,7 @@ def summarize_profiles(root: str, names, copy_mib: int = 1024) -> None:
         short = {k: (re.search(r"::(\w+_kernel(?:<[^>]*>)?)\(", k) or [None, k])[1] for k in stats}
         lines = [f"# {title}", "",
                  f"Environment: one MI355X (gfx950), ROCm 7.2 rocprofv3. Kernel sources digest "
-                 f"`{kernel_source_digest()}`; per-file digests of the counter passes in `profiles/traffic.json`.",
+                 f"`{kernel_source_digest()}`; per-file digests of these counter passes in `profiles/traffic.json`.",
                  "", "Commands (from `/tmp` after `export TMPDIR=/tmp`; `$R` is the repository root; "
                  "each a run of its own):", "", "```",
                  f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/{name}/trace -o run "
@@ -326,6 +333,9 @@ def _bench_rate(j, name):
     if name in ("decode_fp8", "decode_mqa"):
         r = j["decode_fp8_kv_64seq_Hq32_Hkv8" if name == "decode_fp8" else "decode_mqa_64seq_Hq32_Hkv1"]
         return f"median {r['ms']} ms = {r['gbps']} GB/s"
+    if name.startswith("headdim"):
+        r = j[f"prefill_causal_B2_H16_N4096_D{name[7:]}"]
+        return f"median {r['ms']} ms = {r['tflops']} TFLOP/s"
     if name in ("fp8_prefill", "backward"):
         return f"median {j[name]['ms']} ms = {j[name]['tflops']} TFLOP/s"
     if name.startswith("gqa_"):
@@ -442,6 +452,7 @@ def measure_headdims(attn, torch, workloads, dev, flush, reps: int, dims=(96, 19
         ms = st["median"]
         fl = 4.0 * d * c.num_q_heads * c.batch * allowed_pairs(c.seqlen_q, c.seqlen_k, True)
         res[f"prefill_causal_B2_H16_N4096_D{d}"] = {"ms": ms, "batch_spread": st["batch_spread"],
+                                                    "flops_per_launch": fl,
                                                     "tflops": round(fl / ms / 1e9, 1),
                                                     "frac_of_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, o
