@@ -50,7 +50,9 @@ __device__ __forceinline__ int sw8(int key, int c) { return c ^ ((key >> 1) & 7)
 
 // four floats -> four e4m3 codes (round to nearest even), first in the low byte
 __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion writes the low half; its high half (the old value, any register)
+  // is then written by the second
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -191,21 +193,44 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
     const int kt = kbeg + it * BN;
     return wave_live && kt < rr.wend && kt + BN > rr.wbeg;
   };
+  // S^T = K . Q^T: product j = (kb, t) takes its K fragment from a ring that the reads two
+  // products ahead fill (program order fixed by scheduling fences)
   auto scores = [&](const uint8_t* kl) __attribute__((always_inline)) {
+    constexpr int NS = NKB * 2, RA = 2;
+    auto frag = [&](int j) __attribute__((always_inline)) {
+      const int kb = j >> 1, t = j & 1;
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[t][0]);
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[t][1]);
+      return i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    };
+    i32x8_t ring[RA + 1];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int j = 0; j < RA; ++j) ring[j] = frag(j);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[t][0]);
-        const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * D + rd_k[t][1]);
-        const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        s[kb] = mfma_fp8(a, qf[t], t == 0 ? zero16 : s[kb]);
-      }
+    for (int j = 0; j < NS; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + RA < NS) ring[(j + RA) % (RA + 1)] = frag(j + RA);
+      const int kb = j >> 1, t = j & 1;
+      s[kb] = mfma_fp8(ring[j % (RA + 1)], qf[t], t == 0 ? zero16 : s[kb]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto softmax_pv = [&](int it, const uint8_t* vl) __attribute__((always_inline)) {
     const int kt = kbeg + it * BN;
+    // O^T += V^T . P^T (below): product db takes its V^T fragment (four transposing reads)
+    // from a ring that the reads two products ahead fill
+    constexpr int VA = 2;
+    auto vfrag = [&](int db) __attribute__((always_inline)) {
+      i32x8_t a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const i32x2_t w = lds_read_tr8(vl + rd_v[r][db]);
+        a[2 * r] = w[0];
+        a[2 * r + 1] = w[1];
+      }
+      return a;
+    };
+    i32x8_t vr[VA + 1];
     float sc = p.scale_log2;
     if (p.cap_out > 0.0f) {
 #pragma unroll
@@ -250,6 +275,8 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
         for (int i = 0; i < 4; ++i) x[i] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + i], sc, -m_use));
         pf[4 * kb + q4] = pack4_fp8(x[0], x[1], x[2], x[3]);
       }
+#pragma unroll
+    for (int db = 0; db < VA; ++db) vr[db] = vfrag(db);
     {
       // the row sum of the rounded P from the matrix core: an all-ones A operand (e4m3 1.0)
       // puts the column sums of P^T (all 64 keys of the tile) in every row of the result;
@@ -260,17 +287,14 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
       const f32x16_t ts = mfma_fp8(ones, pf, zero16);
       l += 0.5f * ts[0];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      i32x8_t a;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const i32x2_t w = lds_read_tr8(vl + rd_v[r][db]);
-        a[2 * r] = w[0];
-        a[2 * r + 1] = w[1];
-      }
-      o[db] = mfma_fp8(a, pf, o[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (db + VA < NDB) vr[(db + VA) % (VA + 1)] = vfrag(db + VA);
+      o[db] = mfma_fp8(vr[db % (VA + 1)], pf, o[db]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
