@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS load addresses stay scalar
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -156,11 +156,16 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
   auto load_rows = [&](const uint8_t* gbase, int stride, const int* off, int kt, uint8_t* dst)
                        __attribute__((always_inline)) {
     const uint8_t* g = gbase + (int64_t)kt * stride;
+    if (kt + BN <= Lk) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      // tail rows re-read the last key
-      const int shift = kt + BN <= Lk ? 0 : min(ld_row[i], Lk - 1 - kt) - ld_row[i];
-      load_lds16(g, (uint32_t)(off[i] + shift * stride), dst + (wave + NW * i) * 1024);
+      for (int i = 0; i < LPW; ++i) load_lds16(g, (uint32_t)off[i], dst + (wave + NW * i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        // tail rows re-read the last key
+        const int shift = min(ld_row[i], Lk - 1 - kt) - ld_row[i];
+        load_lds16(g, (uint32_t)(off[i] + shift * stride), dst + (wave + NW * i) * 1024);
+      }
     }
   };
 
@@ -172,13 +177,20 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
     for (int c2 = 0; c2 < 2; ++c2) rd_k[t][c2] = l32 * D + sw8(l32, 4 * t + 2 * hi + c2) * 16;
   // V^T reads: read r of head-dim block db
   const int grp = lane >> 4, j16 = lane & 15, e = j16 >> 1, par = j16 & 1;
-  int rd_v[4][NDB];
+  // (the swizzle term (key >> 1) & 7 is the same for the four reads of a lane, whose keys
+  // differ by multiples of 16, so read r sits at a fixed offset from read 0)
+  int rd_v[NDB];
+  {
+    const int key0 = 8 * (e >> 2) + 4 * hi + (e & 3);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int key = 32 * (r >> 1) + 16 * (r & 1) + 8 * (e >> 2) + 4 * hi + (e & 3);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) rd_v[r][db] = key * D + sw8(key, 2 * db + (grp & 1)) * 16 + 8 * par;
+    for (int db = 0; db < NDB; ++db) rd_v[db] = key0 * D + sw8(key0, 2 * db + (grp & 1)) * 16 + 8 * par;
   }
+  auto rd_v_ofs = [](int r) { return (32 * (r >> 1) + 16 * (r & 1)) * D; };
+  // all-ones A operand (e4m3 1.0) of the row-sum product, kept in registers
+  i32x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
+  asm volatile("" : "+v"(ones));
 
   f32x16_t o[NDB];
 #pragma unroll
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
       i32x8_t a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const i32x2_t w = lds_read_tr8(vl + rd_v[r][db]);
+        const i32x2_t w = lds_read_tr8(vl + rd_v[db] + rd_v_ofs(r));
         a[2 * r] = w[0];
         a[2 * r + 1] = w[1];
       }
@@ -278,12 +290,10 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
 #pragma unroll
     for (int db = 0; db < VA; ++db) vr[db] = vfrag(db);
     {
-      // the row sum of the rounded P from the matrix core: an all-ones A operand (e4m3 1.0)
-      // puts the column sums of P^T (all 64 keys of the tile) in every row of the result;
+      // the row sum of the rounded P from the matrix core: the all-ones A operand puts the
+      // column sums of P^T (all 64 keys of the tile) in every row of the result;
       // lanes l and l^32 hold the same query column and their sums are added at the end,
       // so each takes half (exact)
-      const int one4 = 0x38383838;
-      const i32x8_t ones = {one4, one4, one4, one4, one4, one4, one4, one4};
       const f32x16_t ts = mfma_fp8(ones, pf, zero16);
       l += 0.5f * ts[0];
     }

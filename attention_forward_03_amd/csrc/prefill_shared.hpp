@@ -68,10 +68,16 @@ __device__ __forceinline__ RowNorm row_norm(float lt, float m, const float* sink
   return {l2 > 0.0f ? f / l2 : 0.0f, l2 > 0.0f ? (M + fast_log2(l2)) * kLn2 : kNegInf};
 }
 
-// Lanes l and l^32 hold the two halves of a query row's keys; they exchange through the
-// LDS crossbar (ds_bpermute).
-__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, xor_shuffle(x, 32)); }
-__device__ __forceinline__ float pair_sum(float x) { return x + xor_shuffle(x, 32); }
+// Lanes l and l^32 hold the two halves of a query row's keys; they exchange by a swap of
+// the wave's 32-lane halves (v_permlane32_swap: one vector instruction, no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Probabilities are formed against a reference max that may trail the true running max
 // by up to this many binary orders of magnitude; the accumulator is rescaled only when
