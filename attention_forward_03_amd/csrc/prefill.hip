@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load addresses stay scalar
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -202,13 +202,21 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
   auto load_rows = [&](const uint16_t* gbase, int stride, const int (&off)[LPW], int kt,
                        uint16_t* dst) __attribute__((always_inline)) {
     const uint16_t* g = gbase + (int64_t)kt * stride;
-    const bool full_tile = kt + BN <= Lk;
+    if (kt + BN <= Lk) {
 #pragma unroll
-    for (int n = 0; n < LPW; ++n) {
-      const int i = wave + n * NW;
-      if (LOADS % NW == 0 || i < LOADS) {
-        const int shift = full_tile ? 0 : min(ld_row[n], Lk - 1 - kt) - ld_row[n];
-        load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
+      for (int n = 0; n < LPW; ++n) {
+        const int i = wave + n * NW;
+        if (LOADS % NW == 0 || i < LOADS) load_lds16(g, (uint32_t)off[n] * 2u, dst + i * 512);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < LPW; ++n) {
+        const int i = wave + n * NW;
+        if (LOADS % NW == 0 || i < LOADS) {
+          // rows past the last key re-read it
+          const int shift = min(ld_row[n], Lk - 1 - kt) - ld_row[n];
+          load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
+        }
       }
     }
   };
