@@ -197,7 +197,9 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m = kNegInf, l = 0.0f;
+  // m: the row's reference (log2 units); thr: the raw score above which a tile moves it,
+  // (m + kSlack8) / sc; neg_mu: -(m - kPOff), the exponent offset of P (0 while m = -inf)
+  float m = kNegInf, l = 0.0f, thr = kNegInf, neg_mu = 0.0f;
   const f32x16_t zero16 = {};
   f32x16_t s[NKB];
 
@@ -264,9 +266,10 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float mxs = pair_max(mx) * sc;
-    if (__any(mxs > m + kSlack8)) {
-      const float m_new = fmaxf(m, mxs);
+    // a lane's half-row max against the threshold: the row max is formed only when some
+    // row moves its reference
+    if (__any(mx > thr)) {
+      const float m_new = fmaxf(m, pair_max(mx) * sc);
       const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
       l *= alpha;
 #pragma unroll
@@ -274,8 +277,9 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = m_new;
+      thr = (m + kSlack8) / sc;
+      neg_mu = (m == kNegInf) ? 0.0f : kPOff - m;
     }
-    const float m_use = (m == kNegInf) ? 0.0f : m - kPOff;
     // P in e4m3, byte 16 kb + r <- s[kb][r]
     i32x8_t pf;
 #pragma unroll
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
       for (int q4 = 0; q4 < 4; ++q4) {
         float x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + i], sc, -m_use));
+        for (int i = 0; i < 4; ++i) x[i] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + i], sc, neg_mu));
         pf[4 * kb + q4] = pack4_fp8(x[0], x[1], x[2], x[3]);
       }
 #pragma unroll
