@@ -264,7 +264,9 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m = kNegInf, l = 0.0f;
+  // m: the row's reference (log2 units); thr: the raw score above which a tile moves it,
+  // (m + kRescaleSlack) / sc; neg_mu: -m, the exponent offset of P (0 while m = -inf)
+  float m = kNegInf, l = 0.0f, thr = kNegInf, neg_mu = 0.0f;
   const f32x16_t zero16 = {};
   f32x16_t s[NKB];
 
@@ -317,9 +319,10 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float mxs = pair_max(mx) * sc;
-    if (__any(mxs > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mxs);
+    // a lane's half-row max against the threshold: the row max is formed only when some
+    // row moves its reference
+    if (__any(mx > thr)) {
+      const float m_new = fmaxf(m, pair_max(mx) * sc);
       // rows with no allowed key yet keep m = -inf (their l and O are still zero)
       const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
       l *= alpha;
@@ -328,15 +331,16 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = m_new;
+      thr = (m + kRescaleSlack) / sc;
+      neg_mu = (m == kNegInf) ? 0.0f : -m;
     }
-    const float m_use = (m == kNegInf) ? 0.0f : m;
     u32x4_t pf[NPS];
 #pragma unroll
     for (int t = 0; t < NPS; ++t) {
       const int kb = t >> 1, base = (t & 1) * 8;
       float e[8];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][base + x], sc, -m_use));
+      for (int x = 0; x < 8; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][base + x], sc, neg_mu));
       pf[t] = u32x4_t{pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]), pack2<BF16>(e[4], e[5]),
                       pack2<BF16>(e[6], e[7])};
       // row sum in fp32 adds: a packed dot product would hold the matrix core up
