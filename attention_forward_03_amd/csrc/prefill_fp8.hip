@@ -26,9 +26,16 @@
 // odd lane d0+8..d0+15, so lane i of the group ends with 8 keys of head-dim entry
 // d0 + i: exactly its row of V^T.
 //
-// LDS rows are 128 bytes; 16-byte chunk c of key row k sits at chunk c ^ ((k >> 1) & 7).
-// A K read (16 consecutive keys, one chunk) and a V read (8 keys with bits 0, 1, 3
-// varying, one chunk) then touch distinct bank groups.
+// LDS rows are 128 bytes; 16-byte chunk c of key row k sits at chunk c ^ g(k), where g
+// takes bits 1-3 of k with the lower two swapped. With 64 four-byte banks (256 bytes, 16
+// chunk slots, per cycle) a row pair k, k ^ 1 spans the 16 slots, so:
+//   a K read (16 lanes per cycle: 16 consecutive keys at one chunk) has 8 keys of each
+//   parity, whose g values are all distinct;
+//   a V read (32 lanes per cycle: keys {0..3, 8..11} + 4h at chunks 2db and 2db + 1) has
+//   4 keys of each parity per chunk, whose g values take one of each pair {2i, 2i + 1},
+//   so the two chunks fill disjoint slots. (g = (k >> 1) & 7 put both chunks on the same
+//   8 slots: two extra cycles per transposing read, as the counters showed.)
+// g depends on bits 1-3 only, so keys 16 apart share it.
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,7 +53,10 @@ __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int sw8(int key, int c) { return c ^ ((key >> 1) & 7); }
+__device__ __forceinline__ int sw8(int key, int c) {
+  const int x = (key >> 1) & 7;
+  return c ^ ((x & 4) | ((x & 1) << 1) | ((x >> 1) & 1));
+}
 
 // four floats -> four e4m3 codes (round to nearest even), first in the low byte
 __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
@@ -177,8 +187,8 @@ __global__ __launch_bounds__(kNW * 64, 3) void fwd_fp8_kernel(const FwdParams p)
     for (int c2 = 0; c2 < 2; ++c2) rd_k[t][c2] = l32 * D + sw8(l32, 4 * t + 2 * hi + c2) * 16;
   // V^T reads: read r of head-dim block db
   const int grp = lane >> 4, j16 = lane & 15, e = j16 >> 1, par = j16 & 1;
-  // (the swizzle term (key >> 1) & 7 is the same for the four reads of a lane, whose keys
-  // differ by multiples of 16, so read r sits at a fixed offset from read 0)
+  // (the swizzle term is the same for the four reads of a lane, whose keys differ by
+  // multiples of 16, so read r sits at a fixed offset from read 0)
   int rd_v[NDB];
   {
     const int key0 = 8 * (e >> 2) + 4 * hi + (e & 3);
