@@ -34,6 +34,7 @@ struct FwdParams {
   int32_t max_pages, num_pages;
   const float* sinks;   // per query head sink logit (natural log), or NULL
   float o_scale;        // fp8 inputs: the value scale, applied with the normalisation
+  int32_t pair_items;   // 16-bit compiler-built kernel: a workgroup per pair of query tiles
 };
 
 // One backward launch (dense, contiguous [B, H, N, D] tensors, 16-bit).

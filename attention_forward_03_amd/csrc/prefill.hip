@@ -118,318 +118,326 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const WorkItem wi = work_item(blockIdx.x, gridDim.x, p.q_tiles, p.hq, p.hkv, p.batch);
-  const int h = wi.h, b = wi.b;
-  const int qt = p.causal ? p.q_tiles - 1 - wi.qt : wi.qt;  // longest rows first
+  // The work of one query tile; a workgroup runs one, or (p.pair_items) a pair of tiles of
+  // one (sequence, head) whose causal key ranges add up to the same length for every pair:
+  // tile q_tiles - 1 - x and tile x.
+  auto run_item = [&](const int qt, const int h, const int b) __attribute__((always_inline)) {
+    int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
+    if (PAGED || p.cu_q != nullptr) {
+      q_off = p.cu_q[b];
+      Lq = p.cu_q[b + 1] - q_off;
+    }
+    if constexpr (PAGED) {
+      Lk = min(max(p.seq_lens_k[b], 0), p.max_pages * 16);  // a bad length cannot leave the table row
+    } else if (p.cu_q != nullptr) {
+      k_off = p.cu_k[b];
+      Lk = p.cu_k[b + 1] - k_off;
+    }
+    const int r0 = qt * BM;
+    if (r0 >= Lq) return;
+    const int hk = h / p.group;
+    const int delta = Lk - Lq;
+    const bool ragged = PAGED || p.cu_q != nullptr;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (ragged ? 0 : (int64_t)b * p.qs[0]) +
+                         (int64_t)h * p.qs[1] + (int64_t)q_off * p.qs[2];
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)hk * p.ks[1] +
+                         (PAGED ? 0 : (ragged ? 0 : (int64_t)b * p.ks[0]) + (int64_t)k_off * p.ks[2]);
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)hk * p.vs[1] +
+                         (PAGED ? 0 : (ragged ? 0 : (int64_t)b * p.vs[0]) + (int64_t)k_off * p.vs[2]);
+    uint16_t* og = static_cast<uint16_t*>(p.o) + (ragged ? 0 : (int64_t)b * p.os[0]) +
+                   (int64_t)h * p.os[1] + (int64_t)q_off * p.os[2];
+    const int64_t qs2 = p.qs[2], os2 = p.os[2];
+    const int ks2 = (int)p.ks[2], vs2 = (int)p.vs[2];  // host guarantees 64 * stride < 2^31
 
-  int q_off = 0, k_off = 0, Lq = p.nq, Lk = p.nk;
-  if (PAGED || p.cu_q != nullptr) {
-    q_off = p.cu_q[b];
-    Lq = p.cu_q[b + 1] - q_off;
-  }
-  if constexpr (PAGED) {
-    Lk = min(max(p.seq_lens_k[b], 0), p.max_pages * 16);  // a bad length cannot leave the table row
-  } else if (p.cu_q != nullptr) {
-    k_off = p.cu_k[b];
-    Lk = p.cu_k[b + 1] - k_off;
-  }
-  const int r0 = qt * BM;
-  if (r0 >= Lq) return;
-  const int hk = h / p.group;
-  const int delta = Lk - Lq;
-  const bool ragged = PAGED || p.cu_q != nullptr;
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (ragged ? 0 : (int64_t)b * p.qs[0]) +
-                       (int64_t)h * p.qs[1] + (int64_t)q_off * p.qs[2];
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)hk * p.ks[1] +
-                       (PAGED ? 0 : (ragged ? 0 : (int64_t)b * p.ks[0]) + (int64_t)k_off * p.ks[2]);
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)hk * p.vs[1] +
-                       (PAGED ? 0 : (ragged ? 0 : (int64_t)b * p.vs[0]) + (int64_t)k_off * p.vs[2]);
-  uint16_t* og = static_cast<uint16_t*>(p.o) + (ragged ? 0 : (int64_t)b * p.os[0]) +
-                 (int64_t)h * p.os[1] + (int64_t)q_off * p.os[2];
-  const int64_t qs2 = p.qs[2], os2 = p.os[2];
-  const int ks2 = (int)p.ks[2], vs2 = (int)p.vs[2];  // host guarantees 64 * stride < 2^31
+    const int r1 = min(Lq, r0 + BM);
+    const int kend = p.causal ? min(Lk, r1 + delta) : Lk;
+    int kbeg = p.window > 0 ? max(0, r0 + delta - p.window + 1) : 0;
+    kbeg = (kbeg / BN) * BN;
+    const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
-  const int r1 = min(Lq, r0 + BM);
-  const int kend = p.causal ? min(Lk, r1 + delta) : Lk;
-  int kbeg = p.window > 0 ? max(0, r0 + delta - p.window + 1) : 0;
-  kbeg = (kbeg / BN) * BN;
-  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+    const int w0 = r0 + wave * 32;
+    const bool wave_live = w0 < Lq;
+    const int qrow = w0 + l32;
+    const RowRange rr = wave_key_range(p, w0, Lk, delta);
+    // this lane's allowed keys: [key_lo, key_lo + key_n)
+    const int key_lo = p.window > 0 ? qrow + delta - p.window + 1 : 0;
+    const int key_hi = p.causal ? min(Lk, qrow + delta + 1) : Lk;
+    const uint32_t key_n = (uint32_t)max(key_hi - key_lo, 0);
 
-  const int w0 = r0 + wave * 32;
-  const bool wave_live = w0 < Lq;
-  const int qrow = w0 + l32;
-  const RowRange rr = wave_key_range(p, w0, Lk, delta);
-  // this lane's allowed keys: [key_lo, key_lo + key_n)
-  const int key_lo = p.window > 0 ? qrow + delta - p.window + 1 : 0;
-  const int key_hi = p.causal ? min(Lk, qrow + delta + 1) : Lk;
-  const uint32_t key_n = (uint32_t)max(key_hi - key_lo, 0);
-
-  u32x4_t qf[NKS];
+    u32x4_t qf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    qf[ks] = u32x4_t{0, 0, 0, 0};
-    if (qrow < Lq) qf[ks] = load_global<u32x4_t>(qg + qrow * qs2 + ks * 16 + hi * 8);
-  }
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = u32x4_t{0, 0, 0, 0};
+      if (qrow < Lq) qf[ks] = load_global<u32x4_t>(qg + qrow * qs2 + ks * 16 + hi * 8);
+    }
 
-  // Per-lane constant offsets (elements). Direct-to-LDS loads: load n of this wave fills
-  // LDS block i = wave + n * NW (rows i*ROWS_PER_LOAD ...) of a tile.
-  int ld_row[LPW], ld_k[LPW], ld_v[LPW];
+    // Per-lane constant offsets (elements). Direct-to-LDS loads: load n of this wave fills
+    // LDS block i = wave + n * NW (rows i*ROWS_PER_LOAD ...) of a tile.
+    int ld_row[LPW], ld_k[LPW], ld_v[LPW];
 #pragma unroll
-  for (int n = 0; n < LPW; ++n) {
-    const int i = wave + n * NW;
-    const int row = i * ROWS_PER_LOAD + lane / CPRP;
-    const int slot = lane % CPRP;
-    ld_row[n] = row;
-    ld_k[n] = row * ks2 + src_k(row, slot) * 8;
-    ld_v[n] = row * vs2 + src_v(row, slot) * 8;
-  }
-  // K reads: chunk 2*ks + hi of row kb*32 + l32 (the swizzle does not depend on kb)
-  int rd_k[NKS];
+    for (int n = 0; n < LPW; ++n) {
+      const int i = wave + n * NW;
+      const int row = i * ROWS_PER_LOAD + lane / CPRP;
+      const int slot = lane % CPRP;
+      ld_row[n] = row;
+      ld_k[n] = row * ks2 + src_k(row, slot) * 8;
+      ld_v[n] = row * vs2 + src_v(row, slot) * 8;
+    }
+    // K reads: chunk 2*ks + hi of row kb*32 + l32 (the swizzle does not depend on kb)
+    int rd_k[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * DP + SW::k(l32, 2 * ks + hi) * 8;
-  // V transposing reads: rows t*16 + vrow (+8), head-dim block db
-  const int grp = lane >> 4, gi = lane & 15;
-  const int vrow = 4 * hi + (gi >> 2);
-  int rd_v[NDB];
+    for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * DP + SW::k(l32, 2 * ks + hi) * 8;
+    // V transposing reads: rows t*16 + vrow (+8), head-dim block db
+    const int grp = lane >> 4, gi = lane & 15;
+    const int vrow = 4 * hi + (gi >> 2);
+    int rd_v[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
-    rd_v[db] = vrow * DP + SW::v(vrow, c) * 8 + (gi & 1) * 4;
-  }
+    for (int db = 0; db < NDB; ++db) {
+      const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
+      rd_v[db] = vrow * DP + SW::v(vrow, c) * 8 + (gi & 1) * 4;
+    }
 
-  // Direct-to-LDS loads of one K or V tile. In the tail tile, rows past the last key
-  // re-read the last key (always in bounds); the mask gives them zero weight.
-  auto load_rows = [&](const uint16_t* gbase, int stride, const int (&off)[LPW], int kt,
-                       uint16_t* dst) __attribute__((always_inline)) {
-    const uint16_t* g = gbase + (int64_t)kt * stride;
-    if (kt + BN <= Lk) {
+    // Direct-to-LDS loads of one K or V tile. In the tail tile, rows past the last key
+    // re-read the last key (always in bounds); the mask gives them zero weight.
+    auto load_rows = [&](const uint16_t* gbase, int stride, const int (&off)[LPW], int kt,
+                         uint16_t* dst) __attribute__((always_inline)) {
+      const uint16_t* g = gbase + (int64_t)kt * stride;
+      if (kt + BN <= Lk) {
+#pragma unroll
+        for (int n = 0; n < LPW; ++n) {
+          const int i = wave + n * NW;
+          if (LOADS % NW == 0 || i < LOADS) load_lds16(g, (uint32_t)off[n] * 2u, dst + i * 512);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < LPW; ++n) {
+          const int i = wave + n * NW;
+          if (LOADS % NW == 0 || i < LOADS) {
+            // rows past the last key re-read it
+            const int shift = min(ld_row[n], Lk - 1 - kt) - ld_row[n];
+            load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
+          }
+        }
+      }
+    };
+    // Paged form: load n of a tile reads page pg[n]; its rows past the last key re-read the
+    // last key. The page ids come from the block table (clamped to the cache, so a bad
+    // entry gives wrong values, never an access outside the cache).
+    // read through the constant address space: the table does not change during the launch,
+    // so its wave-uniform entries come in by scalar loads (which the loop's memory-clobbering
+    // direct-to-LDS loads would otherwise turn into vector loads with a wait on every load)
+    typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+    const_i32_t* bt = PAGED ? (const_i32_t*)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
+    const int last_page = (Lk - 1) >> 4, last_slot = (Lk - 1) & 15;
+    int ld_col_k[LPW], ld_col_v[LPW];
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      ld_col_k[n] = src_k(ld_row[n], lane % CPRP) * 8;
+      ld_col_v[n] = src_v(ld_row[n], lane % CPRP) * 8;
+    }
+    auto page_ids = [&](int kt, int (&pg)[LPW]) __attribute__((always_inline)) {
 #pragma unroll
       for (int n = 0; n < LPW; ++n) {
-        const int i = wave + n * NW;
-        if (LOADS % NW == 0 || i < LOADS) load_lds16(g, (uint32_t)off[n] * 2u, dst + i * 512);
+        // a wave-uniform index (the compiler cannot see that tid >> 6 is)
+        const int P = __builtin_amdgcn_readfirstlane((kt + (wave + n * NW) * ROWS_PER_LOAD) >> 4);
+        pg[n] = bt[min(P, last_page)];
       }
-    } else {
+    };
+    auto load_rows_paged = [&](const uint16_t* gbase, int64_t pstride, int stride, const int (&col)[LPW],
+                               const int (&pg)[LPW], int kt, uint16_t* dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int n = 0; n < LPW; ++n) {
         const int i = wave + n * NW;
         if (LOADS % NW == 0 || i < LOADS) {
-          // rows past the last key re-read it
-          const int shift = min(ld_row[n], Lk - 1 - kt) - ld_row[n];
-          load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
+          const int P = (kt + i * ROWS_PER_LOAD) >> 4;
+          const int slot = ld_row[n] & 15;
+          const int se = P < last_page ? slot : (P == last_page ? min(slot, last_slot) : last_slot);
+          const int page = min(max(pg[n], 0), p.num_pages - 1);
+          load_lds16(gbase + (int64_t)page * pstride, (uint32_t)(se * stride + col[n]) * 2u, dst + i * 512);
         }
       }
-    }
-  };
-  // Paged form: load n of a tile reads page pg[n]; its rows past the last key re-read the
-  // last key. The page ids come from the block table (clamped to the cache, so a bad
-  // entry gives wrong values, never an access outside the cache).
-  // read through the constant address space: the table does not change during the launch,
-  // so its wave-uniform entries come in by scalar loads (which the loop's memory-clobbering
-  // direct-to-LDS loads would otherwise turn into vector loads with a wait on every load)
-  typedef __attribute__((address_space(4))) const int32_t const_i32_t;
-  const_i32_t* bt = PAGED ? (const_i32_t*)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
-  const int last_page = (Lk - 1) >> 4, last_slot = (Lk - 1) & 15;
-  int ld_col_k[LPW], ld_col_v[LPW];
-#pragma unroll
-  for (int n = 0; n < LPW; ++n) {
-    ld_col_k[n] = src_k(ld_row[n], lane % CPRP) * 8;
-    ld_col_v[n] = src_v(ld_row[n], lane % CPRP) * 8;
-  }
-  auto page_ids = [&](int kt, int (&pg)[LPW]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) {
-      // a wave-uniform index (the compiler cannot see that tid >> 6 is)
-      const int P = __builtin_amdgcn_readfirstlane((kt + (wave + n * NW) * ROWS_PER_LOAD) >> 4);
-      pg[n] = bt[min(P, last_page)];
-    }
-  };
-  auto load_rows_paged = [&](const uint16_t* gbase, int64_t pstride, int stride, const int (&col)[LPW],
-                             const int (&pg)[LPW], int kt, uint16_t* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) {
-      const int i = wave + n * NW;
-      if (LOADS % NW == 0 || i < LOADS) {
-        const int P = (kt + i * ROWS_PER_LOAD) >> 4;
-        const int slot = ld_row[n] & 15;
-        const int se = P < last_page ? slot : (P == last_page ? min(slot, last_slot) : last_slot);
-        const int page = min(max(pg[n], 0), p.num_pages - 1);
-        load_lds16(gbase + (int64_t)page * pstride, (uint32_t)(se * stride + col[n]) * 2u, dst + i * 512);
-      }
-    }
-  };
-  int pg_next[LPW] = {};
-
-  f32x16_t o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  // m: the row's reference (log2 units); thr: the raw score above which a tile moves it,
-  // (m + kRescaleSlack) / sc; neg_mu: -m, the exponent offset of P (0 while m = -inf)
-  float m = kNegInf, l = 0.0f, thr = kNegInf, neg_mu = 0.0f;
-  const f32x16_t zero16 = {};
-  f32x16_t s[NKB];
-
-  auto needs = [&](int it) {
-    const int kt = kbeg + it * BN;
-    return wave_live && kt < rr.wend && kt + BN > rr.wbeg;
-  };
-  // S^T = K Q^T: product j = (kb, ks) takes its K fragment from a ring that the reads four
-  // products ahead fill (program order fixed by scheduling fences, so the fragments of a
-  // whole tile are never held at once)
-  auto scores = [&](const uint16_t* kl) __attribute__((always_inline)) {
-    constexpr int NS = NKB * NKS, RA = 4;
-    auto frag = [&](int j) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4_t*>(kl + (j / NKS) * 32 * DP + rd_k[j % NKS]);
     };
-    u32x4_t ring[RA + 1];
-#pragma unroll
-    for (int j = 0; j < RA && j < NS; ++j) ring[j] = frag(j);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + RA < NS) ring[(j + RA) % (RA + 1)] = frag(j + RA);
-      const int kb = j / NKS, ks = j % NKS;
-      s[kb] = mfma32x32x16<BF16>(ring[j % (RA + 1)], qf[ks], ks == 0 ? zero16 : s[kb]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // softcap / mask / online-softmax update of tile `it` (in s), then O^T += V^T . P^T
-  auto softmax_pv = [&](int it, const uint16_t* vl) __attribute__((always_inline)) {
-    const int kt = kbeg + it * BN;
-    float sc = p.scale_log2;
-    if (p.cap_out > 0.0f) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_out * tanh_via_exp2(s[kb][r] * p.cap_in);
-      sc = 1.0f;
-    }
-    if (!(kt >= rr.fbeg && kt + BN <= rr.fend)) {
-      // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
-      const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) >= key_n) s[kb][r] = kNegInf;
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    // a lane's half-row max against the threshold: the row max is formed only when some
-    // row moves its reference
-    if (__any(mx > thr)) {
-      const float m_new = fmaxf(m, pair_max(mx) * sc);
-      // rows with no allowed key yet keep m = -inf (their l and O are still zero)
-      const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m = m_new;
-      thr = (m + kRescaleSlack) / sc;
-      neg_mu = (m == kNegInf) ? 0.0f : -m;
-    }
-    u32x4_t pf[NPS];
-#pragma unroll
-    for (int t = 0; t < NPS; ++t) {
-      const int kb = t >> 1, base = (t & 1) * 8;
-      float e[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][base + x], sc, neg_mu));
-      pf[t] = u32x4_t{pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]), pack2<BF16>(e[4], e[5]),
-                      pack2<BF16>(e[6], e[7])};
-      // row sum in fp32 adds: a packed dot product would hold the matrix core up
-      l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    }
-    // O^T += V^T P^T: product j = (t, db) takes its V fragment from a ring that the
-    // transposing reads two products ahead fill
-    constexpr int NV = NPS * NDB;
-    auto vfrag = [&](int j) __attribute__((always_inline)) {
-      const int t = j / NDB, db = j % NDB;
-      const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + rd_v[db]);
-      const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + rd_v[db]);
-      return u32x4_t{lo[0], lo[1], up[0], up[1]};
-    };
-    u32x4_t vr[3];
-    vr[0] = vfrag(0);
-    if (NV > 1) vr[1] = vfrag(1);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + 2 < NV) vr[(j + 2) % 3] = vfrag(j + 2);
-      o[j % NDB] = mfma32x32x16<BF16>(vr[j % 3], pf[j / NDB], o[j % NDB]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    int pg_next[LPW] = {};
 
-  auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;  // it % 2
-    const int kt = kbeg + it * BN;
-    if (it + 1 < ntiles) {
-      if constexpr (PAGED) {
-        load_rows_paged(kg, p.ks[0], ks2, ld_col_k, pg_next, kt + BN, k_lds + (BUF ^ 1) * TILE);
-        load_rows_paged(vg, p.vs[0], vs2, ld_col_v, pg_next, kt + BN, v_lds + (BUF ^ 1) * TILE);
-        if (it + 2 < ntiles) page_ids(kt + 2 * BN, pg_next);
-      } else {
-        load_rows(kg, ks2, ld_k, kt + BN, k_lds + (BUF ^ 1) * TILE);
-        load_rows(vg, vs2, ld_v, kt + BN, v_lds + (BUF ^ 1) * TILE);
-      }
-    }
-    if (needs(it)) {
-      scores(k_lds + BUF * TILE);
-      softmax_pv(it, v_lds + BUF * TILE);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
-  settle_global_loads();
-  if constexpr (PAGED) {
-    if (ntiles > 0) {
-      int pg[LPW];
-      page_ids(kbeg, pg);
-      if (ntiles > 1) page_ids(kbeg + BN, pg_next);
-      load_rows_paged(kg, p.ks[0], ks2, ld_col_k, pg, kbeg, k_lds);
-      load_rows_paged(vg, p.vs[0], vs2, ld_col_v, pg, kbeg, v_lds);
-    }
-  } else {
-    if (ntiles > 0) {
-      load_rows(kg, ks2, ld_k, kbeg, k_lds);
-      load_rows(vg, vs2, ld_v, kbeg, v_lds);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    tile(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it + 1);
-  }
-
-  if (!wave_live) return;
-  const RowNorm nrm = row_norm(pair_sum(l), m, p.sinks, h);
-  const float inv = nrm.inv;
-  if (qrow < Lq) {
-    uint16_t* orow = og + qrow * os2;
+    f32x16_t o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + g4 * 8 + hi * 4;
-        const u32x2_t w = {pack2<BF16>(o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv),
-                           pack2<BF16>(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(orow + d) = w;
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    // m: the row's reference (log2 units); thr: the raw score above which a tile moves it,
+    // (m + kRescaleSlack) / sc; neg_mu: -m, the exponent offset of P (0 while m = -inf)
+    float m = kNegInf, l = 0.0f, thr = kNegInf, neg_mu = 0.0f;
+    const f32x16_t zero16 = {};
+    f32x16_t s[NKB];
+
+    auto needs = [&](int it) {
+      const int kt = kbeg + it * BN;
+      return wave_live && kt < rr.wend && kt + BN > rr.wbeg;
+    };
+    // S^T = K Q^T: product j = (kb, ks) takes its K fragment from a ring that the reads four
+    // products ahead fill (program order fixed by scheduling fences, so the fragments of a
+    // whole tile are never held at once)
+    auto scores = [&](const uint16_t* kl) __attribute__((always_inline)) {
+      constexpr int NS = NKB * NKS, RA = 4;
+      auto frag = [&](int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4_t*>(kl + (j / NKS) * 32 * DP + rd_k[j % NKS]);
+      };
+      u32x4_t ring[RA + 1];
+#pragma unroll
+      for (int j = 0; j < RA && j < NS; ++j) ring[j] = frag(j);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + RA < NS) ring[(j + RA) % (RA + 1)] = frag(j + RA);
+        const int kb = j / NKS, ks = j % NKS;
+        s[kb] = mfma32x32x16<BF16>(ring[j % (RA + 1)], qf[ks], ks == 0 ? zero16 : s[kb]);
       }
-    if (hi == 0 && p.lse != nullptr) {
-      const int64_t idx = ragged ? (int64_t)h * p.cu_q[p.batch] + q_off + qrow
-                                 : ((int64_t)b * p.hq + h) * p.nq + qrow;
-      p.lse[idx] = nrm.lse;
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // softcap / mask / online-softmax update of tile `it` (in s), then O^T += V^T . P^T
+    auto softmax_pv = [&](int it, const uint16_t* vl) __attribute__((always_inline)) {
+      const int kt = kbeg + it * BN;
+      float sc = p.scale_log2;
+      if (p.cap_out > 0.0f) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_out * tanh_via_exp2(s[kb][r] * p.cap_in);
+        sc = 1.0f;
+      }
+      if (!(kt >= rr.fbeg && kt + BN <= rr.fend)) {
+        // key kt + kb*32 + (r/4)*8 + hi*4 + r%4 is allowed iff it lies in [key_lo, key_lo + key_n)
+        const uint32_t base = (uint32_t)(kt + hi * 4 - key_lo);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (base + (uint32_t)(kb * 32 + (r >> 2) * 8 + (r & 3)) >= key_n) s[kb][r] = kNegInf;
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      // a lane's half-row max against the threshold: the row max is formed only when some
+      // row moves its reference
+      if (__any(mx > thr)) {
+        const float m_new = fmaxf(m, pair_max(mx) * sc);
+        // rows with no allowed key yet keep m = -inf (their l and O are still zero)
+        const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m = m_new;
+        thr = (m + kRescaleSlack) / sc;
+        neg_mu = (m == kNegInf) ? 0.0f : -m;
+      }
+      u32x4_t pf[NPS];
+#pragma unroll
+      for (int t = 0; t < NPS; ++t) {
+        const int kb = t >> 1, base = (t & 1) * 8;
+        float e[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][base + x], sc, neg_mu));
+        pf[t] = u32x4_t{pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]), pack2<BF16>(e[4], e[5]),
+                        pack2<BF16>(e[6], e[7])};
+        // row sum in fp32 adds: a packed dot product would hold the matrix core up
+        l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
+      // O^T += V^T P^T: product j = (t, db) takes its V fragment from a ring that the
+      // transposing reads two products ahead fill
+      constexpr int NV = NPS * NDB;
+      auto vfrag = [&](int j) __attribute__((always_inline)) {
+        const int t = j / NDB, db = j % NDB;
+        const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + rd_v[db]);
+        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + rd_v[db]);
+        return u32x4_t{lo[0], lo[1], up[0], up[1]};
+      };
+      u32x4_t vr[3];
+      vr[0] = vfrag(0);
+      if (NV > 1) vr[1] = vfrag(1);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 2 < NV) vr[(j + 2) % 3] = vfrag(j + 2);
+        o[j % NDB] = mfma32x32x16<BF16>(vr[j % 3], pf[j / NDB], o[j % NDB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto tile = [&](auto bufc, int it) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(bufc)::value;  // it % 2
+      const int kt = kbeg + it * BN;
+      if (it + 1 < ntiles) {
+        if constexpr (PAGED) {
+          load_rows_paged(kg, p.ks[0], ks2, ld_col_k, pg_next, kt + BN, k_lds + (BUF ^ 1) * TILE);
+          load_rows_paged(vg, p.vs[0], vs2, ld_col_v, pg_next, kt + BN, v_lds + (BUF ^ 1) * TILE);
+          if (it + 2 < ntiles) page_ids(kt + 2 * BN, pg_next);
+        } else {
+          load_rows(kg, ks2, ld_k, kt + BN, k_lds + (BUF ^ 1) * TILE);
+          load_rows(vg, vs2, ld_v, kt + BN, v_lds + (BUF ^ 1) * TILE);
+        }
+      }
+      if (needs(it)) {
+        scores(k_lds + BUF * TILE);
+        softmax_pv(it, v_lds + BUF * TILE);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+
+    settle_global_loads();
+    if constexpr (PAGED) {
+      if (ntiles > 0) {
+        int pg[LPW];
+        page_ids(kbeg, pg);
+        if (ntiles > 1) page_ids(kbeg + BN, pg_next);
+        load_rows_paged(kg, p.ks[0], ks2, ld_col_k, pg, kbeg, k_lds);
+        load_rows_paged(vg, p.vs[0], vs2, ld_col_v, pg, kbeg, v_lds);
+      }
+    } else {
+      if (ntiles > 0) {
+        load_rows(kg, ks2, ld_k, kbeg, k_lds);
+        load_rows(vg, vs2, ld_v, kbeg, v_lds);
+      }
     }
-  }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int it = 0; it < ntiles; it += 2) {
+      tile(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it + 1);
+    }
+
+    if (!wave_live) return;
+    const RowNorm nrm = row_norm(pair_sum(l), m, p.sinks, h);
+    const float inv = nrm.inv;
+    if (qrow < Lq) {
+      uint16_t* orow = og + qrow * os2;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + hi * 4;
+          const u32x2_t w = {pack2<BF16>(o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv),
+                             pack2<BF16>(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(orow + d) = w;
+        }
+      if (hi == 0 && p.lse != nullptr) {
+        const int64_t idx = ragged ? (int64_t)h * p.cu_q[p.batch] + q_off + qrow
+                                   : ((int64_t)b * p.hq + h) * p.nq + qrow;
+        p.lse[idx] = nrm.lse;
+      }
+    }
+  };  // run_item
+
+  // (an item ends with a barrier after its last LDS read, so the next one may load at once)
+  const int units = p.pair_items ? (p.q_tiles + 1) / 2 : p.q_tiles;
+  const WorkItem wi = work_item(blockIdx.x, gridDim.x, units, p.hq, p.hkv, p.batch);
+  const int qa = p.causal ? p.q_tiles - 1 - wi.qt : wi.qt;  // longest rows first
+  const int n_items = p.pair_items && wi.qt != qa ? 2 : 1;
+  for (int i = 0; i < n_items; ++i) run_item(i == 0 ? qa : wi.qt, wi.h, wi.b);
 }
 
 // ------------------------------------------- 16-bit inputs, 64 query rows per wave ----
@@ -1079,8 +1087,13 @@ hipError_t launch16(const FwdParams& p, hipStream_t st) {
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((fwd_mfma16_kernel<D, nw16(D), bn16(D), BF16>), dim3((unsigned)blocks), dim3(nw16(D) * 64), 0,
-                       st, p);
+    // causal dense batches: a workgroup takes a long and a short query tile of one
+    // (sequence, head), so that every workgroup has the same work
+    FwdParams pp = p;
+    pp.pair_items = p.causal && p.window == 0 && p.cu_q == nullptr ? 1 : 0;
+    const int64_t grid = pp.pair_items ? (int64_t)((p.q_tiles + 1) / 2) * p.hq * p.batch : blocks;
+    hipLaunchKernelGGL((fwd_mfma16_kernel<D, nw16(D), bn16(D), BF16>), dim3((unsigned)grid), dim3(nw16(D) * 64), 0,
+                       st, pp);
     return hipGetLastError();
   }
 }
