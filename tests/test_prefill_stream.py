@@ -110,13 +110,22 @@ def _hipcc():
     return p if os.path.exists(p) else shutil.which("hipcc")
 
 
+def _device_asm_cmd(src, out, extra_includes=()):
+    """The library build's compile line for `src` (its common and per-file flags), for the
+    device code only and as assembly: the checks below then read the code that ships."""
+    sys.path.insert(0, ROOT)
+    from attention_forward_03_amd import build
+    cmd = [_hipcc(), *build.common_flags(), *build.SOURCE_FLAGS.get(src, []), "-I", CSRC]
+    for inc in extra_includes:
+        cmd += ["-I", str(inc)]
+    return cmd + ["-x", "hip", "-S", "--offload-device-only", os.path.join(CSRC, src), "-o", str(out)]
+
+
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
 def test_compiled_kernels_keep_the_wait_states(tmp_path):
     gen.main(str(tmp_path / "gen"))
     out = tmp_path / "prefill.s"
-    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, "-I", str(tmp_path / "gen"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-x", "hip", "-S", "--offload-device-only", os.path.join(CSRC, "prefill.hip"), "-o", str(out)]
+    cmd = _device_asm_cmd("prefill.hip", out, [tmp_path / "gen"])
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     funcs = hz.functions(out.read_text())
@@ -131,9 +140,7 @@ def test_compiled_kernels_keep_the_wait_states(tmp_path):
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
 def test_compiled_backward_keeps_the_wait_states(tmp_path):
     out = tmp_path / "backward.s"
-    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-x", "hip", "-S", "--offload-device-only", os.path.join(CSRC, "backward.hip"), "-o", str(out)]
+    cmd = _device_asm_cmd("backward.hip", out)
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     funcs = hz.functions(out.read_text())
