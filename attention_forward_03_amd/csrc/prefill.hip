@@ -1014,10 +1014,11 @@ constexpr int kBN16 = ATTN_PREFILL_KEYS;   // keys per tile, 16-bit inputs
 // share a CU (three waves per SIMD); at 192 (32-key tiles) the kernel fits in 256
 // registers, so two do (two waves per SIMD: one wave's softmax runs beside another's
 // products); at 256 the 128 accumulator registers of the output block, the Q fragments and
-// the scores need more, so one wave per SIMD holds them, on 64-key tiles (two independent
-// 32-key sub-tiles per barrier: 2-3% over 32-key tiles).
+// the scores need more, so one wave per SIMD holds them; on 32-key tiles (64-key tiles, two
+// sub-tiles per barrier, measured 2-3% faster before the loads lost their per-load vector
+// work, 4% slower since).
 constexpr int nw16(int D) { return D >= 192 || D == 96 ? 4 : kNW16; }
-constexpr int bn16(int D) { return D == 192 || D == 96 ? 32 : kBN16; }
+constexpr int bn16(int D) { return D >= 192 || D == 96 ? 32 : kBN16; }
 constexpr int kNW32 = 4;
 constexpr int kBN32 = 32;
 
