@@ -476,6 +476,9 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
   u32x4_t fr[RA + 1];
 #pragma unroll
   for (int k = 0; k < RA; ++k) fr[k] = row_frag(1 % NBUF, k);
+  f32x4_t del[4];  // Delta of the current step's rows
+#pragma unroll
+  for (int j = 0; j < 4; ++j) del[j] = *reinterpret_cast<const f32x4_t*>(stats + (1 * kBwdNW + j) * 64 + 4 * hi);
 
   // One step (buffer BUF). Phase X: the S and dP products of step st + 1 (buffer BUF + 1)
   // beside dS of step st. Phase Y: the dV and dK products of step st beside P of step st + 1.
@@ -488,14 +491,13 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
     constexpr int BUF = decltype(bufc)::value;  // (st - st0) % NBUF
     constexpr int NXT = (BUF + 1) % NBUF;
     constexpr int QO = (BUF < HB ? BUF : BUF - HB) * 2 * TILE;
-    // Delta of this step's rows and LSE2 of the next step's: lane rows
-    // 8 j + 4 hi + i, loaded by wave j into entries 4 hi ..
-    f32x4_t del[4], lsn[4];
+    // LSE2 of the next step's rows (lane rows 8 j + 4 hi + i, loaded by wave j into
+    // entries 4 hi ..; first needed in phase Y); Delta of this step's rows came in at the
+    // end of the step before
+    f32x4_t lsn[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((BUF * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
+    for (int j = 0; j < 4; ++j)
       lsn[j] = *reinterpret_cast<const f32x4_t*>(stats + ((NXT * 2 + 0) * kBwdNW + j) * 64 + 4 * hi);
-    }
     if (++cur_head_t == nqt) cur_head_t = 0;
     const int q0n = tile_q0(cur_head_t);  // the next step's first row
     f32x16_t sn, dpn;
@@ -607,9 +609,13 @@ __device__ __forceinline__ void bwd_dkdv_item(const BwdParams& p, int w, uint16_
 #pragma unroll
       for (int r = 0; r < 16; ++r) t2[r] = t2n[r];
     }
-    // row fragments of the next step's phase X (buffer BUF + 2)
+    // row fragments of the next step's phase X (buffer BUF + 2), Delta of the next step's
+    // rows (buffer BUF + 1)
 #pragma unroll
     for (int k = 0; k < RA; ++k) fr[k] = row_frag((BUF + 2) % NBUF, k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      del[j] = *reinterpret_cast<const f32x4_t*>(stats + ((NXT * 2 + 1) * kBwdNW + j) * 64 + 4 * hi);
   };
   // a pair of steps (st, st + 1) in buffers B0, B0 + 1: the loads of st + 6 and st + 7 go
   // into the buffers of the previous pair (which every wave has finished); at the end the
