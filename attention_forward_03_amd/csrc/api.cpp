@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "../../include/attn.h"
@@ -457,9 +459,24 @@ attn_status_t attn_decode_plan(const attn_decode_args_t* a, int32_t* split_len, 
   attn_status_t st = check_decode_args(a);
   if (st != ATTN_SUCCESS) return st;
   int64_t len;
+  const int coop = attn::decode_coop_slots_per_cu(a->kv_dtype, a->num_q_heads, a->num_kv_heads);
   if (a->num_splits > 0) {
     const int64_t per = ((int64_t)a->max_seq_len + a->num_splits - 1) / a->num_splits;
     len = (per + kPageSize - 1) / kPageSize * kPageSize;
+  } else if (coop > 0) {
+    // The cooperative kernel runs one workgroup per (split, sequence), all KV heads in it.
+    // With the lengths taken as half the maximum on average and every sequence's last
+    // split partial, the splits are sized for about three quarters of the workgroups the
+    // device holds at once: one round of long splits, with room for lengths above the
+    // average (a second round of full splits doubles the time; many short splits pay the
+    // pipeline fill of each). At least 256 tokens; then spread evenly over the maximum.
+    const double slots = 0.75 * coop * attn::device_cus();
+    const double room = slots - 0.5 * a->num_seqs;
+    const double want = room > 0 ? (double)a->num_seqs * 0.5 * a->max_seq_len / room : (double)kMaxSplitTokens;
+    len = std::max<int64_t>(256, (int64_t)std::ceil(want));
+    if (len > kMaxSplitTokens) len = kMaxSplitTokens;
+    const int64_t n = ((int64_t)a->max_seq_len + len - 1) / len;
+    len = (((int64_t)a->max_seq_len + n - 1) / n + kPageSize - 1) / kPageSize * kPageSize;
   } else {
     // Two aims, with the sequences' lengths taken as half the maximum on average:
     // (1) about kDecodeItems single-wave work items (splits x KV heads), so short

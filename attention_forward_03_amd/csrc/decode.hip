@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64 * CO) void decode_split_kernel(const DecodeParam
 
   const int L = p.seq_lens[s];
   const int t0 = split * p.split_len;
-  if (t0 >= L) return;
+  if (t0 >= L || split >= p.max_splits) return;  // (the grid may hold one more split column)
   const int t1 = min(L, t0 + p.split_len);
 
   // Q as the B operand of the score product: k-step ks, slot group quad <-> head_dim
@@ -508,9 +508,16 @@ constexpr int kCoopWaves = ATTN_DECODE_COOP_WAVES;  // at most this many KV head
 #endif
 constexpr int kStagesCoop = ATTN_DECODE_STAGES_COOP;  // whole-page stages per workgroup
 
+// The hardware deals workgroups to the 8 XCDs round-robin by linear index, here split +
+// width * (head group + ... * sequence). With an even width the XCD of a split hardly moves
+// from one sequence to the next (a multiple of 8: split j of every sequence on XCD j % 8),
+// and the early splits, which every sequence has, pile onto a few XCDs. An odd width (one
+// more split column, whose workgroups find no keys and end at once) deals the splits of
+// each index over all 8 XCDs: the fp8 decode workload 0.426 -> 0.38 ms at 16 splits.
 template <int KV, bool QBF16, int NST, int CO>
 hipError_t launch_coop(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, NST, 1, CO>), dim3(p.max_splits, p.hkv / CO, p.num_seqs), dim3(64 * CO),
+  const int width = p.max_splits | 1;
+  hipLaunchKernelGGL((decode_split_kernel<KV, QBF16, NST, 1, CO>), dim3(width, p.hkv / CO, p.num_seqs), dim3(64 * CO),
                      0, st, p);
   return hipGetLastError();
 }
@@ -577,6 +584,19 @@ hipError_t decode_scratch(void** ptr) {
   }
   *ptr = g_scratch_ptr[dev];
   return hipSuccess;
+}
+
+// kv_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3. The same choice of kernel as launch() below;
+// the count is the LDS limit of the workgroup's page stages (at most 32 waves per CU).
+int decode_coop_slots_per_cu(int kv_dtype, int num_q_heads, int num_kv_heads) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  const bool fp8 = kv_dtype == 3;
+  const int group = num_q_heads / num_kv_heads;
+  const int co = min(num_kv_heads & -num_kv_heads, kCoopWaves);
+  if (!(kCoopKinds & (fp8 ? 1 : 2)) || group > 16 || co < 2) return 0;
+  const int stages = fp8 ? kStagesCoop : 2;
+  const int lds = stages * co * 2 * kPage * kD * (fp8 ? 1 : 2);
+  return max(1, min(160 * 1024 / lds, 32 / co));
 }
 
 // q_dtype: 1 = f16, 2 = bf16; kv_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3

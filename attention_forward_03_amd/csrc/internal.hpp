@@ -141,6 +141,11 @@ hipError_t launch_gather_kv_pages(const void* k_cache, const void* v_cache, cons
                                   const int32_t* seq_lens, void* ws_k, void* ws_v, int num_seqs, int max_pages,
                                   int num_pages, int page_bytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype, hipStream_t stream);
+// Workgroups of the cooperative decode split kernel (one per split and sequence, all KV
+// heads) that one CU holds at once, or 0 when these heads take the one-wave kernel.
+int decode_coop_slots_per_cu(int kv_dtype, int num_q_heads, int num_kv_heads);
+// Compute units of the current device (256 when there is none).
+int device_cus();
 // Bytes of the device scratch array behind attn_decode_paged_noalloc (per GPU): the
 // header's ATTN_DECODE_NOALLOC_MAX_WORKSPACE.
 constexpr size_t kDecodeScratchBytes = size_t(64) << 20;

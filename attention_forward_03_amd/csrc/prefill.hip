@@ -1034,18 +1034,6 @@ bool small_grid16(int head_dim, int64_t nq, int64_t units) {
 #define ATTN_PREFILL_PERSISTENT 1
 #endif
 
-// Compute units of the current device (one persistent workgroup each).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 template <bool BF16>
 hipError_t launch_r2p(const FwdParams& p, int items, int grid, hipStream_t st) {
@@ -1142,6 +1130,20 @@ hipError_t launch16_paged(const FwdParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// Compute units of the current device (one persistent prefill workgroup each; the decode
+// plan sizes its splits by them).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 int fwd_paged_block_rows(int head_dim) { return nw16(head_dim) * 32; }
 

@@ -252,7 +252,9 @@ typedef struct {
 /* Split plan: every sequence s is cut into ceil(seq_lens[s] / split_len)
  * pieces of split_len tokens (a multiple of page_size, at most 4096);
  * max_splits = ceil(max_seq_len / split_len). Deterministic function of the
- * args only. */
+ * args and, for fp8 KV with at most 16 query heads per KV head and an even
+ * Hkv (one workgroup per split and sequence), of the current device's
+ * compute-unit count (256 when no device is visible). */
 attn_status_t attn_decode_plan(const attn_decode_args_t *args, int32_t *split_len,
                                int32_t *max_splits);
 

@@ -202,7 +202,7 @@ def test_decode_plan_is_a_deterministic_integer_function():
     # the K/V bytes (at least 512 * G / kv_bytes tokens) ...
     assert attn.decode_plan(**_dec_kw(num_kv_heads=1)) == (2048, 16)
     assert attn.decode_plan(**_dec_kw(num_kv_heads=2)) == (4096, 8)
-    assert attn.decode_plan(**_dec_kw(kv_dtype=_lib.ATTN_FP8_E4M3)) == (2048, 16)
+    assert attn.decode_plan(**_dec_kw(kv_dtype=_lib.ATTN_FP8_E4M3, num_kv_heads=1)) == (2048, 16)
     # ... while the grid keeps at least 384 waves (a wave takes two tiles of 16 query heads)
     assert attn.decode_plan(**_dec_kw(num_seqs=1, num_kv_heads=1)) == (256, 128)
     assert attn.decode_plan(**_dec_kw(num_seqs=8, num_kv_heads=1)) == (256, 128)
@@ -219,6 +219,33 @@ def test_decode_plan_is_a_deterministic_integer_function():
         ln, n = attn.decode_plan(**_dec_kw(num_splits=forced))
         assert ln % 16 == 0 and ln <= 4096 and n == -(-32768 // ln)
         assert (n <= forced and ln == -(-(-(-32768 // forced)) // 16) * 16) or ln == 4096
+
+
+def test_decode_plan_of_the_cooperative_fp8_kernel():
+    """fp8 KV, at most 16 query heads per KV head, even Hkv: one workgroup per (split,
+    sequence), two per CU (the LDS of their page stages). The splits are sized so that the
+    expected workgroup count, with lengths taken as half the maximum and one partial split
+    per sequence, is three quarters of the 2 x 256 workgroups the device holds at once
+    (256 compute units without a device); at least 256 tokens, at most 4096, then spread
+    evenly over the maximum length."""
+    def expect(num_seqs, max_len):
+        room = 0.75 * 2 * 256 - 0.5 * num_seqs
+        want = num_seqs * 0.5 * max_len / room if room > 0 else 4096
+        ln = min(max(256, -(-int(want * 1e6) // 10 ** 6)), 4096)
+        n = -(-max_len // ln)
+        ln = -(-(-(-max_len // n)) // 16) * 16
+        return ln, -(-max_len // ln)
+    fp8 = dict(kv_dtype=_lib.ATTN_FP8_E4M3)
+    cases = [(64, 32768, (2992, 11)), (64, 8192, (752, 11)), (16, 32768, (704, 47)),
+             (128, 16384, (3280, 5)), (1024, 32768, (4096, 8)), (1, 1000, (256, 4))]
+    for num_seqs, max_len, want in cases:
+        got = attn.decode_plan(**_dec_kw(num_seqs=num_seqs, max_seq_len=max_len,
+                                         max_pages_per_seq=-(-max_len // 16), **fp8))
+        assert got == want == expect(num_seqs, max_len), (num_seqs, max_len, got)
+    # an odd Hkv takes the one-wave kernel and its plan: 896-token splits rounded up to a
+    # power of two (1024), then doubled to 512 * G / kv_bytes = 2048 (the grid keeps its
+    # 384 waves)
+    assert attn.decode_plan(**_dec_kw(num_q_heads=28, num_kv_heads=7, **fp8)) == (2048, 16)
 
 
 def test_decode_workspace_size():
