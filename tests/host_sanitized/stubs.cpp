@@ -51,6 +51,16 @@ hipError_t launch_decode(const DecodeParams& p, int, int, hipStream_t) {
   ++attn_stub::launches;
   return hipSuccess;
 }
+// the cooperative decode kernel's residency for fp8 KV with an even Hkv and at most 16
+// query heads per KV head (two 64 KiB workgroups per CU at Hkv 8), none otherwise
+int decode_coop_slots_per_cu(int kv_dtype, int num_q_heads, int num_kv_heads) {
+  if (kv_dtype != 3 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  const int co = (num_kv_heads & -num_kv_heads) < 8 ? (num_kv_heads & -num_kv_heads) : 8;
+  if (num_q_heads / num_kv_heads > 16 || co < 2) return 0;
+  const int by_lds = 160 * 1024 / (2 * co * 2 * 16 * 128);
+  return by_lds < 32 / co ? by_lds : 32 / co;
+}
+int device_cus() { return 256; }
 hipError_t decode_scratch(void** ptr) {
   *ptr = fake_scratch;
   return hipSuccess;
