@@ -540,7 +540,12 @@ hipError_t launch(const DecodeParams& p, hipStream_t st) {
     return hipGetLastError();
   }
 #if ATTN_DECODE_HEAD_MAJOR
-  dim3 grid(p.hkv * wave_tiles, p.max_splits, p.num_seqs);
+  // With a multiple of 8 head columns each XCD takes whole columns; an odd split width
+  // then changes which of the XCD's CUs the splits of consecutive sequences meet (a
+  // multiple of 8 kept split j on the same CUs): -1.6% on the decode workload, -9.5% on
+  // 64 short sequences. With fewer columns (MQA) the even width measured faster.
+  const int cols = p.hkv * wave_tiles;
+  dim3 grid(cols, cols % 8 == 0 ? p.max_splits | 1 : p.max_splits, p.num_seqs);
 #else
   dim3 grid(p.max_splits, p.hkv * wave_tiles, p.num_seqs);
 #endif
