@@ -361,10 +361,12 @@ def batch_stats(ms, batches: int = BATCHES) -> dict:
             "batch_spread": round((max(meds) - min(meds)) / med, 4) if med > 0 else 0.0}
 
 
-def _timed(torch, fn, flush, reps: int, warmup: int = 3) -> dict:
+def _timed(torch, fn, flush, reps: int, warmup: int = 10) -> dict:
     """batch_stats of fn over reps launches, HIP events on the current stream around each
-    launch, caches flushed before each. A few flushed launches first: the first ones after
-    a different workload run measurably slower (clock and cache state)."""
+    launch, caches flushed before each. Flushed launches first: the first ones after a
+    different workload run measurably slower (clock and cache state; with 3 of them the
+    first batch of 5 timed launches of the backward and the fp8 prefill still ran 12-17%
+    slower than the last)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for _ in range(warmup):
         flush()
