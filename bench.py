@@ -179,7 +179,7 @@ def load_traffic(workload: str, kernel_substr):
 # into profiles/traffic.json.
 SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
                "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT")
-PROFILE_STEPS = {"trace": (5, 1), "counters": (2, 1)}  # (steps, warmup) of the profiled runs
+PROFILE_STEPS = {"trace": (10, 10), "counters": (2, 1)}  # (steps, warmup) of the profiled runs
 
 # name: (file, title, kernels of one call, how the work per call is found, unit, peak, algorithmic bytes)
 PROFILES = {
@@ -616,7 +616,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # (the first launches run at lower clocks: with 3 warm-up steps the headline's first batch
+    # of timed steps still ran up to 5% slower than its last)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=ONLY_MAIN + ONLY_EXTRA,
                     help="time one workload alone (profiled runs: one workload per kernel name)")
     ap.add_argument("--no-decode", action="store_true", help="skip the paged decode in the main step")
