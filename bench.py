@@ -361,12 +361,12 @@ def batch_stats(ms, batches: int = BATCHES) -> dict:
             "batch_spread": round((max(meds) - min(meds)) / med, 4) if med > 0 else 0.0}
 
 
-def _timed(torch, fn, flush, reps: int, warmup: int = 10) -> dict:
+def _timed(torch, fn, flush, reps: int, warmup: int = 50) -> dict:
     """batch_stats of fn over reps launches, HIP events on the current stream around each
-    launch, caches flushed before each. Flushed launches first: the first ones after a
-    different workload run measurably slower (clock and cache state; with 3 of them the
-    first batch of 5 timed launches of the backward and the fp8 prefill still ran 12-17%
-    slower than the last)."""
+    launch, caches flushed before each. Flushed launches first: the clocks settle over tens
+    of milliseconds of a workload (with 3 of them the first batch of 5 timed launches of the
+    backward and the fp8 prefill ran 12-17% slower than the last, with 10 the backward's
+    still 8%)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for _ in range(warmup):
         flush()
@@ -617,8 +617,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     # (the first launches run at lower clocks: with 3 warm-up steps the headline's first batch
-    # of timed steps still ran up to 5% slower than its last)
-    ap.add_argument("--warmup", type=int, default=20)
+    # of timed steps still ran up to 5% slower than its last, with 20 about 2%)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", choices=ONLY_MAIN + ONLY_EXTRA,
                     help="time one workload alone (profiled runs: one workload per kernel name)")
     ap.add_argument("--no-decode", action="store_true", help="skip the paged decode in the main step")
