@@ -230,6 +230,20 @@ def _kernel_stats(d):
     return rows
 
 
+def _timed_dispatch_ns(d, n):
+    """Per kernel name: mean duration (ns) of its last n dispatches in the kernel trace of
+    folder d (the timed launches of a bench.py --only run come after its warm-up ones)."""
+    import csv
+    import glob
+    runs = {}
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                runs.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return {k: sum(dur for _, dur in sorted(v)[-n:]) / len(sorted(v)[-n:]) for k, v in runs.items()}
+
+
 def _json_line(path):
     with open(path) as f:
         return json.loads([ln for ln in f if ln.startswith("{")][-1])
@@ -266,7 +280,11 @@ def summarize_profiles(root: str, names, copy_mib: int = 1024) -> None:
                     vs = max(g.values(), key=len)
                     sq.setdefault(k, {})[c] = round(sum(vs) / len(vs))
         mine = {k: r for k, r in stats.items() if any(s in k for s in kernels)}
-        ns = sum(float(r["AverageNs"]) for r in mine.values())
+        # the rate from the timed dispatches: the warm-up ones before them run back to back,
+        # without the cache flush, and at clocks that are still settling
+        n_timed = PROFILE_STEPS["trace"][0]
+        timed = _timed_dispatch_ns(os.path.join(d, "trace"), n_timed)
+        ns = sum(timed[k] for k in mine)
         rate = work / ns * (1e-3 if unit == "TFLOP/s" else 1.0)   # FLOP/ns -> TFLOP/s = 1e-3 x; B/ns = GB/s
         short = {k: (re.search(r"::(\w+_kernel(?:<[^>]*>)?)\(", k) or [None, k])[1] for k in stats}
         lines = [f"# {title}", "",
@@ -295,9 +313,12 @@ def summarize_profiles(root: str, names, copy_mib: int = 1024) -> None:
                          f"{float(r['MaxNs']):.0f} |")
         lines += ["", f"Algorithmic work per call: {work:.6g} {'FLOP' if unit == 'TFLOP/s' else 'bytes'} "
                       f"(bench.py `{'.'.join(work_key)}`). Kernels of one call: "
-                      + ", ".join(f"`{short[k]}` {float(r['AverageNs']) / 1e3:.2f} us" for k, r in mine.items())
-                      + f", together {ns / 1e3:.2f} us -> **{rate:.1f} {unit}** at the rocprof averages "
-                        f"({100 * rate / peak:.1f}% of the {peak:g} {unit} peak).",
+                      + ", ".join(f"`{short[k]}` {timed[k] / 1e3:.2f} us" for k in mine)
+                      + f", together {ns / 1e3:.2f} us -> **{rate:.1f} {unit}** at the rocprof mean of the "
+                        f"timed dispatches (the last {n_timed} of each kernel; {100 * rate / peak:.1f}% of the "
+                        f"{peak:g} {unit} peak). The averages over all dispatches in the table above include the "
+                        f"warm-up launches, which run back to back without the cache flush while the clocks "
+                        f"settle.",
                   "", f"bench.py (HIP events on the launch stream, caches flushed before each launch): unprofiled "
                       f"run {_bench_rate(plain, name)}; in the traced run {_bench_rate(prof, name)}.",
                   "", "## HBM traffic per call (FETCH_SIZE / WRITE_SIZE, calibrated)", "",
