@@ -86,8 +86,11 @@ __device__ __forceinline__ float softmax_tile(const FwdParams& p, f32x16_t (&s)[
 // Key tiles start at multiples of 16, and one direct-to-LDS load covers at most 16 rows,
 // so each load reads inside a single page: its base is the page (a wave-uniform address)
 // and each lane adds its token slot. The page ids of a tile are read one tile ahead.
+//
+// Head dim 256 runs two workgroups per CU: 256 registers, with a few values of the item
+// set-up spilled (one workgroup per CU measured 9% slower).
 template <int D, int NW, int BN, bool BF16, bool PAGED = false>
-__global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (D == 96 ? 3 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
   constexpr int DP = lds_row(D);  // LDS row width
   constexpr int TILE = BN * DP;   // elements per K or V tile in LDS
@@ -172,50 +175,64 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
     }
 
     // Per-lane constant offsets (elements). Direct-to-LDS loads: load n of this wave fills
-    // LDS block i = wave + n * NW (rows i*ROWS_PER_LOAD ...) of a tile.
-    int ld_row[LPW], ld_k[LPW], ld_v[LPW];
+    // LDS block i = wave + n * NW (rows i*ROWS_PER_LOAD ...) of a tile. Both swizzles repeat
+    // every 16 rows, so loads n and n + LP (LP * RSTEP a multiple of 16 rows) differ by whole
+    // rows: LP offsets per lane serve every load, the rest is a scalar row step.
+    constexpr int RSTEP = NW * ROWS_PER_LOAD;
+    static_assert(RSTEP % 16 == 0 || 16 % RSTEP == 0, "swizzle period");
+    constexpr int LP = RSTEP >= 16 ? 1 : (16 / RSTEP < LPW ? 16 / RSTEP : LPW);
+    int ld_row0[LP], ld_k[LP], ld_v[LP];
 #pragma unroll
-    for (int n = 0; n < LPW; ++n) {
+    for (int n = 0; n < LP; ++n) {
       const int i = wave + n * NW;
       const int row = i * ROWS_PER_LOAD + lane / CPRP;
       const int slot = lane % CPRP;
-      ld_row[n] = row;
+      ld_row0[n] = row;
       ld_k[n] = row * ks2 + src_k(row, slot) * 8;
       ld_v[n] = row * vs2 + src_v(row, slot) * 8;
     }
-    // K reads: chunk 2*ks + hi of row kb*32 + l32 (the swizzle does not depend on kb)
-    int rd_k[NKS];
+    auto ld_row = [&](int n) __attribute__((always_inline)) { return ld_row0[n % LP] + (n / LP) * (LP * RSTEP); };
+    // K reads: chunk 2*ks + hi of row kb*32 + l32 (the swizzle does not depend on kb). In
+    // 256-element rows the swizzle (an XOR of the chunk with row & 15) leaves the chunk's
+    // bit 4 alone, so fragment ks + 8 lies 128 elements after fragment ks: 8 offsets serve.
+    constexpr int NKR = DP >= 256 ? 8 : NKS;
+    int rd_k[NKR];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = l32 * DP + SW::k(l32, 2 * ks + hi) * 8;
-    // V transposing reads: rows t*16 + vrow (+8), head-dim block db
+    for (int ks = 0; ks < NKR; ++ks) rd_k[ks] = l32 * DP + SW::k(l32, 2 * ks + hi) * 8;
+    auto k_ofs = [&](int ks) __attribute__((always_inline)) { return rd_k[ks % NKR] + (ks / NKR) * 128; };
+    // V transposing reads: rows t*16 + vrow (+8), head-dim block db; likewise in 256-element
+    // rows block db + 4 lies 128 elements after block db
     const int grp = lane >> 4, gi = lane & 15;
     const int vrow = 4 * hi + (gi >> 2);
-    int rd_v[NDB];
+    constexpr int NVR = DP >= 256 ? 4 : NDB;
+    int rd_v[NVR];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NVR; ++db) {
       const int c = db * 4 + (grp & 1) * 2 + ((gi & 3) >> 1);
       rd_v[db] = vrow * DP + SW::v(vrow, c) * 8 + (gi & 1) * 4;
     }
+    auto v_ofs = [&](int db) __attribute__((always_inline)) { return rd_v[db % NVR] + (db / NVR) * 128; };
 
     // Direct-to-LDS loads of one K or V tile. In the tail tile, rows past the last key
     // re-read the last key (always in bounds); the mask gives them zero weight.
-    auto load_rows = [&](const uint16_t* gbase, int stride, const int (&off)[LPW], int kt,
+    auto load_rows = [&](const uint16_t* gbase, int stride, const int (&off)[LP], int kt,
                          uint16_t* dst) __attribute__((always_inline)) {
       const uint16_t* g = gbase + (int64_t)kt * stride;
       if (kt + BN <= Lk) {
 #pragma unroll
         for (int n = 0; n < LPW; ++n) {
           const int i = wave + n * NW;
-          if (LOADS % NW == 0 || i < LOADS) load_lds16(g, (uint32_t)off[n] * 2u, dst + i * 512);
+          if (LOADS % NW == 0 || i < LOADS)
+            load_lds16(g, (uint32_t)(off[n % LP] + (n / LP) * (LP * RSTEP) * stride) * 2u, dst + i * 512);
         }
       } else {
 #pragma unroll
         for (int n = 0; n < LPW; ++n) {
           const int i = wave + n * NW;
           if (LOADS % NW == 0 || i < LOADS) {
-            // rows past the last key re-read it
-            const int shift = min(ld_row[n], Lk - 1 - kt) - ld_row[n];
-            load_lds16(g, (uint32_t)(off[n] + shift * stride) * 2u, dst + i * 512);
+            // rows past the last key re-read it (off[n % LP] addresses row ld_row0[n % LP])
+            const int shift = min(ld_row(n), Lk - 1 - kt) - ld_row0[n % LP];
+            load_lds16(g, (uint32_t)(off[n % LP] + shift * stride) * 2u, dst + i * 512);
           }
         }
       }
@@ -232,8 +249,8 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
     int ld_col_k[LPW], ld_col_v[LPW];
 #pragma unroll
     for (int n = 0; n < LPW; ++n) {
-      ld_col_k[n] = src_k(ld_row[n], lane % CPRP) * 8;
-      ld_col_v[n] = src_v(ld_row[n], lane % CPRP) * 8;
+      ld_col_k[n] = src_k(ld_row(n), lane % CPRP) * 8;
+      ld_col_v[n] = src_v(ld_row(n), lane % CPRP) * 8;
     }
     auto page_ids = [&](int kt, int (&pg)[LPW]) __attribute__((always_inline)) {
 #pragma unroll
@@ -250,7 +267,7 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
         const int i = wave + n * NW;
         if (LOADS % NW == 0 || i < LOADS) {
           const int P = (kt + i * ROWS_PER_LOAD) >> 4;
-          const int slot = ld_row[n] & 15;
+          const int slot = ld_row(n) & 15;
           const int se = P < last_page ? slot : (P == last_page ? min(slot, last_slot) : last_slot);
           const int page = min(max(pg[n], 0), p.num_pages - 1);
           load_lds16(gbase + (int64_t)page * pstride, (uint32_t)(se * stride + col[n]) * 2u, dst + i * 512);
@@ -278,9 +295,9 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
     // products ahead fill (program order fixed by scheduling fences, so the fragments of a
     // whole tile are never held at once)
     auto scores = [&](const uint16_t* kl) __attribute__((always_inline)) {
-      constexpr int NS = NKB * NKS, RA = 4;
+      constexpr int NS = NKB * NKS, RA = D == 256 ? 2 : 4;
       auto frag = [&](int j) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4_t*>(kl + (j / NKS) * 32 * DP + rd_k[j % NKS]);
+        return *reinterpret_cast<const u32x4_t*>(kl + (j / NKS) * 32 * DP + k_ofs(j % NKS));
       };
       u32x4_t ring[RA + 1];
 #pragma unroll
@@ -351,8 +368,8 @@ __global__ __launch_bounds__(NW * 64, (D == 256 ? 1 : D == 96 ? 3 : 2)) void fwd
       constexpr int NV = NPS * NDB;
       auto vfrag = [&](int j) __attribute__((always_inline)) {
         const int t = j / NDB, db = j % NDB;
-        const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + rd_v[db]);
-        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + rd_v[db]);
+        const u32x2_t lo = lds_read_tr16(vl + t * 16 * DP + v_ofs(db));
+        const u32x2_t up = lds_read_tr16(vl + (t * 16 + 8) * DP + v_ofs(db));
         return u32x4_t{lo[0], lo[1], up[0], up[1]};
       };
       u32x4_t vr[3];
