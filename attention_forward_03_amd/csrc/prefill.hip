@@ -90,7 +90,7 @@ __device__ __forceinline__ float softmax_tile(const FwdParams& p, f32x16_t (&s)[
 // Head dim 256 runs two workgroups per CU: 256 registers, with a few values of the item
 // set-up spilled (one workgroup per CU measured 9% slower).
 template <int D, int NW, int BN, bool BF16, bool PAGED = false>
-__global__ __launch_bounds__(NW * 64, (D == 96 ? 3 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (NW == 8 && D == 96 ? 1 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
   constexpr int DP = lds_row(D);  // LDS row width
   constexpr int TILE = BN * DP;   // elements per K or V tile in LDS
@@ -1027,15 +1027,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f32_kernel(const FwdParams p) 
 #endif
 constexpr int kNW16 = ATTN_PREFILL_WAVES;  // waves per workgroup, 16-bit inputs
 constexpr int kBN16 = ATTN_PREFILL_KEYS;   // keys per tile, 16-bit inputs
-// head dims 96, 192 and 256: 4 waves of 32 rows. At 96 (32-key tiles) three workgroups
-// share a CU (three waves per SIMD); at 192 (32-key tiles) the kernel fits in 256
-// registers, so two do (two waves per SIMD: one wave's softmax runs beside another's
-// products); at 256 the 128 accumulator registers of the output block, the Q fragments and
-// the scores need more, so one wave per SIMD holds them; on 32-key tiles (64-key tiles, two
-// sub-tiles per barrier, measured 2-3% faster before the loads lost their per-load vector
-// work, 4% slower since).
-constexpr int nw16(int D) { return D >= 192 || D == 96 ? 4 : kNW16; }
-constexpr int bn16(int D) { return D >= 192 || D == 96 ? 32 : kBN16; }
+// head dims 192 and 256: 4 waves of 32 rows on 32-key tiles, two workgroups per CU (two
+// waves per SIMD: one wave's softmax runs beside another's products; at 256 with the read
+// and load offsets reduced to fit 256 registers). Head dim 96: the 8-wave, 64-key form of
+// the smaller head dims, one 256-row workgroup per CU at two waves per SIMD (with causal
+// pairing the 4-wave, 128-row form also ran two per CU, and streamed each K/V tile for half
+// the rows: 0.120 -> 0.112 ms).
+constexpr int nw16(int D) { return D >= 192 ? 4 : kNW16; }
+constexpr int bn16(int D) { return D >= 192 ? 32 : kBN16; }
 constexpr int kNW32 = 4;
 constexpr int kBN32 = 32;
 
