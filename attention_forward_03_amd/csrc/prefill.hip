@@ -88,8 +88,7 @@ __device__ __forceinline__ float softmax_tile(const FwdParams& p, f32x16_t (&s)[
 // and each lane adds its token slot. The page ids of a tile are read one tile ahead.
 //
 // Head dim 256 runs two workgroups per CU: 256 registers, with a few values of the item
-// set-up spilled (one workgroup per CU measured 9% slower). Head dim 96 runs one 8-wave
-// workgroup per CU (159 registers, two waves per SIMD).
+// set-up spilled (one workgroup per CU measured 9% slower).
 template <int D, int NW, int BN, bool BF16, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64, (NW == 8 && D == 96 ? 1 : 2)) void fwd_mfma16_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
