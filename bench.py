@@ -241,7 +241,11 @@ def _timed_dispatch_ns(d, n):
             for r in csv.DictReader(f):
                 runs.setdefault(r["Kernel_Name"], []).append(
                     (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    return {k: sum(dur for _, dur in sorted(v)[-n:]) / len(sorted(v)[-n:]) for k, v in runs.items()}
+    out = {}
+    for k, v in runs.items():
+        last = [dur for _, dur in sorted(v)[-n:]]
+        out[k] = sum(last) / len(last)
+    return out
 
 
 def _json_line(path):
